@@ -1,0 +1,147 @@
+"""Seeded synthetic operands for the blocked GEMM C = A.B.
+
+This module is shared by the CPU oracle's tests and by the GPU path's tests and
+benchmark.  It holds no GEMM arithmetic: it draws float64 values from a seeded
+generator, rounds them to 16-bit storage formats and lays them out in memory.
+
+Reading of the workload statement (the pages fix neither generator nor draw
+order, so this is the plainest fixed choice):
+  * generator: ``numpy.random.default_rng(seed)`` (PCG64);
+  * draw order: the logical A as shape (batch, M, K) first, then the logical B as
+    (batch, K, N), both in float64, row by row;
+  * "uniform[lo,hi]" is ``rng.uniform(lo, hi)``; "normal(0,1) scaled by s" is
+    ``rng.standard_normal() * s``;
+  * rounding: round-to-nearest, ties-to-even, straight from float64 to f16 or bf16
+    (no intermediate float32 step), subnormals kept;
+  * a column-major operand is the storage transpose of the drawn logical matrix,
+    so the layout never changes the values.
+
+Large operands are drawn in row chunks; numpy's Generator hands out the same
+stream for one large draw and for consecutive smaller draws, which the tests
+check, so chunking does not change any value.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+F16 = "f16"
+BF16 = "bf16"
+
+# (explicit mantissa bits, minimum normal exponent, exponent bias, +inf pattern)
+_FORMATS = {
+    F16: (10, -14, 15, 0x7C00, 0x7E00),
+    BF16: (7, -126, 127, 0x7F80, 0x7FC0),
+}
+
+
+def round_f64_to_bits(x, fmt: str) -> np.ndarray:
+    """Round float64 values to the nearest ``fmt`` value (ties to even).
+
+    Returns the 16-bit patterns as uint16.  Works on the IEEE-754 bit pattern of
+    the double: the 53-bit significand is shifted right by the number of bits the
+    target format cannot hold at that exponent (more for values below the target's
+    smallest normal), the dropped bits decide the rounding, and a carry out of the
+    kept bits moves the value into the next binade by plain integer addition.
+    """
+    man, emin, bias, inf_bits, nan_bits = _FORMATS[fmt]
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    b = x.view(np.uint64)
+    sign = (b >> np.uint64(63)).astype(np.uint16)
+    efield = ((b >> np.uint64(52)) & np.uint64(0x7FF)).astype(np.int64)
+    frac = b & np.uint64((1 << 52) - 1)
+    special = efield == 0x7FF
+    tiny = efield == 0  # zero or a float64 subnormal: far below half the target's least subnormal
+    e = efield - 1023
+    sig = np.where(tiny, np.uint64(0), frac | np.uint64(1 << 52))
+    drop = (52 - man) + np.maximum(0, emin - e)
+    drop = np.minimum(drop, 62).astype(np.uint64)
+    kept = sig >> drop
+    rem = sig & ((np.uint64(1) << drop) - np.uint64(1))
+    half = np.uint64(1) << (drop - np.uint64(1))
+    up = (rem > half) | ((rem == half) & ((kept & np.uint64(1)) == np.uint64(1)))
+    kept = kept + up.astype(np.uint64)
+    normal = e >= emin
+    ebits = np.where(normal, e + bias - 1, 0).astype(np.int64)
+    mag = np.where(normal, (ebits.astype(np.uint64) << np.uint64(man)) + kept, kept)
+    mag = np.minimum(mag, np.uint64(inf_bits))
+    mag = np.where(special, np.where(frac == 0, np.uint64(inf_bits), np.uint64(nan_bits)), mag)
+    return (mag.astype(np.uint16) | (sign << np.uint16(15))).astype(np.uint16)
+
+
+def bits_to_f64(bits, fmt: str) -> np.ndarray:
+    """Exact float64 values of 16-bit patterns, via numpy's own float types.
+
+    f16 goes through ``numpy.float16``; bf16 is the upper half of a float32, so
+    the pattern shifted left by 16 is reinterpreted as ``numpy.float32``.
+    """
+    bits = np.asarray(bits, dtype=np.uint16)
+    if fmt == F16:
+        return bits.view(np.float16).astype(np.float64)
+    if fmt == BF16:
+        return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    raise ValueError(fmt)
+
+
+def _draw(rng: np.random.Generator, dist: tuple, n: int) -> np.ndarray:
+    kind = dist[0]
+    if kind == "uniform":
+        return rng.uniform(dist[1], dist[2], n)
+    if kind == "normal":
+        return rng.standard_normal(n) * dist[1]
+    raise ValueError(f"unknown distribution {dist!r}")
+
+
+def draw_matrix_bits(rng, dist, rows: int, cols: int, fmt: str, chunk_rows: int | None = None):
+    """Draw a logical rows x cols matrix row by row and round it to ``fmt``."""
+    out = np.empty((rows, cols), dtype=np.uint16)
+    if rows == 0 or cols == 0:
+        return out
+    step = chunk_rows or max(1, (1 << 24) // cols)
+    for r0 in range(0, rows, step):
+        r1 = min(rows, r0 + step)
+        out[r0:r1] = round_f64_to_bits(_draw(rng, dist, (r1 - r0) * cols), fmt).reshape(r1 - r0, cols)
+    return out
+
+
+def make_operands(seed: int, batch: int, M: int, N: int, K: int, fmt: str, dist: tuple,
+                  a_layout: str = "row", b_layout: str = "row", chunk_rows: int | None = None):
+    """Seeded operands for a (batched) GEMM.
+
+    Returns ``(A, B)`` as contiguous uint16 arrays in storage order:
+      A: (batch, M, K) if ``a_layout == "row"``, else (batch, K, M);
+      B: (batch, K, N) if ``b_layout == "row"``, else (batch, N, K).
+    The logical A of every problem is drawn before any B (draw order above).
+    """
+    rng = np.random.default_rng(seed)
+    A = np.empty((batch, M, K), dtype=np.uint16)
+    for z in range(batch):
+        A[z] = draw_matrix_bits(rng, dist, M, K, fmt, chunk_rows)
+    B = np.empty((batch, K, N), dtype=np.uint16)
+    for z in range(batch):
+        B[z] = draw_matrix_bits(rng, dist, K, N, fmt, chunk_rows)
+    if a_layout == "col":
+        A = np.ascontiguousarray(A.transpose(0, 2, 1))
+    if b_layout == "col":
+        B = np.ascontiguousarray(B.transpose(0, 2, 1))
+    return A, B
+
+
+def integer_operands(seed: int, batch: int, M: int, N: int, K: int, fmt: str, lo: int = -2, hi: int = 2,
+                     a_layout: str = "row", b_layout: str = "row"):
+    """Operands with integer entries in [lo, hi] (exact in f16 and bf16).
+
+    With |entries| <= 2 every partial sum of a product is an integer of magnitude
+    at most 4K, exact in float32 for K < 2**22, so any accumulation order gives
+    the same float32 result.
+    """
+    rng = np.random.default_rng(seed)
+    a = rng.integers(lo, hi + 1, size=(batch, M, K)).astype(np.float64)
+    b = rng.integers(lo, hi + 1, size=(batch, K, N)).astype(np.float64)
+    A = round_f64_to_bits(a, fmt).reshape(a.shape)
+    B = round_f64_to_bits(b, fmt).reshape(b.shape)
+    if a_layout == "col":
+        A = np.ascontiguousarray(A.transpose(0, 2, 1))
+    if b_layout == "col":
+        B = np.ascontiguousarray(B.transpose(0, 2, 1))
+    return A, B
