@@ -1,0 +1,135 @@
+/*
+ * tsm_gemm.h -- C ABI of the MI355X (gfx950) blocked GEMM library.
+ *
+ * The operation is the blocked matrix product C = A.B with 16-bit floating-point
+ * operands (f16 or bf16), float32 accumulation and a float32 or f16 result.  It
+ * is the computation of the 64x128x128 f16 example on "The PTSS Cliff: A Kernel
+ * That Won't Build" (sections "The Arithmetic of 'Fully Unrolled K'" and "The
+ * Idea: Stage in SLM, Tile K"): every output cell is sum_k A[i][k] * B[k][j],
+ * computed by workgroups that each own an output tile and walk K in bounded
+ * slices staged through on-chip shared memory (LDS on gfx950).  The masked
+ * K-blocked loop with a float32 accumulator and zero padding outside the matrix
+ * is the one of the Intel XPU Triton README, section "Use Tensor Descriptors to
+ * load tl.dot arguments and save results".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Sizes, leading dimensions and batch strides are counted in ELEMENTS, and
+ *    are 64-bit ("A Dumb Triton Runtime Error", Step 1: strides in elements;
+ *    Intel XPU Triton README, "Avoid int32 Overflow": offsets are formed in
+ *    64 bits).
+ *  - A is logically M x K, B is K x N, C is M x N.
+ *      row-major A: A[i*lda + k], lda >= K      column-major A: A[k*lda + i], lda >= M
+ *      row-major B: B[k*ldb + j], ldb >= N      column-major B: B[j*ldb + k], ldb >= K
+ *      C is always row-major:  C[i*ldc + j], ldc >= N
+ *  - C is OVERWRITTEN with A.B (no accumulate, no atomics): "A Dumb Triton
+ *    Runtime Error", section "Making It Compile, and Why I'd Still Use the
+ *    Original", shows read-modify-write into an output that was not zeroed
+ *    giving wrong rows.  Elements of C outside the M x N region (the ld padding)
+ *    are never written.  K = 0 with M, N > 0 writes zeros (the empty sum).
+ *  - Operand elements outside M, N or K never contribute: tiles are loaded
+ *    with zero padding ("A Dumb Triton Runtime Error", Step 2, on masking with
+ *    the additive identity).
+ *  - Pointers are device pointers owned by the caller (e.g. torch tensors).  The
+ *    library allocates nothing, keeps no mutable global state and never
+ *    synchronises: it enqueues kernels on `stream` (a hipStream_t; NULL = the
+ *    null stream) and returns.  Results are valid once the stream reaches them.
+ *  - Any 2-byte-aligned operand base and any leading dimension is accepted;
+ *    the vector width of the loads is chosen inside the library.  C must be
+ *    4-byte aligned for float32 output and 2-byte aligned for f16 output.
+ *  - Errors: every argument check runs on the host before any HIP call; on an
+ *    error nothing is enqueued and a status code is returned.  No C++ exception
+ *    crosses this boundary.  tsm_last_error_detail() names the failed check.
+ *
+ * Status codes and enums are plain ints so that any FFI can call in.
+ */
+#ifndef TSM_GEMM_H
+#define TSM_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define TSM_SUCCESS 0
+#define TSM_ERROR_INVALID_VALUE 1 /* an argument breaks the contract above      */
+#define TSM_ERROR_NOT_SUPPORTED 2 /* valid, but beyond this library's limits     */
+#define TSM_ERROR_LAUNCH 3        /* the HIP runtime refused or failed a launch */
+
+/* dtype: operand format and output format.  Accumulation is always float32. */
+#define TSM_F16_F32 0
+#define TSM_F16_F16 1
+#define TSM_BF16_F32 2
+#define TSM_BF16_F16 3
+
+/* Storage layout of an operand. */
+#define TSM_ROW 0
+#define TSM_COL 1
+
+/*
+ * gemm -- C := A.B for row-major A (M x K) and row-major B (K x N).
+ *   M, N, K   : sizes, >= 0.
+ *   A, lda    : operand A and its leading dimension (>= max(1, K)).
+ *   B, ldb    : operand B and its leading dimension (>= max(1, N)).
+ *   C, ldc    : result, leading dimension >= max(1, N).
+ *   dtype     : one of TSM_F16_F32, TSM_F16_F16, TSM_BF16_F32, TSM_BF16_F16.
+ *   stream    : hipStream_t to enqueue on (NULL = null stream).
+ * Returns a status code.  M = 0 or N = 0 succeeds without launching.
+ * Errors (TSM_ERROR_INVALID_VALUE): negative size; NULL pointer with work to do;
+ * leading dimension below the row length; unknown dtype; misaligned pointer;
+ * C overlapping A or B.  TSM_ERROR_NOT_SUPPORTED: sizes whose tile grid or
+ * element offsets exceed the launch limits (reported, never truncated).
+ */
+int gemm(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb, void *C,
+         int64_t ldc, int dtype, void *stream);
+
+/*
+ * gemm_ex -- gemm with an explicit storage layout per operand
+ * (layout_a, layout_b in {TSM_ROW, TSM_COL}); gemm is gemm_ex(TSM_ROW, TSM_ROW).
+ * A column-major B (element (k, j) at B[j*ldb + k], ldb >= K) makes both operands
+ * contiguous along K, the layout the square bf16 product uses.
+ */
+int gemm_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a, const void *B,
+            int64_t ldb, int layout_b, void *C, int64_t ldc, int dtype, void *stream);
+
+/*
+ * gemm_strided_batched -- batch independent products, problem z using
+ *   A + z*strideA, B + z*strideB, C + z*strideC   (strides in elements, 64-bit).
+ * strideA or strideB may be 0 (the operand is shared by every problem).
+ * strideC must keep the outputs disjoint: strideC >= (M-1)*ldc + N when batch > 1.
+ * batch = 0 succeeds without launching.  Other rules as for gemm.
+ */
+int gemm_strided_batched(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int64_t strideA,
+                         const void *B, int64_t ldb, int64_t strideB, void *C, int64_t ldc, int64_t strideC,
+                         int64_t batch, int dtype, void *stream);
+
+/* gemm_strided_batched_ex -- gemm_strided_batched with per-operand layouts. */
+int gemm_strided_batched_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a,
+                            int64_t strideA, const void *B, int64_t ldb, int layout_b, int64_t strideB, void *C,
+                            int64_t ldc, int64_t strideC, int64_t batch, int dtype, void *stream);
+
+/* Static text for a status code ("success", "invalid value", ...). */
+const char *tsm_status_string(int status);
+
+/* Text naming the check that made the calling thread's last call fail
+ * (thread-local; empty after a successful call). */
+const char *tsm_last_error_detail(void);
+
+/*
+ * tsm_gemm_kernel_name -- name of the kernel variant a gemm_strided_batched_ex
+ * call with these arguments would launch (same arguments, no stream), or NULL
+ * if the call would be rejected or launch nothing.  Pure host logic: it
+ * validates and selects, it never touches the GPU.  The returned string is
+ * static.
+ */
+const char *tsm_gemm_kernel_name(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a,
+                                 int64_t strideA, const void *B, int64_t ldb, int layout_b, int64_t strideB,
+                                 void *C, int64_t ldc, int64_t strideC, int64_t batch, int dtype);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSM_GEMM_H */

@@ -1,0 +1,140 @@
+"""C-ABI library: loads, exports every declared symbol, and validates arguments on the host.
+
+CPU only: every call here is rejected by the host-side checks (or has nothing
+to compute) before the library makes any HIP call, so no GPU is needed.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import tiled_shared_memory_amd as tsm
+from tiled_shared_memory_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h")]
+
+# fake, suitably aligned device addresses: never dereferenced by these calls
+A0, B0, C0 = 0x7F0000000000, 0x7F1000000000, 0x7F2000000000
+
+
+def declared_functions():
+    names = []
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w \t\*]*?\b([A-Za-z_]\w*)\s*\(", text, flags=re.M):
+            if not m.group(0).lstrip().startswith("#"):
+                names.append(m.group(1))
+    return names
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("gemm", "gemm_ex", "gemm_strided_batched", "gemm_strided_batched_ex", "tsm_status_string",
+              "tsm_last_error_detail", "tsm_gemm_kernel_name"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIBRARY)
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+    assert set(declared_functions()) == set(_lib.SIGNATURES), "binding and header disagree"
+
+
+def test_header_compiles_as_c():
+    import subprocess
+    import tempfile
+
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "t.c")
+        open(src, "w").write('#include "tsm_gemm.h"\nint main(void){return TSM_SUCCESS;}\n')
+        subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), src, "-o",
+                        os.path.join(d, "t")], check=True)
+
+
+def _call(**kw):
+    args = dict(M=64, N=128, K=128, A=A0, lda=128, la=0, sA=0, B=B0, ldb=128, lb=0, sB=0, C=C0, ldc=128, sC=0,
+                batch=1, dtype=0)
+    args.update(kw)
+    return tsm.gemm_strided_batched_ex(args["M"], args["N"], args["K"], args["A"], args["lda"], args["la"],
+                                       args["sA"], args["B"], args["ldb"], args["lb"], args["sB"], args["C"],
+                                       args["ldc"], args["sC"], args["batch"], args["dtype"], 0)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(M=-1), 1, "negative size"),
+    (dict(K=-5), 1, "negative size"),
+    (dict(batch=-1), 1, "negative batch"),
+    (dict(dtype=4), 1, "dtype"),
+    (dict(dtype=-1), 1, "dtype"),
+    (dict(la=2), 1, "layout_a"),
+    (dict(lb=7), 1, "layout_b"),
+    (dict(C=0), 1, "C is NULL"),
+    (dict(A=0), 1, "A is NULL"),
+    (dict(B=0), 1, "B is NULL"),
+    (dict(lda=127), 1, "lda"),
+    (dict(la=1, lda=63), 1, "lda"),
+    (dict(ldb=127), 1, "ldb"),
+    (dict(lb=1, ldb=127), 1, "ldb"),
+    (dict(ldc=127), 1, "ldc"),
+    (dict(A=A0 + 1), 1, "aligned"),
+    (dict(B=B0 + 3), 1, "aligned"),
+    (dict(C=C0 + 2), 1, "aligned"),           # float32 C needs 4-byte alignment
+    (dict(C=A0 + 4096), 1, "C overlaps A"),
+    (dict(C=B0), 1, "C overlaps B"),
+    (dict(batch=2, sC=64 * 128 - 1), 1, "strideC"),
+    (dict(batch=2, sA=-1), 1, "stride"),
+    (dict(M=1 << 31, lda=128), 2, "2^31"),
+    (dict(batch=1 << 40, sA=1 << 40, sB=1 << 40, sC=1 << 40), 2, "overflows"),
+])
+def test_invalid_arguments_are_rejected(kw, status, needle):
+    with pytest.raises(tsm.TsmError) as ei:
+        _call(**kw)
+    assert ei.value.status == status
+    assert needle in ei.value.detail
+
+
+def test_f16_output_needs_only_2_byte_alignment():
+    # dtype 1 = f16 -> f16 output: C + 2 is fine; C + 1 is not
+    assert tsm.tsm_gemm_kernel_name(4, 4, 4, A0, 4, 0, 0, B0, 4, 0, 0, C0 + 2, 4, 0, 1, 1) is not None
+    assert tsm.tsm_gemm_kernel_name(4, 4, 4, A0, 4, 0, 0, B0, 4, 0, 0, C0 + 1, 4, 0, 1, 1) is None
+
+
+@pytest.mark.parametrize("kw", [dict(M=0), dict(N=0), dict(batch=0), dict(M=0, A=0, B=0, C=0)])
+def test_empty_problems_succeed_without_launch(kw):
+    assert _call(**kw) == 0
+    assert tsm.tsm_last_error_detail() == ""
+
+
+def test_k_zero_needs_no_operands():
+    # K = 0 writes zeros into C; A and B are never read, so NULL is accepted
+    name = tsm.tsm_gemm_kernel_name(8, 8, 0, 0, 1, 0, 0, 0, 8, 0, 0, C0, 8, 0, 1, 0)
+    assert name is not None
+
+
+def test_status_strings():
+    assert tsm.tsm_status_string(0) == "success"
+    assert tsm.tsm_status_string(1) == "invalid value"
+    assert tsm.tsm_status_string(2) == "not supported"
+    assert tsm.tsm_status_string(3) == "launch failure"
+    assert tsm.tsm_status_string(99) == "unknown status"
+
+
+def test_kernel_selection_for_the_workloads():
+    from workloads import WORKLOADS
+
+    picks = {}
+    for name, w in WORKLOADS.items():
+        lda, ldb, ldc = w.lds()
+        sA, sB, sC = w.strides()
+        code = {("f16", "f32"): 0, ("f16", "f16"): 1, ("bf16", "f32"): 2, ("bf16", "f16"): 3}[(w.in_fmt, w.out_fmt)]
+        picks[name] = tsm.tsm_gemm_kernel_name(w.M, w.N, w.K, A0, lda, int(w.a_layout == "col"), sA,
+                                               0x7E0000000000, ldb, int(w.b_layout == "col"), sB, C0, ldc, sC,
+                                               w.batch, code)
+        assert picks[name] is not None, name
+    # the ragged workload has K = 777, so rows of A are only 2-byte aligned
+    assert picks["ragged_f16_1000x1500x777"].endswith("vec1")

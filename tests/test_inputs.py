@@ -83,11 +83,18 @@ def test_bf16_no_double_rounding():
     assert bits_to_f64(round_f64_to_bits(x, BF16), BF16)[0] == 1.0 + 2.0 ** -7
 
 
-def test_chunked_draw_is_single_draw():
+def test_values_do_not_depend_on_worker_count():
     for dist in (("uniform", -1.0, 1.0), ("normal", 0.5)):
-        a = draw_matrix_bits(np.random.default_rng(5), dist, 37, 29, F16, chunk_rows=4)
-        b = draw_matrix_bits(np.random.default_rng(5), dist, 37, 29, F16, chunk_rows=37)
+        a = draw_matrix_bits(5, 1, 2, dist, 200, 29, F16, workers=1)
+        b = draw_matrix_bits(5, 1, 2, dist, 200, 29, F16, workers=7)
         assert np.array_equal(a, b)
+
+
+def test_blocks_are_distinct_streams():
+    a = draw_matrix_bits(5, 0, 0, ("uniform", -1.0, 1.0), 128, 16, F16)
+    assert not np.array_equal(a[:64], a[64:])
+    b = draw_matrix_bits(5, 1, 0, ("uniform", -1.0, 1.0), 128, 16, F16)
+    assert not np.array_equal(a, b)
 
 
 def test_layout_is_storage_transpose():

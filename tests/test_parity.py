@@ -1,0 +1,200 @@
+"""GPU path vs the CPU oracle, element by element, through the C ABI (needs an MI355X).
+
+Acceptance per element (fp64): |C_gpu - C_ref| <= K * 2^-24 * sum_k |A_ik * B_kj|,
+plus half an f16 ulp of the stored value for f16 output.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import check, run, say
+from workloads import WORKLOADS
+from workloads.inputs import F16, BF16, integer_operands, make_operands
+
+pytestmark = pytest.mark.gpu
+
+SMALL = ["single_f16_64x128x128", "largek_f16_256x256x8192", "ragged_f16_1000x1500x777"]
+
+
+@pytest.fixture(scope="module")
+def big_inputs():
+    cache = {}
+
+    def get(name):
+        if name not in cache:
+            say(f"[inputs] generating {name}")
+            cache[name] = WORKLOADS[name].operands()
+        return cache[name]
+
+    return get
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_workload_full_parity(orc, name):
+    w = WORKLOADS[name]
+    A, B = w.operands()
+    say(f"[gpu] {name} full parity M={w.M} N={w.N} K={w.K}")
+    C = run(A, B, w.M, w.N, w.K, w.in_fmt, w.out_fmt, batch=w.batch, a_layout=w.a_layout, b_layout=w.b_layout)
+    Cr, S = orc.gemm_rows(A, B, w.M, w.N, w.K, w.in_fmt, batch=w.batch, a_layout=w.a_layout, b_layout=w.b_layout)
+    ratio = check(C, Cr, S, w.K, w.out_fmt, name)
+    say(f"[gpu] {name}: max err/bound = {ratio:.3e}")
+
+
+def _sample_cells(rng, batch, M, N, n):
+    z = rng.integers(0, batch, n)
+    i = rng.integers(0, M, n)
+    j = rng.integers(0, N, n)
+    # corners and tile edges of every problem
+    edge_i = np.array([0, M - 1, min(M - 1, 127), min(M - 1, 128), min(M - 1, 255), min(M - 1, 256)])
+    edge_j = np.array([0, N - 1, min(N - 1, 127), min(N - 1, 128), min(N - 1, 255), min(N - 1, 256)])
+    ez, ei, ej = np.meshgrid(np.arange(batch), edge_i, edge_j, indexing="ij")
+    return (np.concatenate([z, ez.ravel()]), np.concatenate([i, ei.ravel()]), np.concatenate([j, ej.ravel()]))
+
+
+@pytest.mark.parametrize("name", ["square_bf16_8192", "skinny_f16_16x16384x8192_b8"])
+def test_workload_sampled_parity(orc, big_inputs, name):
+    """Full-size workloads: sampled cells and whole rows from the oracle; every output finite."""
+    w = WORKLOADS[name]
+    A, B = big_inputs(name)
+    say(f"[gpu] {name} M={w.M} N={w.N} K={w.K} batch={w.batch}")
+    C = run(A, B, w.M, w.N, w.K, w.in_fmt, w.out_fmt, batch=w.batch, a_layout=w.a_layout, b_layout=w.b_layout)
+    assert np.all(np.isfinite(C))
+    rng = np.random.default_rng(77)
+    z, i, j = _sample_cells(rng, w.batch, w.M, w.N, 3000)
+    Cp, Sp = orc.gemm_points(A, B, w.M, w.N, w.K, w.in_fmt, z, i, j, strideA=A[0].size, strideB=B[0].size,
+                             a_layout=w.a_layout, b_layout=w.b_layout)
+    r1 = check(C[z, i, j], Cp, Sp, w.K, w.out_fmt, name + " cells")
+    # whole rows: the first, last and one in the middle of problem 0 and the last problem
+    rows = sorted({0, w.M // 2, w.M - 1})
+    for zz in sorted({0, w.batch - 1}):
+        for r in rows:
+            Cr, S = orc.gemm_rows(A[zz:zz + 1], B[zz:zz + 1], w.M, w.N, w.K, w.in_fmt, a_layout=w.a_layout,
+                                  b_layout=w.b_layout, row_begin=r, row_end=r + 1)
+            check(C[zz:zz + 1, r:r + 1], Cr, S, w.K, w.out_fmt, f"{name} row {r} of problem {zz}")
+    say(f"[gpu] {name}: max err/bound on sampled cells = {r1:.3e}")
+
+
+EDGE_SHAPES = [(1, 1, 1), (1, 2, 3), (2, 3, 1), (3, 1, 2), (15, 17, 16), (16, 16, 16), (17, 15, 31),
+               (31, 33, 3), (33, 31, 6), (127, 129, 33), (128, 128, 32), (129, 127, 65), (130, 257, 100),
+               (255, 1, 64), (1, 300, 257), (64, 128, 128), (200, 8, 8), (8, 200, 1000)]
+
+
+@pytest.mark.parametrize("shape", EDGE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("in_fmt,out_fmt", [(F16, "f32"), (BF16, "f16"), (F16, "f16"), (BF16, "f32")])
+def test_edge_shapes(orc, shape, in_fmt, out_fmt):
+    M, N, K = shape
+    for a_layout in ("row", "col"):
+        for b_layout in ("row", "col"):
+            A, B = make_operands(M * 7 + N * 3 + K, 1, M, N, K, in_fmt, ("uniform", -1.0, 1.0), a_layout, b_layout)
+            say(f"[gpu] edge {M}x{N}x{K} {in_fmt}->{out_fmt} A:{a_layout} B:{b_layout}")
+            C = run(A, B, M, N, K, in_fmt, out_fmt, a_layout=a_layout, b_layout=b_layout)
+            Cr, S = orc.gemm_rows(A, B, M, N, K, in_fmt, a_layout=a_layout, b_layout=b_layout)
+            check(C, Cr, S, K, out_fmt, f"{shape} {a_layout}/{b_layout}")
+
+
+@pytest.mark.parametrize("a_off,b_off", [(0, 0), (1, 0), (0, 1), (3, 5)])
+def test_padded_and_unaligned_operands(orc, a_off, b_off):
+    """Padded leading dimensions and operands starting at odd element offsets (2-byte alignment only)."""
+    M, N, K = 100, 136, 72
+    lda, ldb, ldc = K + 9, N + 8, N + 5
+    A, B = make_operands(5, 1, M, N, K, F16, ("uniform", -1.0, 1.0))
+    Ap = np.zeros((1, M, lda), np.uint16)
+    Ap[:, :, :K] = A
+    Bp = np.zeros((1, K, ldb), np.uint16)
+    Bp[:, :, :N] = B
+    say(f"[gpu] padded lda={lda} ldb={ldb} ldc={ldc} offsets {a_off},{b_off}")
+    C = run(Ap, Bp, M, N, K, F16, "f32", lda=lda, ldb=ldb, ldc=ldc, a_off=a_off, b_off=b_off)
+    Cr, S = orc.gemm_rows(A, B, M, N, K, F16)
+    check(C, Cr, S, K, "f32", "padded")
+
+
+def test_ldc_padding_untouched_and_inside_overwritten():
+    """Prefill C with a sentinel: every logical cell is overwritten, the ld padding keeps its bits."""
+    import torch
+
+    M, N, K, ldc = 70, 90, 40, 97
+    A, B = integer_operands(9, 1, M, N, K, F16)
+    for fill in (100.0, float("nan")):
+        say(f"[gpu] sentinel fill {fill}")
+        C, raw = run(A, B, M, N, K, F16, "f32", ldc=ldc, fill=fill, keep=True)
+        host = raw.cpu().numpy()
+        ai = np.asarray(A[0].view(np.float16), np.float64)
+        bi = np.asarray(B[0].view(np.float16), np.float64)
+        want = ai @ bi
+        assert np.array_equal(C[0], want)
+        for i in range(M):
+            pad = host[i * ldc + N:(i + 1) * ldc] if i < M - 1 else host[i * ldc + N:i * ldc + N]
+            if np.isnan(fill):
+                assert np.all(np.isnan(pad))
+            else:
+                assert np.all(pad == fill)
+        tail = host[(M - 1) * ldc + N:]
+        assert np.all(np.isnan(tail)) if np.isnan(fill) else np.all(tail == fill)
+        torch.cuda.synchronize()
+
+
+def test_k_zero_writes_zeros():
+    M, N = 33, 65
+    A = np.zeros((1, M, 0), np.uint16)
+    B = np.zeros((1, 0, N), np.uint16)
+    say("[gpu] K=0")
+    C = run(A, B, M, N, 0, F16, "f32", lda=1, ldb=N, fill=float("nan"))
+    assert np.all(C == 0.0)
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_integer_inputs_bit_exact(orc, name):
+    """Entries in {-1, 0, 1}: every float32 partial sum is exact, so the GPU matches the oracle bit for bit
+    (f16 output: exact while |C| <= 2048, else within half an ulp)."""
+    w = WORKLOADS[name]
+    batch = min(w.batch, 2)
+    A, B = integer_operands(31, batch, w.M, w.N, w.K, w.in_fmt, -1, 1, w.a_layout, w.b_layout)
+    say(f"[gpu] integer {name}")
+    C = run(A, B, w.M, w.N, w.K, w.in_fmt, w.out_fmt, batch=batch, a_layout=w.a_layout, b_layout=w.b_layout)
+    rng = np.random.default_rng(5)
+    z, i, j = _sample_cells(rng, batch, w.M, w.N, 4000)
+    Cp, _ = orc.gemm_points(A, B, w.M, w.N, w.K, w.in_fmt, z, i, j, strideA=A[0].size, strideB=B[0].size,
+                            a_layout=w.a_layout, b_layout=w.b_layout)
+    got = C[z, i, j]
+    if w.out_fmt == "f32":
+        assert np.array_equal(got, Cp)
+    else:
+        small = np.abs(Cp) <= 2048
+        assert np.array_equal(got[small], Cp[small])
+        assert np.all(np.abs(got - Cp) <= oracle.half_ulp_f16(got))
+
+
+def test_batched_equals_single(orc):
+    """Problem z of a strided batch equals a single gemm on problem z, bit for bit."""
+    M, N, K, batch = 40, 72, 200, 5
+    A, B = make_operands(12, batch, M, N, K, BF16, ("uniform", -1.0, 1.0))
+    say("[gpu] batched vs single")
+    Cb = run(A, B, M, N, K, BF16, "f32", batch=batch)
+    for z in range(batch):
+        Cs = run(A[z:z + 1], B[z:z + 1], M, N, K, BF16, "f32")
+        assert np.array_equal(Cb[z], Cs[0])
+    Cr, S = orc.gemm_rows(A, B, M, N, K, BF16, batch=batch)
+    check(Cb, Cr, S, K, "f32", "batched")
+
+
+def test_broadcast_operand(orc):
+    """strideB = 0: every problem multiplies by the same B."""
+    M, N, K, batch = 20, 48, 64, 3
+    A, B = make_operands(13, batch, M, N, K, F16, ("uniform", -1.0, 1.0))
+    say("[gpu] broadcast B")
+    C = run(A, B[:1], M, N, K, F16, "f32", batch=batch, sB=0)
+    Cr, S = orc.gemm_rows(A, np.repeat(B[:1], batch, 0), M, N, K, F16, batch=batch)
+    check(C, Cr, S, K, "f32", "broadcast")
+
+
+def test_subnormal_f16_operands(orc):
+    """f16 subnormals are real inputs (uniform draws produce a few); they must not be flushed."""
+    M, N, K = 4, 4, 32
+    A = np.full((1, M, K), 0x0001, np.uint16)     # 2^-24
+    B = np.full((1, K, N), 0x3C00, np.uint16)     # 1.0
+    say("[gpu] f16 subnormal inputs")
+    C = run(A, B, M, N, K, F16, "f32")
+    Cr, S = orc.gemm_rows(A, B, M, N, K, F16)
+    assert np.all(Cr == K * 2.0 ** -24)
+    check(C, Cr, S, K, "f32", "subnormal")

@@ -1,0 +1,242 @@
+// Host side of the C ABI declared in include/tsm_gemm.h: argument checks,
+// kernel selection and launch on the caller's stream.
+//
+// Every check runs on the host before any HIP call, so a rejected call enqueues
+// nothing.  Offsets and extents are computed in 64 bits with explicit overflow
+// checks (Intel XPU Triton README, "Avoid int32 Overflow": a stride product that
+// wraps silently addresses the wrong memory).
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "gemm_internal.hpp"
+#include "tsm_gemm.h"
+
+namespace tsm {
+namespace {
+
+thread_local char g_detail[256];
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_detail, sizeof g_detail, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_mul_overflow(a, b, out); }
+bool add_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_add_overflow(a, b, out); }
+
+// Number of elements spanned by `batch` matrices of rows x cols with leading
+// dimension ld and batch stride s: (batch-1)*s + (rows-1)*ld + cols.
+bool extent(int64_t batch, int64_t s, int64_t rows, int64_t ld, int64_t cols, int64_t *out) {
+  int64_t a, b, c;
+  if (!mul_ok(batch - 1, s, &a) || !mul_ok(rows - 1, ld, &b)) return false;
+  if (!add_ok(a, b, &c) || !add_ok(c, cols, out)) return false;
+  return true;
+}
+
+bool ranges_overlap(const void *p, int64_t pbytes, const void *q, int64_t qbytes) {
+  const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+  return a < b + (uintptr_t)qbytes && b < a + (uintptr_t)pbytes;
+}
+
+enum class Kernel { None, Masked8, Masked1 };
+
+struct Plan {
+  Problem p;
+  Kernel kernel = Kernel::None;
+};
+
+// Can an operand be read with 16-byte vectors along its contiguous dimension?
+// Needs the base 16-byte aligned and the contiguous extent, the leading
+// dimension and the batch stride all multiples of 8 elements.
+bool vec8_ok(const void *X, int64_t contiguous_extent, int64_t ld, int64_t stride, int64_t batch) {
+  if (((uintptr_t)X & 15) != 0) return false;
+  if (contiguous_extent % 8 != 0 || ld % 8 != 0) return false;
+  if (batch > 1 && stride % 8 != 0) return false;
+  return true;
+}
+
+int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a, int64_t strideA, const void *B,
+         int64_t ldb, int layout_b, int64_t strideB, void *C, int64_t ldc, int64_t strideC, int64_t batch, int dtype,
+         Plan *out) {
+  g_detail[0] = '\0';
+  if (dtype < TSM_F16_F32 || dtype > TSM_BF16_F16) return fail(TSM_ERROR_INVALID_VALUE, "unknown dtype %d", dtype);
+  if (layout_a != TSM_ROW && layout_a != TSM_COL)
+    return fail(TSM_ERROR_INVALID_VALUE, "unknown layout_a %d", layout_a);
+  if (layout_b != TSM_ROW && layout_b != TSM_COL)
+    return fail(TSM_ERROR_INVALID_VALUE, "unknown layout_b %d", layout_b);
+  if (M < 0 || N < 0 || K < 0) return fail(TSM_ERROR_INVALID_VALUE, "negative size M=%lld N=%lld K=%lld",
+                                           (long long)M, (long long)N, (long long)K);
+  if (batch < 0) return fail(TSM_ERROR_INVALID_VALUE, "negative batch %lld", (long long)batch);
+
+  Problem &p = out->p;
+  p = Problem{};
+  p.A = (const uint16_t *)A;
+  p.B = (const uint16_t *)B;
+  p.C = C;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.lda = lda;
+  p.ldb = ldb;
+  p.ldc = ldc;
+  p.sA = strideA;
+  p.sB = strideB;
+  p.sC = strideC;
+  p.batch = batch;
+  p.a_col = layout_a == TSM_COL;
+  p.b_col = layout_b == TSM_COL;
+  p.in_bf16 = dtype == TSM_BF16_F32 || dtype == TSM_BF16_F16;
+  p.out_f16 = dtype == TSM_F16_F16 || dtype == TSM_BF16_F16;
+  out->kernel = Kernel::None;
+
+  if (M == 0 || N == 0 || batch == 0) return TSM_SUCCESS;  // nothing to compute
+
+  // ---- launch limits (tile indices and in-kernel loop counts stay in 32 bits)
+  const int64_t kMaxDim = 0x7fffffffLL;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return fail(TSM_ERROR_NOT_SUPPORTED, "a dimension exceeds 2^31-1");
+
+  // ---- C
+  const int64_t csize = p.out_f16 ? 2 : 4;
+  if (!C) return fail(TSM_ERROR_INVALID_VALUE, "C is NULL");
+  if (((uintptr_t)C % (uintptr_t)csize) != 0)
+    return fail(TSM_ERROR_INVALID_VALUE, "C not %lld-byte aligned", (long long)csize);
+  if (ldc < (N > 1 ? N : 1)) return fail(TSM_ERROR_INVALID_VALUE, "ldc=%lld < N=%lld", (long long)ldc, (long long)N);
+  if (batch > 1) {
+    if (strideC < 0) return fail(TSM_ERROR_INVALID_VALUE, "negative strideC");
+    int64_t span;
+    if (!extent(1, 0, M, ldc, N, &span)) return fail(TSM_ERROR_NOT_SUPPORTED, "C extent overflows int64");
+    if (strideC < span)
+      return fail(TSM_ERROR_INVALID_VALUE, "strideC=%lld makes the outputs overlap (needs >= %lld)",
+                  (long long)strideC, (long long)span);
+  }
+  int64_t c_elems, c_bytes;
+  if (!extent(batch, strideC, M, ldc, N, &c_elems) || !mul_ok(c_elems, csize, &c_bytes))
+    return fail(TSM_ERROR_NOT_SUPPORTED, "C extent overflows int64");
+
+  // ---- A and B (only read when K > 0)
+  if (K > 0) {
+    if (!A) return fail(TSM_ERROR_INVALID_VALUE, "A is NULL");
+    if (!B) return fail(TSM_ERROR_INVALID_VALUE, "B is NULL");
+    if (((uintptr_t)A & 1) || ((uintptr_t)B & 1)) return fail(TSM_ERROR_INVALID_VALUE, "A or B not 2-byte aligned");
+    const int64_t a_rows = p.a_col ? K : M, a_cols = p.a_col ? M : K;
+    const int64_t b_rows = p.b_col ? N : K, b_cols = p.b_col ? K : N;
+    if (lda < a_cols)
+      return fail(TSM_ERROR_INVALID_VALUE, "lda=%lld < %lld", (long long)lda, (long long)a_cols);
+    if (ldb < b_cols)
+      return fail(TSM_ERROR_INVALID_VALUE, "ldb=%lld < %lld", (long long)ldb, (long long)b_cols);
+    if (batch > 1 && (strideA < 0 || strideB < 0))
+      return fail(TSM_ERROR_INVALID_VALUE, "negative strideA or strideB");
+    int64_t a_elems, b_elems, a_bytes, b_bytes;
+    if (!extent(batch, batch > 1 ? strideA : 0, a_rows, lda, a_cols, &a_elems) || !mul_ok(a_elems, 2, &a_bytes) ||
+        !extent(batch, batch > 1 ? strideB : 0, b_rows, ldb, b_cols, &b_elems) || !mul_ok(b_elems, 2, &b_bytes))
+      return fail(TSM_ERROR_NOT_SUPPORTED, "operand extent overflows int64");
+    if (ranges_overlap(C, c_bytes, A, a_bytes)) return fail(TSM_ERROR_INVALID_VALUE, "C overlaps A");
+    if (ranges_overlap(C, c_bytes, B, b_bytes)) return fail(TSM_ERROR_INVALID_VALUE, "C overlaps B");
+  }
+  if (batch == 1) {
+    p.sA = p.sB = p.sC = 0;
+  }
+
+  // ---- kernel selection
+  const int64_t tiles = ((M + MaskedInfo::BM - 1) / MaskedInfo::BM) * ((N + MaskedInfo::BN - 1) / MaskedInfo::BN);
+  if (tiles * MaskedInfo::THREADS > 0xffffffffLL)
+    return fail(TSM_ERROR_NOT_SUPPORTED, "tile grid too large (%lld tiles)", (long long)tiles);
+  const bool a8 = K == 0 || vec8_ok(A, p.a_col ? M : K, lda, p.sA, batch);
+  const bool b8 = K == 0 || vec8_ok(B, p.b_col ? K : N, ldb, p.sB, batch);
+  out->kernel = (a8 && b8) ? Kernel::Masked8 : Kernel::Masked1;
+  return TSM_SUCCESS;
+}
+
+const char *kernel_name(Kernel k) {
+  switch (k) {
+    case Kernel::Masked8:
+      return masked_name(8);
+    case Kernel::Masked1:
+      return masked_name(1);
+    default:
+      return nullptr;
+  }
+}
+
+int run(const Plan &pl, void *stream) {
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  switch (pl.kernel) {
+    case Kernel::None:
+      return TSM_SUCCESS;
+    case Kernel::Masked8:
+      e = launch_masked(pl.p, 8, s);
+      break;
+    case Kernel::Masked1:
+      e = launch_masked(pl.p, 1, s);
+      break;
+  }
+  if (e != hipSuccess) return fail(TSM_ERROR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return TSM_SUCCESS;
+}
+
+}  // namespace
+}  // namespace tsm
+
+extern "C" {
+
+int gemm_strided_batched_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a,
+                            int64_t strideA, const void *B, int64_t ldb, int layout_b, int64_t strideB, void *C,
+                            int64_t ldc, int64_t strideC, int64_t batch, int dtype, void *stream) {
+  tsm::Plan pl;
+  int st = tsm::plan(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, strideB, C, ldc, strideC, batch, dtype,
+                     &pl);
+  if (st != TSM_SUCCESS) return st;
+  return tsm::run(pl, stream);
+}
+
+int gemm_strided_batched(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int64_t strideA,
+                         const void *B, int64_t ldb, int64_t strideB, void *C, int64_t ldc, int64_t strideC,
+                         int64_t batch, int dtype, void *stream) {
+  return gemm_strided_batched_ex(M, N, K, A, lda, TSM_ROW, strideA, B, ldb, TSM_ROW, strideB, C, ldc, strideC, batch,
+                                 dtype, stream);
+}
+
+int gemm_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a, const void *B, int64_t ldb,
+            int layout_b, void *C, int64_t ldc, int dtype, void *stream) {
+  return gemm_strided_batched_ex(M, N, K, A, lda, layout_a, 0, B, ldb, layout_b, 0, C, ldc, 0, 1, dtype, stream);
+}
+
+int gemm(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb, void *C,
+         int64_t ldc, int dtype, void *stream) {
+  return gemm_strided_batched_ex(M, N, K, A, lda, TSM_ROW, 0, B, ldb, TSM_ROW, 0, C, ldc, 0, 1, dtype, stream);
+}
+
+const char *tsm_status_string(int status) {
+  switch (status) {
+    case TSM_SUCCESS:
+      return "success";
+    case TSM_ERROR_INVALID_VALUE:
+      return "invalid value";
+    case TSM_ERROR_NOT_SUPPORTED:
+      return "not supported";
+    case TSM_ERROR_LAUNCH:
+      return "launch failure";
+    default:
+      return "unknown status";
+  }
+}
+
+const char *tsm_last_error_detail(void) { return tsm::g_detail; }
+
+const char *tsm_gemm_kernel_name(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a,
+                                 int64_t strideA, const void *B, int64_t ldb, int layout_b, int64_t strideB, void *C,
+                                 int64_t ldc, int64_t strideC, int64_t batch, int dtype) {
+  tsm::Plan pl;
+  if (tsm::plan(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, strideB, C, ldc, strideC, batch, dtype, &pl) !=
+      TSM_SUCCESS)
+    return nullptr;
+  return tsm::kernel_name(pl.kernel);
+}
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// Internal interface between the host dispatch (gemm_api.hip) and the kernel
+// translation units.  Nothing here is part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tsm {
+
+// One (possibly batched) product, already validated by the host code.
+struct Problem {
+  const uint16_t *A;
+  const uint16_t *B;
+  void *C;
+  int64_t M, N, K;
+  int64_t lda, ldb, ldc;
+  int64_t sA, sB, sC;  // batch strides, elements
+  int64_t batch;
+  bool a_col;    // A stored column-major (M-contiguous) instead of row-major (K-contiguous)
+  bool b_col;    // B stored column-major (K-contiguous) instead of row-major (N-contiguous)
+  bool in_bf16;  // operands are bf16 (else f16)
+  bool out_f16;  // C is f16 (else float32)
+};
+
+// Kernel arguments, passed by value.  Offsets are 64-bit throughout.
+struct KernelArgs {
+  const uint16_t *A;
+  const uint16_t *B;
+  void *C;
+  int64_t M, N, K;
+  int64_t lda, ldb, ldc;
+  int64_t sA, sB, sC;
+  int32_t tiles_m, tiles_n;
+  int32_t z0;  // first problem index covered by this launch
+};
+
+// Largest grid.y a launch uses for the batch; bigger batches are split.
+constexpr int64_t kMaxGridY = 65535;
+
+// ---- kernel families -------------------------------------------------------
+// Masked, register-staged LDS kernel: any layout, any alignment, ragged edges.
+// vec = 8 needs 16-byte aligned rows along the contiguous dimension of both
+// operands; vec = 1 accepts anything 2-byte aligned.
+struct MaskedInfo {
+  static constexpr int BM = 128, BN = 128, BK = 32, THREADS = 256;
+};
+hipError_t launch_masked(const Problem &p, int vec, hipStream_t stream);
+const char *masked_name(int vec);
+
+}  // namespace tsm

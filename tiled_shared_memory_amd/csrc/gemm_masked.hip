@@ -1,0 +1,242 @@
+// Masked, register-staged LDS GEMM kernel for gfx950: the general path.
+//
+// It handles every layout, every alignment and ragged M, N and K.  Each
+// 256-thread workgroup owns a 128 x 128 tile of C and walks K in slices of
+// BK = 32 ("The PTSS Cliff", section "The Idea: Stage in SLM, Tile K": only one
+// K slice is live in registers, the float32 accumulator is carried across the
+// loop).  Unlike the page's pass, which stages whole operands once, the slices
+// are streamed: at large K a whole operand panel cannot fit LDS, so each slice
+// is fetched from global memory while the previous one feeds the matrix cores
+// (double-buffered LDS, one barrier per slice).
+//
+// Loads: each thread fetches `VEC` contiguous 16-bit elements of an operand
+// (VEC = 8: one 16-byte load; VEC = 1: single elements) along the operand's
+// contiguous dimension.  Elements outside M, N or K read as zero in both
+// operands: "A Dumb Triton Runtime Error", Step 2 on masked loads, where the
+// padding must be the additive identity (a -inf or garbage pad would poison the
+// sum); the masked K loop of the Intel XPU Triton README ("Use Tensor
+// Descriptors ...", the pointer-based loop) zero-fills the same way.
+//
+// LDS layout: both operand tiles are stored K-contiguous, [outer][BK + 8]
+// 16-bit elements (row pitch 80 bytes, so every 16-byte fragment read stays
+// aligned and consecutive rows start on different banks).  An operand that is
+// contiguous along M or N is transposed element by element on its way into LDS.
+//
+// Compute: 4 waves in a 2 x 2 grid, each owning 64 x 64 of the tile as 2 x 2
+// blocks of v_mfma_f32_32x32x16 (64 accumulator registers per lane, fixed by
+// the tile, never by K).
+//
+// Epilogue: masked stores of rows < M and columns < N, float32 or f16 (round to
+// nearest even); C's padding beyond N is never touched.
+#include "gemm_internal.hpp"
+#include "mfma.hpp"
+
+#include <type_traits>
+
+namespace tsm {
+namespace {
+
+constexpr int BM = MaskedInfo::BM;
+constexpr int BN = MaskedInfo::BN;
+constexpr int BK = MaskedInfo::BK;
+constexpr int THREADS = MaskedInfo::THREADS;
+constexpr int PITCH = BK + 8;  // LDS row pitch in 16-bit elements (80 bytes)
+
+// Staging registers for one operand tile (OUTER x BK elements).
+template <int VEC>
+struct Stage {
+  static constexpr int kLoads = (128 * BK) / (THREADS * VEC);  // loads per thread
+  using Vec = typename std::conditional<VEC == 8, u32x4, uint16_t>::type;
+  Vec v[kLoads];
+};
+
+// Fetch the OUTER x BK slice starting at (o0, k0) of an operand.
+//   KMAJ: element (o, k) at X[o*ld + k]   (K contiguous)
+//  !KMAJ: element (o, k) at X[k*ld + o]   (outer contiguous)
+template <bool KMAJ, int VEC>
+__device__ __forceinline__ void fetch(Stage<VEC> &st, const uint16_t *X, int64_t ld, int64_t outer_total,
+                                      int64_t K, int64_t o0, int64_t k0, int tid) {
+#pragma unroll
+  for (int r = 0; r < Stage<VEC>::kLoads; ++r) {
+    const int v = tid + r * THREADS;
+    int o, k;
+    if constexpr (KMAJ) {
+      constexpr int PER_ROW = BK / VEC;  // vectors per outer row
+      o = v / PER_ROW;
+      k = (v % PER_ROW) * VEC;
+    } else {
+      constexpr int PER_ROW = 128 / VEC;  // vectors per k row
+      k = v / PER_ROW;
+      o = (v % PER_ROW) * VEC;
+    }
+    const int64_t go = o0 + o, gk = k0 + k;
+    // With VEC = 8 the host guarantees the contiguous extent is a multiple of 8,
+    // so a vector is either wholly inside or wholly outside the matrix.
+    const bool ok = go < outer_total && gk < K;
+    const int64_t off = KMAJ ? go * ld + gk : gk * ld + go;
+    if constexpr (VEC == 8) {
+      st.v[r] = ok ? *reinterpret_cast<const u32x4 *>(X + off) : u32x4{0, 0, 0, 0};
+    } else {
+      st.v[r] = ok ? X[off] : (uint16_t)0;
+    }
+  }
+}
+
+// Write the staged slice into an LDS tile laid out [outer][PITCH], K contiguous.
+template <bool KMAJ, int VEC>
+__device__ __forceinline__ void commit(const Stage<VEC> &st, uint16_t *s, int tid) {
+#pragma unroll
+  for (int r = 0; r < Stage<VEC>::kLoads; ++r) {
+    const int v = tid + r * THREADS;
+    if constexpr (KMAJ) {
+      constexpr int PER_ROW = BK / VEC;
+      const int o = v / PER_ROW, k = (v % PER_ROW) * VEC;
+      if constexpr (VEC == 8)
+        *reinterpret_cast<u32x4 *>(s + o * PITCH + k) = st.v[r];
+      else
+        s[o * PITCH + k] = st.v[r];
+    } else {
+      constexpr int PER_ROW = 128 / VEC;
+      const int k = v / PER_ROW, o = (v % PER_ROW) * VEC;
+      if constexpr (VEC == 8) {
+        const u32x4 w = st.v[r];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[(o + e) * PITCH + k] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+      } else {
+        s[o * PITCH + k] = st.v[r];
+      }
+    }
+  }
+}
+
+template <bool BF16, bool OUT_F16, bool A_KMAJ, bool B_KMAJ, int VEC>
+__global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * PITCH];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const int tile = blockIdx.x;
+  const int64_t m0 = (int64_t)(tile / p.tiles_n) * BM;
+  const int64_t n0 = (int64_t)(tile % p.tiles_n) * BN;
+  const int64_t z = (int64_t)p.z0 + blockIdx.y;
+  const uint16_t *A = p.A + z * p.sA;
+  const uint16_t *B = p.B + z * p.sB;
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  const int64_t nk = (p.K + BK - 1) / BK;
+  Stage<VEC> ra, rb;
+  if (nk > 0) {
+    fetch<A_KMAJ, VEC>(ra, A, p.lda, p.M, p.K, m0, 0, tid);
+    fetch<B_KMAJ, VEC>(rb, B, p.ldb, p.N, p.K, n0, 0, tid);
+    commit<A_KMAJ, VEC>(ra, sA[0], tid);
+    commit<B_KMAJ, VEC>(rb, sB[0], tid);
+  }
+  __syncthreads();
+
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) {  // next slice in flight while this one is multiplied
+      fetch<A_KMAJ, VEC>(ra, A, p.lda, p.M, p.K, m0, (kt + 1) * BK, tid);
+      fetch<B_KMAJ, VEC>(rb, B, p.ldb, p.N, p.K, n0, (kt + 1) * BK, tid);
+    }
+    const uint16_t *a_s = sA[cur];
+    const uint16_t *b_s = sB[cur];
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int kk = ks * 16 + (lane >> 5) * 8;
+      u32x4 af[2], bf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        af[i] = *reinterpret_cast<const u32x4 *>(a_s + (wm * 64 + i * 32 + (lane & 31)) * PITCH + kk);
+        bf[i] = *reinterpret_cast<const u32x4 *>(b_s + (wn * 64 + i * 32 + (lane & 31)) * PITCH + kk);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_32x32x16<BF16>(af[i], bf[j], acc[i][j]);
+    }
+    if (more) {
+      commit<A_KMAJ, VEC>(ra, sA[cur ^ 1], tid);
+      commit<B_KMAJ, VEC>(rb, sB[cur ^ 1], tid);
+    }
+    __syncthreads();
+  }
+
+  void *C = OUT_F16 ? (void *)((uint16_t *)p.C + z * p.sC) : (void *)((float *)p.C + z * p.sC);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int64_t col = n0 + wn * 64 + j * 32 + (lane & 31);
+        store_masked<OUT_F16>(C, p.ldc, p.M, p.N, row, col, acc[i][j][r]);
+      }
+}
+
+template <bool BF16, bool OUT_F16, bool A_KMAJ, bool B_KMAJ, int VEC>
+hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
+  const int64_t tiles = (int64_t)base.tiles_m * base.tiles_n;
+  for (int64_t z0 = 0; z0 < batch; z0 += kMaxGridY) {
+    KernelArgs a = base;
+    a.z0 = (int32_t)z0;
+    const int64_t nz = batch - z0 < kMaxGridY ? batch - z0 : kMaxGridY;
+    hipLaunchKernelGGL((gemm_masked_kernel<BF16, OUT_F16, A_KMAJ, B_KMAJ, VEC>), dim3((unsigned)tiles, (unsigned)nz),
+                       dim3(THREADS), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <bool BF16, bool OUT_F16, int VEC>
+hipError_t dispatch_layout(const Problem &p, const KernelArgs &a, hipStream_t s) {
+  const bool a_kmaj = !p.a_col, b_kmaj = p.b_col;
+  if (a_kmaj && b_kmaj) return launch_t<BF16, OUT_F16, true, true, VEC>(a, p.batch, s);
+  if (a_kmaj && !b_kmaj) return launch_t<BF16, OUT_F16, true, false, VEC>(a, p.batch, s);
+  if (!a_kmaj && b_kmaj) return launch_t<BF16, OUT_F16, false, true, VEC>(a, p.batch, s);
+  return launch_t<BF16, OUT_F16, false, false, VEC>(a, p.batch, s);
+}
+
+template <int VEC>
+hipError_t dispatch_types(const Problem &p, const KernelArgs &a, hipStream_t s) {
+  if (p.in_bf16)
+    return p.out_f16 ? dispatch_layout<true, true, VEC>(p, a, s) : dispatch_layout<true, false, VEC>(p, a, s);
+  return p.out_f16 ? dispatch_layout<false, true, VEC>(p, a, s) : dispatch_layout<false, false, VEC>(p, a, s);
+}
+
+}  // namespace
+
+hipError_t launch_masked(const Problem &p, int vec, hipStream_t stream) {
+  KernelArgs a{};
+  a.A = p.A;
+  a.B = p.B;
+  a.C = p.C;
+  a.M = p.M;
+  a.N = p.N;
+  a.K = p.K;
+  a.lda = p.lda;
+  a.ldb = p.ldb;
+  a.ldc = p.ldc;
+  a.sA = p.sA;
+  a.sB = p.sB;
+  a.sC = p.sC;
+  a.tiles_m = (int32_t)((p.M + BM - 1) / BM);
+  a.tiles_n = (int32_t)((p.N + BN - 1) / BN);
+  return vec == 8 ? dispatch_types<8>(p, a, stream) : dispatch_types<1>(p, a, stream);
+}
+
+const char *masked_name(int vec) { return vec == 8 ? "masked_128x128x32_vec8" : "masked_128x128x32_vec1"; }
+
+}  // namespace tsm

@@ -53,9 +53,9 @@ class Workload:
     def strides(self):
         return self.M * self.K, self.K * self.N, self.M * self.N
 
-    def operands(self, chunk_rows=None):
+    def operands(self):
         return make_operands(self.seed, self.batch, self.M, self.N, self.K, self.in_fmt, self.dist,
-                             self.a_layout, self.b_layout, chunk_rows)
+                             self.a_layout, self.b_layout)
 
 
 WORKLOADS = {
