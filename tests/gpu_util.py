@@ -57,10 +57,11 @@ def c_view(c_dev, batch, M, N, ldc, strideC, out_fmt) -> np.ndarray:
 
 
 def run(A, B, M, N, K, in_fmt, out_fmt, *, batch=1, a_layout="row", b_layout="row", lda=None, ldb=None,
-        ldc=None, sA=None, sB=None, sC=None, a_off=0, b_off=0, fill=None, stream=0, keep=False):
+        ldc=None, sA=None, sB=None, sC=None, a_off=0, b_off=0, fill=None, stream=0, keep=False, kernel=None):
     """C = A.B through gemm_strided_batched_ex on the given stored operands.
 
     Returns the float64 (batch, M, N) result (and the raw C buffer if ``keep``).
+    If ``kernel`` is given, the call must be routed to the kernel of that name.
     """
     lda = lda if lda is not None else (K if a_layout == "row" else M)
     ldb = ldb if ldb is not None else (N if b_layout == "row" else K)
@@ -71,6 +72,10 @@ def run(A, B, M, N, K, in_fmt, out_fmt, *, batch=1, a_layout="row", b_layout="ro
     a_buf, a_ptr = to_device(A, a_off)
     b_buf, b_ptr = to_device(B, b_off)
     c = alloc_c(batch, M, N, ldc, sC, out_fmt, fill)
+    if kernel is not None:
+        name = tsm.tsm_gemm_kernel_name(M, N, K, a_ptr, lda, LAYOUT[a_layout], sA, b_ptr, ldb, LAYOUT[b_layout], sB,
+                                        c, ldc, sC, batch, DTYPE[(in_fmt, out_fmt)])
+        assert name == kernel, f"routed to {name}, expected {kernel}"
     tsm.gemm_strided_batched_ex(M, N, K, a_ptr, lda, LAYOUT[a_layout], sA, b_ptr, ldb, LAYOUT[b_layout], sB, c, ldc,
                                 sC, batch, DTYPE[(in_fmt, out_fmt)], stream)
     import torch

@@ -52,13 +52,17 @@ def _sample_cells(rng, batch, M, N, n):
     return (np.concatenate([z, ez.ravel()]), np.concatenate([i, ei.ravel()]), np.concatenate([j, ej.ravel()]))
 
 
+EXPECTED_KERNEL = {"square_bf16_8192": "tile_256x256x64_kk"}
+
+
 @pytest.mark.parametrize("name", ["square_bf16_8192", "skinny_f16_16x16384x8192_b8"])
 def test_workload_sampled_parity(orc, big_inputs, name):
     """Full-size workloads: sampled cells and whole rows from the oracle; every output finite."""
     w = WORKLOADS[name]
     A, B = big_inputs(name)
     say(f"[gpu] {name} M={w.M} N={w.N} K={w.K} batch={w.batch}")
-    C = run(A, B, w.M, w.N, w.K, w.in_fmt, w.out_fmt, batch=w.batch, a_layout=w.a_layout, b_layout=w.b_layout)
+    C = run(A, B, w.M, w.N, w.K, w.in_fmt, w.out_fmt, batch=w.batch, a_layout=w.a_layout, b_layout=w.b_layout,
+            kernel=EXPECTED_KERNEL.get(name))
     assert np.all(np.isfinite(C))
     rng = np.random.default_rng(77)
     z, i, j = _sample_cells(rng, w.batch, w.M, w.N, 3000)
@@ -132,6 +136,38 @@ def test_ldc_padding_untouched_and_inside_overwritten():
         tail = host[(M - 1) * ldc + N:]
         assert np.all(np.isnan(tail)) if np.isnan(fill) else np.all(tail == fill)
         torch.cuda.synchronize()
+
+
+TILE = "tile_256x256x64_kk"
+TILE_SHAPES = [(256, 256, 128, 1), (512, 768, 384, 1), (256, 512, 1024, 3), (768, 256, 256, 2)]
+
+
+@pytest.mark.parametrize("shape", TILE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("in_fmt,out_fmt", [(BF16, "f16"), (F16, "f32"), (BF16, "f32"), (F16, "f16")])
+def test_tile_kernel(orc, shape, in_fmt, out_fmt):
+    """The large-tile kernel (A row-major, B column-major, 256-multiples, K % 128 == 0) against the oracle."""
+    M, N, K, batch = shape
+    A, B = make_operands(M + N + K + batch, batch, M, N, K, in_fmt, ("uniform", -1.0, 1.0), "row", "col")
+    say(f"[gpu] tile kernel {shape} {in_fmt}->{out_fmt}")
+    C = run(A, B, M, N, K, in_fmt, out_fmt, batch=batch, a_layout="row", b_layout="col", kernel=TILE)
+    Cr, S = orc.gemm_rows(A, B, M, N, K, in_fmt, batch=batch, a_layout="row", b_layout="col")
+    check(C, Cr, S, K, out_fmt, f"tile {shape}")
+
+
+def test_tile_kernel_padded_ld_and_strides(orc):
+    """Padded lda/ldb/ldc and batch strides larger than the matrices, still on the tile kernel."""
+    M, N, K, batch = 256, 512, 256, 2
+    lda, ldb, ldc = K + 64, K + 8, N + 4
+    A, B = make_operands(99, batch, M, N, K, BF16, ("uniform", -1.0, 1.0), "row", "col")
+    Ap = np.zeros((batch, M, lda), np.uint16)
+    Ap[:, :, :K] = A
+    Bp = np.zeros((batch, N, ldb), np.uint16)
+    Bp[:, :, :K] = B
+    say("[gpu] tile kernel padded")
+    C = run(Ap, Bp, M, N, K, BF16, "f32", batch=batch, a_layout="row", b_layout="col", lda=lda, ldb=ldb, ldc=ldc,
+            sC=M * ldc + 12, kernel=TILE)
+    Cr, S = orc.gemm_rows(A, B, M, N, K, BF16, batch=batch, a_layout="row", b_layout="col")
+    check(C, Cr, S, K, "f32", "tile padded")
 
 
 def test_k_zero_writes_zeros():

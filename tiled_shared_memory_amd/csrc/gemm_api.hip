@@ -42,7 +42,7 @@ bool ranges_overlap(const void *p, int64_t pbytes, const void *q, int64_t qbytes
   return a < b + (uintptr_t)qbytes && b < a + (uintptr_t)pbytes;
 }
 
-enum class Kernel { None, Masked8, Masked1 };
+enum class Kernel { None, Masked8, Masked1, Tile };
 
 struct Plan {
   Problem p;
@@ -148,7 +148,10 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
     return fail(TSM_ERROR_NOT_SUPPORTED, "tile grid too large (%lld tiles)", (long long)tiles);
   const bool a8 = K == 0 || vec8_ok(A, p.a_col ? M : K, lda, p.sA, batch);
   const bool b8 = K == 0 || vec8_ok(B, p.b_col ? K : N, ldb, p.sB, batch);
-  out->kernel = (a8 && b8) ? Kernel::Masked8 : Kernel::Masked1;
+  if (K > 0 && tile_supports(p))
+    out->kernel = Kernel::Tile;
+  else
+    out->kernel = (a8 && b8) ? Kernel::Masked8 : Kernel::Masked1;
   return TSM_SUCCESS;
 }
 
@@ -158,6 +161,8 @@ const char *kernel_name(Kernel k) {
       return masked_name(8);
     case Kernel::Masked1:
       return masked_name(1);
+    case Kernel::Tile:
+      return tile_name();
     default:
       return nullptr;
   }
@@ -174,6 +179,9 @@ int run(const Plan &pl, void *stream) {
       break;
     case Kernel::Masked1:
       e = launch_masked(pl.p, 1, s);
+      break;
+    case Kernel::Tile:
+      e = launch_tile(pl.p, s);
       break;
   }
   if (e != hipSuccess) return fail(TSM_ERROR_LAUNCH, "launch failed: %s", hipGetErrorString(e));

@@ -47,4 +47,13 @@ struct MaskedInfo {
 hipError_t launch_masked(const Problem &p, int vec, hipStream_t stream);
 const char *masked_name(int vec);
 
+// Large-tile kernel: both operands K-contiguous (A row-major, B column-major),
+// M, N multiples of 256, K a multiple of 64, 16-byte aligned rows.
+struct TileInfo {
+  static constexpr int BM = 256, BN = 256, BK = 64, THREADS = 256;
+};
+bool tile_supports(const Problem &p);
+hipError_t launch_tile(const Problem &p, hipStream_t stream);
+const char *tile_name();
+
 }  // namespace tsm
