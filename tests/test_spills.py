@@ -43,6 +43,7 @@ def test_lds_fits_the_cu(report):
 def test_every_kernel_family_is_built(report):
     names = " ".join(k["name"] for k in report["kernels"])
     assert "gemm_masked_kernel" in names
+    assert "gemm_tile_kernel" in names
 
 
 SPILLER = r"""

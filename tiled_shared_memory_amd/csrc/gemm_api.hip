@@ -7,6 +7,7 @@
 // wraps silently addresses the wrong memory).
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "gemm_internal.hpp"
@@ -42,7 +43,22 @@ bool ranges_overlap(const void *p, int64_t pbytes, const void *q, int64_t qbytes
   return a < b + (uintptr_t)qbytes && b < a + (uintptr_t)pbytes;
 }
 
-enum class Kernel { None, Masked8, Masked1, Tile };
+enum class Kernel { None, Masked8, Masked1, Tile4, Tile8 };
+
+const char *kernel_name(Kernel k) {
+  switch (k) {
+    case Kernel::Masked8:
+      return masked_name(8);
+    case Kernel::Masked1:
+      return masked_name(1);
+    case Kernel::Tile4:
+      return tile_name(4);
+    case Kernel::Tile8:
+      return tile_name(8);
+    default:
+      return nullptr;
+  }
+}
 
 struct Plan {
   Problem p;
@@ -148,24 +164,24 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
     return fail(TSM_ERROR_NOT_SUPPORTED, "tile grid too large (%lld tiles)", (long long)tiles);
   const bool a8 = K == 0 || vec8_ok(A, p.a_col ? M : K, lda, p.sA, batch);
   const bool b8 = K == 0 || vec8_ok(B, p.b_col ? K : N, ldb, p.sB, batch);
-  if (K > 0 && tile_supports(p))
-    out->kernel = Kernel::Tile;
-  else
-    out->kernel = (a8 && b8) ? Kernel::Masked8 : Kernel::Masked1;
-  return TSM_SUCCESS;
-}
+  out->kernel = (a8 && b8) ? Kernel::Masked8 : Kernel::Masked1;
+  if (K > 0 && tile_supports(p)) out->kernel = Kernel::Tile4;
 
-const char *kernel_name(Kernel k) {
-  switch (k) {
-    case Kernel::Masked8:
-      return masked_name(8);
-    case Kernel::Masked1:
-      return masked_name(1);
-    case Kernel::Tile:
-      return tile_name();
-    default:
-      return nullptr;
+  // TSM_GEMM_KERNEL=<name> forces a kernel variant (tests and tuning); a
+  // variant that cannot run this problem is an error, never a silent fallback.
+  const char *force = getenv("TSM_GEMM_KERNEL");
+  if (force && *force) {
+    const Kernel all[] = {Kernel::Masked8, Kernel::Masked1, Kernel::Tile4, Kernel::Tile8};
+    Kernel want = Kernel::None;
+    for (Kernel k : all)
+      if (strcmp(force, kernel_name(k)) == 0) want = k;
+    if (want == Kernel::None) return fail(TSM_ERROR_INVALID_VALUE, "TSM_GEMM_KERNEL=%s names no kernel", force);
+    const bool ok = want == Kernel::Masked1 || (want == Kernel::Masked8 && a8 && b8) ||
+                    ((want == Kernel::Tile4 || want == Kernel::Tile8) && K > 0 && tile_supports(p));
+    if (!ok) return fail(TSM_ERROR_NOT_SUPPORTED, "TSM_GEMM_KERNEL=%s cannot run this problem", force);
+    out->kernel = want;
   }
+  return TSM_SUCCESS;
 }
 
 int run(const Plan &pl, void *stream) {
@@ -180,8 +196,11 @@ int run(const Plan &pl, void *stream) {
     case Kernel::Masked1:
       e = launch_masked(pl.p, 1, s);
       break;
-    case Kernel::Tile:
-      e = launch_tile(pl.p, s);
+    case Kernel::Tile4:
+      e = launch_tile(pl.p, 4, s);
+      break;
+    case Kernel::Tile8:
+      e = launch_tile(pl.p, 8, s);
       break;
   }
   if (e != hipSuccess) return fail(TSM_ERROR_LAUNCH, "launch failed: %s", hipGetErrorString(e));

@@ -48,12 +48,13 @@ hipError_t launch_masked(const Problem &p, int vec, hipStream_t stream);
 const char *masked_name(int vec);
 
 // Large-tile kernel: both operands K-contiguous (A row-major, B column-major),
-// M, N multiples of 256, K a multiple of 64, 16-byte aligned rows.
+// M, N multiples of 256, K a multiple of 128, 16-byte aligned rows.
+// Two variants: 4 waves of 128 x 128 or 8 waves of 128 x 64.
 struct TileInfo {
-  static constexpr int BM = 256, BN = 256, BK = 64, THREADS = 256;
+  static constexpr int BM = 256, BN = 256, BK = 32, STAGES = 4;
 };
 bool tile_supports(const Problem &p);
-hipError_t launch_tile(const Problem &p, hipStream_t stream);
-const char *tile_name();
+hipError_t launch_tile(const Problem &p, int waves, hipStream_t stream);
+const char *tile_name(int waves);
 
 }  // namespace tsm

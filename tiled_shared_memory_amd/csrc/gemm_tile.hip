@@ -1,24 +1,31 @@
 // Large-tile MFMA GEMM for gfx950: operands contiguous along K, full tiles.
 //
 // This is the fast path for A row-major and B column-major (every K slice of
-// both operands is a set of contiguous 128-byte row pieces), M and N multiples
-// of 256 and K a multiple of 64, all rows 16-byte aligned.  The host routes
+// both operands is a set of contiguous 64-byte row pieces), M and N multiples
+// of 256 and K a multiple of 128, all rows 16-byte aligned.  The host routes
 // every other problem to the masked kernel.
 //
 // Blocking ("The PTSS Cliff", sections "The Idea: Stage in SLM, Tile K" and
 // "Choosing K_TILE"): a 256-thread workgroup owns a 256 x 256 tile of C and
-// walks K in slices of 64.  Each wave owns a 128 x 128 quadrant as 4 x 4
+// walks K in slices of 32.  Each wave owns a 128 x 128 quadrant as 4 x 4
 // blocks of v_mfma_f32_32x32x16, i.e. 256 float32 accumulators per lane, a
-// budget fixed by the tile alone; the live operand fragments are one 16-deep
-// step of one slice (32 registers).  K never enters the register budget.
+// budget fixed by the tile alone; the live operand fragments are two 16-deep
+// steps (64 registers).  K never enters the register budget.
 //
-// Staging: the two operand slices (2 x 32 KiB) go global -> LDS with
-// buffer loads that write straight into LDS (no VGPR round trip), double buffered: while the
-// matrix cores consume slice s, slice s+1 is in flight (128 KiB of the CU's
-// 160 KiB LDS).  Each slice row is 128 bytes = 8 chunks of 16 bytes; chunk c of
-// row r is stored at position c ^ (r % 8), so the 32 rows a fragment read
-// touches spread over all banks.  One wave-wide load fills 8 whole rows (1 KiB),
-// each lane fetching the global chunk that belongs at its LDS slot.
+// Staging: operand slices (2 x 16 KiB) go global -> LDS with buffer loads that
+// write straight into LDS (no VGPR round trip), through a ring of 4 stages
+// (128 KiB of the CU's 160 KiB): a slice is requested three slices before it
+// is multiplied, which covers HBM latency at full MFMA rate.  Each slice row
+// is 64 bytes = 4 chunks of 16 bytes; chunk c of row r sits at position
+// c ^ ((r / 4) % 4), so the 16 rows a quarter-wave reads at once fall into 16
+// distinct 4-bank groups of gfx950's 64 LDS banks.  One wave-wide load fills
+// 16 whole rows (1 KiB), each lane fetching the global chunk that belongs at
+// its LDS slot.
+//
+// Per slice: wait for the slice and a workgroup barrier, read the first
+// step's fragments, refill the freed stage, run the previous slice's last
+// step (deferred so it covers the fragment-read latency), read the second
+// step's fragments, run the first step.
 //
 // Tile order: workgroups are dealt to the 8 XCDs round-robin, so consecutive
 // tile indices are first regrouped per XCD, then ordered in groups of 8 tile
@@ -37,14 +44,38 @@ namespace {
 
 constexpr int BM = TileInfo::BM;
 constexpr int BN = TileInfo::BN;
-constexpr int BK = TileInfo::BK;
-constexpr int THREADS = TileInfo::THREADS;
-constexpr int ROW_BYTES = BK * 2;             // 128
-constexpr int TILE_BYTES = BM * ROW_BYTES;    // 32 KiB per operand slice
+constexpr int BK = TileInfo::BK;              // 32
+constexpr int NS = TileInfo::STAGES;          // 4
+constexpr int ROW_BYTES = BK * 2;             // 64: 4 chunks of 16 bytes
+constexpr int TILE_BYTES = BM * ROW_BYTES;    // 16 KiB per operand slice
 constexpr int GROUP_M = 8;
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void global_void;
+
+// The LDS ring: one array per stage and operand, so that the compiler can tell
+// the slice in flight from the one being read.
+__shared__ __attribute__((aligned(1024))) char g_a0[TILE_BYTES], g_b0[TILE_BYTES];
+__shared__ __attribute__((aligned(1024))) char g_a1[TILE_BYTES], g_b1[TILE_BYTES];
+__shared__ __attribute__((aligned(1024))) char g_a2[TILE_BYTES], g_b2[TILE_BYTES];
+__shared__ __attribute__((aligned(1024))) char g_a3[TILE_BYTES], g_b3[TILE_BYTES];
+
+template <int S> struct Ring;
+template <> struct Ring<0> {
+  __device__ static char *a() { return g_a0; }
+  __device__ static char *b() { return g_b0; }
+};
+template <> struct Ring<1> {
+  __device__ static char *a() { return g_a1; }
+  __device__ static char *b() { return g_b1; }
+};
+template <> struct Ring<2> {
+  __device__ static char *a() { return g_a2; }
+  __device__ static char *b() { return g_b2; }
+};
+template <> struct Ring<3> {
+  __device__ static char *a() { return g_a3; }
+  __device__ static char *b() { return g_b3; }
+};
 
 // Buffer resource over `bytes` bytes starting at `base` (raw addressing,
 // dword 3 = the gfx9 default data format).
@@ -52,106 +83,129 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Per-lane byte offsets, relative to the slice origin, of the 8 chunks a lane
-// fetches for one 256 x 64 operand slice (rows ld elements apart).  Lane l of
-// wave w fills LDS slot l of 8-row groups w*8 .. w*8+7; the chunk that belongs
-// at that slot under the XOR swizzle is chunk (l % 8) ^ (l / 8) of its row.
-__device__ __forceinline__ void slice_offsets(uint32_t (&off)[8], int64_t ld, int wave, int lane) {
-  const int r_in = lane >> 3;
-  const int c = (lane & 7) ^ r_in;
+// LDS position of 16-byte chunk c of slice row r: chunk c ^ ((r / 4) % 4) of
+// the row.  The 16 rows a quarter-wave reads in one cycle then cover all 16
+// four-bank groups of gfx950's 64 banks.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 2) & 3); }
+
+// Per-lane byte offsets, relative to the slice origin, of the chunks a lane
+// fetches for one 256 x 32 operand slice (rows ld elements apart).  One
+// wave-wide load fills 16 whole rows (1 KiB): lane l writes LDS slot l, i.e.
+// row l / 4 of its group at position l % 4, so it fetches the chunk whose
+// swizzled position that is.
+template <int LOADS>
+__device__ __forceinline__ void slice_offsets(uint32_t (&off)[LOADS], int64_t ld, int wave, int lane) {
+  const int r_in = lane >> 2;
+  const int c = swz(r_in, lane & 3);  // swz is an involution in its chunk argument
 #pragma unroll
-  for (int g = 0; g < 8; ++g) off[g] = (uint32_t)(((wave * 8 + g) * 8 + r_in) * ld + c * 8) * 2u;
+  for (int g = 0; g < LOADS; ++g) off[g] = (uint32_t)(((wave * LOADS + g) * 16 + r_in) * ld + c * 8) * 2u;
 }
 
-// Issue the asynchronous copy of one slice into LDS: 8 buffer loads per wave,
-// each writing 1 KiB (8 rows) of LDS.  kbytes is the slice's K offset in bytes.
-__device__ __forceinline__ void issue_slice(__amdgpu_buffer_rsrc_t rsrc, const uint32_t (&off)[8], uint32_t kbytes,
-                                            char *lds, int wave) {
+// Asynchronous copy of one operand slice into LDS: 16 buffer loads shared by
+// the waves, each writing 1 KiB of LDS; kbytes is the slice's K offset in bytes.
+template <int LOADS>
+__device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, const uint32_t *off, uint32_t kbytes, char *lds,
+                                      int wave) {
 #pragma unroll
-  for (int g = 0; g < 8; ++g)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)(lds + (wave * 8 + g) * 1024), 16, off[g], kbytes, 0,
-                                             0);
+  for (int g = 0; g < LOADS; ++g)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)(lds + (wave * LOADS + g) * 1024), 16, off[g],
+                                             kbytes, 0, 0);
 }
 
-// Fragments of one 16-deep step: 4 A blocks and 4 B blocks of 32 rows.
-__device__ __forceinline__ void read_frags(const char *sa, const char *sb, u32x4 (&fa)[4], u32x4 (&fb)[4], int ks,
-                                           int wm, int wn, int lane) {
-  const int row = lane & 31;
-  const int chunk = ((2 * ks + (lane >> 5)) ^ (lane & 7)) * 16;  // rows read here have row % 8 == lane % 8
+// Fragments of one 16-deep step: 4 A blocks and NB B blocks of 32 rows.
+template <int NB>
+struct Frags {
+  u32x4 a[4], b[NB];
+};
+
+template <int NB>
+__device__ __forceinline__ void read_frags(const char *sa, const char *sb, Frags<NB> &f, int ks, int wm, int wn,
+                                           int lane) {
+  const int row = lane & 31;  // block rows are multiples of 32, so row % 16 == lane % 16
+  const int chunk = swz(row, 2 * ks + (lane >> 5)) * 16;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    fa[i] = *reinterpret_cast<const u32x4 *>(sa + (wm * 128 + i * 32 + row) * ROW_BYTES + chunk);
+    f.a[i] = *reinterpret_cast<const u32x4 *>(sa + (wm * 128 + i * 32 + row) * ROW_BYTES + chunk);
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    fb[j] = *reinterpret_cast<const u32x4 *>(sb + (wn * 128 + j * 32 + row) * ROW_BYTES + chunk);
+  for (int j = 0; j < NB; ++j)
+    f.b[j] = *reinterpret_cast<const u32x4 *>(sb + (wn * NB * 32 + j * 32 + row) * ROW_BYTES + chunk);
 }
 
-// Scheduling hints (instruction classes of __builtin_amdgcn_sched_group_barrier).
+// 4 x NB MFMAs of one step.  Operands go in as (B, A) so that each
+// accumulator register group holds 4 consecutive columns of one row of C.
+template <bool BF16, int NB>
+__device__ __forceinline__ void mma(const Frags<NB> &f, f32x16 (&acc)[4][NB]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = mfma_32x32x16<BF16>(f.b[j], f.a[i], acc[i][j]);
+}
+
+// Scheduling classes of __builtin_amdgcn_sched_group_barrier.
 constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100;
 
-// One 64-deep slice from LDS (sa, sb), while the next slice is fetched into the
-// other stage: 4 steps of 16, each 8 fragment reads and 16 MFMAs.  The
-// fragments of step ks+1 are read while the MFMAs of step ks run, and the 16
-// buffer loads of the next slice are spread over the first step's MFMAs.
-template <bool BF16, bool ISSUE>
-__device__ __forceinline__ void slice(const char *sa, const char *sb, f32x16 (&acc)[4][4], int wm, int wn, int lane,
-                                      __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                      const uint32_t (&offA)[8], const uint32_t (&offB)[8], uint32_t kbytes,
-                                      char *na, char *nb, int wave) {
-  u32x4 fa[2][4], fb[2][4];
-  read_frags(sa, sb, fa[0], fb[0], 0, wm, wn, lane);
-  if constexpr (ISSUE) {
-    issue_slice(ra, offA, kbytes, na, wave);
-    issue_slice(rb, offB, kbytes, nb, wave);
+template <int NW>
+struct Ctx {
+  static constexpr int LOADS = 16 / NW;  // 1 KiB wave-loads per operand slice per wave
+  static constexpr int NB = 16 / NW;     // 32-column B blocks per wave (wave tile 128 x 32*NB)
+  __amdgpu_buffer_rsrc_t ra, rb;
+  uint32_t offA[LOADS], offB[LOADS];
+  int nk, wave, wm, wn, lane;
+};
+
+// Slice j, resident in stage S.  On entry f1 holds the fragments of the last
+// step of slice j-1, whose MFMAs were deferred past this slice's barrier so
+// that they cover the latency of the first fragment reads of slice j.
+template <bool BF16, int S, int NW>
+__device__ __forceinline__ void slice(Ctx<NW> &c, int j, Frags<Ctx<NW>::NB> &f0, Frags<Ctx<NW>::NB> &f1,
+                                      f32x16 (&acc)[4][Ctx<NW>::NB]) {
+  constexpr int LOADS = Ctx<NW>::LOADS, NB = Ctx<NW>::NB;
+  constexpr int NMFMA = 4 * NB, NREAD = 4 + NB;  // per step
+  // Slice j has landed once at most the two younger slices' loads are pending;
+  // this wave's reads of stage S-1 (refilled below) are complete.  The empty
+  // asm keeps LDS reads from moving above the barrier.
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * 2 * LOADS) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  read_frags(Ring<S>::a(), Ring<S>::b(), f0, 0, c.wm, c.wn, c.lane);
+  // refill the stage freed by slice j-1 with slice j+3 (the last slice again
+  // near the end, which keeps the load count per slice uniform)
+  const int next = min(j + NS - 1, c.nk - 1);
+  issue<LOADS>(c.ra, c.offA, (uint32_t)next * ROW_BYTES, Ring<(S + NS - 1) % NS>::a(), c.wave);
+  issue<LOADS>(c.rb, c.offB, (uint32_t)next * ROW_BYTES, Ring<(S + NS - 1) % NS>::b(), c.wave);
+  mma<BF16>(f1, acc);  // deferred last step of slice j-1
+  read_frags(Ring<S>::a(), Ring<S>::b(), f1, 1, c.wm, c.wn, c.lane);
+  mma<BF16>(f0, acc);
+  // schedule: first-step reads; loads spread over the deferred MFMAs and the
+  // first step, second-step reads among the first step's MFMAs
+  __builtin_amdgcn_sched_group_barrier(SG_DS_READ, NREAD, 0);
+  constexpr int VM_A = LOADS;       // loads placed among the deferred MFMAs
+  constexpr int VM_B = LOADS;       // loads placed among the first step's MFMAs
+#pragma unroll
+  for (int t = 0; t < VM_A; ++t) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, NMFMA / VM_A, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
   }
 #pragma unroll
-  for (int ks = 0; ks < BK / 16; ++ks) {
-    const int cur = ks & 1;
-    if (ks + 1 < BK / 16) read_frags(sa, sb, fa[cur ^ 1], fb[cur ^ 1], ks + 1, wm, wn, lane);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_32x32x16<BF16>(fb[cur][j], fa[cur][i], acc[i][j]);
-  }
-  // schedule: step-0 reads first; then interleave MFMAs with the remaining reads and loads
-  __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 8, 0);
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
+  for (int t = 0; t < NREAD; ++t) {
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-    if constexpr (ISSUE) __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 2, 0);
     __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+    if (t % (NREAD / VM_B) == NREAD / VM_B - 1) __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(SG_MFMA, 8, 0);
-#pragma unroll
-  for (int ks = 1; ks < 3; ++ks) {
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 8, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(SG_MFMA, 16, 0);
+  __builtin_amdgcn_sched_group_barrier(SG_MFMA, NMFMA - NREAD, 0);
 }
 
-__device__ __forceinline__ void wait_slices() {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-}
-
-template <bool BF16, bool OUT_F16>
-__global__ __launch_bounds__(THREADS, 1) void gemm_tile_kernel(KernelArgs p) {
-  // separate arrays per stage so the compiler can tell the in-flight slice
-  // from the one being read
-  __shared__ __attribute__((aligned(1024))) char sA0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sB0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sA1[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sB1[TILE_BYTES];
-
+template <bool BF16, bool OUT_F16, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void gemm_tile_kernel(KernelArgs p) {
+  using C = Ctx<NW>;
+  constexpr int NB = C::NB;
+  C c;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  c.lane = tid & 63;
+  c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  c.wm = c.wave / (NW / 2);  // two rows of waves, 128 rows each
+  c.wn = c.wave % (NW / 2);
+  const int lane = c.lane, wm = c.wm, wn = c.wn;
 
   // ---- tile order: per-XCD regrouping, then GROUP_M rows column by column
   const int T = p.tiles_m * p.tiles_n;
@@ -170,40 +224,45 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_tile_kernel(KernelArgs p) {
   const uint16_t *A = p.A + z * p.sA + m0 * p.lda;  // row m0, k = 0 (row-major A)
   const uint16_t *B = p.B + z * p.sB + n0 * p.ldb;  // column n0, k = 0 (column-major B)
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][NB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
 
   // Buffer resources cover exactly the 256 rows of each operand panel; the
-  // host keeps that extent below 4 GiB, so all offsets are 32-bit.
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)((255 * p.lda + p.K) * 2));
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(B, (uint32_t)((255 * p.ldb + p.K) * 2));
-  uint32_t offA[8], offB[8];
-  slice_offsets(offA, p.lda, wave, lane);
-  slice_offsets(offB, p.ldb, wave, lane);
-  constexpr uint32_t SLICE = BK * 2;  // bytes between consecutive K slices of one row
+  // host keeps that extent below 2 GiB, so all offsets are 32-bit.
+  c.ra = make_rsrc(A, (uint32_t)((255 * p.lda + p.K) * 2));
+  c.rb = make_rsrc(B, (uint32_t)((255 * p.ldb + p.K) * 2));
+  slice_offsets(c.offA, p.lda, c.wave, lane);
+  slice_offsets(c.offB, p.ldb, c.wave, lane);
+  c.nk = (int)(p.K / BK);  // the host guarantees K is a positive multiple of NS * BK
 
-  // The host guarantees K is a positive multiple of 128, so slices come in
-  // pairs: the steady-state loop has no branches, which keeps the 256
-  // accumulators of each lane in place across iterations.
-  const int nk = (int)(p.K / BK);
-  issue_slice(ra, offA, 0, sA0, wave);
-  issue_slice(rb, offB, 0, sB0, wave);
-  wait_slices();
-  int kt = 0;
-  for (; kt + 2 < nk; kt += 2) {
-    // slice kt is in stage 0: multiply it while kt+1 loads into stage 1, then the reverse
-    slice<BF16, true>(sA0, sB0, acc, wm, wn, lane, ra, rb, offA, offB, (kt + 1) * SLICE, sA1, sB1, wave);
-    wait_slices();
-    slice<BF16, true>(sA1, sB1, acc, wm, wn, lane, ra, rb, offA, offB, (kt + 2) * SLICE, sA0, sB0, wave);
-    wait_slices();
+  // prologue: slices 0 .. NS-2 in flight
+  issue<C::LOADS>(c.ra, c.offA, 0 * ROW_BYTES, Ring<0>::a(), c.wave);
+  issue<C::LOADS>(c.rb, c.offB, 0 * ROW_BYTES, Ring<0>::b(), c.wave);
+  issue<C::LOADS>(c.ra, c.offA, 1 * ROW_BYTES, Ring<1>::a(), c.wave);
+  issue<C::LOADS>(c.rb, c.offB, 1 * ROW_BYTES, Ring<1>::b(), c.wave);
+  issue<C::LOADS>(c.ra, c.offA, 2 * ROW_BYTES, Ring<2>::a(), c.wave);
+  issue<C::LOADS>(c.rb, c.offB, 2 * ROW_BYTES, Ring<2>::b(), c.wave);
+
+  // Before slice 0 there is no deferred step: zero fragments add exactly 0.
+  Frags<NB> f0, f1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f1.a[i] = u32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < NB; ++j) f1.b[j] = u32x4{0, 0, 0, 0};
+
+  // The steady-state loop has no data-dependent branches, which keeps the
+  // 256 accumulators of each lane in place across iterations.
+  for (int j = 0; j < c.nk; j += NS) {
+    slice<BF16, 0, NW>(c, j + 0, f0, f1, acc);
+    slice<BF16, 1, NW>(c, j + 1, f0, f1, acc);
+    slice<BF16, 2, NW>(c, j + 2, f0, f1, acc);
+    slice<BF16, 3, NW>(c, j + 3, f0, f1, acc);
   }
-  // last pair: slices nk-2 (stage 0) and nk-1
-  slice<BF16, true>(sA0, sB0, acc, wm, wn, lane, ra, rb, offA, offB, (kt + 1) * SLICE, sA1, sB1, wave);
-  wait_slices();
-  slice<BF16, false>(sA1, sB1, acc, wm, wn, lane, ra, rb, offA, offB, 0, sA0, sB0, wave);
+  mma<BF16>(f1, acc);  // last step of the last slice
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the duplicate tail loads
 
   // ---- epilogue: lane holds C[m][n + 0..3] for m = block row + lane % 32
   const int64_t ldc = p.ldc;
@@ -211,10 +270,10 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_tile_kernel(KernelArgs p) {
   for (int i = 0; i < 4; ++i) {
     const int64_t m = m0 + wm * 128 + i * 32 + (lane & 31);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NB; ++j) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int64_t n = n0 + wn * 128 + j * 32 + 8 * g + 4 * (lane >> 5);
+        const int64_t n = n0 + wn * NB * 32 + j * 32 + 8 * g + 4 * (lane >> 5);
         const f32x16 &a = acc[i][j];
         if constexpr (OUT_F16) {
           uint16_t *C = (uint16_t *)p.C + z * p.sC;
@@ -232,14 +291,14 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_tile_kernel(KernelArgs p) {
   }
 }
 
-template <bool BF16, bool OUT_F16>
+template <bool BF16, bool OUT_F16, int NW>
 hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
   const int64_t tiles = (int64_t)base.tiles_m * base.tiles_n;
   for (int64_t z0 = 0; z0 < batch; z0 += kMaxGridY) {
     KernelArgs a = base;
     a.z0 = (int32_t)z0;
     const int64_t nz = batch - z0 < kMaxGridY ? batch - z0 : kMaxGridY;
-    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT_F16>), dim3((unsigned)tiles, (unsigned)nz), dim3(THREADS), 0,
+    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT_F16, NW>), dim3((unsigned)tiles, (unsigned)nz), dim3(NW * 64), 0,
                        stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -247,21 +306,28 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
   return hipSuccess;
 }
 
+template <int NW>
+hipError_t launch_nw(const Problem &p, const KernelArgs &a, hipStream_t stream) {
+  if (p.in_bf16)
+    return p.out_f16 ? launch_t<true, true, NW>(a, p.batch, stream) : launch_t<true, false, NW>(a, p.batch, stream);
+  return p.out_f16 ? launch_t<false, true, NW>(a, p.batch, stream) : launch_t<false, false, NW>(a, p.batch, stream);
+}
+
 }  // namespace
 
 bool tile_supports(const Problem &p) {
   if (p.a_col || !p.b_col) return false;  // both operands must be K-contiguous
-  if (p.M % BM || p.N % BN || p.K % (2 * BK) || p.K == 0) return false;
-  // one operand panel (256 rows) must span less than 4 GiB: 32-bit buffer offsets
-  if (255 * p.lda + p.K >= (int64_t)1 << 31 || 255 * p.ldb + p.K >= (int64_t)1 << 31) return false;
+  if (p.M % BM || p.N % BN || p.K % (NS * BK) || p.K == 0) return false;
+  // one operand panel (256 rows) must span less than 2 GiB: 32-bit buffer offsets
+  if (255 * p.lda + p.K >= (int64_t)1 << 30 || 255 * p.ldb + p.K >= (int64_t)1 << 30) return false;
   if (((uintptr_t)p.A & 15) || ((uintptr_t)p.B & 15) || ((uintptr_t)p.C & 15)) return false;
   if (p.lda % 8 || p.ldb % 8) return false;
-  if (p.ldc % (p.out_f16 ? 4 : 4)) return false;  // 8-byte (f16) / 16-byte (f32) row stores
+  if (p.ldc % 4) return false;  // 8-byte (f16) / 16-byte (float32) row stores
   if (p.batch > 1 && (p.sA % 8 || p.sB % 8 || p.sC % 4)) return false;
   return true;
 }
 
-hipError_t launch_tile(const Problem &p, hipStream_t stream) {
+hipError_t launch_tile(const Problem &p, int waves, hipStream_t stream) {
   KernelArgs a{};
   a.A = p.A;
   a.B = p.B;
@@ -277,11 +343,9 @@ hipError_t launch_tile(const Problem &p, hipStream_t stream) {
   a.sC = p.sC;
   a.tiles_m = (int32_t)(p.M / BM);
   a.tiles_n = (int32_t)(p.N / BN);
-  if (p.in_bf16)
-    return p.out_f16 ? launch_t<true, true>(a, p.batch, stream) : launch_t<true, false>(a, p.batch, stream);
-  return p.out_f16 ? launch_t<false, true>(a, p.batch, stream) : launch_t<false, false>(a, p.batch, stream);
+  return waves == 8 ? launch_nw<8>(p, a, stream) : launch_nw<4>(p, a, stream);
 }
 
-const char *tile_name() { return "tile_256x256x64_kk"; }
+const char *tile_name(int waves) { return waves == 8 ? "tile_256x256x32_s4_w8" : "tile_256x256x32_s4_w4"; }
 
 }  // namespace tsm
