@@ -52,7 +52,7 @@ def _sample_cells(rng, batch, M, N, n):
     return (np.concatenate([z, ez.ravel()]), np.concatenate([i, ei.ravel()]), np.concatenate([j, ej.ravel()]))
 
 
-EXPECTED_KERNEL = {"square_bf16_8192": "tile_256x256x32_s4_"}
+EXPECTED_KERNEL = {"square_bf16_8192": "tile_256x256x32_"}
 
 
 @pytest.mark.parametrize("name", ["square_bf16_8192", "skinny_f16_16x16384x8192_b8"])
@@ -138,7 +138,7 @@ def test_ldc_padding_untouched_and_inside_overwritten():
         torch.cuda.synchronize()
 
 
-TILE = "tile_256x256x32_s4_"
+TILE = "tile_256x256x32_"
 TILE_SHAPES = [(256, 256, 128, 1), (512, 768, 384, 1), (256, 512, 1024, 3), (768, 256, 256, 2)]
 
 

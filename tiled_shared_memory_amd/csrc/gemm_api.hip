@@ -43,7 +43,7 @@ bool ranges_overlap(const void *p, int64_t pbytes, const void *q, int64_t qbytes
   return a < b + (uintptr_t)qbytes && b < a + (uintptr_t)pbytes;
 }
 
-enum class Kernel { None, Masked8, Masked1, Tile4, Tile8 };
+enum class Kernel { None, Masked8, Masked1, Tile32, Tile16 };
 
 const char *kernel_name(Kernel k) {
   switch (k) {
@@ -51,10 +51,10 @@ const char *kernel_name(Kernel k) {
       return masked_name(8);
     case Kernel::Masked1:
       return masked_name(1);
-    case Kernel::Tile4:
-      return tile_name(4);
-    case Kernel::Tile8:
-      return tile_name(8);
+    case Kernel::Tile32:
+      return tile_name(32);
+    case Kernel::Tile16:
+      return tile_name(16);
     default:
       return nullptr;
   }
@@ -165,19 +165,19 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
   const bool a8 = K == 0 || vec8_ok(A, p.a_col ? M : K, lda, p.sA, batch);
   const bool b8 = K == 0 || vec8_ok(B, p.b_col ? K : N, ldb, p.sB, batch);
   out->kernel = (a8 && b8) ? Kernel::Masked8 : Kernel::Masked1;
-  if (K > 0 && tile_supports(p)) out->kernel = Kernel::Tile4;
+  if (K > 0 && tile_supports(p)) out->kernel = Kernel::Tile16;
 
   // TSM_GEMM_KERNEL=<name> forces a kernel variant (tests and tuning); a
   // variant that cannot run this problem is an error, never a silent fallback.
   const char *force = getenv("TSM_GEMM_KERNEL");
   if (force && *force) {
-    const Kernel all[] = {Kernel::Masked8, Kernel::Masked1, Kernel::Tile4, Kernel::Tile8};
+    const Kernel all[] = {Kernel::Masked8, Kernel::Masked1, Kernel::Tile32, Kernel::Tile16};
     Kernel want = Kernel::None;
     for (Kernel k : all)
       if (strcmp(force, kernel_name(k)) == 0) want = k;
     if (want == Kernel::None) return fail(TSM_ERROR_INVALID_VALUE, "TSM_GEMM_KERNEL=%s names no kernel", force);
     const bool ok = want == Kernel::Masked1 || (want == Kernel::Masked8 && a8 && b8) ||
-                    ((want == Kernel::Tile4 || want == Kernel::Tile8) && K > 0 && tile_supports(p));
+                    ((want == Kernel::Tile32 || want == Kernel::Tile16) && K > 0 && tile_supports(p));
     if (!ok) return fail(TSM_ERROR_NOT_SUPPORTED, "TSM_GEMM_KERNEL=%s cannot run this problem", force);
     out->kernel = want;
   }
@@ -196,11 +196,11 @@ int run(const Plan &pl, void *stream) {
     case Kernel::Masked1:
       e = launch_masked(pl.p, 1, s);
       break;
-    case Kernel::Tile4:
-      e = launch_tile(pl.p, 4, s);
+    case Kernel::Tile32:
+      e = launch_tile(pl.p, 32, s);
       break;
-    case Kernel::Tile8:
-      e = launch_tile(pl.p, 8, s);
+    case Kernel::Tile16:
+      e = launch_tile(pl.p, 16, s);
       break;
   }
   if (e != hipSuccess) return fail(TSM_ERROR_LAUNCH, "launch failed: %s", hipGetErrorString(e));

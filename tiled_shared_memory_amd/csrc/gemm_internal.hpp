@@ -49,12 +49,12 @@ const char *masked_name(int vec);
 
 // Large-tile kernel: both operands K-contiguous (A row-major, B column-major),
 // M, N multiples of 256, K a multiple of 128, 16-byte aligned rows.
-// Two variants: 4 waves of 128 x 128 or 8 waves of 128 x 64.
+// Two variants by MFMA shape: mi = 32 (32x32x16) or mi = 16 (16x16x32).
 struct TileInfo {
   static constexpr int BM = 256, BN = 256, BK = 32, STAGES = 4;
 };
 bool tile_supports(const Problem &p);
-hipError_t launch_tile(const Problem &p, int waves, hipStream_t stream);
-const char *tile_name(int waves);
+hipError_t launch_tile(const Problem &p, int mi, hipStream_t stream);
+const char *tile_name(int mi);
 
 }  // namespace tsm

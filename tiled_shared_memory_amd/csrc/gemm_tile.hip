@@ -112,99 +112,122 @@ __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, const uint32_
                                              kbytes, 0, 0);
 }
 
-// Fragments of one 16-deep step: 4 A blocks and NB B blocks of 32 rows.
-template <int NB>
+// Fragments of one whole 32-deep slice for one wave (128 x 128 of C):
+//  MI = 32: two 16-deep steps, each 4 A and 4 B blocks of 32 rows
+//           (v_mfma_f32_32x32x16 operands);
+//  MI = 16: one 32-deep step, 8 A and 8 B blocks of 16 rows
+//           (v_mfma_f32_16x16x32 operands).
+// Either way 16 reads of 16 bytes per lane, 64 registers.
+template <int MI>
 struct Frags {
-  u32x4 a[4], b[NB];
+  static constexpr int NA = MI == 32 ? 4 : 8;  // blocks per operand per step
+  static constexpr int NSTEP = MI == 32 ? 2 : 1;
+  u32x4 a[NSTEP][NA], b[NSTEP][NA];
 };
 
-template <int NB>
-__device__ __forceinline__ void read_frags(const char *sa, const char *sb, Frags<NB> &f, int ks, int wm, int wn,
-                                           int lane) {
-  const int row = lane & 31;  // block rows are multiples of 32, so row % 16 == lane % 16
-  const int chunk = swz(row, 2 * ks + (lane >> 5)) * 16;
+template <int MI>
+__device__ __forceinline__ void read_frags(const char *sa, const char *sb, Frags<MI> &f, int wm, int wn, int lane) {
+  constexpr int NA = Frags<MI>::NA;
+  // lane reads row (lane % MI) of each block, K chunk (lane / MI) of the step;
+  // block rows are multiples of 16, so row % 16 == lane % 16
+  const int row = lane % MI;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    f.a[i] = *reinterpret_cast<const u32x4 *>(sa + (wm * 128 + i * 32 + row) * ROW_BYTES + chunk);
+  for (int s = 0; s < Frags<MI>::NSTEP; ++s) {
+    const int chunk = swz(lane, s * (4 / Frags<MI>::NSTEP) + lane / MI) * 16;
 #pragma unroll
-  for (int j = 0; j < NB; ++j)
-    f.b[j] = *reinterpret_cast<const u32x4 *>(sb + (wn * NB * 32 + j * 32 + row) * ROW_BYTES + chunk);
+    for (int i = 0; i < NA; ++i)
+      f.a[s][i] = *reinterpret_cast<const u32x4 *>(sa + (wm * 128 + i * MI + row) * ROW_BYTES + chunk);
+#pragma unroll
+    for (int j = 0; j < NA; ++j)
+      f.b[s][j] = *reinterpret_cast<const u32x4 *>(sb + (wn * 128 + j * MI + row) * ROW_BYTES + chunk);
+  }
 }
 
-// 4 x NB MFMAs of one step.  Operands go in as (B, A) so that each
-// accumulator register group holds 4 consecutive columns of one row of C.
-template <bool BF16, int NB>
-__device__ __forceinline__ void mma(const Frags<NB> &f, f32x16 (&acc)[4][NB]) {
+// Accumulators of one wave: 128 x 128 float32 = 256 registers per lane.
+template <int MI>
+struct Acc;
+template <>
+struct Acc<32> {
+  f32x16 v[4][4];
+};
+template <>
+struct Acc<16> {
+  f32x4 v[8][8];
+};
+
+// All MFMAs of one slice.  Operands go in as (B, A) so that each accumulator
+// register group holds 4 consecutive columns of one row of C.
+template <bool BF16, int MI>
+__device__ __forceinline__ void mma(const Frags<MI> &f, Acc<MI> &acc) {
+  constexpr int NA = Frags<MI>::NA;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int s = 0; s < Frags<MI>::NSTEP; ++s)
 #pragma unroll
-    for (int j = 0; j < NB; ++j) acc[i][j] = mfma_32x32x16<BF16>(f.b[j], f.a[i], acc[i][j]);
+    for (int i = 0; i < NA; ++i)
+#pragma unroll
+      for (int j = 0; j < NA; ++j) {
+        if constexpr (MI == 32)
+          acc.v[i][j] = mfma_32x32x16<BF16>(f.b[s][j], f.a[s][i], acc.v[i][j]);
+        else
+          acc.v[i][j] = mfma_16x16x32<BF16>(f.b[s][j], f.a[s][i], acc.v[i][j]);
+      }
 }
 
 // Scheduling classes of __builtin_amdgcn_sched_group_barrier.
 constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100;
+constexpr int LOADS = 4;  // 1 KiB wave-loads per operand slice per wave
 
-template <int NW>
 struct Ctx {
-  static constexpr int LOADS = 16 / NW;  // 1 KiB wave-loads per operand slice per wave
-  static constexpr int NB = 16 / NW;     // 32-column B blocks per wave (wave tile 128 x 32*NB)
   __amdgpu_buffer_rsrc_t ra, rb;
   uint32_t offA[LOADS], offB[LOADS];
   int nk, wave, wm, wn, lane;
 };
 
-// Slice j, resident in stage S.  On entry f1 holds the fragments of the last
-// step of slice j-1, whose MFMAs were deferred past this slice's barrier so
-// that they cover the latency of the first fragment reads of slice j.
-template <bool BF16, int S, int NW>
-__device__ __forceinline__ void slice(Ctx<NW> &c, int j, Frags<Ctx<NW>::NB> &f0, Frags<Ctx<NW>::NB> &f1,
-                                      f32x16 (&acc)[4][Ctx<NW>::NB]) {
-  constexpr int LOADS = Ctx<NW>::LOADS, NB = Ctx<NW>::NB;
-  constexpr int NMFMA = 4 * NB, NREAD = 4 + NB;  // per step
+// Slice j, resident in stage S: after its barrier, read all of its fragments
+// into one register set while the MFMAs of slice j-1 run from the other set,
+// and refill the stage that slice j-1 freed with slice j+3.
+template <bool BF16, int MI, int S>
+__device__ __forceinline__ void slice(Ctx &c, int j, Frags<MI> (&fr)[2], Acc<MI> &acc) {
+  // Keep every MFMA of the previous slice above this point: sinking them past
+  // the fragment reads below would need a third fragment register set.
+  __builtin_amdgcn_sched_barrier(0);
   // Slice j has landed once at most the two younger slices' loads are pending;
   // this wave's reads of stage S-1 (refilled below) are complete.  The empty
   // asm keeps LDS reads from moving above the barrier.
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * 2 * LOADS) : "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  read_frags(Ring<S>::a(), Ring<S>::b(), f0, 0, c.wm, c.wn, c.lane);
-  // refill the stage freed by slice j-1 with slice j+3 (the last slice again
-  // near the end, which keeps the load count per slice uniform)
+  read_frags<MI>(Ring<S>::a(), Ring<S>::b(), fr[S & 1], c.wm, c.wn, c.lane);
+  // the last slice again near the end keeps the load count per slice uniform
   const int next = min(j + NS - 1, c.nk - 1);
   issue<LOADS>(c.ra, c.offA, (uint32_t)next * ROW_BYTES, Ring<(S + NS - 1) % NS>::a(), c.wave);
   issue<LOADS>(c.rb, c.offB, (uint32_t)next * ROW_BYTES, Ring<(S + NS - 1) % NS>::b(), c.wave);
-  mma<BF16>(f1, acc);  // deferred last step of slice j-1
-  read_frags(Ring<S>::a(), Ring<S>::b(), f1, 1, c.wm, c.wn, c.lane);
-  mma<BF16>(f0, acc);
-  // schedule: first-step reads; loads spread over the deferred MFMAs and the
-  // first step, second-step reads among the first step's MFMAs
-  __builtin_amdgcn_sched_group_barrier(SG_DS_READ, NREAD, 0);
-  constexpr int VM_A = LOADS;       // loads placed among the deferred MFMAs
-  constexpr int VM_B = LOADS;       // loads placed among the first step's MFMAs
+  mma<BF16, MI>(fr[(S & 1) ^ 1], acc);  // slice j-1
+  // schedule: one fragment read or load after every other MFMA, spread over
+  // the whole slice (bursts of memory instructions stall the in-order wave
+  // and with it the MFMA pipe)
+  constexpr int NMFMA = MI == 32 ? 32 : 64;
+  constexpr int G = NMFMA / 8;  // MFMAs per group of 2 reads + 1 load
 #pragma unroll
-  for (int t = 0; t < VM_A; ++t) {
-    __builtin_amdgcn_sched_group_barrier(SG_MFMA, NMFMA / VM_A, 0);
-    __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
-  }
-#pragma unroll
-  for (int t = 0; t < NREAD; ++t) {
-    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+  for (int t = 0; t < 8; ++t) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, G / 4, 0);
     __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
-    if (t % (NREAD / VM_B) == NREAD / VM_B - 1) __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, G / 4, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, G / 4, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, G / 4, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(SG_MFMA, NMFMA - NREAD, 0);
 }
 
-template <bool BF16, bool OUT_F16, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void gemm_tile_kernel(KernelArgs p) {
-  using C = Ctx<NW>;
-  constexpr int NB = C::NB;
-  C c;
+template <bool BF16, bool OUT_F16, int MI>
+__global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
+  Ctx c;
   const int tid = threadIdx.x;
   c.lane = tid & 63;
   c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  c.wm = c.wave / (NW / 2);  // two rows of waves, 128 rows each
-  c.wn = c.wave % (NW / 2);
+  c.wm = c.wave >> 1;  // 2 x 2 waves of 128 x 128
+  c.wn = c.wave & 1;
   const int lane = c.lane, wm = c.wm, wn = c.wn;
 
   // ---- tile order: per-XCD regrouping, then GROUP_M rows column by column
@@ -224,81 +247,100 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_tile_kernel(KernelArgs p) {
   const uint16_t *A = p.A + z * p.sA + m0 * p.lda;  // row m0, k = 0 (row-major A)
   const uint16_t *B = p.B + z * p.sB + n0 * p.ldb;  // column n0, k = 0 (column-major B)
 
-  f32x16 acc[4][NB];
+  Acc<MI> acc;
+  if constexpr (MI == 32) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
+      for (int j = 0; j < 4; ++j) acc.v[i][j] = f32x16{};
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc.v[i][j] = f32x4{};
+  }
 
   // Buffer resources cover exactly the 256 rows of each operand panel; the
-  // host keeps that extent below 2 GiB, so all offsets are 32-bit.
+  // host keeps that extent below 1 GiB, so all offsets are 32-bit.
   c.ra = make_rsrc(A, (uint32_t)((255 * p.lda + p.K) * 2));
   c.rb = make_rsrc(B, (uint32_t)((255 * p.ldb + p.K) * 2));
-  slice_offsets(c.offA, p.lda, c.wave, lane);
-  slice_offsets(c.offB, p.ldb, c.wave, lane);
+  slice_offsets<LOADS>(c.offA, p.lda, c.wave, lane);
+  slice_offsets<LOADS>(c.offB, p.ldb, c.wave, lane);
   c.nk = (int)(p.K / BK);  // the host guarantees K is a positive multiple of NS * BK
 
   // prologue: slices 0 .. NS-2 in flight
-  issue<C::LOADS>(c.ra, c.offA, 0 * ROW_BYTES, Ring<0>::a(), c.wave);
-  issue<C::LOADS>(c.rb, c.offB, 0 * ROW_BYTES, Ring<0>::b(), c.wave);
-  issue<C::LOADS>(c.ra, c.offA, 1 * ROW_BYTES, Ring<1>::a(), c.wave);
-  issue<C::LOADS>(c.rb, c.offB, 1 * ROW_BYTES, Ring<1>::b(), c.wave);
-  issue<C::LOADS>(c.ra, c.offA, 2 * ROW_BYTES, Ring<2>::a(), c.wave);
-  issue<C::LOADS>(c.rb, c.offB, 2 * ROW_BYTES, Ring<2>::b(), c.wave);
+  issue<LOADS>(c.ra, c.offA, 0 * ROW_BYTES, Ring<0>::a(), c.wave);
+  issue<LOADS>(c.rb, c.offB, 0 * ROW_BYTES, Ring<0>::b(), c.wave);
+  issue<LOADS>(c.ra, c.offA, 1 * ROW_BYTES, Ring<1>::a(), c.wave);
+  issue<LOADS>(c.rb, c.offB, 1 * ROW_BYTES, Ring<1>::b(), c.wave);
+  issue<LOADS>(c.ra, c.offA, 2 * ROW_BYTES, Ring<2>::a(), c.wave);
+  issue<LOADS>(c.rb, c.offB, 2 * ROW_BYTES, Ring<2>::b(), c.wave);
 
-  // Before slice 0 there is no deferred step: zero fragments add exactly 0.
-  Frags<NB> f0, f1;
+  // Before slice 0 there is no previous slice: zero fragments add exactly 0.
+  Frags<MI> fr[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f1.a[i] = u32x4{0, 0, 0, 0};
+  for (int s = 0; s < Frags<MI>::NSTEP; ++s)
 #pragma unroll
-  for (int j = 0; j < NB; ++j) f1.b[j] = u32x4{0, 0, 0, 0};
+    for (int i = 0; i < Frags<MI>::NA; ++i) fr[1].a[s][i] = fr[1].b[s][i] = u32x4{0, 0, 0, 0};
 
   // The steady-state loop has no data-dependent branches, which keeps the
   // 256 accumulators of each lane in place across iterations.
   for (int j = 0; j < c.nk; j += NS) {
-    slice<BF16, 0, NW>(c, j + 0, f0, f1, acc);
-    slice<BF16, 1, NW>(c, j + 1, f0, f1, acc);
-    slice<BF16, 2, NW>(c, j + 2, f0, f1, acc);
-    slice<BF16, 3, NW>(c, j + 3, f0, f1, acc);
+    slice<BF16, MI, 0>(c, j + 0, fr, acc);
+    slice<BF16, MI, 1>(c, j + 1, fr, acc);
+    slice<BF16, MI, 2>(c, j + 2, fr, acc);
+    slice<BF16, MI, 3>(c, j + 3, fr, acc);
   }
-  mma<BF16>(f1, acc);  // last step of the last slice
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  mma<BF16, MI>(fr[1], acc);  // the last slice (nk is a multiple of 4, so it sits in set 1)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the duplicate tail loads
 
-  // ---- epilogue: lane holds C[m][n + 0..3] for m = block row + lane % 32
+  // ---- epilogue: each register group holds C[m][n + 0..3]
   const int64_t ldc = p.ldc;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t m = m0 + wm * 128 + i * 32 + (lane & 31);
+  for (int i = 0; i < 128 / MI; ++i) {
+    const int64_t m = m0 + wm * 128 + i * MI + (lane % MI);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
+    for (int j = 0; j < 128 / MI; ++j) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int64_t n = n0 + wn * NB * 32 + j * 32 + 8 * g + 4 * (lane >> 5);
-        const f32x16 &a = acc[i][j];
+      for (int g = 0; g < (MI == 32 ? 4 : 1); ++g) {
+        // 32x32: group g covers columns 8g + 4*(lane/32) .. +3; 16x16: 4*(lane/16) .. +3
+        const int64_t n = n0 + wn * 128 + j * MI + (MI == 32 ? 8 * g + 4 * (lane >> 5) : 4 * (lane >> 4));
+        float v0, v1, v2, v3;
+        if constexpr (MI == 32) {
+          v0 = acc.v[i][j][4 * g + 0];
+          v1 = acc.v[i][j][4 * g + 1];
+          v2 = acc.v[i][j][4 * g + 2];
+          v3 = acc.v[i][j][4 * g + 3];
+        } else {
+          v0 = acc.v[i][j][0];
+          v1 = acc.v[i][j][1];
+          v2 = acc.v[i][j][2];
+          v3 = acc.v[i][j][3];
+        }
         if constexpr (OUT_F16) {
           uint16_t *C = (uint16_t *)p.C + z * p.sC;
           u32x2 v;
-          v[0] = (uint32_t)f32_to_f16_bits(a[4 * g + 0]) | ((uint32_t)f32_to_f16_bits(a[4 * g + 1]) << 16);
-          v[1] = (uint32_t)f32_to_f16_bits(a[4 * g + 2]) | ((uint32_t)f32_to_f16_bits(a[4 * g + 3]) << 16);
+          v[0] = (uint32_t)f32_to_f16_bits(v0) | ((uint32_t)f32_to_f16_bits(v1) << 16);
+          v[1] = (uint32_t)f32_to_f16_bits(v2) | ((uint32_t)f32_to_f16_bits(v3) << 16);
           *reinterpret_cast<u32x2 *>(C + m * ldc + n) = v;
         } else {
           float *C = (float *)p.C + z * p.sC;
-          f32x4 v = {a[4 * g + 0], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
-          *reinterpret_cast<f32x4 *>(C + m * ldc + n) = v;
+          *reinterpret_cast<f32x4 *>(C + m * ldc + n) = f32x4{v0, v1, v2, v3};
         }
       }
     }
   }
 }
 
-template <bool BF16, bool OUT_F16, int NW>
+template <bool BF16, bool OUT_F16, int MI>
 hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
   const int64_t tiles = (int64_t)base.tiles_m * base.tiles_n;
   for (int64_t z0 = 0; z0 < batch; z0 += kMaxGridY) {
     KernelArgs a = base;
     a.z0 = (int32_t)z0;
     const int64_t nz = batch - z0 < kMaxGridY ? batch - z0 : kMaxGridY;
-    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT_F16, NW>), dim3((unsigned)tiles, (unsigned)nz), dim3(NW * 64), 0,
+    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT_F16, MI>), dim3((unsigned)tiles, (unsigned)nz), dim3(256), 0,
                        stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -306,11 +348,11 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
   return hipSuccess;
 }
 
-template <int NW>
-hipError_t launch_nw(const Problem &p, const KernelArgs &a, hipStream_t stream) {
+template <int MI>
+hipError_t launch_mi(const Problem &p, const KernelArgs &a, hipStream_t stream) {
   if (p.in_bf16)
-    return p.out_f16 ? launch_t<true, true, NW>(a, p.batch, stream) : launch_t<true, false, NW>(a, p.batch, stream);
-  return p.out_f16 ? launch_t<false, true, NW>(a, p.batch, stream) : launch_t<false, false, NW>(a, p.batch, stream);
+    return p.out_f16 ? launch_t<true, true, MI>(a, p.batch, stream) : launch_t<true, false, MI>(a, p.batch, stream);
+  return p.out_f16 ? launch_t<false, true, MI>(a, p.batch, stream) : launch_t<false, false, MI>(a, p.batch, stream);
 }
 
 }  // namespace
@@ -327,7 +369,7 @@ bool tile_supports(const Problem &p) {
   return true;
 }
 
-hipError_t launch_tile(const Problem &p, int waves, hipStream_t stream) {
+hipError_t launch_tile(const Problem &p, int mi, hipStream_t stream) {
   KernelArgs a{};
   a.A = p.A;
   a.B = p.B;
@@ -343,9 +385,9 @@ hipError_t launch_tile(const Problem &p, int waves, hipStream_t stream) {
   a.sC = p.sC;
   a.tiles_m = (int32_t)(p.M / BM);
   a.tiles_n = (int32_t)(p.N / BN);
-  return waves == 8 ? launch_nw<8>(p, a, stream) : launch_nw<4>(p, a, stream);
+  return mi == 16 ? launch_mi<16>(p, a, stream) : launch_mi<32>(p, a, stream);
 }
 
-const char *tile_name(int waves) { return waves == 8 ? "tile_256x256x32_s4_w8" : "tile_256x256x32_s4_w4"; }
+const char *tile_name(int mi) { return mi == 16 ? "tile_256x256x32_mi16" : "tile_256x256x32_mi32"; }
 
 }  // namespace tsm
