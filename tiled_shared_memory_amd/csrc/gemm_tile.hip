@@ -16,9 +16,8 @@
 // write straight into LDS (no VGPR round trip), through a ring of 4 stages
 // (128 KiB of the CU's 160 KiB): a slice is requested three slices before it
 // is multiplied, which covers HBM latency at full MFMA rate.  Each slice row
-// is 64 bytes = 4 chunks of 16 bytes; chunk c of row r sits at position
-// c ^ ((r / 4) % 4), so the 16 rows a quarter-wave reads at once fall into 16
-// distinct 4-bank groups of gfx950's 64 LDS banks.  One wave-wide load fills
+// is 64 bytes = 4 chunks of 16 bytes, XOR-swizzled per row (see swz) so that
+// fragment reads are free of bank conflicts.  One wave-wide load fills
 // 16 whole rows (1 KiB), each lane fetching the global chunk that belongs at
 // its LDS slot.
 //
@@ -83,10 +82,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// LDS position of 16-byte chunk c of slice row r: chunk c ^ ((r / 4) % 4) of
-// the row.  The 16 rows a quarter-wave reads in one cycle then cover all 16
-// four-bank groups of gfx950's 64 banks.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 2) & 3); }
+// LDS position of 16-byte chunk c of slice row r: chunk c ^ (3 * bit 3 of r).
+// gfx950 serves a 64-lane 16-byte read in two halves of 32 lanes (lanes 0-15
+// with 32-47, then 16-31 with 48-63) across 512 bytes of banks; with 64-byte
+// rows, rows r and r + 8 share a bank window, and this XOR sends their chunks
+// to complementary positions, so both fragment shapes (32 rows x 2 chunks,
+// 16 rows x 2 chunks per half) read without bank conflicts.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r >> 3) & 1) * 3); }
 
 // Per-lane byte offsets, relative to the slice origin, of the chunks a lane
 // fetches for one 256 x 32 operand slice (rows ld elements apart).  One
@@ -129,7 +131,7 @@ template <int MI>
 __device__ __forceinline__ void read_frags(const char *sa, const char *sb, Frags<MI> &f, int wm, int wn, int lane) {
   constexpr int NA = Frags<MI>::NA;
   // lane reads row (lane % MI) of each block, K chunk (lane / MI) of the step;
-  // block rows are multiples of 16, so row % 16 == lane % 16
+  // block rows are multiples of 16, so the swizzle sees row % 16 == lane % 16
   const int row = lane % MI;
 #pragma unroll
   for (int s = 0; s < Frags<MI>::NSTEP; ++s) {
