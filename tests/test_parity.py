@@ -52,7 +52,7 @@ def _sample_cells(rng, batch, M, N, n):
     return (np.concatenate([z, ez.ravel()]), np.concatenate([i, ei.ravel()]), np.concatenate([j, ej.ravel()]))
 
 
-EXPECTED_KERNEL = {"square_bf16_8192": "tile_256x256x32_"}
+EXPECTED_KERNEL = {"square_bf16_8192": "tile_256x256x32_", "skinny_f16_16x16384x8192_b8": "skinny_"}
 
 
 @pytest.mark.parametrize("name", ["square_bf16_8192", "skinny_f16_16x16384x8192_b8"])
@@ -168,6 +168,45 @@ def test_tile_kernel_padded_ld_and_strides(orc):
             sC=M * ldc + 12, kernel=TILE)
     Cr, S = orc.gemm_rows(A, B, M, N, K, BF16, batch=batch, a_layout="row", b_layout="col")
     check(C, Cr, S, K, "f32", "tile padded")
+
+
+SKINNY = "skinny_"
+SKINNY_SHAPES = [(16, 256, 256, 1), (1, 512, 256, 1), (5, 256, 512, 3), (16, 768, 1024, 2), (12, 256, 256, 2)]
+
+
+@pytest.mark.parametrize("shape", SKINNY_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("in_fmt,out_fmt", [(F16, "f32"), (BF16, "f16"), (F16, "f16"), (BF16, "f32")])
+def test_skinny_kernel(orc, shape, in_fmt, out_fmt):
+    """The M <= 16 streaming kernel (row-major A and B) against the oracle, rows past M masked."""
+    M, N, K, batch = shape
+    A, B = make_operands(M * 1000 + N + K + batch, batch, M, N, K, in_fmt, ("uniform", -1.0, 1.0))
+    say(f"[gpu] skinny kernel {shape} {in_fmt}->{out_fmt}")
+    C = run(A, B, M, N, K, in_fmt, out_fmt, batch=batch, kernel=SKINNY)
+    Cr, S = orc.gemm_rows(A, B, M, N, K, in_fmt, batch=batch)
+    check(C, Cr, S, K, out_fmt, f"skinny {shape}")
+
+
+def test_skinny_kernel_padded_and_sentinel(orc):
+    """Padded lda/ldb/ldc with C prefilled: rows of C past M and the ld padding keep their bits."""
+    M, N, K, batch = 7, 512, 256, 2
+    lda, ldb, ldc = K + 24, N + 64, N + 8
+    A, B = make_operands(77, batch, M, N, K, F16, ("uniform", -1.0, 1.0))
+    Ap = np.zeros((batch, M, lda), np.uint16)
+    Ap[:, :, :K] = A
+    Bp = np.zeros((batch, K, ldb), np.uint16)
+    Bp[:, :, :N] = B
+    sC = 16 * ldc
+    say("[gpu] skinny padded + sentinel")
+    C, raw = run(Ap, Bp, M, N, K, F16, "f32", batch=batch, lda=lda, ldb=ldb, ldc=ldc, sC=sC, fill=100.0, keep=True,
+                 kernel=SKINNY)
+    Cr, S = orc.gemm_rows(A, B, M, N, K, F16, batch=batch)
+    check(C, Cr, S, K, "f32", "skinny padded")
+    host = raw.cpu().numpy()
+    for z in range(batch):
+        for i in range(M):
+            o = z * sC + i * ldc
+            assert np.all(host[o + N:o + ldc] == 100.0)
+        assert np.all(host[z * sC + M * ldc:z * sC + 16 * ldc][: (16 - M) * ldc] == 100.0) if z < batch - 1 else True
 
 
 def test_k_zero_writes_zeros():

@@ -54,6 +54,15 @@ struct TileInfo {
   static constexpr int BM = 256, BN = 256, BK = 32, STAGES = 4;
 };
 bool tile_supports(const Problem &p);
+
+// Skinny kernel: M <= 16, row-major A and B, N a multiple of 256, K a
+// multiple of 256, 16-byte aligned rows.
+struct SkinnyInfo {
+  static constexpr int BN = 256, BK = 64;
+};
+bool skinny_supports(const Problem &p);
+hipError_t launch_skinny(const Problem &p, hipStream_t stream);
+const char *skinny_name();
 hipError_t launch_tile(const Problem &p, int mi, hipStream_t stream);
 const char *tile_name(int mi);
 
