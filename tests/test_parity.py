@@ -35,7 +35,8 @@ def test_workload_full_parity(orc, name):
     w = WORKLOADS[name]
     A, B = w.operands()
     say(f"[gpu] {name} full parity M={w.M} N={w.N} K={w.K}")
-    C = run(A, B, w.M, w.N, w.K, w.in_fmt, w.out_fmt, batch=w.batch, a_layout=w.a_layout, b_layout=w.b_layout)
+    C = run(A, B, w.M, w.N, w.K, w.in_fmt, w.out_fmt, batch=w.batch, a_layout=w.a_layout, b_layout=w.b_layout,
+            kernel=EXPECTED_KERNEL.get(name))
     Cr, S = orc.gemm_rows(A, B, w.M, w.N, w.K, w.in_fmt, batch=w.batch, a_layout=w.a_layout, b_layout=w.b_layout)
     ratio = check(C, Cr, S, w.K, w.out_fmt, name)
     say(f"[gpu] {name}: max err/bound = {ratio:.3e}")
@@ -52,7 +53,8 @@ def _sample_cells(rng, batch, M, N, n):
     return (np.concatenate([z, ez.ravel()]), np.concatenate([i, ei.ravel()]), np.concatenate([j, ej.ravel()]))
 
 
-EXPECTED_KERNEL = {"square_bf16_8192": "tile_256x256x32_", "skinny_f16_16x16384x8192_b8": "skinny_"}
+EXPECTED_KERNEL = {"square_bf16_8192": "tile_256x256x32_", "skinny_f16_16x16384x8192_b8": "skinny_",
+                   "largek_f16_256x256x8192": "splitk_"}
 
 
 @pytest.mark.parametrize("name", ["square_bf16_8192", "skinny_f16_16x16384x8192_b8"])
@@ -207,6 +209,24 @@ def test_skinny_kernel_padded_and_sentinel(orc):
             o = z * sC + i * ldc
             assert np.all(host[o + N:o + ldc] == 100.0)
         assert np.all(host[z * sC + M * ldc:z * sC + 16 * ldc][: (16 - M) * ldc] == 100.0) if z < batch - 1 else True
+
+
+SPLITK = "splitk_"
+SPLITK_SHAPES = [(16, 16, 2048, 1), (256, 256, 8192, 1), (48, 80, 4096, 2), (128, 32, 2048, 3)]
+
+
+@pytest.mark.parametrize("shape", SPLITK_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("in_fmt,out_fmt", [(F16, "f32"), (BF16, "f16"), (BF16, "f32")])
+def test_splitk_kernel(orc, shape, in_fmt, out_fmt):
+    """The deep-K kernel (16 x 16 tiles, K split over 16 waves, fixed-order LDS reduction) against the oracle."""
+    M, N, K, batch = shape
+    A, B = make_operands(M + 7 * N + K + batch, batch, M, N, K, in_fmt, ("uniform", -1.0, 1.0))
+    say(f"[gpu] splitk kernel {shape} {in_fmt}->{out_fmt}")
+    C = run(A, B, M, N, K, in_fmt, out_fmt, batch=batch, kernel=SPLITK)
+    Cr, S = orc.gemm_rows(A, B, M, N, K, in_fmt, batch=batch)
+    check(C, Cr, S, K, out_fmt, f"splitk {shape}")
+    # deterministic: the reduction order is fixed
+    assert np.array_equal(run(A, B, M, N, K, in_fmt, out_fmt, batch=batch, kernel=SPLITK), C)
 
 
 def test_k_zero_writes_zeros():

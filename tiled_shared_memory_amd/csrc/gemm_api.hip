@@ -43,7 +43,7 @@ bool ranges_overlap(const void *p, int64_t pbytes, const void *q, int64_t qbytes
   return a < b + (uintptr_t)qbytes && b < a + (uintptr_t)pbytes;
 }
 
-enum class Kernel { None, Masked8, Masked1, Tile32, Tile16, Skinny };
+enum class Kernel { None, Masked8, Masked1, Tile32, Tile16, Skinny, SplitK };
 
 const char *kernel_name(Kernel k) {
   switch (k) {
@@ -57,6 +57,8 @@ const char *kernel_name(Kernel k) {
       return tile_name(16);
     case Kernel::Skinny:
       return skinny_name();
+    case Kernel::SplitK:
+      return splitk_name();
     default:
       return nullptr;
   }
@@ -167,6 +169,9 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
   const bool a8 = K == 0 || vec8_ok(A, p.a_col ? M : K, lda, p.sA, batch);
   const bool b8 = K == 0 || vec8_ok(B, p.b_col ? K : N, ldb, p.sB, batch);
   out->kernel = (a8 && b8) ? Kernel::Masked8 : Kernel::Masked1;
+  // few output tiles and deep K: take the parallelism from K
+  const int64_t masked_tiles = tiles * batch;
+  if (K > 0 && masked_tiles < 256 && splitk_supports(p)) out->kernel = Kernel::SplitK;
   if (K > 0 && tile_supports(p)) out->kernel = Kernel::Tile16;
   if (K > 0 && skinny_supports(p)) out->kernel = Kernel::Skinny;
 
@@ -174,14 +179,15 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
   // variant that cannot run this problem is an error, never a silent fallback.
   const char *force = getenv("TSM_GEMM_KERNEL");
   if (force && *force) {
-    const Kernel all[] = {Kernel::Masked8, Kernel::Masked1, Kernel::Tile32, Kernel::Tile16, Kernel::Skinny};
+    const Kernel all[] = {Kernel::Masked8, Kernel::Masked1, Kernel::Tile32, Kernel::Tile16, Kernel::Skinny, Kernel::SplitK};
     Kernel want = Kernel::None;
     for (Kernel k : all)
       if (strcmp(force, kernel_name(k)) == 0) want = k;
     if (want == Kernel::None) return fail(TSM_ERROR_INVALID_VALUE, "TSM_GEMM_KERNEL=%s names no kernel", force);
     const bool ok = want == Kernel::Masked1 || (want == Kernel::Masked8 && a8 && b8) ||
                     ((want == Kernel::Tile32 || want == Kernel::Tile16) && K > 0 && tile_supports(p)) ||
-                    (want == Kernel::Skinny && K > 0 && skinny_supports(p));
+                    (want == Kernel::Skinny && K > 0 && skinny_supports(p)) ||
+                    (want == Kernel::SplitK && K > 0 && splitk_supports(p));
     if (!ok) return fail(TSM_ERROR_NOT_SUPPORTED, "TSM_GEMM_KERNEL=%s cannot run this problem", force);
     out->kernel = want;
   }
@@ -208,6 +214,9 @@ int run(const Plan &pl, void *stream) {
       break;
     case Kernel::Skinny:
       e = launch_skinny(pl.p, s);
+      break;
+    case Kernel::SplitK:
+      e = launch_splitk(pl.p, s);
       break;
   }
   if (e != hipSuccess) return fail(TSM_ERROR_LAUNCH, "launch failed: %s", hipGetErrorString(e));

@@ -61,6 +61,16 @@ struct SkinnyInfo {
   static constexpr int BN = 256, BK = 64;
 };
 bool skinny_supports(const Problem &p);
+
+// Split-K kernel for small M x N and deep K: 16 x 16 tiles, K split across the
+// 16 waves of a workgroup; row-major A and B, M, N multiples of 16, K a
+// multiple of 2048.
+struct SplitKInfo {
+  static constexpr int WAVES = 16;
+};
+bool splitk_supports(const Problem &p);
+hipError_t launch_splitk(const Problem &p, hipStream_t stream);
+const char *splitk_name();
 hipError_t launch_skinny(const Problem &p, hipStream_t stream);
 const char *skinny_name();
 hipError_t launch_tile(const Problem &p, int mi, hipStream_t stream);
