@@ -138,3 +138,18 @@ def test_kernel_selection_for_the_workloads():
         assert picks[name] is not None, name
     # the ragged workload has K = 777, so rows of A are only 2-byte aligned
     assert picks["ragged_f16_1000x1500x777"].endswith("vec1")
+
+
+def test_kernel_selection_by_layout_and_shape():
+    """Aligned 256-multiples go to the large-tile kernel for both B layouts, K-contiguous B on the direct
+    variant and row-major B on the transpose-read variant; a misaligned ldb falls back to the masked kernel."""
+    B0 = 0x7E0000000000
+    n = 1024
+    col = tsm.tsm_gemm_kernel_name(n, n, n, A0, n, 0, 0, B0, n, 1, 0, C0, n, 0, 1, 2)
+    row = tsm.tsm_gemm_kernel_name(n, n, n, A0, n, 0, 0, B0, n, 0, 0, C0, n, 0, 1, 2)
+    assert col == "tile_256x256x64_mi16"
+    assert row == "tile_256x256x32_mi16_nn"
+    odd = tsm.tsm_gemm_kernel_name(n, n, n, A0, n, 0, 0, B0, n + 4, 0, 0, C0, n, 0, 1, 2)
+    assert odd.startswith("masked_")
+    # K not a multiple of 128: masked
+    assert tsm.tsm_gemm_kernel_name(n, n, n + 64, A0, n + 64, 0, 0, B0, n, 0, 0, C0, n, 0, 1, 2).startswith("masked_")

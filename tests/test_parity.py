@@ -53,7 +53,7 @@ def _sample_cells(rng, batch, M, N, n):
     return (np.concatenate([z, ez.ravel()]), np.concatenate([i, ei.ravel()]), np.concatenate([j, ej.ravel()]))
 
 
-EXPECTED_KERNEL = {"square_bf16_8192": "tile_256x256x32_", "skinny_f16_16x16384x8192_b8": "skinny_",
+EXPECTED_KERNEL = {"square_bf16_8192": "tile_256x256x", "skinny_f16_16x16384x8192_b8": "skinny_",
                    "largek_f16_256x256x8192": "splitk_"}
 
 
@@ -140,24 +140,61 @@ def test_ldc_padding_untouched_and_inside_overwritten():
         torch.cuda.synchronize()
 
 
-TILE = "tile_256x256x32_"
+TILE = "tile_256x256x"
 TILE_SHAPES = [(256, 256, 128, 1), (512, 768, 384, 1), (256, 512, 1024, 3), (768, 256, 256, 2)]
+# every large-tile variant with the B layout it reads
+TILE_VARIANTS = [("tile_256x256x32_mi32", "col"), ("tile_256x256x32_mi16", "col"), ("tile_256x256x32_mi16_nn", "row"),
+                 ("tile_256x256x64_mi16", "col"), ("tile_256x256x64_mi16_nn", "row")]
 
 
 @pytest.mark.parametrize("shape", TILE_SHAPES, ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("in_fmt,out_fmt", [(BF16, "f16"), (F16, "f32"), (BF16, "f32"), (F16, "f16")])
-def test_tile_kernel(orc, shape, in_fmt, out_fmt):
-    """The large-tile kernel (A row-major, B column-major, 256-multiples, K % 128 == 0) against the oracle."""
+@pytest.mark.parametrize("variant,b_layout", TILE_VARIANTS, ids=[v for v, _ in TILE_VARIANTS])
+def test_tile_kernel(orc, monkeypatch, shape, in_fmt, out_fmt, variant, b_layout):
+    """Each large-tile variant (A row-major, 256-multiples, K % 128 == 0; 32- or 64-deep K slabs; B K-contiguous
+    or row-major, the latter through the LDS transpose reads) against the oracle."""
+    monkeypatch.setenv("TSM_GEMM_KERNEL", variant)
     M, N, K, batch = shape
-    A, B = make_operands(M + N + K + batch, batch, M, N, K, in_fmt, ("uniform", -1.0, 1.0), "row", "col")
-    say(f"[gpu] tile kernel {shape} {in_fmt}->{out_fmt}")
-    C = run(A, B, M, N, K, in_fmt, out_fmt, batch=batch, a_layout="row", b_layout="col", kernel=TILE)
-    Cr, S = orc.gemm_rows(A, B, M, N, K, in_fmt, batch=batch, a_layout="row", b_layout="col")
-    check(C, Cr, S, K, out_fmt, f"tile {shape}")
+    A, B = make_operands(M + N + K + batch, batch, M, N, K, in_fmt, ("uniform", -1.0, 1.0), "row", b_layout)
+    say(f"[gpu] {variant} {shape} {in_fmt}->{out_fmt}")
+    C = run(A, B, M, N, K, in_fmt, out_fmt, batch=batch, a_layout="row", b_layout=b_layout, kernel=variant)
+    Cr, S = orc.gemm_rows(A, B, M, N, K, in_fmt, batch=batch, a_layout="row", b_layout=b_layout)
+    check(C, Cr, S, K, out_fmt, f"{variant} {shape}")
 
 
-def test_tile_kernel_padded_ld_and_strides(orc):
+@pytest.mark.parametrize("variant", ["tile_256x256x32_mi16_nn", "tile_256x256x64_mi16_nn"])
+def test_tile_nn_padded_ld_and_strides(orc, monkeypatch, variant):
+    """Row-major B with padded ldb (rows of N + 8) and batch strides larger than the matrices."""
+    monkeypatch.setenv("TSM_GEMM_KERNEL", variant)
+    M, N, K, batch = 512, 256, 384, 2
+    lda, ldb, ldc = K + 8, N + 8, N + 12
+    A, B = make_operands(98, batch, M, N, K, F16, ("uniform", -1.0, 1.0), "row", "row")
+    Ap = np.zeros((batch, M, lda), np.uint16)
+    Ap[:, :, :K] = A
+    Bp = np.zeros((batch, K + 3, ldb), np.uint16)
+    Bp[:, :K, :N] = B
+    say(f"[gpu] {variant} padded")
+    C = run(Ap, Bp, M, N, K, F16, "f16", batch=batch, lda=lda, ldb=ldb, ldc=ldc, sC=M * ldc + 4, kernel=variant)
+    Cr, S = orc.gemm_rows(A, B, M, N, K, F16, batch=batch)
+    check(C, Cr, S, K, "f16", "tile nn padded")
+
+
+def test_tile_nn_large_sampled(orc):
+    """A 4096 x 4096 x 4096 row-major product on the default transpose-read kernel, checked on sampled cells."""
+    M = N = K = 4096
+    A, B = make_operands(97, 1, M, N, K, BF16, ("normal", 0.0, 1.0 / 64.0), "row", "row")
+    say("[gpu] tile nn 4096^3 sampled")
+    C = run(A, B, M, N, K, BF16, "f32", kernel=TILE)
+    rng = np.random.default_rng(11)
+    z, i, j = _sample_cells(rng, 1, M, N, 2000)
+    Cp, Sp = orc.gemm_points(A, B, M, N, K, BF16, z, i, j)
+    check(C[z, i, j], Cp, Sp, K, "f32", "tile nn 4096 sampled")
+
+
+@pytest.mark.parametrize("variant", ["tile_256x256x32_mi16", "tile_256x256x64_mi16"])
+def test_tile_kernel_padded_ld_and_strides(orc, monkeypatch, variant):
     """Padded lda/ldb/ldc and batch strides larger than the matrices, still on the tile kernel."""
+    monkeypatch.setenv("TSM_GEMM_KERNEL", variant)
     M, N, K, batch = 256, 512, 256, 2
     lda, ldb, ldc = K + 64, K + 8, N + 4
     A, B = make_operands(99, batch, M, N, K, BF16, ("uniform", -1.0, 1.0), "row", "col")
@@ -167,9 +204,9 @@ def test_tile_kernel_padded_ld_and_strides(orc):
     Bp[:, :, :K] = B
     say("[gpu] tile kernel padded")
     C = run(Ap, Bp, M, N, K, BF16, "f32", batch=batch, a_layout="row", b_layout="col", lda=lda, ldb=ldb, ldc=ldc,
-            sC=M * ldc + 12, kernel=TILE)
+            sC=M * ldc + 12, kernel=variant)
     Cr, S = orc.gemm_rows(A, B, M, N, K, BF16, batch=batch, a_layout="row", b_layout="col")
-    check(C, Cr, S, K, "f32", "tile padded")
+    check(C, Cr, S, K, "f32", f"{variant} padded")
 
 
 SKINNY = "skinny_"

@@ -43,7 +43,7 @@ bool ranges_overlap(const void *p, int64_t pbytes, const void *q, int64_t qbytes
   return a < b + (uintptr_t)qbytes && b < a + (uintptr_t)pbytes;
 }
 
-enum class Kernel { None, Masked8, Masked1, Tile32, Tile16, Skinny, SplitK };
+enum class Kernel { None, Masked8, Masked1, Tile32, Tile16, Tile16NN, TileW, TileWNN, Skinny, SplitK };
 
 const char *kernel_name(Kernel k) {
   switch (k) {
@@ -52,9 +52,15 @@ const char *kernel_name(Kernel k) {
     case Kernel::Masked1:
       return masked_name(1);
     case Kernel::Tile32:
-      return tile_name(32);
+      return tile_name(0);
     case Kernel::Tile16:
-      return tile_name(16);
+      return tile_name(1);
+    case Kernel::Tile16NN:
+      return tile_name(2);
+    case Kernel::TileW:
+      return tile_name(3);
+    case Kernel::TileWNN:
+      return tile_name(4);
     case Kernel::Skinny:
       return skinny_name();
     case Kernel::SplitK:
@@ -172,20 +178,23 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
   // few output tiles and deep K: take the parallelism from K
   const int64_t masked_tiles = tiles * batch;
   if (K > 0 && masked_tiles < 256 && splitk_supports(p)) out->kernel = Kernel::SplitK;
-  if (K > 0 && tile_supports(p)) out->kernel = Kernel::Tile16;
+  if (K > 0 && tile_supports(p, false)) out->kernel = Kernel::TileW;
+  if (K > 0 && tile_supports(p, true)) out->kernel = Kernel::Tile16NN;
   if (K > 0 && skinny_supports(p)) out->kernel = Kernel::Skinny;
 
   // TSM_GEMM_KERNEL=<name> forces a kernel variant (tests and tuning); a
   // variant that cannot run this problem is an error, never a silent fallback.
   const char *force = getenv("TSM_GEMM_KERNEL");
   if (force && *force) {
-    const Kernel all[] = {Kernel::Masked8, Kernel::Masked1, Kernel::Tile32, Kernel::Tile16, Kernel::Skinny, Kernel::SplitK};
+    const Kernel all[] = {Kernel::Masked8, Kernel::Masked1, Kernel::Tile32, Kernel::Tile16, Kernel::Tile16NN, Kernel::TileW, Kernel::TileWNN, Kernel::Skinny, Kernel::SplitK};
     Kernel want = Kernel::None;
     for (Kernel k : all)
       if (strcmp(force, kernel_name(k)) == 0) want = k;
     if (want == Kernel::None) return fail(TSM_ERROR_INVALID_VALUE, "TSM_GEMM_KERNEL=%s names no kernel", force);
     const bool ok = want == Kernel::Masked1 || (want == Kernel::Masked8 && a8 && b8) ||
-                    ((want == Kernel::Tile32 || want == Kernel::Tile16) && K > 0 && tile_supports(p)) ||
+                    ((want == Kernel::Tile32 || want == Kernel::Tile16 || want == Kernel::TileW) && K > 0 &&
+                     tile_supports(p, false)) ||
+                    ((want == Kernel::Tile16NN || want == Kernel::TileWNN) && K > 0 && tile_supports(p, true)) ||
                     (want == Kernel::Skinny && K > 0 && skinny_supports(p)) ||
                     (want == Kernel::SplitK && K > 0 && splitk_supports(p));
     if (!ok) return fail(TSM_ERROR_NOT_SUPPORTED, "TSM_GEMM_KERNEL=%s cannot run this problem", force);
@@ -207,10 +216,19 @@ int run(const Plan &pl, void *stream) {
       e = launch_masked(pl.p, 1, s);
       break;
     case Kernel::Tile32:
-      e = launch_tile(pl.p, 32, s);
+      e = launch_tile(pl.p, 0, s);
       break;
     case Kernel::Tile16:
-      e = launch_tile(pl.p, 16, s);
+      e = launch_tile(pl.p, 1, s);
+      break;
+    case Kernel::Tile16NN:
+      e = launch_tile(pl.p, 2, s);
+      break;
+    case Kernel::TileW:
+      e = launch_tile(pl.p, 3, s);
+      break;
+    case Kernel::TileWNN:
+      e = launch_tile(pl.p, 4, s);
       break;
     case Kernel::Skinny:
       e = launch_skinny(pl.p, s);

@@ -47,13 +47,15 @@ struct MaskedInfo {
 hipError_t launch_masked(const Problem &p, int vec, hipStream_t stream);
 const char *masked_name(int vec);
 
-// Large-tile kernel: both operands K-contiguous (A row-major, B column-major),
-// M, N multiples of 256, K a multiple of 128, 16-byte aligned rows.
-// Two variants by MFMA shape: mi = 32 (32x32x16) or mi = 16 (16x16x32).
+// Large-tile kernel: A row-major, B either layout, M, N multiples of 256, K a
+// multiple of 128, 16-byte aligned rows.
+// Variants (K slab depth, MFMA shape, B layout): 0 = 32-deep, 32x32x16,
+// column-major B; 1 = 32-deep, 16x16x32, column-major; 2 = 32-deep, 16x16x32,
+// row-major B (transposed out of LDS); 3, 4 = as 1, 2 with 64-deep slabs.
 struct TileInfo {
   static constexpr int BM = 256, BN = 256, BK = 32, STAGES = 4;
 };
-bool tile_supports(const Problem &p);
+bool tile_supports(const Problem &p, bool b_row);
 
 // Skinny kernel: M <= 16, row-major A and B, N a multiple of 256, K a
 // multiple of 256, 16-byte aligned rows.
@@ -73,7 +75,7 @@ hipError_t launch_splitk(const Problem &p, hipStream_t stream);
 const char *splitk_name();
 hipError_t launch_skinny(const Problem &p, hipStream_t stream);
 const char *skinny_name();
-hipError_t launch_tile(const Problem &p, int mi, hipStream_t stream);
-const char *tile_name(int mi);
+hipError_t launch_tile(const Problem &p, int variant, hipStream_t stream);
+const char *tile_name(int variant);
 
 }  // namespace tsm

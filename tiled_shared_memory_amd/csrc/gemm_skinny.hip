@@ -19,9 +19,9 @@
 //    the problem and L2-resident) rides along: each stage also holds the
 //    16 x 64 A slice (2 KiB, filled with 4-byte buffer loads into LDS), so
 //    the only waits on loads are the explicit per-slice ones.
-//  * LDS rows are 512 bytes (32 chunks of 16 bytes); chunk c of row r sits
-//    at position c ^ (2 * (r % 16)), which spreads the 16 rows a transpose
-//    read touches over distinct bank positions.
+//  * LDS rows are 512 bytes (32 chunks of 16 bytes), XOR-swizzled per row
+//    (see swz) so that the 16 rows one transpose read touches land on 32
+//    distinct 16-byte positions.
 //
 // Strided batches use gridDim.y and 64-bit problem offsets (Intel XPU Triton
 // README, "Avoid int32 Overflow": the B block of the 8-problem workload spans
@@ -70,8 +70,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Swizzled position of 16-byte chunk c (0..31) of slice row r.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r & 15) << 1); }
+// Swizzled position of 16-byte chunk c (0..31) of slice row r.  One
+// transpose read covers rows {0..3, 8..11, 16..19, 24..27} + 4h (+ 32t) and a
+// 32-byte column block (chunks 2b, 2b+1); the XOR maps those 16 rows to 16
+// distinct even offsets, so the 32 chunks read land on 32 distinct positions.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (2 * ((r & 3) | ((r >> 1) & 12))); }
 
 struct Ctx {
   __amdgpu_buffer_rsrc_t rb, ra;

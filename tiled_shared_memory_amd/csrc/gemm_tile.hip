@@ -1,30 +1,37 @@
-// Large-tile MFMA GEMM for gfx950: operands contiguous along K, full tiles.
+// Large-tile MFMA GEMM for gfx950: A row-major, full tiles.
 //
-// This is the fast path for A row-major and B column-major (every K slice of
-// both operands is a set of contiguous 64-byte row pieces), M and N multiples
-// of 256 and K a multiple of 128, all rows 16-byte aligned.  The host routes
-// every other problem to the masked kernel.
+// This is the fast path for M and N multiples of 256, K a multiple of 128 and
+// all rows 16-byte aligned, with B either K-contiguous (column-major) or
+// row-major.  The host routes every other problem to the masked kernel.
 //
 // Blocking ("The PTSS Cliff", sections "The Idea: Stage in SLM, Tile K" and
 // "Choosing K_TILE"): a 256-thread workgroup owns a 256 x 256 tile of C and
-// walks K in slices of 32.  Each wave owns a 128 x 128 quadrant as 4 x 4
-// blocks of v_mfma_f32_32x32x16, i.e. 256 float32 accumulators per lane, a
-// budget fixed by the tile alone; the live operand fragments are two 16-deep
-// steps (64 registers).  K never enters the register budget.
+// walks K in slabs.  Each wave owns a 128 x 128 quadrant, i.e. 256 float32
+// accumulators per lane (8 x 8 blocks of v_mfma_f32_16x16x32, or 4 x 4 of
+// v_mfma_f32_32x32x16), a budget fixed by the tile alone; the live operand
+// fragments are two 32-deep sub-slices (128 registers).  K never enters the
+// register budget.
 //
-// Staging: operand slices (2 x 16 KiB) go global -> LDS with buffer loads that
-// write straight into LDS (no VGPR round trip), through a ring of 4 stages
-// (128 KiB of the CU's 160 KiB): a slice is requested three slices before it
-// is multiplied, which covers HBM latency at full MFMA rate.  Each slice row
-// is 64 bytes = 4 chunks of 16 bytes, XOR-swizzled per row (see swz) so that
-// fragment reads are free of bank conflicts.  One wave-wide load fills
-// 16 whole rows (1 KiB), each lane fetching the global chunk that belongs at
-// its LDS slot.
+// Staging: operand slabs go global -> LDS with buffer loads that write
+// straight into LDS (no VGPR round trip); one wave-wide load fills 1 KiB of
+// LDS, each lane fetching the global chunk that belongs at its LDS slot.  Rows
+// are XOR-swizzled in 16-byte chunks (see swz, swz_row) so that fragment reads
+// are free of bank conflicts.  Two ring shapes, both 128 KiB of the CU's
+// 160 KiB:
+//  * 32-deep slices, 4 stages: a slice is requested three slices before it is
+//    multiplied.  K-contiguous rows are 64 bytes.
+//  * 64-deep slabs, 2 stages: a slab is requested one slab (two 32-deep
+//    sub-slices) before use.  K-contiguous rows are 128 bytes, so every L2
+//    request carries a whole 128-byte line: half the requests of 64-byte rows
+//    for the same bytes, which is what limits the 32-deep ring on K-contiguous
+//    operands.
+// Row-major B slices are 256 columns wide (512-byte rows); the B operand is
+// transposed on its way out of LDS by ds_read_b64_tr_b16.
 //
-// Per slice: wait for the slice and a workgroup barrier, read the first
-// step's fragments, refill the freed stage, run the previous slice's last
-// step (deferred so it covers the fragment-read latency), read the second
-// step's fragments, run the first step.
+// Per 32-deep sub-slice: (at a slab boundary) wait for the slab and a
+// workgroup barrier, then refill the freed stage; read the sub-slice's
+// fragments into one register set while the previous sub-slice's MFMAs run
+// from the other, reads and loads interleaved with the MFMAs.
 //
 // Tile order: workgroups are dealt to the 8 XCDs round-robin, so consecutive
 // tile indices are first regrouped per XCD, then ordered in groups of 8 tile
@@ -50,6 +57,9 @@ constexpr int TILE_BYTES = BM * ROW_BYTES;    // 16 KiB per operand slice
 constexpr int GROUP_M = 8;
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 // The LDS ring: one array per stage and operand, so that the compiler can tell
 // the slice in flight from the one being read.
@@ -57,6 +67,12 @@ __shared__ __attribute__((aligned(1024))) char g_a0[TILE_BYTES], g_b0[TILE_BYTES
 __shared__ __attribute__((aligned(1024))) char g_a1[TILE_BYTES], g_b1[TILE_BYTES];
 __shared__ __attribute__((aligned(1024))) char g_a2[TILE_BYTES], g_b2[TILE_BYTES];
 __shared__ __attribute__((aligned(1024))) char g_a3[TILE_BYTES], g_b3[TILE_BYTES];
+
+// Wide variant: 64-deep slabs (128-byte rows, 32 KiB per operand), 2 stages.
+constexpr int WROW_BYTES = 128;
+constexpr int WTILE_BYTES = BM * WROW_BYTES;
+__shared__ __attribute__((aligned(1024))) char w_a0[WTILE_BYTES], w_b0[WTILE_BYTES];
+__shared__ __attribute__((aligned(1024))) char w_a1[WTILE_BYTES], w_b1[WTILE_BYTES];
 
 template <int S> struct Ring;
 template <> struct Ring<0> {
@@ -76,31 +92,74 @@ template <> struct Ring<3> {
   __device__ static char *b() { return g_b3; }
 };
 
+template <int S> struct WRing;
+template <> struct WRing<0> {
+  __device__ static char *a() { return w_a0; }
+  __device__ static char *b() { return w_b0; }
+};
+template <> struct WRing<1> {
+  __device__ static char *a() { return w_a1; }
+  __device__ static char *b() { return w_b1; }
+};
+
 // Buffer resource over `bytes` bytes starting at `base` (raw addressing,
 // dword 3 = the gfx9 default data format).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// LDS position of 16-byte chunk c of slice row r: chunk c ^ (3 * bit 3 of r).
-// gfx950 serves a 64-lane 16-byte read in two halves of 32 lanes (lanes 0-15
-// with 32-47, then 16-31 with 48-63) across 512 bytes of banks; with 64-byte
-// rows, rows r and r + 8 share a bank window, and this XOR sends their chunks
-// to complementary positions, so both fragment shapes (32 rows x 2 chunks,
-// 16 rows x 2 chunks per half) read without bank conflicts.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r >> 3) & 1) * 3); }
+// LDS position of 16-byte chunk c of row r of a K-contiguous slab, KB = slab
+// depth / 32.  gfx950 serves a 64-lane 16-byte read in two halves of 32 lanes
+// (lanes 0-15 with 32-47, then 16-31 with 48-63) across 512 bytes of banks.
+//  KB = 1 (64-byte rows): rows r and r + 8 share a bank window; c ^ (3 * bit 3
+//    of r) sends their chunks to complementary positions, so both fragment
+//    shapes (32 rows x 2 chunks, 16 rows x 2 chunks per half) are conflict-free.
+//  KB = 2 (128-byte rows): rows r, r + 4, r + 8, r + 12 share a window; the
+//    XOR value 0, 3, 5, 6 for (r / 4) % 4 keeps 16 rows x chunks {c, c + 2}
+//    (and {c, c + 1}, should the halves be lanes 0-31 and 32-63) on 32
+//    distinct positions.
+template <int KB>
+__device__ __forceinline__ int swz(int r, int c) {
+  if constexpr (KB == 1) {
+    return c ^ (((r >> 3) & 1) * 3);
+  } else {
+    const int t = (r >> 2) & 3;
+    return c ^ (2 * t + ((t ^ (t >> 1)) & 1));
+  }
+}
 
-// Per-lane byte offsets, relative to the slice origin, of the chunks a lane
-// fetches for one 256 x 32 operand slice (rows ld elements apart).  One
-// wave-wide load fills 16 whole rows (1 KiB): lane l writes LDS slot l, i.e.
-// row l / 4 of its group at position l % 4, so it fetches the chunk whose
-// swizzled position that is.
+// Row-major B: a slice is 32 rows of k, 256 columns (512 bytes); position of
+// 16-byte chunk c (0..31) of row r.  One transpose read covers rows
+// {0..3, 8..11, 16..19, 24..27} + 4h and a 32-byte column block; the XOR
+// sends those 16 rows to 16 distinct even offsets (32 distinct positions).
+__device__ __forceinline__ int swz_row(int r, int c) { return c ^ (2 * ((r & 3) | ((r >> 1) & 12))); }
+
+// Per-lane byte offsets of the chunks a lane fetches for one row-major B
+// slice: wave-load g of wave w fills rows 2*(w*LOADS+g) + lane/32, position
+// lane % 32, i.e. the chunk whose swizzled position that is.
 template <int LOADS>
-__device__ __forceinline__ void slice_offsets(uint32_t (&off)[LOADS], int64_t ld, int wave, int lane) {
-  const int r_in = lane >> 2;
-  const int c = swz(r_in, lane & 3);  // swz is an involution in its chunk argument
+__device__ __forceinline__ void slice_offsets_row(uint32_t (&off)[LOADS], int64_t ld, int wave, int lane) {
 #pragma unroll
-  for (int g = 0; g < LOADS; ++g) off[g] = (uint32_t)(((wave * LOADS + g) * 16 + r_in) * ld + c * 8) * 2u;
+  for (int g = 0; g < LOADS; ++g) {
+    const int r = 2 * (wave * LOADS + g) + (lane >> 5);
+    off[g] = (uint32_t)(r * ld + swz_row(r, lane & 31) * 8) * 2u;
+  }
+}
+
+// Per-lane byte offsets, relative to the slab origin, of the chunks a lane
+// fetches for one 256 x 32KB K-contiguous operand slab (rows ld elements
+// apart).  One wave-wide load fills 1 KiB = 16 / KB whole rows: lane l writes
+// LDS slot l, i.e. row l / (4 KB) of its group at position l % (4 KB), so it
+// fetches the chunk whose swizzled position that is (swz is an involution in
+// its chunk argument).
+template <int LOADS, int KB>
+__device__ __forceinline__ void slice_offsets(uint32_t (&off)[LOADS], int64_t ld, int wave, int lane) {
+  constexpr int CPR = 4 * KB;  // chunks per row
+#pragma unroll
+  for (int g = 0; g < LOADS; ++g) {
+    const int r = (wave * LOADS + g) * (64 / CPR) + lane / CPR;
+    off[g] = (uint32_t)(r * ld + swz<KB>(r, lane % CPR) * 8) * 2u;
+  }
 }
 
 // Asynchronous copy of one operand slice into LDS: 16 buffer loads shared by
@@ -127,21 +186,44 @@ struct Frags {
   u32x4 a[NSTEP][NA], b[NSTEP][NA];
 };
 
-template <int MI>
+// Fragments of sub-slice U (k = 32U .. 32U + 31) of a slab of depth 32 KB.
+template <int MI, bool BROW, int KB, int U>
 __device__ __forceinline__ void read_frags(const char *sa, const char *sb, Frags<MI> &f, int wm, int wn, int lane) {
   constexpr int NA = Frags<MI>::NA;
+  constexpr int RB = 64 * KB;  // bytes per K-contiguous row
+  static_assert(!BROW || MI == 16, "row-major B is read with 16x16x32 operands");
+  static_assert(KB == 1 || MI == 16, "64-deep slabs are read with 16x16x32 operands");
   // lane reads row (lane % MI) of each block, K chunk (lane / MI) of the step;
   // block rows are multiples of 16, so the swizzle sees row % 16 == lane % 16
   const int row = lane % MI;
 #pragma unroll
   for (int s = 0; s < Frags<MI>::NSTEP; ++s) {
-    const int chunk = swz(lane, s * (4 / Frags<MI>::NSTEP) + lane / MI) * 16;
+    const int chunk = swz<KB>(lane, 4 * U + s * (4 / Frags<MI>::NSTEP) + lane / MI) * 16;
 #pragma unroll
     for (int i = 0; i < NA; ++i)
-      f.a[s][i] = *reinterpret_cast<const u32x4 *>(sa + (wm * 128 + i * MI + row) * ROW_BYTES + chunk);
+      f.a[s][i] = *reinterpret_cast<const u32x4 *>(sa + (wm * 128 + i * MI + row) * RB + chunk);
+    if constexpr (!BROW) {
 #pragma unroll
-    for (int j = 0; j < NA; ++j)
-      f.b[s][j] = *reinterpret_cast<const u32x4 *>(sb + (wn * 128 + j * MI + row) * ROW_BYTES + chunk);
+      for (int j = 0; j < NA; ++j)
+        f.b[s][j] = *reinterpret_cast<const u32x4 *>(sb + (wn * 128 + j * MI + row) * RB + chunk);
+    } else {
+      // B operand of 16x16x32 from row-major B: lane needs B[8*(lane/16) .. +7][column lane % 16]
+      // of its block; two ds_read_b64_tr_b16, each 4 rows deep (in each 16-lane group,
+      // lane j points at row 4h + j/4 of the group's 8 rows, columns 4*(j%4) .. +3)
+#pragma unroll
+      for (int j = 0; j < NA; ++j) {
+        const int col = wn * 128 + j * 16 + 4 * (lane & 3);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int r = 32 * U + 8 * (lane >> 4) + 4 * h + ((lane & 15) >> 2);
+          const int off = r * 512 + swz_row(r, col >> 3) * 16 + (col & 7) * 2;
+          const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)((lds_char *)sb + off));
+          const u32x2 d = __builtin_bit_cast(u32x2, v);
+          f.b[s][j][2 * h] = d[0];
+          f.b[s][j][2 * h + 1] = d[1];
+        }
+      }
+    }
   }
 }
 
@@ -177,18 +259,22 @@ __device__ __forceinline__ void mma(const Frags<MI> &f, Acc<MI> &acc) {
 
 // Scheduling classes of __builtin_amdgcn_sched_group_barrier.
 constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100;
-constexpr int LOADS = 4;  // 1 KiB wave-loads per operand slice per wave
+constexpr int LOADS = 4;  // 1 KiB wave-loads per operand slice per wave (8 per 64-deep slab)
 
-struct Ctx {
+template <int L>
+struct CtxT {
   __amdgpu_buffer_rsrc_t ra, rb;
-  uint32_t offA[LOADS], offB[LOADS];
+  uint32_t offA[L], offB[L];
+  uint32_t kstepB;  // bytes between consecutive slabs of B (row bytes if K-contiguous, 32 KB rows if row-major)
   int nk, wave, wm, wn, lane;
 };
+using Ctx = CtxT<LOADS>;
+using CtxW = CtxT<2 * LOADS>;
 
 // Slice j, resident in stage S: after its barrier, read all of its fragments
 // into one register set while the MFMAs of slice j-1 run from the other set,
 // and refill the stage that slice j-1 freed with slice j+3.
-template <bool BF16, int MI, int S>
+template <bool BF16, int MI, bool BROW, int S>
 __device__ __forceinline__ void slice(Ctx &c, int j, Frags<MI> (&fr)[2], Acc<MI> &acc) {
   // Keep every MFMA of the previous slice above this point: sinking them past
   // the fragment reads below would need a third fragment register set.
@@ -199,32 +285,69 @@ __device__ __forceinline__ void slice(Ctx &c, int j, Frags<MI> (&fr)[2], Acc<MI>
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * 2 * LOADS) : "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  read_frags<MI>(Ring<S>::a(), Ring<S>::b(), fr[S & 1], c.wm, c.wn, c.lane);
+  read_frags<MI, BROW, 1, 0>(Ring<S>::a(), Ring<S>::b(), fr[S & 1], c.wm, c.wn, c.lane);
   // the last slice again near the end keeps the load count per slice uniform
   const int next = min(j + NS - 1, c.nk - 1);
   issue<LOADS>(c.ra, c.offA, (uint32_t)next * ROW_BYTES, Ring<(S + NS - 1) % NS>::a(), c.wave);
-  issue<LOADS>(c.rb, c.offB, (uint32_t)next * ROW_BYTES, Ring<(S + NS - 1) % NS>::b(), c.wave);
+  issue<LOADS>(c.rb, c.offB, (uint32_t)next * c.kstepB, Ring<(S + NS - 1) % NS>::b(), c.wave);
   mma<BF16, MI>(fr[(S & 1) ^ 1], acc);  // slice j-1
   // schedule: one fragment read or load after every other MFMA, spread over
   // the whole slice (bursts of memory instructions stall the in-order wave
   // and with it the MFMA pipe)
   constexpr int NMFMA = MI == 32 ? 32 : 64;
-  constexpr int G = NMFMA / 8;  // MFMAs per group of 2 reads + 1 load
+  constexpr int G = NMFMA / 8;          // MFMAs per group of reads + 1 load
+  constexpr int R = BROW ? 3 : 2;       // reads per group: 8 A reads + (16 or 8) B reads over 8 groups
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, G / 4, 0);
-    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, R - R / 2, 0);
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, G / 4, 0);
     __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, G / 4, 0);
-    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, R / 2, 0);
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, G / 4, 0);
   }
 }
 
-template <bool BF16, bool OUT_F16, int MI>
+// Wide variant, sub-slice U of slab j (resident in stage S): U = 0 waits for
+// the slab and the barrier, reads sub-slice 0's fragments and refills the
+// other stage (freed by that barrier) with slab j+1 while the previous
+// sub-slice's MFMAs run; U = 1 only reads and multiplies.  A slab is thus
+// requested one slab (two sub-slices) before it is used.
+template <bool BF16, bool BROW, int S, int U>
+__device__ __forceinline__ void substep_w(CtxW &c, int j, Frags<16> (&fr)[2], Acc<16> &acc) {
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (U == 0) {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+  read_frags<16, BROW, 2, U>(WRing<S>::a(), WRing<S>::b(), fr[U], c.wm, c.wn, c.lane);
+  if constexpr (U == 0) {
+    // the last slab again at the end keeps the load count per slab uniform
+    const int next = min(j + 1, c.nk - 1);
+    issue<2 * LOADS>(c.ra, c.offA, (uint32_t)next * WROW_BYTES, WRing<S ^ 1>::a(), c.wave);
+    issue<2 * LOADS>(c.rb, c.offB, (uint32_t)next * c.kstepB, WRing<S ^ 1>::b(), c.wave);
+  }
+  mma<BF16, 16>(fr[U ^ 1], acc);  // the previous sub-slice
+  constexpr int R = BROW ? 3 : 2;  // fragment reads per group of 8 MFMAs
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, R - R / 2, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);
+    if constexpr (U == 0) __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, R / 2, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);
+    if constexpr (U == 0) __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
+  }
+}
+
+template <bool BF16, bool OUT_F16, int MI, bool BROW, int KB>
 __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
-  Ctx c;
+  static_assert(KB == 1 || MI == 16, "64-deep slabs use 16x16x32 operands");
+  CtxT<LOADS * KB> c;
   const int tid = threadIdx.x;
   c.lane = tid & 63;
   c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -247,7 +370,8 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t z = (int64_t)p.z0 + blockIdx.y;
   const uint16_t *A = p.A + z * p.sA + m0 * p.lda;  // row m0, k = 0 (row-major A)
-  const uint16_t *B = p.B + z * p.sB + n0 * p.ldb;  // column n0, k = 0 (column-major B)
+  // column n0, k = 0: column-major B starts its panel at row n0, row-major B at column n0
+  const uint16_t *B = p.B + z * p.sB + (BROW ? n0 : n0 * p.ldb);
 
   Acc<MI> acc;
   if constexpr (MI == 32) {
@@ -265,18 +389,41 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
   // Buffer resources cover exactly the 256 rows of each operand panel; the
   // host keeps that extent below 1 GiB, so all offsets are 32-bit.
   c.ra = make_rsrc(A, (uint32_t)((255 * p.lda + p.K) * 2));
-  c.rb = make_rsrc(B, (uint32_t)((255 * p.ldb + p.K) * 2));
-  slice_offsets<LOADS>(c.offA, p.lda, c.wave, lane);
-  slice_offsets<LOADS>(c.offB, p.ldb, c.wave, lane);
-  c.nk = (int)(p.K / BK);  // the host guarantees K is a positive multiple of NS * BK
+  c.rb = make_rsrc(B, (uint32_t)((BROW ? (p.K - 1) * p.ldb + 256 : 255 * p.ldb + p.K) * 2));
+  slice_offsets<LOADS * KB, KB>(c.offA, p.lda, c.wave, lane);
+  if constexpr (BROW) {
+    slice_offsets_row<LOADS * KB>(c.offB, p.ldb, c.wave, lane);
+    c.kstepB = (uint32_t)(32 * KB * p.ldb * 2);
+  } else {
+    slice_offsets<LOADS * KB, KB>(c.offB, p.ldb, c.wave, lane);
+    c.kstepB = 64 * KB;
+  }
+  // the host guarantees K is a positive multiple of 128
+  c.nk = (int)(p.K / (BK * KB));
 
+  if constexpr (KB == 2) {
+    issue<2 * LOADS>(c.ra, c.offA, 0, WRing<0>::a(), c.wave);
+    issue<2 * LOADS>(c.rb, c.offB, 0, WRing<0>::b(), c.wave);
+    Frags<16> fr[2];
+#pragma unroll
+    for (int i = 0; i < Frags<16>::NA; ++i) fr[1].a[0][i] = fr[1].b[0][i] = u32x4{0, 0, 0, 0};
+    for (int j = 0; j < c.nk; j += 2) {
+      substep_w<BF16, BROW, 0, 0>(c, j, fr, acc);
+      substep_w<BF16, BROW, 0, 1>(c, j, fr, acc);
+      substep_w<BF16, BROW, 1, 0>(c, j + 1, fr, acc);
+      substep_w<BF16, BROW, 1, 1>(c, j + 1, fr, acc);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    mma<BF16, 16>(fr[1], acc);  // the last sub-slice
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the duplicate tail loads
+  } else {
   // prologue: slices 0 .. NS-2 in flight
   issue<LOADS>(c.ra, c.offA, 0 * ROW_BYTES, Ring<0>::a(), c.wave);
-  issue<LOADS>(c.rb, c.offB, 0 * ROW_BYTES, Ring<0>::b(), c.wave);
+  issue<LOADS>(c.rb, c.offB, 0 * c.kstepB, Ring<0>::b(), c.wave);
   issue<LOADS>(c.ra, c.offA, 1 * ROW_BYTES, Ring<1>::a(), c.wave);
-  issue<LOADS>(c.rb, c.offB, 1 * ROW_BYTES, Ring<1>::b(), c.wave);
+  issue<LOADS>(c.rb, c.offB, 1 * c.kstepB, Ring<1>::b(), c.wave);
   issue<LOADS>(c.ra, c.offA, 2 * ROW_BYTES, Ring<2>::a(), c.wave);
-  issue<LOADS>(c.rb, c.offB, 2 * ROW_BYTES, Ring<2>::b(), c.wave);
+  issue<LOADS>(c.rb, c.offB, 2 * c.kstepB, Ring<2>::b(), c.wave);
 
   // Before slice 0 there is no previous slice: zero fragments add exactly 0.
   Frags<MI> fr[2];
@@ -288,14 +435,15 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
   // The steady-state loop has no data-dependent branches, which keeps the
   // 256 accumulators of each lane in place across iterations.
   for (int j = 0; j < c.nk; j += NS) {
-    slice<BF16, MI, 0>(c, j + 0, fr, acc);
-    slice<BF16, MI, 1>(c, j + 1, fr, acc);
-    slice<BF16, MI, 2>(c, j + 2, fr, acc);
-    slice<BF16, MI, 3>(c, j + 3, fr, acc);
+    slice<BF16, MI, BROW, 0>(c, j + 0, fr, acc);
+    slice<BF16, MI, BROW, 1>(c, j + 1, fr, acc);
+    slice<BF16, MI, BROW, 2>(c, j + 2, fr, acc);
+    slice<BF16, MI, BROW, 3>(c, j + 3, fr, acc);
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   mma<BF16, MI>(fr[1], acc);  // the last slice (nk is a multiple of 4, so it sits in set 1)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the duplicate tail loads
+  }
 
   // ---- epilogue: each register group holds C[m][n + 0..3]
   const int64_t ldc = p.ldc;
@@ -335,14 +483,14 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
   }
 }
 
-template <bool BF16, bool OUT_F16, int MI>
+template <bool BF16, bool OUT_F16, int MI, bool BROW, int KB>
 hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
   const int64_t tiles = (int64_t)base.tiles_m * base.tiles_n;
   for (int64_t z0 = 0; z0 < batch; z0 += kMaxGridY) {
     KernelArgs a = base;
     a.z0 = (int32_t)z0;
     const int64_t nz = batch - z0 < kMaxGridY ? batch - z0 : kMaxGridY;
-    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT_F16, MI>), dim3((unsigned)tiles, (unsigned)nz), dim3(256), 0,
+    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT_F16, MI, BROW, KB>), dim3((unsigned)tiles, (unsigned)nz), dim3(256), 0,
                        stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -350,20 +498,25 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
   return hipSuccess;
 }
 
-template <int MI>
+template <int MI, bool BROW, int KB>
 hipError_t launch_mi(const Problem &p, const KernelArgs &a, hipStream_t stream) {
   if (p.in_bf16)
-    return p.out_f16 ? launch_t<true, true, MI>(a, p.batch, stream) : launch_t<true, false, MI>(a, p.batch, stream);
-  return p.out_f16 ? launch_t<false, true, MI>(a, p.batch, stream) : launch_t<false, false, MI>(a, p.batch, stream);
+    return p.out_f16 ? launch_t<true, true, MI, BROW, KB>(a, p.batch, stream)
+                     : launch_t<true, false, MI, BROW, KB>(a, p.batch, stream);
+  return p.out_f16 ? launch_t<false, true, MI, BROW, KB>(a, p.batch, stream)
+                   : launch_t<false, false, MI, BROW, KB>(a, p.batch, stream);
 }
 
 }  // namespace
 
-bool tile_supports(const Problem &p) {
-  if (p.a_col || !p.b_col) return false;  // both operands must be K-contiguous
+bool tile_supports(const Problem &p, bool b_row) {
+  if (p.a_col) return false;              // A must be K-contiguous
+  if (p.b_col == b_row) return false;     // the requested B layout
   if (p.M % BM || p.N % BN || p.K % (NS * BK) || p.K == 0) return false;
-  // one operand panel (256 rows) must span less than 2 GiB: 32-bit buffer offsets
-  if (255 * p.lda + p.K >= (int64_t)1 << 30 || 255 * p.ldb + p.K >= (int64_t)1 << 30) return false;
+  // 32-bit buffer offsets: an A panel (256 rows) and a B panel (256 rows or K
+  // rows x 256 columns) must span less than 1 GiB
+  if (255 * p.lda + p.K >= (int64_t)1 << 29) return false;
+  if ((b_row ? (p.K - 1) * p.ldb + 256 : 255 * p.ldb + p.K) >= (int64_t)1 << 29) return false;
   if (((uintptr_t)p.A & 15) || ((uintptr_t)p.B & 15) || ((uintptr_t)p.C & 15)) return false;
   if (p.lda % 8 || p.ldb % 8) return false;
   if (p.ldc % 4) return false;  // 8-byte (f16) / 16-byte (float32) row stores
@@ -371,7 +524,7 @@ bool tile_supports(const Problem &p) {
   return true;
 }
 
-hipError_t launch_tile(const Problem &p, int mi, hipStream_t stream) {
+hipError_t launch_tile(const Problem &p, int variant, hipStream_t stream) {
   KernelArgs a{};
   a.A = p.A;
   a.B = p.B;
@@ -387,9 +540,24 @@ hipError_t launch_tile(const Problem &p, int mi, hipStream_t stream) {
   a.sC = p.sC;
   a.tiles_m = (int32_t)(p.M / BM);
   a.tiles_n = (int32_t)(p.N / BN);
-  return mi == 16 ? launch_mi<16>(p, a, stream) : launch_mi<32>(p, a, stream);
+  switch (variant) {
+    case 0:
+      return launch_mi<32, false, 1>(p, a, stream);
+    case 1:
+      return launch_mi<16, false, 1>(p, a, stream);
+    case 2:
+      return launch_mi<16, true, 1>(p, a, stream);
+    case 3:
+      return launch_mi<16, false, 2>(p, a, stream);
+    default:
+      return launch_mi<16, true, 2>(p, a, stream);
+  }
 }
 
-const char *tile_name(int mi) { return mi == 16 ? "tile_256x256x32_mi16" : "tile_256x256x32_mi32"; }
+const char *tile_name(int variant) {
+  static const char *const names[] = {"tile_256x256x32_mi32", "tile_256x256x32_mi16", "tile_256x256x32_mi16_nn",
+                                      "tile_256x256x64_mi16", "tile_256x256x64_mi16_nn"};
+  return names[variant];
+}
 
 }  // namespace tsm
