@@ -109,22 +109,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 }
 
 // LDS position of 16-byte chunk c of row r of a K-contiguous slab, KB = slab
-// depth / 32.  gfx950 serves a 64-lane 16-byte read in two halves of 32 lanes
-// (lanes 0-15 with 32-47, then 16-31 with 48-63) across 512 bytes of banks.
-//  KB = 1 (64-byte rows): rows r and r + 8 share a bank window; c ^ (3 * bit 3
-//    of r) sends their chunks to complementary positions, so both fragment
-//    shapes (32 rows x 2 chunks, 16 rows x 2 chunks per half) are conflict-free.
-//  KB = 2 (128-byte rows): rows r, r + 4, r + 8, r + 12 share a window; the
-//    XOR value 0, 3, 5, 6 for (r / 4) % 4 keeps 16 rows x chunks {c, c + 2}
-//    (and {c, c + 1}, should the halves be lanes 0-31 and 32-63) on 32
-//    distinct positions.
+// depth / 32.  The fragment reads take rows (lane % 16) + 16i at chunk
+// 4U + lane / 16 (16x16x32 operands).  Both swizzles were chosen by measuring
+// the LDS bank-conflict counter on that read pattern, over every swizzle of
+// the form c ^ (XOR-linear function of row bits 0..3) and random ones: with
+// these, the reads are conflict-free (4 LDS cycles per 64-lane 16-byte read);
+// unswizzled rows cost 2x (64-byte rows) and 4x (128-byte rows).
+//  KB = 1 (64-byte rows): c ^ (3 * bit 3 of r).
+//  KB = 2 (128-byte rows): c ^ ((r / 2) % 8).
 template <int KB>
 __device__ __forceinline__ int swz(int r, int c) {
   if constexpr (KB == 1) {
     return c ^ (((r >> 3) & 1) * 3);
   } else {
-    const int t = (r >> 2) & 3;
-    return c ^ (2 * t + ((t ^ (t >> 1)) & 1));
+    return c ^ ((r >> 1) & 7);
   }
 }
 
@@ -215,8 +213,9 @@ __device__ __forceinline__ void read_frags(const char *sa, const char *sb, Frags
         const int col = wn * 128 + j * 16 + 4 * (lane & 3);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int r = 32 * U + 8 * (lane >> 4) + 4 * h + ((lane & 15) >> 2);
-          const int off = r * 512 + swz_row(r, col >> 3) * 16 + (col & 7) * 2;
+          // the swizzle sees the row within the 32-row sub-slice, so sub-slice U is a constant offset
+          const int r = 8 * (lane >> 4) + 4 * h + ((lane & 15) >> 2);
+          const int off = (32 * U + r) * 512 + swz_row(r, col >> 3) * 16 + (col & 7) * 2;
           const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)((lds_char *)sb + off));
           const u32x2 d = __builtin_bit_cast(u32x2, v);
           f.b[s][j][2 * h] = d[0];
