@@ -64,6 +64,132 @@ def traffic_from_profiles(workload, kernel):
     return rec.get("hbm_bytes_per_launch")
 
 
+# The measurement run that --summarize reads: each command's output directory
+# under RUN_DIR, and the command (run from /tmp, with TMPDIR=/tmp).
+PROFILE_COMMANDS = {
+    "bench.json": "python3 bench.py > RUN_DIR/bench.json",
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d RUN_DIR/trace -o bench -- "
+             "python3 bench.py --no-cpu-baseline",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d RUN_DIR/fetch -o p -- "
+             "python3 bench.py --no-cpu-baseline --steps 5 --warmup 2",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d RUN_DIR/write -o p -- "
+             "python3 bench.py --no-cpu-baseline --steps 5 --warmup 2",
+    "cal_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d RUN_DIR/cal_fetch -o c -- "
+                 "python3 bench.py --calibrate-copy 1024",
+    "cal_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d RUN_DIR/cal_write -o c -- "
+                 "python3 bench.py --calibrate-copy 1024",
+    "sq": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS "
+          "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F16 GRBM_GUI_ACTIVE --output-format csv "
+          "-d RUN_DIR/sq -o p -- python3 bench.py --no-cpu-baseline --steps 5 --warmup 2",
+}
+KERNEL_SYMBOL = {"tile_": "gemm_tile_kernel", "skinny_": "gemm_skinny_kernel", "splitk_": "gemm_splitk_kernel",
+                 "masked_": "gemm_masked_kernel"}
+
+
+def _csv(path):
+    import csv
+    import glob
+
+    files = glob.glob(path)
+    if not files:
+        raise SystemExit(f"--summarize: no file matches {path}")
+    return list(csv.DictReader(open(files[0])))
+
+
+def _counters(directory):
+    """{kernel name: {counter: mean value per dispatch}} from one rocprofv3 --pmc run."""
+    acc = {}
+    for r in _csv(os.path.join(directory, "*counter_collection.csv")):
+        d = acc.setdefault(r["Kernel_Name"], {})
+        d.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in acc.items()}
+
+
+def _pick(table, kernel):
+    """The rocprofv3 kernel entry of a library kernel name (most frequent instantiation of its family)."""
+    fam = next(v for k, v in KERNEL_SYMBOL.items() if kernel.startswith(k))
+    names = [n for n in table if fam + "<" in n]
+    if not names:
+        raise SystemExit(f"--summarize: no {fam} entry")
+    return max(names, key=lambda n: table[n][1] if isinstance(table[n], tuple) else 0)
+
+
+def summarize(run_dir):
+    """Write profiles/ (kernel-trace and counter summaries, HBM traffic records) from one measurement run."""
+    from workloads import WORKLOADS
+
+    bench = json.load(open(os.path.join(run_dir, "bench.json")))
+    jobs = [(bench["config"]["workload"], bench["roofline"]["kernel"], bench["ms_per_step"])]
+    if "secondary" in bench:
+        jobs.append((bench["secondary"]["workload"], bench["secondary"]["kernel"], bench["secondary"]["ms_per_step"]))
+    src = bench.get("kernel_source_hash")
+    if src != kernel_source_hash():
+        print(f"--summarize: the run measured kernel source {src}, the tree now holds {kernel_source_hash()}; "
+              "the traffic records will not be used by bench.py", file=sys.stderr)
+    cmd = lambda k: "cd /tmp && " + PROFILE_COMMANDS[k]  # noqa: E731
+    stats = _csv(os.path.join(run_dir, "trace", "*kernel_stats.csv"))
+    by_name = {r["Name"]: (r, int(r["Calls"])) for r in stats}
+    out = os.path.join(ROOT, "profiles")
+    os.makedirs(out, exist_ok=True)
+
+    lines = ["# rocprofv3 --kernel-trace --stats summary (kernel_stats.csv), one MI355X",
+             f"# command: {cmd('trace')}", f"# kernel source hash (bench.kernel_source_hash): {src}"]
+    for wl, kern, _ in jobs:
+        lines.append(f"# {wl}: {kern} = {_pick(by_name, kern)}")
+    lines.append("# __amd_rocclr_copyBuffer = input uploads")
+    lines.append(",".join(f'"{c}"' for c in stats[0].keys()))
+    for r in stats:
+        lines.append(",".join(f'"{v}"' if k == "Name" else v for k, v in r.items()))
+    name = "kernel_trace_stats__" + "__".join(j[0] for j in jobs) + ".txt"
+    open(os.path.join(out, name), "w").write("\n".join(lines) + "\n")
+
+    fetch, write = _counters(os.path.join(run_dir, "fetch")), _counters(os.path.join(run_dir, "write"))
+    cal_f = _counters(os.path.join(run_dir, "cal_fetch"))
+    cal_w = _counters(os.path.join(run_dir, "cal_write"))
+    sq = _counters(os.path.join(run_dir, "sq"))
+    copy_kib = 1024 * 1024  # --calibrate-copy 1024: 1 GiB read and written per copy
+    copy_f = max(v["FETCH_SIZE"] for v in cal_f.values())
+    copy_w = max(v["WRITE_SIZE"] for v in cal_w.values())
+    fscale, wscale = copy_kib / copy_f, copy_kib / copy_w
+    for wl, kern, ms in jobs:
+        w = WORKLOADS[wl]
+        trace_row = by_name[_pick(by_name, kern)][0]
+        sym_f = _pick({n: (None, 1) for n in fetch}, kern)
+        f_kib, w_kib = fetch[sym_f]["FETCH_SIZE"], write[_pick({n: (None, 1) for n in write}, kern)]["WRITE_SIZE"]
+        c = sq[_pick({n: (None, 1) for n in sq}, kern)]
+        hbm_r, hbm_w = f_kib * 1024 * fscale, w_kib * 1024 * wscale
+        mops = c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0) + c.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0)
+        lds = c.get("SQ_LDS_IDX_ACTIVE", 0)
+        txt = [f"# rocprofv3 counters for {kern} on {wl}, averages per dispatch, one MI355X",
+               f"# kernel source hash: {src}",
+               f"# SQ counters: {cmd('sq')}",
+               f"# FETCH_SIZE: {cmd('fetch')}",
+               f"# WRITE_SIZE: {cmd('write')}",
+               f"# copy calibration: {cmd('cal_fetch')} ; {cmd('cal_write')}",
+               f"[{sym_f}]"]
+        txt += [f"{k} = {v:.6g}" for k, v in sorted(c.items())]
+        txt += [f"# LDS bank-conflict cycles / LDS active cycles = "
+                f"{c.get('SQ_LDS_BANK_CONFLICT', 0) / lds if lds else 0:.3f}",
+                f"# MFMA ops x 512 = {mops * 512:.6g} (2*M*N*K*batch = {w.flops:.6g})",
+                f"FETCH_SIZE = {f_kib:.6g} KiB, WRITE_SIZE = {w_kib:.6g} KiB",
+                f"# 1 GiB device copy: FETCH_SIZE = {copy_f:.6g} KiB, WRITE_SIZE = {copy_w:.6g} KiB "
+                f"-> read scale {fscale:.3f}, write scale {wscale:.3f}",
+                f"# HBM bytes per launch = {hbm_r + hbm_w:.6g} (read {hbm_r:.6g}, write {hbm_w:.6g}); "
+                f"algorithmic {w.bytes:.6g} ({(hbm_r + hbm_w) / w.bytes:.2f}x)",
+                f"# kernel-trace average {float(trace_row['AverageNs']) / 1e6:.4f} ms over {trace_row['Calls']} "
+                f"calls; bench.py ms_per_step in the same run {ms:.4f} ms"]
+        open(os.path.join(out, f"counters__{kern}__{wl}.txt"), "w").write("\n".join(txt) + "\n")
+        rec = {"kernel": kern, "workload": wl, "source_hash": src, "hbm_bytes_per_launch": hbm_r + hbm_w,
+               "hbm_read_bytes_per_launch": hbm_r, "hbm_write_bytes_per_launch": hbm_w,
+               "algorithmic_bytes_per_launch": w.bytes, "fetch_size_kib": f_kib, "write_size_kib": w_kib,
+               "fetch_scale": fscale, "write_scale": wscale, "avg_duration_ns": float(trace_row["AverageNs"]),
+               "calibration": f"FETCH_SIZE/WRITE_SIZE of a 1 GiB device-to-device copy (bench.py --calibrate-copy "
+                              f"1024): {copy_f:.0f} KiB fetched, {copy_w:.0f} KiB written",
+               "commands": [cmd("fetch"), cmd("write"), cmd("cal_fetch"), cmd("cal_write")]}
+        json.dump(rec, open(os.path.join(out, f"traffic_{wl}.json"), "w"), indent=1)
+        print(f"{wl}: {kern}, HBM {hbm_r + hbm_w:.4g} B/launch ({(hbm_r + hbm_w) / w.bytes:.2f}x algorithmic)")
+
+
 class Setup:
     """Inputs of one workload uploaded to the GPU, and a closure that runs one step."""
 
@@ -174,7 +300,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (to scale HBM counters)")
+    ap.add_argument("--summarize", metavar="RUN_DIR",
+                    help="no GPU: write profiles/ from the rocprofv3 output of the commands in PROFILE_COMMANDS")
     args = ap.parse_args()
+
+    if args.summarize:
+        summarize(args.summarize)
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -251,6 +383,7 @@ def main():
         "ms_per_step_interleaved_median": ms_interleaved,
         "check": check,
         "roofline": roof,
+        "kernel_source_hash": kernel_source_hash(),
     }
     # free the headline operands before the secondary workload
     s_main = s

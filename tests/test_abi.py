@@ -141,15 +141,23 @@ def test_kernel_selection_for_the_workloads():
 
 
 def test_kernel_selection_by_layout_and_shape():
-    """Aligned 256-multiples go to the large-tile kernel for both B layouts, K-contiguous B on the direct
-    variant and row-major B on the transpose-read variant; a misaligned ldb falls back to the masked kernel."""
+    """Aligned 256-multiples with at least 256 tiles go to the large-tile kernel for both B layouts (K-contiguous
+    B on the 64-deep variant, row-major B on the transpose-read variant); fewer tiles, a misaligned ldb or K not a
+    multiple of 128 go elsewhere."""
     B0 = 0x7E0000000000
-    n = 1024
+    n = 4096
     col = tsm.tsm_gemm_kernel_name(n, n, n, A0, n, 0, 0, B0, n, 1, 0, C0, n, 0, 1, 2)
     row = tsm.tsm_gemm_kernel_name(n, n, n, A0, n, 0, 0, B0, n, 0, 0, C0, n, 0, 1, 2)
     assert col == "tile_256x256x64_mi16"
     assert row == "tile_256x256x32_mi16_nn"
+    # 16 tiles of 256 x 256 but a batch of 16: 256 workgroups
+    assert tsm.tsm_gemm_kernel_name(1024, 1024, 1024, A0, 1024, 0, 1 << 20, B0, 1024, 1, 1 << 20, C0, 1024, 1 << 20,
+                                    16, 2) == "tile_256x256x64_mi16"
+    # 16 tiles, one problem: the 128 x 128 kernel spreads over more CUs
+    assert tsm.tsm_gemm_kernel_name(1024, 1024, 1024, A0, 1024, 0, 0, B0, 1024, 1, 0, C0, 1024, 0, 1,
+                                    2).startswith("masked_")
     odd = tsm.tsm_gemm_kernel_name(n, n, n, A0, n, 0, 0, B0, n + 4, 0, 0, C0, n, 0, 1, 2)
     assert odd.startswith("masked_")
-    # K not a multiple of 128: masked
     assert tsm.tsm_gemm_kernel_name(n, n, n + 64, A0, n + 64, 0, 0, B0, n, 0, 0, C0, n, 0, 1, 2).startswith("masked_")
+    # few output tiles and deep K: split-K
+    assert tsm.tsm_gemm_kernel_name(256, 256, 8192, A0, 8192, 0, 0, B0, 256, 0, 0, C0, 256, 0, 1, 0).startswith("splitk_")

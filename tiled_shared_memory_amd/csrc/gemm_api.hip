@@ -178,8 +178,10 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
   // few output tiles and deep K: take the parallelism from K
   const int64_t masked_tiles = tiles * batch;
   if (K > 0 && masked_tiles < 256 && splitk_supports(p)) out->kernel = Kernel::SplitK;
-  if (K > 0 && tile_supports(p, false)) out->kernel = Kernel::TileW;
-  if (K > 0 && tile_supports(p, true)) out->kernel = Kernel::Tile16NN;
+  // the 256 x 256 kernels once their tiles (one workgroup per CU) fill the chip
+  const bool many = (M / TileInfo::BM) * (N / TileInfo::BN) * batch >= 256;
+  if (K > 0 && many && tile_supports(p, false)) out->kernel = Kernel::TileW;
+  if (K > 0 && many && tile_supports(p, true)) out->kernel = Kernel::Tile16NN;
   if (K > 0 && skinny_supports(p)) out->kernel = Kernel::Skinny;
 
   // TSM_GEMM_KERNEL=<name> forces a kernel variant (tests and tuning); a
