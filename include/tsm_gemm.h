@@ -110,6 +110,28 @@ int gemm_strided_batched_ex(int64_t M, int64_t N, int64_t K, const void *A, int6
                             int64_t strideA, const void *B, int64_t ldb, int layout_b, int64_t strideB, void *C,
                             int64_t ldc, int64_t strideC, int64_t batch, int dtype, void *stream);
 
+/*
+ * gemm_grouped -- `groups` independent products of different heights: problem g
+ * uses the first m_g rows of A + g*strideA and C + g*strideC, and B + g*strideB,
+ *     C_g[0:m_g, :] := A_g[0:m_g, :] . B_g,
+ * where m_g = min(max(rows[g], 0), M).  This is the mixture-of-experts slice of
+ * the Intel XPU Triton README (section "Use Tensor Descriptors to load tl.dot
+ * arguments and save results", its A[expert, :tokens, :] example): each
+ * expert's token count is read from device memory by the kernels, workgroups
+ * whose tile starts at or past m_g exit early, and rows past m_g are masked.
+ *   M         : the largest row count a problem may have (the row capacity of
+ *               every A_g and C_g); sizes and strides are validated against it.
+ *   rows      : DEVICE pointer to `groups` int32 counts, 4-byte aligned, read in
+ *               stream order (a kernel earlier on `stream` may produce them).
+ *               Values outside [0, M] are clamped, never an error: the host
+ *               cannot see them.  Must be non-NULL when M, N and groups are > 0.
+ *   Rows m_g .. M-1 of every C_g are not written.  Other arguments and rules as
+ *   for gemm_strided_batched_ex (groups plays the role of batch).
+ */
+int gemm_grouped(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a, int64_t strideA,
+                 const void *B, int64_t ldb, int layout_b, int64_t strideB, void *C, int64_t ldc, int64_t strideC,
+                 const int32_t *rows, int64_t groups, int dtype, void *stream);
+
 /* Static text for a status code ("success", "invalid value", ...). */
 const char *tsm_status_string(int status);
 
@@ -127,6 +149,12 @@ const char *tsm_last_error_detail(void);
 const char *tsm_gemm_kernel_name(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a,
                                  int64_t strideA, const void *B, int64_t ldb, int layout_b, int64_t strideB,
                                  void *C, int64_t ldc, int64_t strideC, int64_t batch, int dtype);
+
+/* tsm_gemm_grouped_kernel_name -- the same for a gemm_grouped call. */
+const char *tsm_gemm_grouped_kernel_name(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a,
+                                         int64_t strideA, const void *B, int64_t ldb, int layout_b, int64_t strideB,
+                                         void *C, int64_t ldc, int64_t strideC, const int32_t *rows, int64_t groups,
+                                         int dtype);
 
 #ifdef __cplusplus
 }

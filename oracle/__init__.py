@@ -8,6 +8,7 @@ wrapper, and it reads the same 16-bit patterns the GPU receives.
 Functions:
   gemm_rows(...)   -> (C, S): full rows of every problem, float64
   gemm_points(...) -> (C, S): selected cells (sampled checks at full size)
+  gemm_grouped(...) -> [(C_g, S_g)]: the first m_g rows of each problem
   decode(bits, fmt)         : the oracle's own exact 16-bit -> float64 decode
   bound(...)                : the per-element acceptance bound
 
@@ -121,6 +122,31 @@ class Oracle:
                                         n, z.ctypes.data, i.ctypes.data, j.ctypes.data,
                                         C.ctypes.data, S.ctypes.data)
         return C, S
+
+
+    def gemm_grouped(self, A, B, M, N, K, fmt, rows, *, lda=None, ldb=None, strideA=None, strideB=None,
+                     a_layout="row", b_layout="row"):
+        """Grouped product: for problem g, C_g = A_g[0:m_g] . B_g with m_g = rows[g] clamped to [0, M].
+
+        The mixture-of-experts slice of the Intel XPU Triton README (section "Use
+        Tensor Descriptors to load tl.dot arguments and save results"): expert g
+        multiplies only its first m_g token rows.  Each group is gemm_rows on
+        that problem alone, rows 0 .. m_g - 1.  Returns a list of (C_g, S_g) of
+        shape (m_g, N).
+        """
+        groups = len(rows)
+        Af = np.ascontiguousarray(A, dtype=np.uint16).reshape(-1)
+        Bf = np.ascontiguousarray(B, dtype=np.uint16).reshape(-1)
+        strideA = Af.size // max(groups, 1) if strideA is None else strideA
+        strideB = Bf.size // max(groups, 1) if strideB is None else strideB
+        out = []
+        for g in range(groups):
+            m = min(max(int(rows[g]), 0), M)
+            C, S = self.gemm_rows(Af[g * strideA:], Bf[g * strideB:], M, N, K, fmt, batch=1, lda=lda, ldb=ldb,
+                                  strideA=0, strideB=0, a_layout=a_layout, b_layout=b_layout, row_begin=0,
+                                  row_end=m)
+            out.append((C[0], S[0]))
+        return out
 
 
 _DEFAULT = None

@@ -280,6 +280,34 @@ def pin_random_vs_numpy(orc):
             assert np.all(np.abs(Cp - want[z, i, j]) <= 2 * K * 2.0 ** -53 * S[z, i, j])
 
 
+# ---------------------------------------------------------------- grouped (per-problem row counts)
+def pin_grouped_integer(orc):
+    """Grouped products on integer entries: group g equals numpy's int64 product of A_g's first m_g rows
+    with B_g, where m_g is rows[g] clamped to [0, M] (counts below 0, inside, at and above M)."""
+    M, N, K, groups = 10, 7, 33, 5
+    rows = [-3, 0, 4, M, M + 6]
+    for fmt in (F16, BF16):
+        for a_layout, b_layout in (("row", "row"), ("row", "col"), ("col", "row")):
+            A, B = integer_operands(8, groups, M, N, K, fmt, -2, 2)
+            ai = bits_to_f64(A, fmt).astype(np.int64)
+            bi = bits_to_f64(B, fmt).astype(np.int64)
+            As, Bs = _store(A, a_layout), _store(B, b_layout)
+            # trailing zero slack keeps a wrongly indexed read (a planted mistake) inside the buffer
+            slack = 4 * (M + N + K) ** 2
+            Ap = np.zeros(As.size + slack, np.uint16)
+            Ap[:As.size] = As.reshape(-1)
+            Bp = np.zeros(Bs.size + slack, np.uint16)
+            Bp[:Bs.size] = Bs.reshape(-1)
+            got = orc.gemm_grouped(Ap, Bp, M, N, K, fmt, rows, strideA=As[0].size, strideB=Bs[0].size,
+                                   a_layout=a_layout, b_layout=b_layout)
+            assert len(got) == groups
+            for g, (C, S) in enumerate(got):
+                m = min(max(rows[g], 0), M)
+                assert C.shape == (m, N) and S.shape == (m, N)
+                assert np.array_equal(C, np.matmul(ai[g, :m], bi[g]))
+                assert np.array_equal(S, np.matmul(np.abs(ai[g, :m]), np.abs(bi[g])))
+
+
 ALL_PINS = [
     pin_decode_f16_all_patterns,
     pin_decode_bf16_all_patterns,
@@ -290,4 +318,5 @@ ALL_PINS = [
     pin_linearity_in_a,
     pin_integer_exact,
     pin_random_vs_numpy,
+    pin_grouped_integer,
 ]

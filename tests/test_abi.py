@@ -33,8 +33,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("gemm", "gemm_ex", "gemm_strided_batched", "gemm_strided_batched_ex", "tsm_status_string",
-              "tsm_last_error_detail", "tsm_gemm_kernel_name"):
+    for n in ("gemm", "gemm_ex", "gemm_strided_batched", "gemm_strided_batched_ex", "gemm_grouped",
+              "tsm_status_string", "tsm_last_error_detail", "tsm_gemm_kernel_name", "tsm_gemm_grouped_kernel_name"):
         assert n in names
 
 
@@ -161,3 +161,58 @@ def test_kernel_selection_by_layout_and_shape():
     assert tsm.tsm_gemm_kernel_name(n, n, n + 64, A0, n + 64, 0, 0, B0, n, 0, 0, C0, n, 0, 1, 2).startswith("masked_")
     # few output tiles and deep K: split-K
     assert tsm.tsm_gemm_kernel_name(256, 256, 8192, A0, 8192, 0, 0, B0, 256, 0, 0, C0, 256, 0, 1, 0).startswith("splitk_")
+
+
+R0 = 0x7F3000000000  # fake device address of the row counts
+
+
+def _grouped(**kw):
+    args = dict(M=64, N=128, K=128, A=A0, lda=128, la=0, sA=64 * 128, B=B0, ldb=128, lb=0, sB=128 * 128, C=C0,
+                ldc=128, sC=64 * 128, rows=R0, groups=4, dtype=0)
+    args.update(kw)
+    return [args[k] for k in ("M", "N", "K", "A", "lda", "la", "sA", "B", "ldb", "lb", "sB", "C", "ldc", "sC",
+                              "rows", "groups", "dtype")]
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(rows=0), 1, "rows is NULL"),
+    (dict(rows=R0 + 2), 1, "rows not 4-byte aligned"),
+    (dict(groups=-1), 1, "negative batch"),
+    (dict(sC=64 * 128 - 1), 1, "strideC"),
+    (dict(dtype=9), 1, "dtype"),
+])
+def test_grouped_invalid_arguments_are_rejected(kw, status, needle):
+    with pytest.raises(tsm.TsmError) as ei:
+        tsm.gemm_grouped(*_grouped(**kw), 0)
+    assert ei.value.status == status
+    assert needle in ei.value.detail
+
+
+@pytest.mark.parametrize("kw", [dict(groups=0), dict(M=0), dict(N=0, rows=0)])
+def test_grouped_empty_succeeds_without_launch(kw):
+    assert tsm.gemm_grouped(*_grouped(**kw), 0) == 0
+
+
+def test_grouped_kernel_selection():
+    """Grouped products route like batched ones (any M on the large-tile kernel, M <= 16 on the skinny kernel),
+    except that split-K, which stores whole 16 x 16 tiles, is never used."""
+    # MoE-like: 8 experts, up to 2048 tokens, 1024 x 1024 weights stored K-contiguous
+    big = _grouped(M=2048, N=1024, K=1024, lda=1024, sA=2048 * 1024, ldb=1024, lb=1, sB=1024 * 1024, ldc=1024,
+                   sC=2048 * 1024, groups=8, dtype=3)
+    assert tsm.tsm_gemm_grouped_kernel_name(*big) == "tile_256x256x64_mi16"
+    big[9] = 0  # row-major weights
+    assert tsm.tsm_gemm_grouped_kernel_name(*big) == "tile_256x256x32_mi16_nn"
+    # up to 16 rows per group: the skinny kernel
+    sk = _grouped(M=16, N=1024, K=1024, lda=1024, sA=16 * 1024, ldb=1024, sB=1024 * 1024, ldc=1024, sC=16 * 1024)
+    assert tsm.tsm_gemm_grouped_kernel_name(*sk).startswith("skinny_")
+    # deep K, few tiles: a batched call would take split-K, a grouped one must not
+    dk = _grouped(M=256, N=256, K=8192, lda=8192, sA=256 * 8192, ldb=256, sB=8192 * 256, ldc=256, sC=256 * 256,
+                  groups=1)
+    assert tsm.tsm_gemm_kernel_name(256, 256, 8192, A0, 8192, 0, 0, B0, 256, 0, 0, C0, 256, 0, 1, 0).startswith("splitk")
+    assert tsm.tsm_gemm_grouped_kernel_name(*dk).startswith("masked_")
+
+
+def test_plain_products_with_ragged_m_use_the_tile_kernel():
+    """M need not be a multiple of 256 for the large-tile kernels: rows past M load as zero and are not stored."""
+    assert tsm.tsm_gemm_kernel_name(8000, 8192, 8192, A0, 8192, 0, 0, B0, 8192, 1, 0, C0, 8192, 0, 1,
+                                    3) == "tile_256x256x64_mi16"

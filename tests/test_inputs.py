@@ -129,3 +129,9 @@ def test_algorithmic_bytes():
     assert WORKLOADS["single_f16_64x128x128"].bytes == 16384 + 32768 + 32768
     assert WORKLOADS["square_bf16_8192"].bytes == 3 * 8192 * 8192 * 2
     assert WORKLOADS["skinny_f16_16x16384x8192_b8"].bytes == 8 * (16 * 8192 * 2 + 8192 * 16384 * 2 + 16 * 16384 * 4)
+
+
+@pytest.mark.parametrize("dist", [("normal", 0.0, 1.0), ("uniform", -1.0), ("laplace", 1.0)])
+def test_malformed_distribution_is_rejected(dist):
+    with pytest.raises(ValueError):
+        draw_matrix_bits(0, 0, 0, dist, 4, 4, F16)

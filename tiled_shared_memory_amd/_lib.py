@@ -42,6 +42,10 @@ SIGNATURES = {
     "tsm_last_error_detail": ([], ctypes.c_char_p),
     "tsm_gemm_kernel_name": ([_I64, _I64, _I64, _PTR, _I64, _INT, _I64, _PTR, _I64, _INT, _I64, _PTR, _I64, _I64,
                               _I64, _INT], ctypes.c_char_p),
+    "gemm_grouped": ([_I64, _I64, _I64, _PTR, _I64, _INT, _I64, _PTR, _I64, _INT, _I64, _PTR, _I64, _I64, _PTR, _I64,
+                      _INT, _PTR], _INT),
+    "tsm_gemm_grouped_kernel_name": ([_I64, _I64, _I64, _PTR, _I64, _INT, _I64, _PTR, _I64, _INT, _I64, _PTR, _I64,
+                                      _I64, _PTR, _I64, _INT], ctypes.c_char_p),
 }
 
 
@@ -128,6 +132,13 @@ def gemm_strided_batched_ex(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b
                                                    strideB, _ptr(C), ldc, strideC, batch, dtype, _stream(stream)))
 
 
+def gemm_grouped(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, strideB, C, ldc, strideC, rows, groups, dtype,
+                 stream=None):
+    lib = load()
+    return _check(lib, lib.gemm_grouped(M, N, K, _ptr(A), lda, layout_a, strideA, _ptr(B), ldb, layout_b, strideB,
+                                        _ptr(C), ldc, strideC, _ptr(rows), groups, dtype, _stream(stream)))
+
+
 def tsm_status_string(status: int) -> str:
     return load().tsm_status_string(status).decode()
 
@@ -140,4 +151,11 @@ def tsm_gemm_kernel_name(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, s
                          dtype):
     r = load().tsm_gemm_kernel_name(M, N, K, _ptr(A), lda, layout_a, strideA, _ptr(B), ldb, layout_b, strideB,
                                     _ptr(C), ldc, strideC, batch, dtype)
+    return r.decode() if r else None
+
+
+def tsm_gemm_grouped_kernel_name(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, strideB, C, ldc, strideC, rows,
+                                 groups, dtype):
+    r = load().tsm_gemm_grouped_kernel_name(M, N, K, _ptr(A), lda, layout_a, strideA, _ptr(B), ldb, layout_b, strideB,
+                                            _ptr(C), ldc, strideC, _ptr(rows), groups, dtype)
     return r.decode() if r else None

@@ -85,9 +85,11 @@ bool vec8_ok(const void *X, int64_t contiguous_extent, int64_t ld, int64_t strid
   return true;
 }
 
+// rows: null for plain (batched) products; for grouped products the device
+// array of per-problem row counts (each clamped to [0, M] by the kernels).
 int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a, int64_t strideA, const void *B,
          int64_t ldb, int layout_b, int64_t strideB, void *C, int64_t ldc, int64_t strideC, int64_t batch, int dtype,
-         Plan *out) {
+         const int32_t *rows, bool grouped, Plan *out) {
   g_detail[0] = '\0';
   if (dtype < TSM_F16_F32 || dtype > TSM_BF16_F16) return fail(TSM_ERROR_INVALID_VALUE, "unknown dtype %d", dtype);
   if (layout_a != TSM_ROW && layout_a != TSM_COL)
@@ -117,9 +119,14 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
   p.b_col = layout_b == TSM_COL;
   p.in_bf16 = dtype == TSM_BF16_F32 || dtype == TSM_BF16_F16;
   p.out_f16 = dtype == TSM_F16_F16 || dtype == TSM_BF16_F16;
+  p.rows = rows;
   out->kernel = Kernel::None;
 
   if (M == 0 || N == 0 || batch == 0) return TSM_SUCCESS;  // nothing to compute
+  if (grouped) {
+    if (!rows) return fail(TSM_ERROR_INVALID_VALUE, "rows is NULL");
+    if ((uintptr_t)rows % 4) return fail(TSM_ERROR_INVALID_VALUE, "rows not 4-byte aligned");
+  }
 
   // ---- launch limits (tile indices and in-kernel loop counts stay in 32 bits)
   const int64_t kMaxDim = 0x7fffffffLL;
@@ -179,7 +186,7 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
   const int64_t masked_tiles = tiles * batch;
   if (K > 0 && masked_tiles < 256 && splitk_supports(p)) out->kernel = Kernel::SplitK;
   // the 256 x 256 kernels once their tiles (one workgroup per CU) fill the chip
-  const bool many = (M / TileInfo::BM) * (N / TileInfo::BN) * batch >= 256;
+  const bool many = ((M + TileInfo::BM - 1) / TileInfo::BM) * (N / TileInfo::BN) * batch >= 256;
   if (K > 0 && many && tile_supports(p, false)) out->kernel = Kernel::TileW;
   if (K > 0 && many && tile_supports(p, true)) out->kernel = Kernel::Tile16NN;
   if (K > 0 && skinny_supports(p)) out->kernel = Kernel::Skinny;
@@ -253,7 +260,17 @@ int gemm_strided_batched_ex(int64_t M, int64_t N, int64_t K, const void *A, int6
                             int64_t ldc, int64_t strideC, int64_t batch, int dtype, void *stream) {
   tsm::Plan pl;
   int st = tsm::plan(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, strideB, C, ldc, strideC, batch, dtype,
-                     &pl);
+                     nullptr, false, &pl);
+  if (st != TSM_SUCCESS) return st;
+  return tsm::run(pl, stream);
+}
+
+int gemm_grouped(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a, int64_t strideA,
+                 const void *B, int64_t ldb, int layout_b, int64_t strideB, void *C, int64_t ldc, int64_t strideC,
+                 const int32_t *rows, int64_t groups, int dtype, void *stream) {
+  tsm::Plan pl;
+  int st = tsm::plan(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, strideB, C, ldc, strideC, groups, dtype,
+                     rows, true, &pl);
   if (st != TSM_SUCCESS) return st;
   return tsm::run(pl, stream);
 }
@@ -296,8 +313,19 @@ const char *tsm_gemm_kernel_name(int64_t M, int64_t N, int64_t K, const void *A,
                                  int64_t strideA, const void *B, int64_t ldb, int layout_b, int64_t strideB, void *C,
                                  int64_t ldc, int64_t strideC, int64_t batch, int dtype) {
   tsm::Plan pl;
-  if (tsm::plan(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, strideB, C, ldc, strideC, batch, dtype, &pl) !=
-      TSM_SUCCESS)
+  if (tsm::plan(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, strideB, C, ldc, strideC, batch, dtype, nullptr,
+                false, &pl) != TSM_SUCCESS)
+    return nullptr;
+  return tsm::kernel_name(pl.kernel);
+}
+
+const char *tsm_gemm_grouped_kernel_name(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a,
+                                         int64_t strideA, const void *B, int64_t ldb, int layout_b, int64_t strideB,
+                                         void *C, int64_t ldc, int64_t strideC, const int32_t *rows, int64_t groups,
+                                         int dtype) {
+  tsm::Plan pl;
+  if (tsm::plan(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, strideB, C, ldc, strideC, groups, dtype, rows,
+                true, &pl) != TSM_SUCCESS)
     return nullptr;
   return tsm::kernel_name(pl.kernel);
 }

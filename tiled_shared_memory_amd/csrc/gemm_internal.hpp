@@ -20,6 +20,7 @@ struct Problem {
   bool b_col;    // B stored column-major (K-contiguous) instead of row-major (N-contiguous)
   bool in_bf16;  // operands are bf16 (else f16)
   bool out_f16;  // C is f16 (else float32)
+  const int32_t *rows;  // grouped products: device array of per-problem row counts (else null)
 };
 
 // Kernel arguments, passed by value.  Offsets are 64-bit throughout.
@@ -32,7 +33,16 @@ struct KernelArgs {
   int64_t sA, sB, sC;
   int32_t tiles_m, tiles_n;
   int32_t z0;  // first problem index covered by this launch
+  const int32_t *rows;  // per-problem row counts in device memory, or null (every problem has M rows)
 };
+
+// Rows of problem z: M, or for a grouped product the caller's count for z
+// clamped to [0, M].  Uniform across the workgroup (a scalar load).
+__device__ __forceinline__ int64_t rows_of(const KernelArgs &p, int64_t z) {
+  if (!p.rows) return p.M;
+  const int64_t r = p.rows[z];
+  return r < 0 ? 0 : (r > p.M ? p.M : r);
+}
 
 // Largest grid.y a launch uses for the batch; bigger batches are split.
 constexpr int64_t kMaxGridY = 65535;
@@ -47,8 +57,9 @@ struct MaskedInfo {
 hipError_t launch_masked(const Problem &p, int vec, hipStream_t stream);
 const char *masked_name(int vec);
 
-// Large-tile kernel: A row-major, B either layout, M, N multiples of 256, K a
-// multiple of 128, 16-byte aligned rows.
+// Large-tile kernel: A row-major, B either layout, N a multiple of 256, K a
+// multiple of 128, 16-byte aligned rows; any M (rows past M, or past a grouped
+// problem's count, read as zero and are not stored).
 // Variants (K slab depth, MFMA shape, B layout): 0 = 32-deep, 32x32x16,
 // column-major B; 1 = 32-deep, 16x16x32, column-major; 2 = 32-deep, 16x16x32,
 // row-major B (transposed out of LDS); 3, 4 = as 1, 2 with 64-deep slabs.

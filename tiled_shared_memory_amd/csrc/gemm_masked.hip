@@ -123,6 +123,8 @@ __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
   const int64_t m0 = (int64_t)(tile / p.tiles_n) * BM;
   const int64_t n0 = (int64_t)(tile % p.tiles_n) * BN;
   const int64_t z = (int64_t)p.z0 + blockIdx.y;
+  const int64_t M = rows_of(p, z);  // this problem's rows
+  if (m0 >= M) return;              // the whole tile lies past them (uniform)
   const uint16_t *A = p.A + z * p.sA;
   const uint16_t *B = p.B + z * p.sB;
 
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
   const int64_t nk = (p.K + BK - 1) / BK;
   Stage<VEC> ra, rb;
   if (nk > 0) {
-    fetch<A_KMAJ, VEC>(ra, A, p.lda, p.M, p.K, m0, 0, tid);
+    fetch<A_KMAJ, VEC>(ra, A, p.lda, M, p.K, m0, 0, tid);
     fetch<B_KMAJ, VEC>(rb, B, p.ldb, p.N, p.K, n0, 0, tid);
     commit<A_KMAJ, VEC>(ra, sA[0], tid);
     commit<B_KMAJ, VEC>(rb, sB[0], tid);
@@ -146,7 +148,7 @@ __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
     const int cur = kt & 1;
     const bool more = kt + 1 < nk;
     if (more) {  // next slice in flight while this one is multiplied
-      fetch<A_KMAJ, VEC>(ra, A, p.lda, p.M, p.K, m0, (kt + 1) * BK, tid);
+      fetch<A_KMAJ, VEC>(ra, A, p.lda, M, p.K, m0, (kt + 1) * BK, tid);
       fetch<B_KMAJ, VEC>(rb, B, p.ldb, p.N, p.K, n0, (kt + 1) * BK, tid);
     }
     const uint16_t *a_s = sA[cur];
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
       for (int r = 0; r < 16; ++r) {
         const int64_t row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         const int64_t col = n0 + wn * 64 + j * 32 + (lane & 31);
-        store_masked<OUT_F16>(C, p.ldc, p.M, p.N, row, col, acc[i][j][r]);
+        store_masked<OUT_F16>(C, p.ldc, M, p.N, row, col, acc[i][j][r]);
       }
 }
 
@@ -232,6 +234,7 @@ hipError_t launch_masked(const Problem &p, int vec, hipStream_t stream) {
   a.sA = p.sA;
   a.sB = p.sB;
   a.sC = p.sC;
+  a.rows = p.rows;
   a.tiles_m = (int32_t)((p.M + BM - 1) / BM);
   a.tiles_n = (int32_t)((p.N + BN - 1) / BN);
   return vec == 8 ? dispatch_types<8>(p, a, stream) : dispatch_types<1>(p, a, stream);

@@ -150,6 +150,8 @@ __global__ __launch_bounds__(256, 1) void gemm_skinny_kernel(KernelArgs p) {
 
   const int64_t n0 = (int64_t)blockIdx.x * BN;
   const int64_t z = (int64_t)p.z0 + blockIdx.y;
+  const int64_t M = rows_of(p, z);  // this problem's rows (<= 16)
+  if (M == 0) return;               // uniform: nothing to compute or store
   const uint16_t *A = p.A + z * p.sA;
   const uint16_t *B = p.B + z * p.sB + n0;
 
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(256, 1) void gemm_skinny_kernel(KernelArgs p) {
   // B resource: K rows of the 256-column panel (host keeps it below 2 GiB)
   c.rb = make_rsrc(B, (uint32_t)(((p.K - 1) * p.ldb + BN) * 2));
   // A resource: the M (<= 16) rows of A
-  c.ra = make_rsrc(A, (uint32_t)(((p.M - 1) * p.lda + p.K) * 2));
+  c.ra = make_rsrc(A, (uint32_t)(((M - 1) * p.lda + p.K) * 2));
   // rows at or beyond M point past the end of the resource: the hardware
   // returns zeros for them
   // A dwords: wave-load g of this wave fills LDS bytes [(wave*A_LOADS+g)*256, +256),
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(256, 1) void gemm_skinny_kernel(KernelArgs p) {
 #pragma unroll
   for (int g = 0; g < A_LOADS; ++g) {
     const int r = 2 * (c.wave * A_LOADS + g) + (lane >> 5);
-    c.offA[g] = r < p.M ? (uint32_t)(r * p.lda + 2 * (lane & 31)) * 2u : 0x80000000u;
+    c.offA[g] = r < M ? (uint32_t)(r * p.lda + 2 * (lane & 31)) * 2u : 0x80000000u;
   }
   // B chunks: wave-load g of this wave fills LDS bytes [(wave*LOADS+g)*1024, +1024),
   // i.e. rows 2*(wave*LOADS+g) + lane/32, positions lane%32
@@ -194,7 +196,7 @@ __global__ __launch_bounds__(256, 1) void gemm_skinny_kernel(KernelArgs p) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the duplicate tail loads
 
   // ---- epilogue: lane holds C[m][n .. n+3], m = lane % 16
-  if (m < p.M) {
+  if (m < M) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int64_t n = n0 + c.wave * 64 + nb * 16 + 4 * (lane >> 4);
@@ -255,6 +257,7 @@ hipError_t launch_skinny(const Problem &p, hipStream_t stream) {
   a.sA = p.sA;
   a.sB = p.sB;
   a.sC = p.sC;
+  a.rows = p.rows;
   a.tiles_m = 1;
   a.tiles_n = (int32_t)(p.N / BN);
   if (p.in_bf16)

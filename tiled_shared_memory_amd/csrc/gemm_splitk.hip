@@ -183,6 +183,7 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
 
 bool splitk_supports(const Problem &p) {
   if (p.a_col || p.b_col) return false;  // row-major A and B
+  if (p.rows) return false;  // stores whole 16 x 16 tiles: no per-problem row counts
   if (p.M % 16 || p.N % 16 || p.K % (32 * WAVES * NS) || p.K == 0) return false;
   if (((uintptr_t)p.A & 15) || ((uintptr_t)p.B & 15) || ((uintptr_t)p.C & 15)) return false;
   if (p.lda % 8 || p.ldb % 8 || p.ldc % 4) return false;
@@ -207,6 +208,7 @@ hipError_t launch_splitk(const Problem &p, hipStream_t stream) {
   a.sA = p.sA;
   a.sB = p.sB;
   a.sC = p.sC;
+  a.rows = p.rows;
   a.tiles_m = (int32_t)(p.M / 16);
   a.tiles_n = (int32_t)(p.N / 16);
   if (p.in_bf16)

@@ -368,6 +368,9 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
 
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t z = (int64_t)p.z0 + blockIdx.y;
+  const int64_t M = rows_of(p, z);  // this problem's rows
+  if (m0 >= M) return;              // the whole tile lies past them (uniform)
+  const int64_t vrows = M - m0 < BM ? M - m0 : BM;
   const uint16_t *A = p.A + z * p.sA + m0 * p.lda;  // row m0, k = 0 (row-major A)
   // column n0, k = 0: column-major B starts its panel at row n0, row-major B at column n0
   const uint16_t *B = p.B + z * p.sB + (BROW ? n0 : n0 * p.ldb);
@@ -385,9 +388,10 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
       for (int j = 0; j < 8; ++j) acc.v[i][j] = f32x4{};
   }
 
-  // Buffer resources cover exactly the 256 rows of each operand panel; the
-  // host keeps that extent below 1 GiB, so all offsets are 32-bit.
-  c.ra = make_rsrc(A, (uint32_t)((255 * p.lda + p.K) * 2));
+  // Buffer resources cover exactly the operand panels: the tile's valid rows
+  // of A (rows past M load as zero) and 256 rows, or K rows x 256 columns, of
+  // B.  The host keeps each extent below 1 GiB, so all offsets are 32-bit.
+  c.ra = make_rsrc(A, (uint32_t)(((vrows - 1) * p.lda + p.K) * 2));
   c.rb = make_rsrc(B, (uint32_t)((BROW ? (p.K - 1) * p.ldb + 256 : 255 * p.ldb + p.K) * 2));
   slice_offsets<LOADS * KB, KB>(c.offA, p.lda, c.wave, lane);
   if constexpr (BROW) {
@@ -449,6 +453,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
 #pragma unroll
   for (int i = 0; i < 128 / MI; ++i) {
     const int64_t m = m0 + wm * 128 + i * MI + (lane % MI);
+    if (m >= M) continue;  // rows past M (ragged or grouped problems)
 #pragma unroll
     for (int j = 0; j < 128 / MI; ++j) {
 #pragma unroll
@@ -511,9 +516,9 @@ hipError_t launch_mi(const Problem &p, const KernelArgs &a, hipStream_t stream) 
 bool tile_supports(const Problem &p, bool b_row) {
   if (p.a_col) return false;              // A must be K-contiguous
   if (p.b_col == b_row) return false;     // the requested B layout
-  if (p.M % BM || p.N % BN || p.K % (NS * BK) || p.K == 0) return false;
-  // 32-bit buffer offsets: an A panel (256 rows) and a B panel (256 rows or K
-  // rows x 256 columns) must span less than 1 GiB
+  if (p.N % BN || p.K % (NS * BK) || p.K == 0) return false;  // any M: rows past it are masked
+  // 32-bit buffer offsets: an A panel (up to 256 rows) and a B panel (256 rows
+  // or K rows x 256 columns) must span less than 1 GiB
   if (255 * p.lda + p.K >= (int64_t)1 << 29) return false;
   if ((b_row ? (p.K - 1) * p.ldb + 256 : 255 * p.ldb + p.K) >= (int64_t)1 << 29) return false;
   if (((uintptr_t)p.A & 15) || ((uintptr_t)p.B & 15) || ((uintptr_t)p.C & 15)) return false;
@@ -537,7 +542,8 @@ hipError_t launch_tile(const Problem &p, int variant, hipStream_t stream) {
   a.sA = p.sA;
   a.sB = p.sB;
   a.sC = p.sC;
-  a.tiles_m = (int32_t)(p.M / BM);
+  a.rows = p.rows;
+  a.tiles_m = (int32_t)((p.M + BM - 1) / BM);
   a.tiles_n = (int32_t)(p.N / BN);
   switch (variant) {
     case 0:

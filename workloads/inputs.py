@@ -116,11 +116,11 @@ def bits_to_f64(bits, fmt: str) -> np.ndarray:
 
 def _draw(rng: np.random.Generator, dist: tuple, n: int) -> np.ndarray:
     kind = dist[0]
-    if kind == "uniform":
+    if kind == "uniform" and len(dist) == 3:
         return rng.uniform(dist[1], dist[2], n)
-    if kind == "normal":
+    if kind == "normal" and len(dist) == 2:
         return rng.standard_normal(n) * dist[1]
-    raise ValueError(f"unknown distribution {dist!r}")
+    raise ValueError(f"distribution {dist!r}: expected ('uniform', lo, hi) or ('normal', scale)")
 
 
 ROWS_PER_BLOCK = 64
