@@ -66,22 +66,35 @@ def traffic_from_profiles(workload, kernel):
 
 # The measurement run that --summarize reads: each command's output directory
 # under RUN_DIR, and the command (run from /tmp, with TMPDIR=/tmp).
+# WORKLOAD_ARGS stands for the run's workload flags (none for the default run).
 PROFILE_COMMANDS = {
-    "bench.json": "python3 bench.py > RUN_DIR/bench.json",
+    "bench.json": "python3 bench.py WORKLOAD_ARGS > RUN_DIR/bench.json",
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d RUN_DIR/trace -o bench -- "
-             "python3 bench.py --no-cpu-baseline",
+             "python3 bench.py WORKLOAD_ARGS --no-cpu-baseline",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d RUN_DIR/fetch -o p -- "
-             "python3 bench.py --no-cpu-baseline --steps 5 --warmup 2",
+             "python3 bench.py WORKLOAD_ARGS --no-cpu-baseline --steps 5 --warmup 2",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d RUN_DIR/write -o p -- "
-             "python3 bench.py --no-cpu-baseline --steps 5 --warmup 2",
+             "python3 bench.py WORKLOAD_ARGS --no-cpu-baseline --steps 5 --warmup 2",
     "cal_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d RUN_DIR/cal_fetch -o c -- "
                  "python3 bench.py --calibrate-copy 1024",
     "cal_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d RUN_DIR/cal_write -o c -- "
                  "python3 bench.py --calibrate-copy 1024",
     "sq": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS "
           "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F16 GRBM_GUI_ACTIVE --output-format csv "
-          "-d RUN_DIR/sq -o p -- python3 bench.py --no-cpu-baseline --steps 5 --warmup 2",
+          "-d RUN_DIR/sq -o p -- python3 bench.py WORKLOAD_ARGS --no-cpu-baseline --steps 5 --warmup 2",
 }
+WORKLOAD_FLAGS = ("--workload", "--secondary", "--no-secondary")
+
+
+def workload_args(argv):
+    """The workload flags (with their values) among bench.py's arguments."""
+    out, it = [], iter(argv)
+    for a in it:
+        if a.split("=")[0] in WORKLOAD_FLAGS:
+            out.append(a)
+            if a in ("--workload", "--secondary"):
+                out.append(next(it, ""))
+    return " ".join(out)
 KERNEL_SYMBOL = {"tile_": "gemm_tile_kernel", "skinny_": "gemm_skinny_kernel", "splitk_": "gemm_splitk_kernel",
                  "masked_": "gemm_masked_kernel"}
 
@@ -116,7 +129,7 @@ def _pick(table, kernel):
 
 def summarize(run_dir):
     """Write profiles/ (kernel-trace and counter summaries, HBM traffic records) from one measurement run."""
-    from workloads import WORKLOADS
+    from workloads import lookup
 
     bench = json.load(open(os.path.join(run_dir, "bench.json")))
     jobs = [(bench["config"]["workload"], bench["roofline"]["kernel"], bench["ms_per_step"])]
@@ -126,7 +139,8 @@ def summarize(run_dir):
     if src != kernel_source_hash():
         print(f"--summarize: the run measured kernel source {src}, the tree now holds {kernel_source_hash()}; "
               "the traffic records will not be used by bench.py", file=sys.stderr)
-    cmd = lambda k: "cd /tmp && " + PROFILE_COMMANDS[k]  # noqa: E731
+    wargs = workload_args(bench.get("argv", []))
+    cmd = lambda k: " ".join(("cd /tmp && " + PROFILE_COMMANDS[k].replace("WORKLOAD_ARGS", wargs)).split())  # noqa: E731
     stats = _csv(os.path.join(run_dir, "trace", "*kernel_stats.csv"))
     by_name = {r["Name"]: (r, int(r["Calls"])) for r in stats}
     out = os.path.join(ROOT, "profiles")
@@ -152,7 +166,7 @@ def summarize(run_dir):
     copy_w = max(v["WRITE_SIZE"] for v in cal_w.values())
     fscale, wscale = copy_kib / copy_f, copy_kib / copy_w
     for wl, kern, ms in jobs:
-        w = WORKLOADS[wl]
+        w = lookup(wl)
         trace_row = by_name[_pick(by_name, kern)][0]
         sym_f = _pick({n: (None, 1) for n in fetch}, kern)
         f_kib, w_kib = fetch[sym_f]["FETCH_SIZE"], write[_pick({n: (None, 1) for n in write}, kern)]["WRITE_SIZE"]
@@ -215,12 +229,22 @@ class Setup:
         self.handle = self.stream.cuda_stream
         self.tsm = tsm
         self.torch = torch
-        self.args = (w.M, w.N, w.K, self.a, self.lda, self.la, self.sA, self.b, self.ldb, self.lb, self.sB, self.c,
-                     self.ldc, self.sC, w.batch, self.code)
-        self.kernel = tsm.tsm_gemm_kernel_name(*self.args)
+        # a grouped workload carries per-problem row counts, uploaded once like the operands
+        self.rows = w.rows() if hasattr(w, "rows") else None
+        if self.rows is not None:
+            self.rows_t = torch.from_numpy(self.rows).cuda()
+            self.args = (w.M, w.N, w.K, self.a, self.lda, self.la, self.sA, self.b, self.ldb, self.lb, self.sB,
+                         self.c, self.ldc, self.sC, self.rows_t, w.batch, self.code)
+            self.kernel = tsm.tsm_gemm_grouped_kernel_name(*self.args)
+            self.call = tsm.gemm_grouped
+        else:
+            self.args = (w.M, w.N, w.K, self.a, self.lda, self.la, self.sA, self.b, self.ldb, self.lb, self.sB,
+                         self.c, self.ldc, self.sC, w.batch, self.code)
+            self.kernel = tsm.tsm_gemm_kernel_name(*self.args)
+            self.call = tsm.gemm_strided_batched_ex
 
     def step(self):
-        self.tsm.gemm_strided_batched_ex(*self.args, self.handle)
+        self.call(*self.args, self.handle)
 
     def time_steps(self, n):
         torch = self.torch
@@ -252,7 +276,11 @@ class Setup:
         self.torch.cuda.synchronize()
         rng = np.random.default_rng(2024)
         z = rng.integers(0, w.batch, ncells)
-        i = rng.integers(0, w.M, ncells)
+        if self.rows is not None:  # only the rows each group computes
+            z = rng.choice(np.flatnonzero(self.rows > 0), ncells)
+            i = (rng.random(ncells) * self.rows[z]).astype(np.int64)
+        else:
+            i = rng.integers(0, w.M, ncells)
         j = rng.integers(0, w.N, ncells)
         host = self.c.cpu().numpy().astype(np.float64).reshape(w.batch, w.M, w.N)
         got = host[z, i, j]
@@ -316,7 +344,7 @@ def main():
     import torch
 
     import tiled_shared_memory_amd as tsm
-    from workloads import WORKLOADS
+    from workloads import lookup
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -332,7 +360,7 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": 2 * n}), flush=True)
         return
     tsm.load()
-    w = WORKLOADS[args.workload]
+    w = lookup(args.workload)
     s = Setup(w, torch, tsm)
     log(f"kernel {s.kernel}; warm-up {args.warmup}")
     for _ in range(args.warmup):
@@ -384,13 +412,16 @@ def main():
         "check": check,
         "roofline": roof,
         "kernel_source_hash": kernel_source_hash(),
+        "argv": sys.argv[1:],
     }
+    if s.rows is not None:
+        result["config"]["rows"] = s.rows.tolist()
     # free the headline operands before the secondary workload
     s_main = s
     del s
 
     if not args.no_secondary and args.secondary:
-        w2 = WORKLOADS[args.secondary]
+        w2 = lookup(args.secondary)
         s2 = Setup(w2, torch, tsm)
         for _ in range(max(3, args.warmup // 2)):
             s2.step()

@@ -34,6 +34,7 @@ struct KernelArgs {
   int32_t tiles_m, tiles_n;
   int32_t z0;  // first problem index covered by this launch
   const int32_t *rows;  // per-problem row counts in device memory, or null (every problem has M rows)
+  int32_t compact_groups;  // large-tile kernel, grouped call: number of groups, tiles numbered over valid ones only
 };
 
 // Rows of problem z: M, or for a grouped product the caller's count for z

@@ -55,6 +55,7 @@ constexpr int NS = TileInfo::STAGES;          // 4
 constexpr int ROW_BYTES = BK * 2;             // 64: 4 chunks of 16 bytes
 constexpr int TILE_BYTES = BM * ROW_BYTES;    // 16 KiB per operand slice
 constexpr int GROUP_M = 8;
+constexpr int64_t kMaxCompactGroups = 256;  // groups whose counts every workgroup scans
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) char lds_char;
@@ -308,6 +309,28 @@ __device__ __forceinline__ void slice(Ctx &c, int j, Frags<MI> (&fr)[2], Acc<MI>
   }
 }
 
+// Tile-rows of 256 that hold rows of problem g of a grouped call.
+__device__ __forceinline__ int work_rows(const KernelArgs &p, int g) { return (int)((rows_of(p, g) + BM - 1) / BM); }
+
+// The 8 XCDs take workgroups round-robin; re-deal index b of T so that each
+// XCD gets a contiguous run of tiles (the last T % 8 keep their index).
+__device__ __forceinline__ int xcd_remap(int b, int T) {
+  const int T8 = T & ~7;
+  return b < T8 ? (b & 7) * (T8 >> 3) + (b >> 3) : b;
+}
+
+// Tile (tm, tn) of run index pid over a tiles_m x tiles_n grid: groups of
+// GROUP_M tile rows, walked column by column.
+__device__ __forceinline__ void tile_order(int pid, int tiles_m, int tiles_n, int &tm, int &tn) {
+  const int per_group = GROUP_M * tiles_n;
+  const int group = pid / per_group;
+  const int first_m = group * GROUP_M;
+  const int gm = min(tiles_m - first_m, GROUP_M);
+  const int in_group = pid - group * per_group;
+  tm = first_m + in_group % gm;
+  tn = in_group / gm;
+}
+
 // Wide variant, sub-slice U of slab j (resident in stage S): U = 0 waits for
 // the slab and the barrier, reads sub-slice 0's fragments and refills the
 // other stage (freed by that barrier) with slab j+1 while the previous
@@ -355,19 +378,32 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
   const int lane = c.lane, wm = c.wm, wn = c.wn;
 
   // ---- tile order: per-XCD regrouping, then GROUP_M rows column by column
-  const int T = p.tiles_m * p.tiles_n;
-  int pid = blockIdx.x;
-  if ((T & 7) == 0) pid = (pid & 7) * (T >> 3) + (pid >> 3);
-  const int per_group = GROUP_M * p.tiles_n;
-  const int group = pid / per_group;
-  const int first_m = group * GROUP_M;
-  const int gm = min(p.tiles_m - first_m, GROUP_M);
-  const int in_group = pid - group * per_group;
-  const int tm = first_m + in_group % gm;
-  const int tn = in_group / gm;
+  int tm, tn;
+  int64_t z;
+  if (p.compact_groups) {
+    // Grouped call: number only the tiles that hold rows, group after group,
+    // so the per-XCD regrouping spreads the real work evenly over the XCDs
+    // (the counts are in device memory; every workgroup reads them).
+    const int G = p.compact_groups;
+    int V = 0;
+    for (int g = 0; g < G; ++g) V += work_rows(p, g);
+    V *= p.tiles_n;
+    if ((int)blockIdx.x >= V) return;  // uniform
+    int pid = xcd_remap(blockIdx.x, V);
+    int g = 0;
+    for (; g < G - 1; ++g) {
+      const int t = work_rows(p, g) * p.tiles_n;
+      if (pid < t) break;
+      pid -= t;
+    }
+    tile_order(pid, work_rows(p, g), p.tiles_n, tm, tn);
+    z = g;
+  } else {
+    tile_order(xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n), p.tiles_m, p.tiles_n, tm, tn);
+    z = (int64_t)p.z0 + blockIdx.y;
+  }
 
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int64_t z = (int64_t)p.z0 + blockIdx.y;
   const int64_t M = rows_of(p, z);  // this problem's rows
   if (m0 >= M) return;              // the whole tile lies past them (uniform)
   const int64_t vrows = M - m0 < BM ? M - m0 : BM;
@@ -490,6 +526,16 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
 template <bool BF16, bool OUT_F16, int MI, bool BROW, int KB>
 hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
   const int64_t tiles = (int64_t)base.tiles_m * base.tiles_n;
+  if (base.rows && batch <= kMaxCompactGroups && tiles * batch <= 0x7fffffffLL) {
+    // grouped call: one 1-D grid over every tile of every group; the kernel
+    // maps the first (valid) ones to real tiles and the rest exit
+    KernelArgs a = base;
+    a.z0 = 0;
+    a.compact_groups = (int32_t)batch;
+    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT_F16, MI, BROW, KB>), dim3((unsigned)(tiles * batch)), dim3(256), 0,
+                       stream, a);
+    return hipGetLastError();
+  }
   for (int64_t z0 = 0; z0 < batch; z0 += kMaxGridY) {
     KernelArgs a = base;
     a.z0 = (int32_t)z0;

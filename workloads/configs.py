@@ -17,6 +17,8 @@ from __future__ import annotations
 import math
 from dataclasses import dataclass, field
 
+import numpy as np
+
 from .inputs import BF16, F16, make_operands
 
 
@@ -75,3 +77,74 @@ WORKLOADS = {
 }
 
 ORDER = list(WORKLOADS)
+
+
+@dataclass(frozen=True)
+class GroupedWorkload:
+    """A grouped product: `groups` problems of capacity M rows, problem g using its first rows()[g] rows.
+
+    Shaped like a mixture-of-experts layer (the A[expert, :tokens, :] slice of
+    the Intel XPU Triton README): `tokens` routed rows are spread over the
+    groups by a seeded multinomial draw whose probabilities come from a
+    symmetric Dirichlet(2) draw, so the groups are unevenly loaded; each count
+    is capped at the capacity M.
+    """
+    name: str
+    groups: int
+    M: int               # row capacity of every group
+    N: int
+    K: int
+    tokens: int          # rows routed in total, before capping
+    in_fmt: str
+    out_fmt: str
+    a_layout: str
+    b_layout: str
+    dist: tuple = field(default=("uniform", -1.0, 1.0))
+    seed: int = 0
+
+    @property
+    def batch(self) -> int:
+        return self.groups
+
+    def rows(self) -> np.ndarray:
+        rng = np.random.default_rng([self.seed, 7])
+        p = rng.dirichlet([2.0] * self.groups)
+        return np.minimum(rng.multinomial(self.tokens, p), self.M).astype(np.int32)
+
+    @property
+    def flops(self) -> int:
+        return 2 * int(self.rows().sum()) * self.N * self.K
+
+    @property
+    def bytes(self) -> int:
+        """Algorithmic HBM bytes: the valid rows of A, every B, the valid rows of C."""
+        out_b = 4 if self.out_fmt == "f32" else 2
+        m = int(self.rows().sum())
+        return 2 * m * self.K + self.groups * 2 * self.K * self.N + out_b * m * self.N
+
+    def lds(self):
+        lda = self.K if self.a_layout == "row" else self.M
+        ldb = self.N if self.b_layout == "row" else self.K
+        return lda, ldb, self.N
+
+    def strides(self):
+        return self.M * self.K, self.K * self.N, self.M * self.N
+
+    def operands(self):
+        return make_operands(self.seed, self.groups, self.M, self.N, self.K, self.in_fmt, self.dist,
+                             self.a_layout, self.b_layout)
+
+
+# Measured beside the five workloads above; not one of them.
+GROUPED = {
+    w.name: w
+    for w in [
+        GroupedWorkload("moe_bf16_e8_t16384_n2048_k4096", 8, 4096, 2048, 4096, 16384, BF16, "f16", "row", "col",
+                        ("normal", 1.0 / 64.0), 5),
+    ]
+}
+
+
+def lookup(name: str):
+    """A workload of either kind by name."""
+    return WORKLOADS[name] if name in WORKLOADS else GROUPED[name]
