@@ -96,7 +96,8 @@ def workload_args(argv):
                 out.append(next(it, ""))
     return " ".join(out)
 KERNEL_SYMBOL = {"tile_": "gemm_tile_kernel", "skinny_": "gemm_skinny_kernel", "splitk_": "gemm_splitk_kernel",
-                 "masked_": "gemm_masked_kernel"}
+                 "masked_": "gemm_masked_kernel", "rowsum_wave": "rowsum_wave_kernel",
+                 "rowsum_block": "rowsum_block_kernel"}
 
 
 def _csv(path):
@@ -184,7 +185,8 @@ def summarize(run_dir):
         txt += [f"{k} = {v:.6g}" for k, v in sorted(c.items())]
         txt += [f"# LDS bank-conflict cycles / LDS active cycles = "
                 f"{c.get('SQ_LDS_BANK_CONFLICT', 0) / lds if lds else 0:.3f}",
-                f"# MFMA ops x 512 = {mops * 512:.6g} (2*M*N*K*batch = {w.flops:.6g})",
+                (f"# MFMA ops x 512 = {mops * 512:.6g} (2*M*N*K*batch = {w.flops:.6g})" if mops else
+                 "# no MFMA work"),
                 f"FETCH_SIZE = {f_kib:.6g} KiB, WRITE_SIZE = {w_kib:.6g} KiB",
                 f"# 1 GiB device copy: FETCH_SIZE = {copy_f:.6g} KiB, WRITE_SIZE = {copy_w:.6g} KiB "
                 f"-> read scale {fscale:.3f}, write scale {wscale:.3f}",
@@ -316,6 +318,57 @@ def cpu_baseline(orc, w, A, B, target_s):
             "seconds": t}
 
 
+def rowsum_bench(args, w, torch, tsm):
+    """Row-sum workload: one step is one rowsum call; HBM-bound, reported in GB/s."""
+    import numpy as np
+
+    import oracle
+
+    log(f"generating {w.name} inputs on the host")
+    X = w.operand()
+    code = {"f32": tsm.TSM_ROWSUM_F32, "f16": tsm.TSM_ROWSUM_F16, "bf16": tsm.TSM_ROWSUM_BF16}[w.fmt]
+    x = torch.from_numpy(X.view(np.float32 if w.fmt == "f32" else np.int16)).cuda()
+    out = torch.empty(w.R, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    kernel = tsm.tsm_rowsum_kernel_name(w.R, w.C, x, w.C, 1, code, out)
+
+    def time_steps(n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            tsm.rowsum(w.R, w.C, x, w.C, 1, code, out, stream.cuda_stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    time_steps(args.warmup)
+    ms = time_steps(args.steps) / args.steps
+    ms_i = statistics.median([(time_steps(12) - time_steps(2)) / 10 for _ in range(7)])
+    orc = oracle.default()
+    t0 = time.perf_counter()
+    ref, S = orc.rowsum(X, w.R, w.C, w.C, 1, w.fmt)
+    cpu_s = time.perf_counter() - t0
+    got = out.cpu().numpy().astype(np.float64)
+    ratio = float(np.max(np.abs(got - ref) / np.maximum(w.C * 2.0 ** -24 * S, 1e-300)))
+    gbs = w.bytes / (ms * 1e-3) / 1e9
+    return {
+        "metric": "row-sum GB/s (% of MI355X HBM peak)", "value": gbs, "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.fmt, "data": "synthetic",
+        "config": {"workload": w.name, "R": w.R, "C": w.C, "in": w.fmt, "seed": w.seed, "parallelism": "single GPU",
+                   "accumulate": "f32"},
+        "ms_per_step_interleaved_median": ms_i,
+        "check": {"rows": w.R, "max_err_over_bound": ratio, "pass": bool(ratio <= 1.0 and np.all(np.isfinite(got)))},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": traffic_from_profiles(w.name, kernel), "kernel": kernel,
+                     "algorithmic_bytes_per_launch": w.bytes, "algorithmic_flops_per_launch": w.flops},
+        "cpu_baseline": {"value": w.bytes / cpu_s / 1e9, "unit": "GB/s", "cores": orc.threads(), "kind": "oracle",
+                         "sample": f"all {w.R} rows, {cpu_s:.2f} s"},
+        "kernel_source_hash": kernel_source_hash(), "argv": sys.argv[1:],
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -361,6 +414,9 @@ def main():
         return
     tsm.load()
     w = lookup(args.workload)
+    if hasattr(w, "operand"):  # a row-sum workload
+        print(json.dumps(rowsum_bench(args, w, torch, tsm)), flush=True)
+        return
     s = Setup(w, torch, tsm)
     log(f"kernel {s.kernel}; warm-up {args.warmup}")
     for _ in range(args.warmup):

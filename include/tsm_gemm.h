@@ -132,6 +132,36 @@ int gemm_grouped(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, in
                  const void *B, int64_t ldb, int layout_b, int64_t strideB, void *C, int64_t ldc, int64_t strideC,
                  const int32_t *rows, int64_t groups, int dtype, void *stream);
 
+/* Element format of a row-sum input.  Sums are always float32. */
+#define TSM_ROWSUM_F32 0
+#define TSM_ROWSUM_F16 1
+#define TSM_ROWSUM_BF16 2
+
+/*
+ * rowsum -- out[r] := sum_c X[r*row_stride + c*col_stride], r < R, c < C.
+ * The tiled row-sum kernel of "A Dumb Triton Runtime Error" (sections "The
+ * kernel itself" through "Step 3: Cross-Lane Tree Reduction (tl.sum) and Scalar
+ * Store"): each element is converted to float32 and added into lane-local
+ * float32 accumulators, tiles past the row end contribute 0, and one
+ * cross-lane reduction per row is followed by one plain store.
+ *   R, C        : rows and columns, >= 0.  C = 0 writes zeros.
+ *   X           : device pointer, aligned to its element size (TSM_ROWSUM_*).
+ *   row_stride,
+ *   col_stride  : element strides, >= 0 (any view: transposed, sliced).
+ *   out         : device float32 array of R sums, 4-byte aligned, OVERWRITTEN
+ *                 (its previous contents never matter: "Making It Compile, and
+ *                 Why I'd Still Use the Original").  Must not overlap X.
+ * Accuracy: |out[r] - exact| <= C * 2^-24 * sum_c |X[r][c]|.  The reduction
+ * order is fixed, so results are bitwise reproducible.
+ * Errors and stream semantics as for gemm.
+ */
+int rowsum(int64_t R, int64_t C, const void *X, int64_t row_stride, int64_t col_stride, int xdtype, float *out,
+           void *stream);
+
+/* tsm_rowsum_kernel_name -- the kernel a rowsum call would launch, or NULL. */
+const char *tsm_rowsum_kernel_name(int64_t R, int64_t C, const void *X, int64_t row_stride, int64_t col_stride,
+                                   int xdtype, const float *out);
+
 /* Static text for a status code ("success", "invalid value", ...). */
 const char *tsm_status_string(int status);
 

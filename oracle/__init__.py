@@ -9,6 +9,7 @@ Functions:
   gemm_rows(...)   -> (C, S): full rows of every problem, float64
   gemm_points(...) -> (C, S): selected cells (sampled checks at full size)
   gemm_grouped(...) -> [(C_g, S_g)]: the first m_g rows of each problem
+  rowsum(...)       -> (out, S): row sums of a strided matrix, float64
   decode(bits, fmt)         : the oracle's own exact 16-bit -> float64 decode
   bound(...)                : the per-element acceptance bound
 
@@ -47,7 +48,8 @@ class Oracle:
     """ctypes handle on one build of the oracle library."""
 
     def __init__(self, path: str = LIBRARY):
-        if not os.path.exists(path):
+        stale = path == LIBRARY and os.path.exists(path) and os.path.getmtime(SOURCE) > os.path.getmtime(path)
+        if not os.path.exists(path) or stale:
             build(out=path)
         self.path = path
         lib = ctypes.CDLL(path)
@@ -64,6 +66,8 @@ class Oracle:
         lib.tsm_oracle_gemm_points.restype = None
         lib.tsm_oracle_decode.argtypes = [ptr, i64, i32, ptr]
         lib.tsm_oracle_decode.restype = None
+        lib.tsm_oracle_rowsum.argtypes = [i64, i64, ptr, i64, i64, i32, ptr, ptr]
+        lib.tsm_oracle_rowsum.restype = None
         lib.tsm_oracle_threads.argtypes = []
         lib.tsm_oracle_threads.restype = i32
         self.lib = lib
@@ -147,6 +151,20 @@ class Oracle:
                                   row_end=m)
             out.append((C[0], S[0]))
         return out
+
+
+    def rowsum(self, X, R, C, row_stride, col_stride, fmt):
+        """Row sums out[r] = sum_c X[r*row_stride + c*col_stride] and S[r] = sum_c |.| (float64).
+
+        X is the flat storage (uint16 patterns for "f16"/"bf16", float32 for "f32").
+        """
+        code = {"f16": 0, "bf16": 1, "f32": 2}[fmt]
+        X = np.ascontiguousarray(X, dtype=np.float32 if fmt == "f32" else np.uint16).reshape(-1)
+        out = np.zeros(R, dtype=np.float64)
+        S = np.zeros(R, dtype=np.float64)
+        self.lib.tsm_oracle_rowsum(R, C, X.ctypes.data, row_stride, col_stride, code, out.ctypes.data,
+                                   S.ctypes.data)
+        return out, S
 
 
 _DEFAULT = None

@@ -36,6 +36,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
+#include <string.h>
 
 /* f16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.  Exponent field
  * 0 holds zero and subnormals (fraction * 2^-24); field 31 holds inf/NaN. */
@@ -177,4 +178,39 @@ int tsm_oracle_threads(void) {
 #else
     return 1;
 #endif
+}
+
+/*
+ * Row sums -- the reduction of "A Dumb Triton Runtime Error" (section "The
+ * kernel itself": one sum per row of a strided matrix, each element widened
+ * before it is added):
+ *
+ *   out[r] = sum_{c=0..C-1} X[r*row_stride + c*col_stride], in float64, in
+ *            increasing c;   S[r] = sum_c |X[r][c]| (NULL: not wanted).
+ *
+ * fmt: 0 = f16, 1 = bf16, 2 = float32.  A float32 pattern widens to float64
+ * exactly (C's float -> double conversion).  Past-the-end columns do not exist
+ * in this definition, so the additive-identity padding of a tiled kernel is
+ * implicit.  Threads: OpenMP over rows; each row is one sequential sum.
+ */
+static double widen_f32(uint32_t bits) {
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+void tsm_oracle_rowsum(int64_t R, int64_t C, const void *X, int64_t row_stride, int64_t col_stride, int fmt,
+                       double *out, double *S) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r) {
+        double total = 0.0, magnitude = 0.0;
+        for (int64_t c = 0; c < C; ++c) {
+            const int64_t at = r * row_stride + c * col_stride;
+            const double v = fmt == 2 ? widen_f32(((const uint32_t *)X)[at]) : decode(((const uint16_t *)X)[at], fmt);
+            total += v;
+            magnitude += fabs(v);
+        }
+        out[r] = total;
+        if (S) S[r] = magnitude;
+    }
 }

@@ -308,6 +308,63 @@ def pin_grouped_integer(orc):
                 assert np.array_equal(S, np.matmul(np.abs(ai[g, :m]), np.abs(bi[g])))
 
 
+# ---------------------------------------------------------------- row sums
+def pin_rowsum_printed_examples(orc):
+    """The 2x3 matrix of ones sums to [3.0, 3.0] ("A Dumb Triton Runtime Error", "What I ran"), in every
+    input format; six ones across a ragged tile window sum to 6 (its Step 2, n_cols = 6)."""
+    g = _read_golden("rowsum_ones_2x3.txt")
+    R, C = int(g["M"][0]), int(g["K"][0])
+    x = np.array([float(v) for v in g["A"]]).reshape(R, C)
+    want = np.array([float(v) for v in g["C"]])
+    for fmt in ("f32", F16, BF16):
+        X = x.astype(np.float32) if fmt == "f32" else round_f64_to_bits(x, fmt).reshape(R, C)
+        out, S = orc.rowsum(X, R, C, C, 1, fmt)
+        assert np.array_equal(out, want) and np.array_equal(S, want)
+        out, _ = orc.rowsum(np.ones(6, np.float32) if fmt == "f32" else round_f64_to_bits(np.ones(6), fmt),
+                            1, 6, 6, 1, fmt)
+        assert out[0] == 6.0
+
+
+def pin_rowsum_integer_views(orc):
+    """Integer entries: exact sums, equal to numpy's int64 row sums of the same logical matrix, through a
+    contiguous, a padded, a column-strided and a transposed view (and empty rows give 0)."""
+    rng = np.random.default_rng(12)
+    R, C = 7, 45
+    for fmt in ("f32", F16, BF16):
+        vals = rng.integers(-50, 51, (R, C))
+        store = (lambda a: a.astype(np.float32)) if fmt == "f32" else (lambda a: round_f64_to_bits(a.astype(float), fmt))
+        want = vals.sum(axis=1)
+        want_s = np.abs(vals).sum(axis=1)
+        out, S = orc.rowsum(store(vals).reshape(-1), R, C, C, 1, fmt)
+        assert np.array_equal(out, want) and np.array_equal(S, want_s)
+        padded = np.zeros((R, C + 9), np.int64)
+        padded[:, :C] = vals
+        out, _ = orc.rowsum(store(padded).reshape(-1), R, C, C + 9, 1, fmt)
+        assert np.array_equal(out, want)
+        strided = np.zeros((R, 3 * C), np.int64)
+        strided[:, ::3] = vals
+        out, _ = orc.rowsum(store(strided).reshape(-1), R, C, 3 * C, 3, fmt)
+        assert np.array_equal(out, want)
+        # the transposed storage: element (r, c) at c*R + r
+        out, _ = orc.rowsum(store(np.ascontiguousarray(vals.T)).reshape(-1), R, C, 1, R, fmt)
+        assert np.array_equal(out, want)
+        out, S = orc.rowsum(store(vals).reshape(-1), R, 0, C, 1, fmt)
+        assert not out.any() and not S.any()
+
+
+def pin_rowsum_random_vs_fsum(orc):
+    """Random float32 rows (the page's 8 x 1000 shape): within the float64 summation bound of math.fsum,
+    the correctly rounded exact sum."""
+    rng = np.random.default_rng(13)
+    R, C = 8, 1000
+    x = rng.standard_normal((R, C)).astype(np.float32)
+    out, S = orc.rowsum(x.reshape(-1), R, C, C, 1, "f32")
+    for r in range(R):
+        exact = math.fsum(float(v) for v in x[r])
+        assert abs(out[r] - exact) <= (C - 1) * 2.0 ** -53 * S[r]
+        assert abs(S[r] - math.fsum(abs(float(v)) for v in x[r])) <= (C - 1) * 2.0 ** -53 * S[r]
+
+
 ALL_PINS = [
     pin_decode_f16_all_patterns,
     pin_decode_bf16_all_patterns,
@@ -319,4 +376,7 @@ ALL_PINS = [
     pin_integer_exact,
     pin_random_vs_numpy,
     pin_grouped_integer,
+    pin_rowsum_printed_examples,
+    pin_rowsum_integer_views,
+    pin_rowsum_random_vs_fsum,
 ]

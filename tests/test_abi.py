@@ -33,8 +33,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("gemm", "gemm_ex", "gemm_strided_batched", "gemm_strided_batched_ex", "gemm_grouped",
-              "tsm_status_string", "tsm_last_error_detail", "tsm_gemm_kernel_name", "tsm_gemm_grouped_kernel_name"):
+    for n in ("gemm", "gemm_ex", "gemm_strided_batched", "gemm_strided_batched_ex", "gemm_grouped", "rowsum",
+              "tsm_status_string", "tsm_last_error_detail", "tsm_gemm_kernel_name", "tsm_gemm_grouped_kernel_name",
+              "tsm_rowsum_kernel_name"):
         assert n in names
 
 
@@ -216,3 +217,41 @@ def test_plain_products_with_ragged_m_use_the_tile_kernel():
     """M need not be a multiple of 256 for the large-tile kernels: rows past M load as zero and are not stored."""
     assert tsm.tsm_gemm_kernel_name(8000, 8192, 8192, A0, 8192, 0, 0, B0, 8192, 1, 0, C0, 8192, 0, 1,
                                     3) == "tile_256x256x64_mi16"
+
+
+X0, O0 = 0x7F4000000000, 0x7F5000000000
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    ((-1, 3, X0, 3, 1, 0, O0), 1, "negative size"),
+    ((2, 3, X0, -3, 1, 0, O0), 1, "negative stride"),
+    ((2, 3, X0, 3, 1, 7, O0), 1, "xdtype"),
+    ((2, 3, 0, 3, 1, 0, O0), 1, "X is NULL"),
+    ((2, 3, X0, 3, 1, 0, 0), 1, "out is NULL"),
+    ((2, 3, X0 + 2, 3, 1, 0, O0), 1, "X not 4-byte aligned"),
+    ((2, 3, X0 + 1, 3, 1, 1, O0), 1, "X not 2-byte aligned"),
+    ((2, 3, X0, 3, 1, 0, O0 + 2), 1, "out not 4-byte aligned"),
+    ((2, 3, X0, 3, 1, 0, X0 + 8), 1, "out overlaps X"),
+    ((1 << 31, 3, X0, 3, 1, 0, O0), 2, "2^31"),
+    ((2, 1 << 62, X0, 1, 1 << 3, 0, O0), 2, "overflows"),
+])
+def test_rowsum_invalid_arguments_are_rejected(args, status, needle):
+    with pytest.raises(tsm.TsmError) as ei:
+        tsm.rowsum(*args, 0)
+    assert ei.value.status == status
+    assert needle in ei.value.detail
+
+
+def test_rowsum_empty_succeeds_without_launch():
+    assert tsm.rowsum(0, 5, 0, 5, 1, 0, 0, 0) == 0
+    assert tsm.tsm_rowsum_kernel_name(0, 5, X0, 5, 1, 0, O0) is None
+
+
+def test_rowsum_kernel_selection():
+    # many short contiguous aligned rows: a wave per row with 16-byte loads
+    assert tsm.tsm_rowsum_kernel_name(16384, 1000, X0, 1000, 1, 0, O0) == "rowsum_wave_vec16"
+    # rows whose starts are not 16-byte aligned, or a column stride: element loads
+    assert tsm.tsm_rowsum_kernel_name(16384, 1001, X0, 1001, 1, 0, O0) == "rowsum_wave_elem"
+    assert tsm.tsm_rowsum_kernel_name(16384, 1000, X0, 1, 16384, 1, O0) == "rowsum_wave_elem"
+    # few long rows: a workgroup per row
+    assert tsm.tsm_rowsum_kernel_name(8, 1 << 20, X0, 1 << 20, 1, 2, O0) == "rowsum_block_vec16"

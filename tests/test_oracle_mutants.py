@@ -31,6 +31,10 @@ MUTANTS = {
                                "const uint16_t *Bz = B;\n        /* step 1"),
     "row_window_offset_ignored": ("element(Az, row_begin + r, k, lda, a_col)", "element(Az, r, k, lda, a_col)"),
     "negated_sum": ("c += p;\n                    s += fabs(p);", "c -= p;\n                    s += fabs(p);"),
+    "rowsum_dropped_last_column": ("for (int64_t c = 0; c < C; ++c) {\n            const int64_t at",
+                                   "for (int64_t c = 0; c < C - 1; ++c) {\n            const int64_t at"),
+    "rowsum_col_stride_ignored": ("r * row_stride + c * col_stride;", "r * row_stride + c;"),
+    "rowsum_f32_read_as_f16": ("fmt == 2 ? widen_f32", "fmt == 3 ? widen_f32"),
 }
 
 

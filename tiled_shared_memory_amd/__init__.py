@@ -10,9 +10,10 @@ HIP kernels.
 from __future__ import annotations
 
 from ._lib import (TSM_BF16_F16, TSM_BF16_F32, TSM_COL, TSM_ERROR_INVALID_VALUE,  # noqa: F401
-                   TSM_ERROR_LAUNCH, TSM_ERROR_NOT_SUPPORTED, TSM_F16_F16, TSM_F16_F32, TSM_ROW, TSM_SUCCESS,
-                   TsmError, gemm, gemm_ex, gemm_grouped, gemm_strided_batched, gemm_strided_batched_ex, load,
-                   tsm_gemm_grouped_kernel_name, tsm_gemm_kernel_name, tsm_last_error_detail, tsm_status_string)
+                   TSM_ERROR_LAUNCH, TSM_ERROR_NOT_SUPPORTED, TSM_F16_F16, TSM_F16_F32, TSM_ROW, TSM_ROWSUM_BF16,
+                   TSM_ROWSUM_F16, TSM_ROWSUM_F32, TSM_SUCCESS, TsmError, gemm, gemm_ex, gemm_grouped,
+                   gemm_strided_batched, gemm_strided_batched_ex, load, rowsum, tsm_gemm_grouped_kernel_name,
+                   tsm_gemm_kernel_name, tsm_last_error_detail, tsm_rowsum_kernel_name, tsm_status_string)
 
 
 def dtype_code(in_dtype, out_dtype) -> int:

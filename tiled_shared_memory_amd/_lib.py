@@ -29,6 +29,10 @@ TSM_BF16_F16 = 3
 TSM_ROW = 0
 TSM_COL = 1
 
+TSM_ROWSUM_F32 = 0
+TSM_ROWSUM_F16 = 1
+TSM_ROWSUM_BF16 = 2
+
 # Every function the header declares, with its ctypes signature.
 _I64, _PTR, _INT = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
 SIGNATURES = {
@@ -46,6 +50,8 @@ SIGNATURES = {
                       _INT, _PTR], _INT),
     "tsm_gemm_grouped_kernel_name": ([_I64, _I64, _I64, _PTR, _I64, _INT, _I64, _PTR, _I64, _INT, _I64, _PTR, _I64,
                                       _I64, _PTR, _I64, _INT], ctypes.c_char_p),
+    "rowsum": ([_I64, _I64, _PTR, _I64, _I64, _INT, _PTR, _PTR], _INT),
+    "tsm_rowsum_kernel_name": ([_I64, _I64, _PTR, _I64, _I64, _INT, _PTR], ctypes.c_char_p),
 }
 
 
@@ -158,4 +164,14 @@ def tsm_gemm_grouped_kernel_name(M, N, K, A, lda, layout_a, strideA, B, ldb, lay
                                  groups, dtype):
     r = load().tsm_gemm_grouped_kernel_name(M, N, K, _ptr(A), lda, layout_a, strideA, _ptr(B), ldb, layout_b, strideB,
                                             _ptr(C), ldc, strideC, _ptr(rows), groups, dtype)
+    return r.decode() if r else None
+
+
+def rowsum(R, C, X, row_stride, col_stride, xdtype, out, stream=None):
+    lib = load()
+    return _check(lib, lib.rowsum(R, C, _ptr(X), row_stride, col_stride, xdtype, _ptr(out), _stream(stream)))
+
+
+def tsm_rowsum_kernel_name(R, C, X, row_stride, col_stride, xdtype, out):
+    r = load().tsm_rowsum_kernel_name(R, C, _ptr(X), row_stride, col_stride, xdtype, _ptr(out))
     return r.decode() if r else None

@@ -250,10 +250,54 @@ int run(const Plan &pl, void *stream) {
   return TSM_SUCCESS;
 }
 
+// Host checks of a row-sum call; on success `a` is filled (a.R == 0: nothing to do).
+int rowsum_check(int64_t R, int64_t C, const void *X, int64_t row_stride, int64_t col_stride, int xdtype,
+                 const float *out, RowsumArgs *a) {
+  g_detail[0] = '\0';
+  if (xdtype != TSM_ROWSUM_F32 && xdtype != TSM_ROWSUM_F16 && xdtype != TSM_ROWSUM_BF16)
+    return fail(TSM_ERROR_INVALID_VALUE, "unknown xdtype %d", xdtype);
+  if (R < 0 || C < 0) return fail(TSM_ERROR_INVALID_VALUE, "negative size R=%lld C=%lld", (long long)R, (long long)C);
+  if (row_stride < 0 || col_stride < 0) return fail(TSM_ERROR_INVALID_VALUE, "negative stride");
+  *a = RowsumArgs{X, (float *)out, R, C, row_stride, col_stride,
+                  xdtype == TSM_ROWSUM_F32 ? (int)RowsumInfo::F32
+                                           : xdtype == TSM_ROWSUM_F16 ? (int)RowsumInfo::F16 : (int)RowsumInfo::BF16};
+  if (R == 0) return TSM_SUCCESS;
+  if (R > 0x7fffffffLL) return fail(TSM_ERROR_NOT_SUPPORTED, "R exceeds 2^31-1");
+  if (!out) return fail(TSM_ERROR_INVALID_VALUE, "out is NULL");
+  if ((uintptr_t)out % 4) return fail(TSM_ERROR_INVALID_VALUE, "out not 4-byte aligned");
+  if (C == 0) return TSM_SUCCESS;  // empty sums: out := 0
+  const int64_t es = xdtype == TSM_ROWSUM_F32 ? 4 : 2;
+  if (!X) return fail(TSM_ERROR_INVALID_VALUE, "X is NULL");
+  if ((uintptr_t)X % (uintptr_t)es) return fail(TSM_ERROR_INVALID_VALUE, "X not %lld-byte aligned", (long long)es);
+  int64_t a1, a2, span, bytes;
+  if (!mul_ok(R - 1, row_stride, &a1) || !mul_ok(C - 1, col_stride, &a2) || !add_ok(a1, a2, &span) ||
+      !add_ok(span, 1, &span) || !mul_ok(span, es, &bytes))
+    return fail(TSM_ERROR_NOT_SUPPORTED, "X extent overflows int64");
+  if (ranges_overlap(out, R * 4, X, bytes)) return fail(TSM_ERROR_INVALID_VALUE, "out overlaps X");
+  return TSM_SUCCESS;
+}
+
 }  // namespace
 }  // namespace tsm
 
 extern "C" {
+
+int rowsum(int64_t R, int64_t C, const void *X, int64_t row_stride, int64_t col_stride, int xdtype, float *out,
+           void *stream) {
+  tsm::RowsumArgs a;
+  const int st = tsm::rowsum_check(R, C, X, row_stride, col_stride, xdtype, out, &a);
+  if (st != TSM_SUCCESS || R == 0) return st;
+  const hipError_t e = tsm::launch_rowsum(a, (hipStream_t)stream);
+  if (e != hipSuccess) return tsm::fail(TSM_ERROR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return TSM_SUCCESS;
+}
+
+const char *tsm_rowsum_kernel_name(int64_t R, int64_t C, const void *X, int64_t row_stride, int64_t col_stride,
+                                   int xdtype, const float *out) {
+  tsm::RowsumArgs a;
+  if (tsm::rowsum_check(R, C, X, row_stride, col_stride, xdtype, out, &a) != TSM_SUCCESS || R == 0) return nullptr;
+  return tsm::rowsum_name(a);
+}
 
 int gemm_strided_batched_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a,
                             int64_t strideA, const void *B, int64_t ldb, int layout_b, int64_t strideB, void *C,

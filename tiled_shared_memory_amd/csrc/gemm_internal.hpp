@@ -90,4 +90,24 @@ const char *skinny_name();
 hipError_t launch_tile(const Problem &p, int variant, hipStream_t stream);
 const char *tile_name(int variant);
 
+// ---- row sums ----------------------------------------------------------------
+// out[r] = sum_c X[r*row_stride + c*col_stride], float32 accumulation.
+struct RowsumInfo {
+  enum { F32 = 0, F16 = 1, BF16 = 2 };  // element format of X
+};
+struct RowsumArgs {
+  const void *X;
+  float *out;
+  int64_t R, C;
+  int64_t row_stride, col_stride;  // elements
+  int fmt;
+};
+struct RowsumPlan {
+  bool vec;    // 16-byte loads (contiguous, 16-byte aligned rows)
+  bool block;  // one workgroup per row (few long rows), else one wave per row
+};
+RowsumPlan rowsum_plan(const RowsumArgs &a);
+hipError_t launch_rowsum(const RowsumArgs &a, hipStream_t stream);
+const char *rowsum_name(const RowsumArgs &a);
+
 }  // namespace tsm

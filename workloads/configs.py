@@ -145,6 +145,48 @@ GROUPED = {
 }
 
 
+@dataclass(frozen=True)
+class RowsumWorkload:
+    """Row sums of an R x C matrix (contiguous rows), values uniform[-1, 1]."""
+    name: str
+    R: int
+    C: int
+    fmt: str             # "f32" | "f16" | "bf16"
+    seed: int = 0
+
+    @property
+    def flops(self) -> int:
+        return self.R * self.C  # one add per element
+
+    @property
+    def bytes(self) -> int:
+        """Algorithmic HBM bytes: X read once, the R float32 sums written once."""
+        return self.R * self.C * (4 if self.fmt == "f32" else 2) + 4 * self.R
+
+    def operand(self):
+        """Flat storage: float32 values, or 16-bit patterns (the shared generator, rows of C)."""
+        from .inputs import draw_matrix_bits
+
+        if self.fmt == "f32":
+            rng = np.random.default_rng([self.seed, 9])
+            return rng.uniform(-1.0, 1.0, self.R * self.C).astype(np.float32)
+        return draw_matrix_bits(self.seed, 0, 0, ("uniform", -1.0, 1.0), self.R, self.C, self.fmt).reshape(-1)
+
+
+ROWSUM = {
+    w.name: w
+    for w in [
+        # 1 GiB of float32: many rows, one wave each
+        RowsumWorkload("rowsum_f32_16384x16384", 16384, 16384, "f32", 6),
+        # the page's 8 x 1000 float32 rows (launch-bound)
+        RowsumWorkload("rowsum_f32_8x1000", 8, 1000, "f32", 7),
+    ]
+}
+
+
 def lookup(name: str):
-    """A workload of either kind by name."""
-    return WORKLOADS[name] if name in WORKLOADS else GROUPED[name]
+    """A workload of any kind by name."""
+    for table in (WORKLOADS, GROUPED, ROWSUM):
+        if name in table:
+            return table[name]
+    raise KeyError(name)
