@@ -84,6 +84,11 @@ struct Ctx {
   int nk, wave, lane;
 };
 
+// Cache-policy operand of the buffer loads: non-temporal.  B is read exactly
+// once, and streaming it past the caches measured 6.83 TB/s against 6.62 TB/s
+// with the default policy on the skinny batch.
+constexpr int kNonTemporal = 2;
+
 // Issue the loads of slice `k` into LDS stage (s, sa): B rows k*64 .. +63 of
 // the panel and the matching 16 x 64 A slice.
 __device__ __forceinline__ void issue(const Ctx &c, int k, char *s, char *sa) {
@@ -91,7 +96,7 @@ __device__ __forceinline__ void issue(const Ctx &c, int k, char *s, char *sa) {
 #pragma unroll
   for (int g = 0; g < LOADS; ++g)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rb, (lds_void *)(s + (c.wave * LOADS + g) * 1024), 16, c.offB[g], krow,
-                                             0, 0);
+                                             0, kNonTemporal);
   const uint32_t kbytes = (uint32_t)k * A_ROW_BYTES;
 #pragma unroll
   for (int g = 0; g < A_LOADS; ++g)
