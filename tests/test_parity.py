@@ -86,6 +86,32 @@ EDGE_SHAPES = [(1, 1, 1), (1, 2, 3), (2, 3, 1), (3, 1, 2), (15, 17, 16), (16, 16
                (255, 1, 64), (1, 300, 257), (64, 128, 128), (200, 8, 8), (8, 200, 1000)]
 
 
+MASKED_VARIANTS = ["masked_128x128x32_vec1", "masked_64x64x32_vec1", "masked_128x128x32_vec8",
+                   "masked_64x64x32_vec8"]
+
+
+@pytest.mark.parametrize("variant", MASKED_VARIANTS)
+@pytest.mark.parametrize("shape", [(1, 1, 1), (65, 63, 33), (130, 257, 100), (200, 72, 1000)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_masked_variants(orc, monkeypatch, variant, shape):
+    """Both tile sizes of the general kernel, forced, in all four layout pairs (16-byte loads where the
+    contiguous extents allow them)."""
+    M, N, K = shape
+    monkeypatch.setenv("TSM_GEMM_KERNEL", variant)
+    vec8 = variant.endswith("vec8")
+    for a_layout in ("row", "col"):
+        for b_layout in ("row", "col"):
+            ext_a = K if a_layout == "row" else M
+            ext_b = N if b_layout == "row" else K
+            if vec8 and (ext_a % 8 or ext_b % 8):
+                continue
+            A, B = make_operands(M + 2 * N + 3 * K, 1, M, N, K, F16, ("uniform", -1.0, 1.0), a_layout, b_layout)
+            say(f"[gpu] {variant} {shape} A:{a_layout} B:{b_layout}")
+            C = run(A, B, M, N, K, F16, "f32", a_layout=a_layout, b_layout=b_layout, kernel=variant)
+            Cr, S = orc.gemm_rows(A, B, M, N, K, F16, a_layout=a_layout, b_layout=b_layout)
+            check(C, Cr, S, K, "f32", f"{variant} {shape} {a_layout}/{b_layout}")
+
+
 @pytest.mark.parametrize("shape", EDGE_SHAPES, ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("in_fmt,out_fmt", [(F16, "f32"), (BF16, "f16"), (F16, "f16"), (BF16, "f32")])
 def test_edge_shapes(orc, shape, in_fmt, out_fmt):

@@ -43,14 +43,18 @@ bool ranges_overlap(const void *p, int64_t pbytes, const void *q, int64_t qbytes
   return a < b + (uintptr_t)qbytes && b < a + (uintptr_t)pbytes;
 }
 
-enum class Kernel { None, Masked8, Masked1, Tile32, Tile16, Tile16NN, TileW, TileWNN, Skinny, SplitK };
+enum class Kernel { None, Masked8, Masked1, Small8, Small1, Tile32, Tile16, Tile16NN, TileW, TileWNN, Skinny, SplitK };
 
 const char *kernel_name(Kernel k) {
   switch (k) {
     case Kernel::Masked8:
-      return masked_name(8);
+      return masked_name(8, 128);
     case Kernel::Masked1:
-      return masked_name(1);
+      return masked_name(1, 128);
+    case Kernel::Small8:
+      return masked_name(8, 64);
+    case Kernel::Small1:
+      return masked_name(1, 64);
     case Kernel::Tile32:
       return tile_name(0);
     case Kernel::Tile16:
@@ -184,6 +188,8 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
   out->kernel = (a8 && b8) ? Kernel::Masked8 : Kernel::Masked1;
   // few output tiles and deep K: take the parallelism from K
   const int64_t masked_tiles = tiles * batch;
+  // few 128 x 128 tiles otherwise: 64 x 64 tiles, four times the workgroups
+  if (masked_tiles < 256) out->kernel = (a8 && b8) ? Kernel::Small8 : Kernel::Small1;
   if (K > 0 && masked_tiles < 256 && splitk_supports(p)) out->kernel = Kernel::SplitK;
   // the 256 x 256 kernels once their tiles (one workgroup per CU) fill the chip
   const bool many = ((M + TileInfo::BM - 1) / TileInfo::BM) * (N / TileInfo::BN) * batch >= 256;
@@ -195,12 +201,13 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
   // variant that cannot run this problem is an error, never a silent fallback.
   const char *force = getenv("TSM_GEMM_KERNEL");
   if (force && *force) {
-    const Kernel all[] = {Kernel::Masked8, Kernel::Masked1, Kernel::Tile32, Kernel::Tile16, Kernel::Tile16NN, Kernel::TileW, Kernel::TileWNN, Kernel::Skinny, Kernel::SplitK};
+    const Kernel all[] = {Kernel::Masked8, Kernel::Masked1, Kernel::Small8, Kernel::Small1, Kernel::Tile32, Kernel::Tile16, Kernel::Tile16NN, Kernel::TileW, Kernel::TileWNN, Kernel::Skinny, Kernel::SplitK};
     Kernel want = Kernel::None;
     for (Kernel k : all)
       if (strcmp(force, kernel_name(k)) == 0) want = k;
     if (want == Kernel::None) return fail(TSM_ERROR_INVALID_VALUE, "TSM_GEMM_KERNEL=%s names no kernel", force);
-    const bool ok = want == Kernel::Masked1 || (want == Kernel::Masked8 && a8 && b8) ||
+    const bool ok = want == Kernel::Masked1 || want == Kernel::Small1 ||
+                    ((want == Kernel::Masked8 || want == Kernel::Small8) && a8 && b8) ||
                     ((want == Kernel::Tile32 || want == Kernel::Tile16 || want == Kernel::TileW) && K > 0 &&
                      tile_supports(p, false)) ||
                     ((want == Kernel::Tile16NN || want == Kernel::TileWNN) && K > 0 && tile_supports(p, true)) ||
@@ -219,10 +226,16 @@ int run(const Plan &pl, void *stream) {
     case Kernel::None:
       return TSM_SUCCESS;
     case Kernel::Masked8:
-      e = launch_masked(pl.p, 8, s);
+      e = launch_masked(pl.p, 8, 128, s);
       break;
     case Kernel::Masked1:
-      e = launch_masked(pl.p, 1, s);
+      e = launch_masked(pl.p, 1, 128, s);
+      break;
+    case Kernel::Small8:
+      e = launch_masked(pl.p, 8, 64, s);
+      break;
+    case Kernel::Small1:
+      e = launch_masked(pl.p, 1, 64, s);
       break;
     case Kernel::Tile32:
       e = launch_tile(pl.p, 0, s);

@@ -55,8 +55,9 @@ constexpr int64_t kMaxGridY = 65535;
 struct MaskedInfo {
   static constexpr int BM = 128, BN = 128, BK = 32, THREADS = 256;
 };
-hipError_t launch_masked(const Problem &p, int vec, hipStream_t stream);
-const char *masked_name(int vec);
+// tile: 128 (128 x 128) or 64 (64 x 64, for problems with few 128-tiles).
+hipError_t launch_masked(const Problem &p, int vec, int tile, hipStream_t stream);
+const char *masked_name(int vec, int tile);
 
 // Large-tile kernel: A row-major, B either layout, N a multiple of 256, K a
 // multiple of 128, 16-byte aligned rows; any M (rows past M, or past a grouped

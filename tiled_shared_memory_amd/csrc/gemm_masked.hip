@@ -1,7 +1,8 @@
 // Masked, register-staged LDS GEMM kernel for gfx950: the general path.
 //
 // It handles every layout, every alignment and ragged M, N and K.  Each
-// 256-thread workgroup owns a 128 x 128 tile of C and walks K in slices of
+// 256-thread workgroup owns a T x T tile of C (T = 128, or 64 when the
+// 128-tile grid is too small to occupy the chip) and walks K in slices of
 // BK = 32 ("The PTSS Cliff", section "The Idea: Stage in SLM, Tile K": only one
 // K slice is live in registers, the float32 accumulator is carried across the
 // loop).  Unlike the page's pass, which stages whole operands once, the slices
@@ -22,9 +23,9 @@
 // aligned and consecutive rows start on different banks).  An operand that is
 // contiguous along M or N is transposed element by element on its way into LDS.
 //
-// Compute: 4 waves in a 2 x 2 grid, each owning 64 x 64 of the tile as 2 x 2
-// blocks of v_mfma_f32_32x32x16 (64 accumulator registers per lane, fixed by
-// the tile, never by K).
+// Compute: 4 waves in a 2 x 2 grid, each owning (T/2) x (T/2) of the tile as
+// blocks of v_mfma_f32_32x32x16 (2 x 2 blocks, 64 accumulator registers per
+// lane, for T = 128; one block for T = 64): fixed by the tile, never by K.
 //
 // Epilogue: masked stores of rows < M and columns < N, float32 or f16 (round to
 // nearest even); C's padding beyond N is never touched.
@@ -36,16 +37,14 @@
 namespace tsm {
 namespace {
 
-constexpr int BM = MaskedInfo::BM;
-constexpr int BN = MaskedInfo::BN;
 constexpr int BK = MaskedInfo::BK;
 constexpr int THREADS = MaskedInfo::THREADS;
 constexpr int PITCH = BK + 8;  // LDS row pitch in 16-bit elements (80 bytes)
 
-// Staging registers for one operand tile (OUTER x BK elements).
-template <int VEC>
+// Staging registers for one operand tile (T x BK elements).
+template <int T, int VEC>
 struct Stage {
-  static constexpr int kLoads = (128 * BK) / (THREADS * VEC);  // loads per thread
+  static constexpr int kLoads = (T * BK) / (THREADS * VEC);  // loads per thread
   using Vec = typename std::conditional<VEC == 8, u32x4, uint16_t>::type;
   Vec v[kLoads];
 };
@@ -53,11 +52,11 @@ struct Stage {
 // Fetch the OUTER x BK slice starting at (o0, k0) of an operand.
 //   KMAJ: element (o, k) at X[o*ld + k]   (K contiguous)
 //  !KMAJ: element (o, k) at X[k*ld + o]   (outer contiguous)
-template <bool KMAJ, int VEC>
-__device__ __forceinline__ void fetch(Stage<VEC> &st, const uint16_t *X, int64_t ld, int64_t outer_total,
+template <int T, bool KMAJ, int VEC>
+__device__ __forceinline__ void fetch(Stage<T, VEC> &st, const uint16_t *X, int64_t ld, int64_t outer_total,
                                       int64_t K, int64_t o0, int64_t k0, int tid) {
 #pragma unroll
-  for (int r = 0; r < Stage<VEC>::kLoads; ++r) {
+  for (int r = 0; r < Stage<T, VEC>::kLoads; ++r) {
     const int v = tid + r * THREADS;
     int o, k;
     if constexpr (KMAJ) {
@@ -65,7 +64,7 @@ __device__ __forceinline__ void fetch(Stage<VEC> &st, const uint16_t *X, int64_t
       o = v / PER_ROW;
       k = (v % PER_ROW) * VEC;
     } else {
-      constexpr int PER_ROW = 128 / VEC;  // vectors per k row
+      constexpr int PER_ROW = T / VEC;  // vectors per k row
       k = v / PER_ROW;
       o = (v % PER_ROW) * VEC;
     }
@@ -83,10 +82,10 @@ __device__ __forceinline__ void fetch(Stage<VEC> &st, const uint16_t *X, int64_t
 }
 
 // Write the staged slice into an LDS tile laid out [outer][PITCH], K contiguous.
-template <bool KMAJ, int VEC>
-__device__ __forceinline__ void commit(const Stage<VEC> &st, uint16_t *s, int tid) {
+template <int T, bool KMAJ, int VEC>
+__device__ __forceinline__ void commit(const Stage<T, VEC> &st, uint16_t *s, int tid) {
 #pragma unroll
-  for (int r = 0; r < Stage<VEC>::kLoads; ++r) {
+  for (int r = 0; r < Stage<T, VEC>::kLoads; ++r) {
     const int v = tid + r * THREADS;
     if constexpr (KMAJ) {
       constexpr int PER_ROW = BK / VEC;
@@ -96,7 +95,7 @@ __device__ __forceinline__ void commit(const Stage<VEC> &st, uint16_t *s, int ti
       else
         s[o * PITCH + k] = st.v[r];
     } else {
-      constexpr int PER_ROW = 128 / VEC;
+      constexpr int PER_ROW = T / VEC;
       const int k = v / PER_ROW, o = (v % PER_ROW) * VEC;
       if constexpr (VEC == 8) {
         const u32x4 w = st.v[r];
@@ -109,10 +108,12 @@ __device__ __forceinline__ void commit(const Stage<VEC> &st, uint16_t *s, int ti
   }
 }
 
-template <bool BF16, bool OUT_F16, bool A_KMAJ, bool B_KMAJ, int VEC>
+template <int T, bool BF16, bool OUT_F16, bool A_KMAJ, bool B_KMAJ, int VEC>
 __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * PITCH];
+  constexpr int W = T / 2;    // wave tile
+  constexpr int NB = W / 32;  // 32 x 32 MFMA blocks per wave and dimension
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][T * PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][T * PITCH];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -120,27 +121,27 @@ __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
   const int wm = wave >> 1, wn = wave & 1;
 
   const int tile = blockIdx.x;
-  const int64_t m0 = (int64_t)(tile / p.tiles_n) * BM;
-  const int64_t n0 = (int64_t)(tile % p.tiles_n) * BN;
+  const int64_t m0 = (int64_t)(tile / p.tiles_n) * T;
+  const int64_t n0 = (int64_t)(tile % p.tiles_n) * T;
   const int64_t z = (int64_t)p.z0 + blockIdx.y;
   const int64_t M = rows_of(p, z);  // this problem's rows
   if (m0 >= M) return;              // the whole tile lies past them (uniform)
   const uint16_t *A = p.A + z * p.sA;
   const uint16_t *B = p.B + z * p.sB;
 
-  f32x16 acc[2][2];
+  f32x16 acc[NB][NB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
 
   const int64_t nk = (p.K + BK - 1) / BK;
-  Stage<VEC> ra, rb;
+  Stage<T, VEC> ra, rb;
   if (nk > 0) {
-    fetch<A_KMAJ, VEC>(ra, A, p.lda, M, p.K, m0, 0, tid);
-    fetch<B_KMAJ, VEC>(rb, B, p.ldb, p.N, p.K, n0, 0, tid);
-    commit<A_KMAJ, VEC>(ra, sA[0], tid);
-    commit<B_KMAJ, VEC>(rb, sB[0], tid);
+    fetch<T, A_KMAJ, VEC>(ra, A, p.lda, M, p.K, m0, 0, tid);
+    fetch<T, B_KMAJ, VEC>(rb, B, p.ldb, p.N, p.K, n0, 0, tid);
+    commit<T, A_KMAJ, VEC>(ra, sA[0], tid);
+    commit<T, B_KMAJ, VEC>(rb, sB[0], tid);
   }
   __syncthreads();
 
@@ -148,53 +149,53 @@ __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
     const int cur = kt & 1;
     const bool more = kt + 1 < nk;
     if (more) {  // next slice in flight while this one is multiplied
-      fetch<A_KMAJ, VEC>(ra, A, p.lda, M, p.K, m0, (kt + 1) * BK, tid);
-      fetch<B_KMAJ, VEC>(rb, B, p.ldb, p.N, p.K, n0, (kt + 1) * BK, tid);
+      fetch<T, A_KMAJ, VEC>(ra, A, p.lda, M, p.K, m0, (kt + 1) * BK, tid);
+      fetch<T, B_KMAJ, VEC>(rb, B, p.ldb, p.N, p.K, n0, (kt + 1) * BK, tid);
     }
     const uint16_t *a_s = sA[cur];
     const uint16_t *b_s = sB[cur];
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       const int kk = ks * 16 + (lane >> 5) * 8;
-      u32x4 af[2], bf[2];
+      u32x4 af[NB], bf[NB];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        af[i] = *reinterpret_cast<const u32x4 *>(a_s + (wm * 64 + i * 32 + (lane & 31)) * PITCH + kk);
-        bf[i] = *reinterpret_cast<const u32x4 *>(b_s + (wn * 64 + i * 32 + (lane & 31)) * PITCH + kk);
+      for (int i = 0; i < NB; ++i) {
+        af[i] = *reinterpret_cast<const u32x4 *>(a_s + (wm * W + i * 32 + (lane & 31)) * PITCH + kk);
+        bf[i] = *reinterpret_cast<const u32x4 *>(b_s + (wn * W + i * 32 + (lane & 31)) * PITCH + kk);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < NB; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_32x32x16<BF16>(af[i], bf[j], acc[i][j]);
+        for (int j = 0; j < NB; ++j) acc[i][j] = mfma_32x32x16<BF16>(af[i], bf[j], acc[i][j]);
     }
     if (more) {
-      commit<A_KMAJ, VEC>(ra, sA[cur ^ 1], tid);
-      commit<B_KMAJ, VEC>(rb, sB[cur ^ 1], tid);
+      commit<T, A_KMAJ, VEC>(ra, sA[cur ^ 1], tid);
+      commit<T, B_KMAJ, VEC>(rb, sB[cur ^ 1], tid);
     }
     __syncthreads();
   }
 
   void *C = OUT_F16 ? (void *)((uint16_t *)p.C + z * p.sC) : (void *)((float *)p.C + z * p.sC);
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int64_t col = n0 + wn * 64 + j * 32 + (lane & 31);
+        const int64_t row = m0 + wm * W + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int64_t col = n0 + wn * W + j * 32 + (lane & 31);
         store_masked<OUT_F16>(C, p.ldc, M, p.N, row, col, acc[i][j][r]);
       }
 }
 
-template <bool BF16, bool OUT_F16, bool A_KMAJ, bool B_KMAJ, int VEC>
+template <int T, bool BF16, bool OUT_F16, bool A_KMAJ, bool B_KMAJ, int VEC>
 hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
   const int64_t tiles = (int64_t)base.tiles_m * base.tiles_n;
   for (int64_t z0 = 0; z0 < batch; z0 += kMaxGridY) {
     KernelArgs a = base;
     a.z0 = (int32_t)z0;
     const int64_t nz = batch - z0 < kMaxGridY ? batch - z0 : kMaxGridY;
-    hipLaunchKernelGGL((gemm_masked_kernel<BF16, OUT_F16, A_KMAJ, B_KMAJ, VEC>), dim3((unsigned)tiles, (unsigned)nz),
+    hipLaunchKernelGGL((gemm_masked_kernel<T, BF16, OUT_F16, A_KMAJ, B_KMAJ, VEC>), dim3((unsigned)tiles, (unsigned)nz),
                        dim3(THREADS), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -202,25 +203,25 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
   return hipSuccess;
 }
 
-template <bool BF16, bool OUT_F16, int VEC>
+template <int T, bool BF16, bool OUT_F16, int VEC>
 hipError_t dispatch_layout(const Problem &p, const KernelArgs &a, hipStream_t s) {
   const bool a_kmaj = !p.a_col, b_kmaj = p.b_col;
-  if (a_kmaj && b_kmaj) return launch_t<BF16, OUT_F16, true, true, VEC>(a, p.batch, s);
-  if (a_kmaj && !b_kmaj) return launch_t<BF16, OUT_F16, true, false, VEC>(a, p.batch, s);
-  if (!a_kmaj && b_kmaj) return launch_t<BF16, OUT_F16, false, true, VEC>(a, p.batch, s);
-  return launch_t<BF16, OUT_F16, false, false, VEC>(a, p.batch, s);
+  if (a_kmaj && b_kmaj) return launch_t<T, BF16, OUT_F16, true, true, VEC>(a, p.batch, s);
+  if (a_kmaj && !b_kmaj) return launch_t<T, BF16, OUT_F16, true, false, VEC>(a, p.batch, s);
+  if (!a_kmaj && b_kmaj) return launch_t<T, BF16, OUT_F16, false, true, VEC>(a, p.batch, s);
+  return launch_t<T, BF16, OUT_F16, false, false, VEC>(a, p.batch, s);
 }
 
-template <int VEC>
+template <int T, int VEC>
 hipError_t dispatch_types(const Problem &p, const KernelArgs &a, hipStream_t s) {
   if (p.in_bf16)
-    return p.out_f16 ? dispatch_layout<true, true, VEC>(p, a, s) : dispatch_layout<true, false, VEC>(p, a, s);
-  return p.out_f16 ? dispatch_layout<false, true, VEC>(p, a, s) : dispatch_layout<false, false, VEC>(p, a, s);
+    return p.out_f16 ? dispatch_layout<T, true, true, VEC>(p, a, s) : dispatch_layout<T, true, false, VEC>(p, a, s);
+  return p.out_f16 ? dispatch_layout<T, false, true, VEC>(p, a, s) : dispatch_layout<T, false, false, VEC>(p, a, s);
 }
 
 }  // namespace
 
-hipError_t launch_masked(const Problem &p, int vec, hipStream_t stream) {
+hipError_t launch_masked(const Problem &p, int vec, int tile, hipStream_t stream) {
   KernelArgs a{};
   a.A = p.A;
   a.B = p.B;
@@ -235,11 +236,15 @@ hipError_t launch_masked(const Problem &p, int vec, hipStream_t stream) {
   a.sB = p.sB;
   a.sC = p.sC;
   a.rows = p.rows;
-  a.tiles_m = (int32_t)((p.M + BM - 1) / BM);
-  a.tiles_n = (int32_t)((p.N + BN - 1) / BN);
-  return vec == 8 ? dispatch_types<8>(p, a, stream) : dispatch_types<1>(p, a, stream);
+  a.tiles_m = (int32_t)((p.M + tile - 1) / tile);
+  a.tiles_n = (int32_t)((p.N + tile - 1) / tile);
+  if (tile == 64) return vec == 8 ? dispatch_types<64, 8>(p, a, stream) : dispatch_types<64, 1>(p, a, stream);
+  return vec == 8 ? dispatch_types<128, 8>(p, a, stream) : dispatch_types<128, 1>(p, a, stream);
 }
 
-const char *masked_name(int vec) { return vec == 8 ? "masked_128x128x32_vec8" : "masked_128x128x32_vec1"; }
+const char *masked_name(int vec, int tile) {
+  if (tile == 64) return vec == 8 ? "masked_64x64x32_vec8" : "masked_64x64x32_vec1";
+  return vec == 8 ? "masked_128x128x32_vec8" : "masked_128x128x32_vec1";
+}
 
 }  // namespace tsm
