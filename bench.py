@@ -209,8 +209,9 @@ def summarize(run_dir):
 class Setup:
     """Inputs of one workload uploaded to the GPU, and a closure that runs one step."""
 
-    def __init__(self, w, torch, tsm):
+    def __init__(self, w, torch, tsm, act=0, slope=0.0):
         self.w = w
+        self.act, self.slope = act, slope
         log(f"generating {w.name} inputs on the host")
         t0 = time.time()
         self.A, self.B = w.operands()
@@ -244,6 +245,9 @@ class Setup:
                          self.c, self.ldc, self.sC, w.batch, self.code)
             self.kernel = tsm.tsm_gemm_kernel_name(*self.args)
             self.call = tsm.gemm_strided_batched_ex
+            if act:  # the same product with an activation fused into the epilogue
+                self.args = self.args + (act, slope)
+                self.call = tsm.gemm_strided_batched_act
 
     def step(self):
         self.call(*self.args, self.handle)
@@ -284,11 +288,12 @@ class Setup:
         else:
             i = rng.integers(0, w.M, ncells)
         j = rng.integers(0, w.N, ncells)
-        host = self.c.cpu().numpy().astype(np.float64).reshape(w.batch, w.M, w.N)
+        host = self.c.float().cpu().numpy().astype(np.float64).reshape(w.batch, w.M, w.N)
         got = host[z, i, j]
         ref, S = orc.gemm_points(self.A, self.B, w.M, w.N, w.K, w.in_fmt, z, i, j, strideA=self.A[0].size,
                                  strideB=self.B[0].size, a_layout=w.a_layout, b_layout=w.b_layout)
-        bnd = oracle.bound(w.K, S, w.out_fmt, got)
+        ref = oracle.activate(ref, self.act, self.slope)
+        bnd = oracle.bound(w.K, S, w.out_fmt, got, self.act, self.slope)
         ratio = float(np.max(np.abs(got - ref) / np.where(bnd > 0, bnd, 1.0)))
         return {"cells": ncells, "max_err_over_bound": ratio, "pass": bool(ratio <= 1.0 and np.all(np.isfinite(got)))}
 
@@ -381,6 +386,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (to scale HBM counters)")
+    ap.add_argument("--activation", choices=["none", "relu", "leaky_relu"], default="none",
+                    help="fuse an activation into the epilogue (the result is checked through it)")
+    ap.add_argument("--slope", type=float, default=0.01, help="leaky ReLU slope")
     ap.add_argument("--summarize", metavar="RUN_DIR",
                     help="no GPU: write profiles/ from the rocprofv3 output of the commands in PROFILE_COMMANDS")
     args = ap.parse_args()
@@ -417,7 +425,8 @@ def main():
     if hasattr(w, "operand"):  # a row-sum workload
         print(json.dumps(rowsum_bench(args, w, torch, tsm)), flush=True)
         return
-    s = Setup(w, torch, tsm)
+    act = {"none": 0, "relu": 1, "leaky_relu": 2}[args.activation]
+    s = Setup(w, torch, tsm, act, args.slope if act == 2 else 0.0)
     log(f"kernel {s.kernel}; warm-up {args.warmup}")
     for _ in range(args.warmup):
         s.step()
@@ -472,6 +481,10 @@ def main():
     }
     if s.rows is not None:
         result["config"]["rows"] = s.rows.tolist()
+    if act:
+        result["config"]["activation"] = args.activation
+        if act == 2:
+            result["config"]["slope"] = args.slope
     # free the headline operands before the secondary workload
     s_main = s
     del s

@@ -58,11 +58,20 @@ extern "C" {
 #define TSM_ERROR_NOT_SUPPORTED 2 /* valid, but beyond this library's limits     */
 #define TSM_ERROR_LAUNCH 3        /* the HIP runtime refused or failed a launch */
 
-/* dtype: operand format and output format.  Accumulation is always float32. */
+/* dtype: operand format and output format.  Accumulation is always float32;
+ * a 16-bit output is rounded to nearest even from the float32 result. */
 #define TSM_F16_F32 0
 #define TSM_F16_F16 1
 #define TSM_BF16_F32 2
 #define TSM_BF16_F16 3
+#define TSM_F16_BF16 4
+#define TSM_BF16_BF16 5
+
+/* Epilogue activation of gemm_strided_batched_act, applied to the float32
+ * result before the output conversion. */
+#define TSM_ACT_NONE 0
+#define TSM_ACT_RELU 1       /* x > 0 ? x : 0          */
+#define TSM_ACT_LEAKY_RELU 2 /* x > 0 ? x : slope * x  */
 
 /* Storage layout of an operand. */
 #define TSM_ROW 0
@@ -74,7 +83,8 @@ extern "C" {
  *   A, lda    : operand A and its leading dimension (>= max(1, K)).
  *   B, ldb    : operand B and its leading dimension (>= max(1, N)).
  *   C, ldc    : result, leading dimension >= max(1, N).
- *   dtype     : one of TSM_F16_F32, TSM_F16_F16, TSM_BF16_F32, TSM_BF16_F16.
+ *   dtype     : operand -> output format: TSM_F16_F32, TSM_F16_F16, TSM_BF16_F32,
+ *               TSM_BF16_F16, TSM_F16_BF16 or TSM_BF16_BF16.
  *   stream    : hipStream_t to enqueue on (NULL = null stream).
  * Returns a status code.  M = 0 or N = 0 succeeds without launching.
  * Errors (TSM_ERROR_INVALID_VALUE): negative size; NULL pointer with work to do;
@@ -161,6 +171,23 @@ int rowsum(int64_t R, int64_t C, const void *X, int64_t row_stride, int64_t col_
 /* tsm_rowsum_kernel_name -- the kernel a rowsum call would launch, or NULL. */
 const char *tsm_rowsum_kernel_name(int64_t R, int64_t C, const void *X, int64_t row_stride, int64_t col_stride,
                                    int xdtype, const float *out);
+
+/*
+ * gemm_strided_batched_act -- gemm_strided_batched_ex with an elementwise
+ * activation fused into the epilogue: C := act(A.B), act applied to each
+ * float32 result before it is converted and stored.  The ACTIVATION
+ * meta-parameter of the Intel XPU Triton README's matmul signature ("Use
+ * Proper Type Annotations") names such a fused activation; the pages do not
+ * say which, so the plainest piecewise-linear ones are offered.
+ *   activation: TSM_ACT_NONE, TSM_ACT_RELU or TSM_ACT_LEAKY_RELU.
+ *   slope     : the factor leaky ReLU applies to negative values (finite);
+ *               ignored otherwise.
+ * Other arguments and rules as for gemm_strided_batched_ex.
+ */
+int gemm_strided_batched_act(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a,
+                             int64_t strideA, const void *B, int64_t ldb, int layout_b, int64_t strideB, void *C,
+                             int64_t ldc, int64_t strideC, int64_t batch, int dtype, int activation, float slope,
+                             void *stream);
 
 /* Static text for a status code ("success", "invalid value", ...). */
 const char *tsm_status_string(int status);

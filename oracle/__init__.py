@@ -190,14 +190,43 @@ def half_ulp_f16(x) -> np.ndarray:
     return 0.5 * np.exp2(e - 10.0)
 
 
-def bound(K: int, S, out_fmt: str, c_gpu=None) -> np.ndarray:
-    """Per-element acceptance bound |C_gpu - C_ref| <= K * 2^-24 * S (+ f16 half-ulp).
+def half_ulp_bf16(x) -> np.ndarray:
+    """Half the spacing of bf16 numbers at |x| (float64), 2^-134 at and below the subnormal range."""
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    e = np.where(ax > 0, np.maximum(e, -126.0), -126.0)
+    return 0.5 * np.exp2(e - 7.0)
 
-    The float32-accumulation term holds for any summation order under
-    round-to-nearest; for f16 output, half an f16 ulp at the stored value is
-    added for the final conversion.
+
+ACT_NONE, ACT_RELU, ACT_LEAKY_RELU = 0, 1, 2
+
+
+def activate(C, act: int, slope: float = 0.0) -> np.ndarray:
+    """The epilogue activation on exact (float64) results: x, max(x, 0), or x > 0 ? x : slope * x."""
+    C = np.asarray(C, dtype=np.float64)
+    if act == ACT_NONE:
+        return C
+    if act == ACT_RELU:
+        return np.where(C > 0, C, 0.0)
+    return np.where(C > 0, C, float(slope) * C)
+
+
+def bound(K: int, S, out_fmt: str, c_gpu=None, act: int = ACT_NONE, slope: float = 0.0) -> np.ndarray:
+    """Per-element acceptance bound on |C_gpu - act(C_ref)|.
+
+    K * 2^-24 * S bounds the float32 accumulation for any summation order under
+    round-to-nearest.  An activation with Lipschitz constant L (1 for ReLU,
+    max(1, |slope|) for leaky ReLU) scales it by L, and leaky ReLU's float32
+    product adds half a float32 ulp of the result.  A 16-bit output adds half an
+    ulp of its format at the stored value.
     """
-    b = float(K) * U * np.asarray(S, dtype=np.float64)
+    lip = max(1.0, abs(float(slope))) if act == ACT_LEAKY_RELU else 1.0
+    b = lip * float(K) * U * np.asarray(S, dtype=np.float64)
+    if act == ACT_LEAKY_RELU:
+        b = b + U * np.abs(np.asarray(c_gpu, dtype=np.float64))
     if out_fmt == "f16":
         b = b + half_ulp_f16(c_gpu)
+    elif out_fmt == "bf16":
+        b = b + half_ulp_bf16(c_gpu)
     return b

@@ -14,7 +14,8 @@ import oracle
 import tiled_shared_memory_amd as tsm
 
 DTYPE = {("f16", "f32"): tsm.TSM_F16_F32, ("f16", "f16"): tsm.TSM_F16_F16,
-         ("bf16", "f32"): tsm.TSM_BF16_F32, ("bf16", "f16"): tsm.TSM_BF16_F16}
+         ("bf16", "f32"): tsm.TSM_BF16_F32, ("bf16", "f16"): tsm.TSM_BF16_F16,
+         ("f16", "bf16"): tsm.TSM_F16_BF16, ("bf16", "bf16"): tsm.TSM_BF16_BF16}
 LAYOUT = {"row": tsm.TSM_ROW, "col": tsm.TSM_COL}
 
 
@@ -38,7 +39,7 @@ def alloc_c(batch, M, N, ldc, strideC, out_fmt, fill=None):
     import torch
 
     n = (batch - 1) * strideC + (M - 1) * ldc + N if batch and M and N else 1
-    dt = torch.float32 if out_fmt == "f32" else torch.float16
+    dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[out_fmt]
     c = torch.empty(n + 4, dtype=dt, device="cuda")
     if fill is not None:
         c.fill_(fill)
@@ -47,7 +48,7 @@ def alloc_c(batch, M, N, ldc, strideC, out_fmt, fill=None):
 
 def c_view(c_dev, batch, M, N, ldc, strideC, out_fmt) -> np.ndarray:
     """(batch, M, N) float64 copy of the logical C region."""
-    host = c_dev.cpu().numpy().astype(np.float64)
+    host = c_dev.float().cpu().numpy().astype(np.float64)  # exact for every output format
     out = np.empty((batch, M, N))
     for z in range(batch):
         for i in range(M):
@@ -57,8 +58,10 @@ def c_view(c_dev, batch, M, N, ldc, strideC, out_fmt) -> np.ndarray:
 
 
 def run(A, B, M, N, K, in_fmt, out_fmt, *, batch=1, a_layout="row", b_layout="row", lda=None, ldb=None,
-        ldc=None, sA=None, sB=None, sC=None, a_off=0, b_off=0, fill=None, stream=0, keep=False, kernel=None):
-    """C = A.B through gemm_strided_batched_ex on the given stored operands.
+        ldc=None, sA=None, sB=None, sC=None, a_off=0, b_off=0, fill=None, stream=0, keep=False, kernel=None,
+        act=None, slope=0.0):
+    """C = A.B through gemm_strided_batched_ex (or, with ``act``, act(A.B) through gemm_strided_batched_act)
+    on the given stored operands.
 
     Returns the float64 (batch, M, N) result (and the raw C buffer if ``keep``).
     If ``kernel`` is given, the call must be routed to the kernel of that name.
@@ -76,8 +79,12 @@ def run(A, B, M, N, K, in_fmt, out_fmt, *, batch=1, a_layout="row", b_layout="ro
         name = tsm.tsm_gemm_kernel_name(M, N, K, a_ptr, lda, LAYOUT[a_layout], sA, b_ptr, ldb, LAYOUT[b_layout], sB,
                                         c, ldc, sC, batch, DTYPE[(in_fmt, out_fmt)])
         assert name is not None and name.startswith(kernel), f"routed to {name}, expected {kernel}"
-    tsm.gemm_strided_batched_ex(M, N, K, a_ptr, lda, LAYOUT[a_layout], sA, b_ptr, ldb, LAYOUT[b_layout], sB, c, ldc,
-                                sC, batch, DTYPE[(in_fmt, out_fmt)], stream)
+    if act is None:
+        tsm.gemm_strided_batched_ex(M, N, K, a_ptr, lda, LAYOUT[a_layout], sA, b_ptr, ldb, LAYOUT[b_layout], sB, c,
+                                    ldc, sC, batch, DTYPE[(in_fmt, out_fmt)], stream)
+    else:
+        tsm.gemm_strided_batched_act(M, N, K, a_ptr, lda, LAYOUT[a_layout], sA, b_ptr, ldb, LAYOUT[b_layout], sB, c,
+                                     ldc, sC, batch, DTYPE[(in_fmt, out_fmt)], act, slope, stream)
     import torch
 
     torch.cuda.synchronize()
@@ -85,11 +92,13 @@ def run(A, B, M, N, K, in_fmt, out_fmt, *, batch=1, a_layout="row", b_layout="ro
     return (res, c) if keep else res
 
 
-def check(C_gpu, C_ref, S, K, out_fmt, what=""):
-    """Element-wise acceptance: |C_gpu - C_ref| <= K*2^-24*S (+ f16 half-ulp); returns max err/bound."""
+def check(C_gpu, C_ref, S, K, out_fmt, what="", act=0, slope=0.0):
+    """Element-wise acceptance: |C_gpu - act(C_ref)| <= oracle.bound(...) (K*2^-24*S scaled for the
+    activation, plus half an ulp of a 16-bit output); returns max err/bound."""
     assert np.all(np.isfinite(C_gpu)), f"{what}: non-finite output"
+    C_ref = oracle.activate(C_ref, act, slope)
     err = np.abs(C_gpu - C_ref)
-    bnd = oracle.bound(K, S, out_fmt, C_gpu)
+    bnd = oracle.bound(K, S, out_fmt, C_gpu, act, slope)
     ok = err <= bnd
     if not np.all(ok):
         idx = np.argwhere(~ok)[:5]

@@ -70,7 +70,7 @@ def _call(**kw):
     (dict(M=-1), 1, "negative size"),
     (dict(K=-5), 1, "negative size"),
     (dict(batch=-1), 1, "negative batch"),
-    (dict(dtype=4), 1, "dtype"),
+    (dict(dtype=6), 1, "dtype"),
     (dict(dtype=-1), 1, "dtype"),
     (dict(la=2), 1, "layout_a"),
     (dict(lb=7), 1, "layout_b"),

@@ -1,5 +1,6 @@
 """The CPU oracle against its pins (CPU only)."""
 
+import numpy as np
 import pytest
 
 import oracle_pins
@@ -8,6 +9,22 @@ import oracle_pins
 @pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda f: f.__name__)
 def test_oracle_pin(orc, pin):
     pin(orc)
+
+
+def test_bf16_half_ulp_and_activation_helpers(orc):
+    """half_ulp_bf16 is half the gap to the next bf16 value (every positive finite pattern, decoded by the
+    oracle); the activations match their definitions on hand-picked values."""
+    import oracle as o
+
+    bits = np.arange(0x0001, 0x7F7F, dtype=np.uint32).astype(np.uint16)  # positive finite bf16 below the largest
+    x = orc.decode(bits, "bf16")
+    nxt = orc.decode((bits.astype(np.uint32) + 1).astype(np.uint16), "bf16")
+    assert np.array_equal(o.half_ulp_bf16(x), (nxt - x) / 2)
+    assert np.array_equal(o.half_ulp_bf16(-x), (nxt - x) / 2)
+    v = np.array([-3.0, -0.5, -0.0, 0.0, 0.25, 7.0])
+    assert np.array_equal(o.activate(v, o.ACT_NONE), v)
+    assert np.array_equal(o.activate(v, o.ACT_RELU), [0.0, 0.0, 0.0, 0.0, 0.25, 7.0])
+    assert np.array_equal(o.activate(v, o.ACT_LEAKY_RELU, 0.125), [-0.375, -0.0625, 0.0, 0.0, 0.25, 7.0])
 
 
 def test_oracle_bound_helpers():

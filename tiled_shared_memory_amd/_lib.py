@@ -25,6 +25,12 @@ TSM_F16_F32 = 0
 TSM_F16_F16 = 1
 TSM_BF16_F32 = 2
 TSM_BF16_F16 = 3
+TSM_F16_BF16 = 4
+TSM_BF16_BF16 = 5
+
+TSM_ACT_NONE = 0
+TSM_ACT_RELU = 1
+TSM_ACT_LEAKY_RELU = 2
 
 TSM_ROW = 0
 TSM_COL = 1
@@ -51,6 +57,8 @@ SIGNATURES = {
     "tsm_gemm_grouped_kernel_name": ([_I64, _I64, _I64, _PTR, _I64, _INT, _I64, _PTR, _I64, _INT, _I64, _PTR, _I64,
                                       _I64, _PTR, _I64, _INT], ctypes.c_char_p),
     "rowsum": ([_I64, _I64, _PTR, _I64, _I64, _INT, _PTR, _PTR], _INT),
+    "gemm_strided_batched_act": ([_I64, _I64, _I64, _PTR, _I64, _INT, _I64, _PTR, _I64, _INT, _I64, _PTR, _I64, _I64,
+                                  _I64, _INT, _INT, ctypes.c_float, _PTR], _INT),
     "tsm_rowsum_kernel_name": ([_I64, _I64, _PTR, _I64, _I64, _INT, _PTR], ctypes.c_char_p),
 }
 
@@ -136,6 +144,14 @@ def gemm_strided_batched_ex(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b
     lib = load()
     return _check(lib, lib.gemm_strided_batched_ex(M, N, K, _ptr(A), lda, layout_a, strideA, _ptr(B), ldb, layout_b,
                                                    strideB, _ptr(C), ldc, strideC, batch, dtype, _stream(stream)))
+
+
+def gemm_strided_batched_act(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, strideB, C, ldc, strideC, batch,
+                             dtype, activation, slope, stream=None):
+    lib = load()
+    return _check(lib, lib.gemm_strided_batched_act(M, N, K, _ptr(A), lda, layout_a, strideA, _ptr(B), ldb, layout_b,
+                                                    strideB, _ptr(C), ldc, strideC, batch, dtype, activation, slope,
+                                                    _stream(stream)))
 
 
 def gemm_grouped(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, strideB, C, ldc, strideC, rows, groups, dtype,

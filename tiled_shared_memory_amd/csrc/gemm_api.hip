@@ -91,11 +91,16 @@ bool vec8_ok(const void *X, int64_t contiguous_extent, int64_t ld, int64_t strid
 
 // rows: null for plain (batched) products; for grouped products the device
 // array of per-problem row counts (each clamped to [0, M] by the kernels).
+// act, slope: the epilogue activation (TSM_ACT_*) and the leaky-ReLU slope.
 int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a, int64_t strideA, const void *B,
          int64_t ldb, int layout_b, int64_t strideB, void *C, int64_t ldc, int64_t strideC, int64_t batch, int dtype,
-         const int32_t *rows, bool grouped, Plan *out) {
+         const int32_t *rows, bool grouped, int act, float slope, Plan *out) {
   g_detail[0] = '\0';
-  if (dtype < TSM_F16_F32 || dtype > TSM_BF16_F16) return fail(TSM_ERROR_INVALID_VALUE, "unknown dtype %d", dtype);
+  if (dtype < TSM_F16_F32 || dtype > TSM_BF16_BF16) return fail(TSM_ERROR_INVALID_VALUE, "unknown dtype %d", dtype);
+  if (act != TSM_ACT_NONE && act != TSM_ACT_RELU && act != TSM_ACT_LEAKY_RELU)
+    return fail(TSM_ERROR_INVALID_VALUE, "unknown activation %d", act);
+  if (act == TSM_ACT_LEAKY_RELU && !__builtin_isfinite(slope))
+    return fail(TSM_ERROR_INVALID_VALUE, "leaky ReLU slope is not finite");
   if (layout_a != TSM_ROW && layout_a != TSM_COL)
     return fail(TSM_ERROR_INVALID_VALUE, "unknown layout_a %d", layout_a);
   if (layout_b != TSM_ROW && layout_b != TSM_COL)
@@ -121,8 +126,11 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
   p.batch = batch;
   p.a_col = layout_a == TSM_COL;
   p.b_col = layout_b == TSM_COL;
-  p.in_bf16 = dtype == TSM_BF16_F32 || dtype == TSM_BF16_F16;
-  p.out_f16 = dtype == TSM_F16_F16 || dtype == TSM_BF16_F16;
+  p.in_bf16 = dtype == TSM_BF16_F32 || dtype == TSM_BF16_F16 || dtype == TSM_BF16_BF16;
+  p.out16 = dtype != TSM_F16_F32 && dtype != TSM_BF16_F32;
+  p.out_bf16 = dtype == TSM_F16_BF16 || dtype == TSM_BF16_BF16;
+  p.act = act;
+  p.slope = act == TSM_ACT_LEAKY_RELU ? slope : 0.f;
   p.rows = rows;
   out->kernel = Kernel::None;
 
@@ -138,7 +146,7 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
     return fail(TSM_ERROR_NOT_SUPPORTED, "a dimension exceeds 2^31-1");
 
   // ---- C
-  const int64_t csize = p.out_f16 ? 2 : 4;
+  const int64_t csize = p.out16 ? 2 : 4;
   if (!C) return fail(TSM_ERROR_INVALID_VALUE, "C is NULL");
   if (((uintptr_t)C % (uintptr_t)csize) != 0)
     return fail(TSM_ERROR_INVALID_VALUE, "C not %lld-byte aligned", (long long)csize);
@@ -317,7 +325,18 @@ int gemm_strided_batched_ex(int64_t M, int64_t N, int64_t K, const void *A, int6
                             int64_t ldc, int64_t strideC, int64_t batch, int dtype, void *stream) {
   tsm::Plan pl;
   int st = tsm::plan(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, strideB, C, ldc, strideC, batch, dtype,
-                     nullptr, false, &pl);
+                     nullptr, false, TSM_ACT_NONE, 0.f, &pl);
+  if (st != TSM_SUCCESS) return st;
+  return tsm::run(pl, stream);
+}
+
+int gemm_strided_batched_act(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a,
+                             int64_t strideA, const void *B, int64_t ldb, int layout_b, int64_t strideB, void *C,
+                             int64_t ldc, int64_t strideC, int64_t batch, int dtype, int activation, float slope,
+                             void *stream) {
+  tsm::Plan pl;
+  int st = tsm::plan(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, strideB, C, ldc, strideC, batch, dtype,
+                     nullptr, false, activation, slope, &pl);
   if (st != TSM_SUCCESS) return st;
   return tsm::run(pl, stream);
 }
@@ -327,7 +346,7 @@ int gemm_grouped(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, in
                  const int32_t *rows, int64_t groups, int dtype, void *stream) {
   tsm::Plan pl;
   int st = tsm::plan(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, strideB, C, ldc, strideC, groups, dtype,
-                     rows, true, &pl);
+                     rows, true, TSM_ACT_NONE, 0.f, &pl);
   if (st != TSM_SUCCESS) return st;
   return tsm::run(pl, stream);
 }
@@ -371,7 +390,7 @@ const char *tsm_gemm_kernel_name(int64_t M, int64_t N, int64_t K, const void *A,
                                  int64_t ldc, int64_t strideC, int64_t batch, int dtype) {
   tsm::Plan pl;
   if (tsm::plan(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, strideB, C, ldc, strideC, batch, dtype, nullptr,
-                false, &pl) != TSM_SUCCESS)
+                false, TSM_ACT_NONE, 0.f, &pl) != TSM_SUCCESS)
     return nullptr;
   return tsm::kernel_name(pl.kernel);
 }
@@ -382,7 +401,7 @@ const char *tsm_gemm_grouped_kernel_name(int64_t M, int64_t N, int64_t K, const 
                                          int dtype) {
   tsm::Plan pl;
   if (tsm::plan(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, strideB, C, ldc, strideC, groups, dtype, rows,
-                true, &pl) != TSM_SUCCESS)
+                true, TSM_ACT_NONE, 0.f, &pl) != TSM_SUCCESS)
     return nullptr;
   return tsm::kernel_name(pl.kernel);
 }

@@ -19,7 +19,10 @@ struct Problem {
   bool a_col;    // A stored column-major (M-contiguous) instead of row-major (K-contiguous)
   bool b_col;    // B stored column-major (K-contiguous) instead of row-major (N-contiguous)
   bool in_bf16;  // operands are bf16 (else f16)
-  bool out_f16;  // C is f16 (else float32)
+  bool out16;     // C is 16-bit (else float32)
+  bool out_bf16;  // the 16-bit output format is bf16 (else f16)
+  int act;        // epilogue activation: 0 none, 1 ReLU, 2 leaky ReLU
+  float slope;    // leaky ReLU slope
   const int32_t *rows;  // grouped products: device array of per-problem row counts (else null)
 };
 
@@ -35,6 +38,9 @@ struct KernelArgs {
   int32_t z0;  // first problem index covered by this launch
   const int32_t *rows;  // per-problem row counts in device memory, or null (every problem has M rows)
   int32_t compact_groups;  // large-tile kernel, grouped call: number of groups, tiles numbered over valid ones only
+  int32_t act;             // epilogue: 0 none, 1 ReLU, 2 leaky ReLU
+  float slope;             // leaky ReLU slope
+  int32_t out_bf16;        // 16-bit output is bf16 (else f16)
 };
 
 // Rows of problem z: M, or for a grouped product the caller's count for z

@@ -108,7 +108,7 @@ __device__ __forceinline__ void commit(const Stage<T, VEC> &st, uint16_t *s, int
   }
 }
 
-template <int T, bool BF16, bool OUT_F16, bool A_KMAJ, bool B_KMAJ, int VEC>
+template <int T, bool BF16, bool OUT16, bool A_KMAJ, bool B_KMAJ, int VEC>
 __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
   constexpr int W = T / 2;    // wave tile
   constexpr int NB = W / 32;  // 32 x 32 MFMA blocks per wave and dimension
@@ -126,6 +126,7 @@ __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
   const int64_t z = (int64_t)p.z0 + blockIdx.y;
   const int64_t M = rows_of(p, z);  // this problem's rows
   if (m0 >= M) return;              // the whole tile lies past them (uniform)
+  const Epilogue ep = epilogue_in_vgprs(p);  // kept out of the scalar registers the loop needs
   const uint16_t *A = p.A + z * p.sA;
   const uint16_t *B = p.B + z * p.sB;
 
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
     __syncthreads();
   }
 
-  void *C = OUT_F16 ? (void *)((uint16_t *)p.C + z * p.sC) : (void *)((float *)p.C + z * p.sC);
+  void *C = OUT16 ? (void *)((uint16_t *)p.C + z * p.sC) : (void *)((float *)p.C + z * p.sC);
 #pragma unroll
   for (int i = 0; i < NB; ++i)
 #pragma unroll
@@ -184,18 +185,18 @@ __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
       for (int r = 0; r < 16; ++r) {
         const int64_t row = m0 + wm * W + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         const int64_t col = n0 + wn * W + j * 32 + (lane & 31);
-        store_masked<OUT_F16>(C, p.ldc, M, p.N, row, col, acc[i][j][r]);
+        store_masked<OUT16>(C, p.ldc, M, p.N, row, col, acc[i][j][r], ep);
       }
 }
 
-template <int T, bool BF16, bool OUT_F16, bool A_KMAJ, bool B_KMAJ, int VEC>
+template <int T, bool BF16, bool OUT16, bool A_KMAJ, bool B_KMAJ, int VEC>
 hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
   const int64_t tiles = (int64_t)base.tiles_m * base.tiles_n;
   for (int64_t z0 = 0; z0 < batch; z0 += kMaxGridY) {
     KernelArgs a = base;
     a.z0 = (int32_t)z0;
     const int64_t nz = batch - z0 < kMaxGridY ? batch - z0 : kMaxGridY;
-    hipLaunchKernelGGL((gemm_masked_kernel<T, BF16, OUT_F16, A_KMAJ, B_KMAJ, VEC>), dim3((unsigned)tiles, (unsigned)nz),
+    hipLaunchKernelGGL((gemm_masked_kernel<T, BF16, OUT16, A_KMAJ, B_KMAJ, VEC>), dim3((unsigned)tiles, (unsigned)nz),
                        dim3(THREADS), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -203,20 +204,20 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
   return hipSuccess;
 }
 
-template <int T, bool BF16, bool OUT_F16, int VEC>
+template <int T, bool BF16, bool OUT16, int VEC>
 hipError_t dispatch_layout(const Problem &p, const KernelArgs &a, hipStream_t s) {
   const bool a_kmaj = !p.a_col, b_kmaj = p.b_col;
-  if (a_kmaj && b_kmaj) return launch_t<T, BF16, OUT_F16, true, true, VEC>(a, p.batch, s);
-  if (a_kmaj && !b_kmaj) return launch_t<T, BF16, OUT_F16, true, false, VEC>(a, p.batch, s);
-  if (!a_kmaj && b_kmaj) return launch_t<T, BF16, OUT_F16, false, true, VEC>(a, p.batch, s);
-  return launch_t<T, BF16, OUT_F16, false, false, VEC>(a, p.batch, s);
+  if (a_kmaj && b_kmaj) return launch_t<T, BF16, OUT16, true, true, VEC>(a, p.batch, s);
+  if (a_kmaj && !b_kmaj) return launch_t<T, BF16, OUT16, true, false, VEC>(a, p.batch, s);
+  if (!a_kmaj && b_kmaj) return launch_t<T, BF16, OUT16, false, true, VEC>(a, p.batch, s);
+  return launch_t<T, BF16, OUT16, false, false, VEC>(a, p.batch, s);
 }
 
 template <int T, int VEC>
 hipError_t dispatch_types(const Problem &p, const KernelArgs &a, hipStream_t s) {
   if (p.in_bf16)
-    return p.out_f16 ? dispatch_layout<T, true, true, VEC>(p, a, s) : dispatch_layout<T, true, false, VEC>(p, a, s);
-  return p.out_f16 ? dispatch_layout<T, false, true, VEC>(p, a, s) : dispatch_layout<T, false, false, VEC>(p, a, s);
+    return p.out16 ? dispatch_layout<T, true, true, VEC>(p, a, s) : dispatch_layout<T, true, false, VEC>(p, a, s);
+  return p.out16 ? dispatch_layout<T, false, true, VEC>(p, a, s) : dispatch_layout<T, false, false, VEC>(p, a, s);
 }
 
 }  // namespace
@@ -236,6 +237,9 @@ hipError_t launch_masked(const Problem &p, int vec, int tile, hipStream_t stream
   a.sB = p.sB;
   a.sC = p.sC;
   a.rows = p.rows;
+  a.act = p.act;
+  a.slope = p.slope;
+  a.out_bf16 = p.out_bf16;
   a.tiles_m = (int32_t)((p.M + tile - 1) / tile);
   a.tiles_n = (int32_t)((p.N + tile - 1) / tile);
   if (tile == 64) return vec == 8 ? dispatch_types<64, 8>(p, a, stream) : dispatch_types<64, 1>(p, a, stream);

@@ -145,7 +145,7 @@ __device__ __forceinline__ void slice(Ctx &c, int j, f32x4 (&acc)[4]) {
   }
 }
 
-template <bool BF16, bool OUT_F16>
+template <bool BF16, bool OUT16>
 __global__ __launch_bounds__(256, 1) void gemm_skinny_kernel(KernelArgs p) {
   Ctx c;
   const int tid = threadIdx.x;
@@ -201,31 +201,25 @@ __global__ __launch_bounds__(256, 1) void gemm_skinny_kernel(KernelArgs p) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the duplicate tail loads
 
   // ---- epilogue: lane holds C[m][n .. n+3], m = lane % 16
+  const Epilogue ep = epilogue_of(p);
   if (m < M) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int64_t n = n0 + c.wave * 64 + nb * 16 + 4 * (lane >> 4);
-      if constexpr (OUT_F16) {
-        uint16_t *C = (uint16_t *)p.C + z * p.sC + (int64_t)m * p.ldc + n;
-        u32x2 v;
-        v[0] = (uint32_t)f32_to_f16_bits(acc[nb][0]) | ((uint32_t)f32_to_f16_bits(acc[nb][1]) << 16);
-        v[1] = (uint32_t)f32_to_f16_bits(acc[nb][2]) | ((uint32_t)f32_to_f16_bits(acc[nb][3]) << 16);
-        *reinterpret_cast<u32x2 *>(C) = v;
-      } else {
-        float *C = (float *)p.C + z * p.sC + (int64_t)m * p.ldc + n;
-        *reinterpret_cast<f32x4 *>(C) = acc[nb];
-      }
+      const int64_t at = z * p.sC + (int64_t)m * p.ldc + n;
+      store4<OUT16>(OUT16 ? (void *)((uint16_t *)p.C + at) : (void *)((float *)p.C + at), ep, acc[nb][0], acc[nb][1],
+                    acc[nb][2], acc[nb][3]);
     }
   }
 }
 
-template <bool BF16, bool OUT_F16>
+template <bool BF16, bool OUT16>
 hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
   for (int64_t z0 = 0; z0 < batch; z0 += kMaxGridY) {
     KernelArgs a = base;
     a.z0 = (int32_t)z0;
     const int64_t nz = batch - z0 < kMaxGridY ? batch - z0 : kMaxGridY;
-    hipLaunchKernelGGL((gemm_skinny_kernel<BF16, OUT_F16>), dim3((unsigned)base.tiles_n, (unsigned)nz), dim3(256), 0,
+    hipLaunchKernelGGL((gemm_skinny_kernel<BF16, OUT16>), dim3((unsigned)base.tiles_n, (unsigned)nz), dim3(256), 0,
                        stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -263,11 +257,14 @@ hipError_t launch_skinny(const Problem &p, hipStream_t stream) {
   a.sB = p.sB;
   a.sC = p.sC;
   a.rows = p.rows;
+  a.act = p.act;
+  a.slope = p.slope;
+  a.out_bf16 = p.out_bf16;
   a.tiles_m = 1;
   a.tiles_n = (int32_t)(p.N / BN);
   if (p.in_bf16)
-    return p.out_f16 ? launch_t<true, true>(a, p.batch, stream) : launch_t<true, false>(a, p.batch, stream);
-  return p.out_f16 ? launch_t<false, true>(a, p.batch, stream) : launch_t<false, false>(a, p.batch, stream);
+    return p.out16 ? launch_t<true, true>(a, p.batch, stream) : launch_t<true, false>(a, p.batch, stream);
+  return p.out16 ? launch_t<false, true>(a, p.batch, stream) : launch_t<false, false>(a, p.batch, stream);
 }
 
 const char *skinny_name() { return "skinny_m16_n256_k64"; }

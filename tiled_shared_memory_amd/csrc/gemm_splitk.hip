@@ -95,7 +95,7 @@ __device__ __forceinline__ void step(Ctx &c, int t, f32x4 &acc) {
   acc = mfma_16x16x32<BF16>(bf, af, acc);
 }
 
-template <bool BF16, bool OUT_F16>
+template <bool BF16, bool OUT16>
 __global__ __launch_bounds__(WAVES * 64, 1) void gemm_splitk_kernel(KernelArgs p) {
   Ctx c;
   const int tid = threadIdx.x;
@@ -151,27 +151,20 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_splitk_kernel(KernelArgs p
     // lane holds C[m0 + lane % 16][n0 + 4 * (lane / 16) .. +3]
     const int64_t m = m0 + (lane & 15);
     const int64_t n = n0 + 4 * (lane >> 4);
-    if constexpr (OUT_F16) {
-      uint16_t *C = (uint16_t *)p.C + z * p.sC + m * p.ldc + n;
-      u32x2 v;
-      v[0] = (uint32_t)f32_to_f16_bits(sum[0]) | ((uint32_t)f32_to_f16_bits(sum[1]) << 16);
-      v[1] = (uint32_t)f32_to_f16_bits(sum[2]) | ((uint32_t)f32_to_f16_bits(sum[3]) << 16);
-      *reinterpret_cast<u32x2 *>(C) = v;
-    } else {
-      float *C = (float *)p.C + z * p.sC + m * p.ldc + n;
-      *reinterpret_cast<f32x4 *>(C) = sum;
-    }
+    const int64_t at = z * p.sC + m * p.ldc + n;
+    store4<OUT16>(OUT16 ? (void *)((uint16_t *)p.C + at) : (void *)((float *)p.C + at), epilogue_of(p), sum[0], sum[1],
+                  sum[2], sum[3]);
   }
 }
 
-template <bool BF16, bool OUT_F16>
+template <bool BF16, bool OUT16>
 hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
   const int64_t tiles = (int64_t)base.tiles_m * base.tiles_n;
   for (int64_t z0 = 0; z0 < batch; z0 += kMaxGridY) {
     KernelArgs a = base;
     a.z0 = (int32_t)z0;
     const int64_t nz = batch - z0 < kMaxGridY ? batch - z0 : kMaxGridY;
-    hipLaunchKernelGGL((gemm_splitk_kernel<BF16, OUT_F16>), dim3((unsigned)tiles, (unsigned)nz), dim3(WAVES * 64), 0,
+    hipLaunchKernelGGL((gemm_splitk_kernel<BF16, OUT16>), dim3((unsigned)tiles, (unsigned)nz), dim3(WAVES * 64), 0,
                        stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -209,11 +202,14 @@ hipError_t launch_splitk(const Problem &p, hipStream_t stream) {
   a.sB = p.sB;
   a.sC = p.sC;
   a.rows = p.rows;
+  a.act = p.act;
+  a.slope = p.slope;
+  a.out_bf16 = p.out_bf16;
   a.tiles_m = (int32_t)(p.M / 16);
   a.tiles_n = (int32_t)(p.N / 16);
   if (p.in_bf16)
-    return p.out_f16 ? launch_t<true, true>(a, p.batch, stream) : launch_t<true, false>(a, p.batch, stream);
-  return p.out_f16 ? launch_t<false, true>(a, p.batch, stream) : launch_t<false, false>(a, p.batch, stream);
+    return p.out16 ? launch_t<true, true>(a, p.batch, stream) : launch_t<true, false>(a, p.batch, stream);
+  return p.out16 ? launch_t<false, true>(a, p.batch, stream) : launch_t<false, false>(a, p.batch, stream);
 }
 
 const char *splitk_name() { return "splitk_16x16_w16"; }

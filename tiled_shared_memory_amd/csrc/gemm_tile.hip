@@ -366,7 +366,7 @@ __device__ __forceinline__ void substep_w(CtxW &c, int j, Frags<16> (&fr)[2], Ac
   }
 }
 
-template <bool BF16, bool OUT_F16, int MI, bool BROW, int KB>
+template <bool BF16, bool OUT16, int MI, bool BROW, int KB>
 __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
   static_assert(KB == 1 || MI == 16, "64-deep slabs use 16x16x32 operands");
   CtxT<LOADS * KB> c;
@@ -486,6 +486,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
 
   // ---- epilogue: each register group holds C[m][n + 0..3]
   const int64_t ldc = p.ldc;
+  const Epilogue ep = epilogue_of(p);
 #pragma unroll
   for (int i = 0; i < 128 / MI; ++i) {
     const int64_t m = m0 + wm * 128 + i * MI + (lane % MI);
@@ -508,22 +509,14 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
           v2 = acc.v[i][j][2];
           v3 = acc.v[i][j][3];
         }
-        if constexpr (OUT_F16) {
-          uint16_t *C = (uint16_t *)p.C + z * p.sC;
-          u32x2 v;
-          v[0] = (uint32_t)f32_to_f16_bits(v0) | ((uint32_t)f32_to_f16_bits(v1) << 16);
-          v[1] = (uint32_t)f32_to_f16_bits(v2) | ((uint32_t)f32_to_f16_bits(v3) << 16);
-          *reinterpret_cast<u32x2 *>(C + m * ldc + n) = v;
-        } else {
-          float *C = (float *)p.C + z * p.sC;
-          *reinterpret_cast<f32x4 *>(C + m * ldc + n) = f32x4{v0, v1, v2, v3};
-        }
+        const int64_t at = z * p.sC + m * ldc + n;
+        store4<OUT16>(OUT16 ? (void *)((uint16_t *)p.C + at) : (void *)((float *)p.C + at), ep, v0, v1, v2, v3);
       }
     }
   }
 }
 
-template <bool BF16, bool OUT_F16, int MI, bool BROW, int KB>
+template <bool BF16, bool OUT16, int MI, bool BROW, int KB>
 hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
   const int64_t tiles = (int64_t)base.tiles_m * base.tiles_n;
   if (base.rows && batch <= kMaxCompactGroups && tiles * batch <= 0x7fffffffLL) {
@@ -532,7 +525,7 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
     KernelArgs a = base;
     a.z0 = 0;
     a.compact_groups = (int32_t)batch;
-    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT_F16, MI, BROW, KB>), dim3((unsigned)(tiles * batch)), dim3(256), 0,
+    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT16, MI, BROW, KB>), dim3((unsigned)(tiles * batch)), dim3(256), 0,
                        stream, a);
     return hipGetLastError();
   }
@@ -540,7 +533,7 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
     KernelArgs a = base;
     a.z0 = (int32_t)z0;
     const int64_t nz = batch - z0 < kMaxGridY ? batch - z0 : kMaxGridY;
-    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT_F16, MI, BROW, KB>), dim3((unsigned)tiles, (unsigned)nz), dim3(256), 0,
+    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT16, MI, BROW, KB>), dim3((unsigned)tiles, (unsigned)nz), dim3(256), 0,
                        stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -551,9 +544,9 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
 template <int MI, bool BROW, int KB>
 hipError_t launch_mi(const Problem &p, const KernelArgs &a, hipStream_t stream) {
   if (p.in_bf16)
-    return p.out_f16 ? launch_t<true, true, MI, BROW, KB>(a, p.batch, stream)
+    return p.out16 ? launch_t<true, true, MI, BROW, KB>(a, p.batch, stream)
                      : launch_t<true, false, MI, BROW, KB>(a, p.batch, stream);
-  return p.out_f16 ? launch_t<false, true, MI, BROW, KB>(a, p.batch, stream)
+  return p.out16 ? launch_t<false, true, MI, BROW, KB>(a, p.batch, stream)
                    : launch_t<false, false, MI, BROW, KB>(a, p.batch, stream);
 }
 
@@ -589,6 +582,9 @@ hipError_t launch_tile(const Problem &p, int variant, hipStream_t stream) {
   a.sB = p.sB;
   a.sC = p.sC;
   a.rows = p.rows;
+  a.act = p.act;
+  a.slope = p.slope;
+  a.out_bf16 = p.out_bf16;
   a.tiles_m = (int32_t)((p.M + BM - 1) / BM);
   a.tiles_n = (int32_t)(p.N / BN);
   switch (variant) {

@@ -58,13 +58,67 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
+// float32 -> bf16, round to nearest even (converted in hardware on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  __bf16 h = (__bf16)x;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// The epilogue every kernel applies to a float32 accumulator value before it
+// is stored: an optional activation (the ACTIVATION meta-parameter of the Intel
+// XPU Triton README's matmul signature, "Use Proper Type Annotations"), then
+// the conversion to the output format.  Uniform across a launch.
+struct Epilogue {
+  int act;      // 0 none, 1 ReLU, 2 leaky ReLU
+  float slope;  // leaky ReLU: the factor applied to negative values
+  bool bf16;    // a 16-bit output is bf16 (else f16)
+
+  __device__ __forceinline__ float apply(float v) const {
+    if (act == 0) return v;
+    return v > 0.f ? v : (act == 1 ? 0.f : v * slope);
+  }
+  __device__ __forceinline__ uint16_t to16(float v) const { return bf16 ? f32_to_bf16_bits(v) : f32_to_f16_bits(v); }
+};
+
+__device__ __forceinline__ Epilogue epilogue_of(const KernelArgs &p) { return Epilogue{p.act, p.slope, p.out_bf16 != 0}; }
+
+// The same, copied into vector registers at once: for kernels whose scalar
+// registers are the scarce ones (the values are uniform either way).
+__device__ __forceinline__ Epilogue epilogue_in_vgprs(const KernelArgs &p) {
+  int act, bf16;
+  float slope;
+  asm("v_mov_b32 %0, %1" : "=v"(act) : "s"(p.act));
+  asm("v_mov_b32 %0, %1" : "=v"(slope) : "s"(p.slope));
+  asm("v_mov_b32 %0, %1" : "=v"(bf16) : "s"(p.out_bf16));
+  return Epilogue{act, slope, bf16 != 0};
+}
+
+// Four consecutive values of one row of C, at C (16 bytes of float32 or
+// 8 bytes of 16-bit values; the callers keep the address aligned).
+template <bool OUT16>
+__device__ __forceinline__ void store4(void *C, const Epilogue &e, float v0, float v1, float v2, float v3) {
+  v0 = e.apply(v0);
+  v1 = e.apply(v1);
+  v2 = e.apply(v2);
+  v3 = e.apply(v3);
+  if constexpr (OUT16) {
+    u32x2 v;
+    v[0] = (uint32_t)e.to16(v0) | ((uint32_t)e.to16(v1) << 16);
+    v[1] = (uint32_t)e.to16(v2) | ((uint32_t)e.to16(v3) << 16);
+    *reinterpret_cast<u32x2 *>(C) = v;
+  } else {
+    *reinterpret_cast<f32x4 *>(C) = f32x4{v0, v1, v2, v3};
+  }
+}
+
 // Store one accumulator value into row-major C if it lies inside M x N.
-template <bool OUT_F16>
+template <bool OUT16>
 __device__ __forceinline__ void store_masked(void *C, int64_t ldc, int64_t M, int64_t N, int64_t row, int64_t col,
-                                             float v) {
+                                             float v, const Epilogue &e) {
   if (row < M && col < N) {
-    if constexpr (OUT_F16)
-      reinterpret_cast<uint16_t *>(C)[row * ldc + col] = f32_to_f16_bits(v);
+    v = e.apply(v);
+    if constexpr (OUT16)
+      reinterpret_cast<uint16_t *>(C)[row * ldc + col] = e.to16(v);
     else
       reinterpret_cast<float *>(C)[row * ldc + col] = v;
   }
