@@ -255,3 +255,13 @@ def test_rowsum_kernel_selection():
     assert tsm.tsm_rowsum_kernel_name(16384, 1000, X0, 1, 16384, 1, O0) == "rowsum_wave_elem"
     # few long rows: a workgroup per row
     assert tsm.tsm_rowsum_kernel_name(8, 1 << 20, X0, 1 << 20, 1, 2, O0) == "rowsum_block_vec16"
+
+
+def test_ragged_n_routes_to_the_tile_kernel():
+    """N a multiple of 8 (not of 256) stays on the large-tile kernels; N not a multiple of 8 does not."""
+    assert tsm.tsm_gemm_kernel_name(4096, 50256, 4096, A0, 4096, 0, 0, B0, 4096, 1, 0, C0, 50256, 0, 1,
+                                    3) == "tile_256x256x64_mi16"
+    assert tsm.tsm_gemm_kernel_name(4096, 50256, 4096, A0, 4096, 0, 0, B0, 50256, 0, 0, C0, 50256, 0, 1,
+                                    3) == "tile_256x256x32_mi16_nn"
+    assert tsm.tsm_gemm_kernel_name(4096, 50257, 4096, A0, 4096, 0, 0, B0, 4096, 1, 0, C0, 50260, 0, 1,
+                                    3).startswith("masked_")

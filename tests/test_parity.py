@@ -356,3 +356,36 @@ def test_subnormal_f16_operands(orc):
     Cr, S = orc.gemm_rows(A, B, M, N, K, F16)
     assert np.all(Cr == K * 2.0 ** -24)
     check(C, Cr, S, K, "f32", "subnormal")
+
+
+RAGGED_N = [(600, 1000, 256, 1), (256, 8, 128, 2), (300, 264, 384, 1), (512, 1304, 128, 1)]
+
+
+@pytest.mark.parametrize("shape", RAGGED_N, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("variant,b_layout", TILE_VARIANTS, ids=[v for v, _ in TILE_VARIANTS])
+def test_tile_ragged_n(orc, monkeypatch, shape, variant, b_layout):
+    """N a multiple of 8 but not of 256 (and ragged M) on every large-tile variant.  Row-major B is stored with
+    padding columns full of NaN and C with padding full of NaN: neither may leak into or be written by the
+    result."""
+    monkeypatch.setenv("TSM_GEMM_KERNEL", variant)
+    M, N, K, batch = shape
+    A, B = make_operands(M + N + K, batch, M, N, K, BF16, ("uniform", -1.0, 1.0), "row", b_layout)
+    nan16 = 0x7E00 if BF16 == "f16" else 0x7FC0  # a quiet NaN pattern of the operand format
+    if b_layout == "row":
+        ldb = N + 24
+        Bp = np.full((batch, K, ldb), nan16, np.uint16)
+        Bp[:, :, :N] = B
+    else:
+        ldb = K
+        Bp = B
+    ldc = N + 8
+    say(f"[gpu] ragged N {variant} {shape}")
+    C, raw = run(A, Bp, M, N, K, BF16, "f32", batch=batch, b_layout=b_layout, ldb=ldb, ldc=ldc, fill=float("nan"),
+                 keep=True, kernel=variant)
+    Cr, S = orc.gemm_rows(A, B, M, N, K, BF16, batch=batch, b_layout=b_layout)
+    check(C, Cr, S, K, "f32", f"{variant} ragged N {shape}")
+    host = raw.cpu().numpy()
+    for z in range(batch):
+        for i in range(M):
+            o = z * M * ldc + i * ldc
+            assert np.all(np.isnan(host[o + N:o + ldc])), f"C padding written at problem {z} row {i}"

@@ -200,7 +200,7 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
   if (masked_tiles < 256) out->kernel = (a8 && b8) ? Kernel::Small8 : Kernel::Small1;
   if (K > 0 && masked_tiles < 256 && splitk_supports(p)) out->kernel = Kernel::SplitK;
   // the 256 x 256 kernels once their tiles (one workgroup per CU) fill the chip
-  const bool many = ((M + TileInfo::BM - 1) / TileInfo::BM) * (N / TileInfo::BN) * batch >= 256;
+  const bool many = ((M + TileInfo::BM - 1) / TileInfo::BM) * ((N + TileInfo::BN - 1) / TileInfo::BN) * batch >= 256;
   if (K > 0 && many && tile_supports(p, false)) out->kernel = Kernel::TileW;
   if (K > 0 && many && tile_supports(p, true)) out->kernel = Kernel::Tile16NN;
   if (K > 0 && skinny_supports(p)) out->kernel = Kernel::Skinny;

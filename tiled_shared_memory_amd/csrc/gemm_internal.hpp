@@ -65,9 +65,9 @@ struct MaskedInfo {
 hipError_t launch_masked(const Problem &p, int vec, int tile, hipStream_t stream);
 const char *masked_name(int vec, int tile);
 
-// Large-tile kernel: A row-major, B either layout, N a multiple of 256, K a
-// multiple of 128, 16-byte aligned rows; any M (rows past M, or past a grouped
-// problem's count, read as zero and are not stored).
+// Large-tile kernel: A row-major, B either layout, N a multiple of 8, K a
+// multiple of 128, 16-byte aligned rows; any M (rows past M or N, or past a
+// grouped problem's count, read as zero and are not stored).
 // Variants (K slab depth, MFMA shape, B layout): 0 = 32-deep, 32x32x16,
 // column-major B; 1 = 32-deep, 16x16x32, column-major; 2 = 32-deep, 16x16x32,
 // row-major B (transposed out of LDS); 3, 4 = as 1, 2 with 64-deep slabs.

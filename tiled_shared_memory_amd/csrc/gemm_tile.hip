@@ -103,6 +103,10 @@ template <> struct WRing<1> {
   __device__ static char *b() { return w_b1; }
 };
 
+// A per-lane offset past every buffer resource (which the host keeps below
+// 1 GiB): such a load returns zeros.  Slice offsets added to it stay below 2^32.
+constexpr uint32_t kOutside = 0x80000000u;
+
 // Buffer resource over `bytes` bytes starting at `base` (raw addressing,
 // dword 3 = the gfx9 default data format).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
@@ -135,13 +139,17 @@ __device__ __forceinline__ int swz_row(int r, int c) { return c ^ (2 * ((r & 3) 
 
 // Per-lane byte offsets of the chunks a lane fetches for one row-major B
 // slice: wave-load g of wave w fills rows 2*(w*LOADS+g) + lane/32, position
-// lane % 32, i.e. the chunk whose swizzled position that is.
+// lane % 32, i.e. the chunk whose swizzled position that is.  A chunk's
+// columns are the same in every slice, so chunks at or past the panel's
+// `vcols` valid columns get an offset beyond the buffer resource: they load
+// as zero (and never touch memory past the matrix).
 template <int LOADS>
-__device__ __forceinline__ void slice_offsets_row(uint32_t (&off)[LOADS], int64_t ld, int wave, int lane) {
+__device__ __forceinline__ void slice_offsets_row(uint32_t (&off)[LOADS], int64_t ld, int wave, int lane, int vcols) {
 #pragma unroll
   for (int g = 0; g < LOADS; ++g) {
     const int r = 2 * (wave * LOADS + g) + (lane >> 5);
-    off[g] = (uint32_t)(r * ld + swz_row(r, lane & 31) * 8) * 2u;
+    const int c = swz_row(r, lane & 31);
+    off[g] = c * 8 < vcols ? (uint32_t)(r * ld + c * 8) * 2u : kOutside;
   }
 }
 
@@ -407,6 +415,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
   const int64_t M = rows_of(p, z);  // this problem's rows
   if (m0 >= M) return;              // the whole tile lies past them (uniform)
   const int64_t vrows = M - m0 < BM ? M - m0 : BM;
+  const int vcols = (int)(p.N - n0 < BN ? p.N - n0 : BN);  // valid columns of this tile (N is a multiple of 8)
   const uint16_t *A = p.A + z * p.sA + m0 * p.lda;  // row m0, k = 0 (row-major A)
   // column n0, k = 0: column-major B starts its panel at row n0, row-major B at column n0
   const uint16_t *B = p.B + z * p.sB + (BROW ? n0 : n0 * p.ldb);
@@ -428,10 +437,10 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
   // of A (rows past M load as zero) and 256 rows, or K rows x 256 columns, of
   // B.  The host keeps each extent below 1 GiB, so all offsets are 32-bit.
   c.ra = make_rsrc(A, (uint32_t)(((vrows - 1) * p.lda + p.K) * 2));
-  c.rb = make_rsrc(B, (uint32_t)((BROW ? (p.K - 1) * p.ldb + 256 : 255 * p.ldb + p.K) * 2));
+  c.rb = make_rsrc(B, (uint32_t)((BROW ? (p.K - 1) * p.ldb + vcols : (vcols - 1) * p.ldb + p.K) * 2));
   slice_offsets<LOADS * KB, KB>(c.offA, p.lda, c.wave, lane);
   if constexpr (BROW) {
-    slice_offsets_row<LOADS * KB>(c.offB, p.ldb, c.wave, lane);
+    slice_offsets_row<LOADS * KB>(c.offB, p.ldb, c.wave, lane, vcols);
     c.kstepB = (uint32_t)(32 * KB * p.ldb * 2);
   } else {
     slice_offsets<LOADS * KB, KB>(c.offB, p.ldb, c.wave, lane);
@@ -497,6 +506,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
       for (int g = 0; g < (MI == 32 ? 4 : 1); ++g) {
         // 32x32: group g covers columns 8g + 4*(lane/32) .. +3; 16x16: 4*(lane/16) .. +3
         const int64_t n = n0 + wn * 128 + j * MI + (MI == 32 ? 8 * g + 4 * (lane >> 5) : 4 * (lane >> 4));
+        if (n >= p.N) continue;  // columns past N (N is a multiple of 8: groups of 4 lie wholly on one side)
         float v0, v1, v2, v3;
         if constexpr (MI == 32) {
           v0 = acc.v[i][j][4 * g + 0];
@@ -555,7 +565,9 @@ hipError_t launch_mi(const Problem &p, const KernelArgs &a, hipStream_t stream) 
 bool tile_supports(const Problem &p, bool b_row) {
   if (p.a_col) return false;              // A must be K-contiguous
   if (p.b_col == b_row) return false;     // the requested B layout
-  if (p.N % BN || p.K % (NS * BK) || p.K == 0) return false;  // any M: rows past it are masked
+  // any M and any N that is a multiple of 8: rows and columns past them load
+  // as zero and are not stored
+  if (p.N % 8 || p.K % (NS * BK) || p.K == 0) return false;
   // 32-bit buffer offsets: an A panel (up to 256 rows) and a B panel (256 rows
   // or K rows x 256 columns) must span less than 1 GiB
   if (255 * p.lda + p.K >= (int64_t)1 << 29) return false;
@@ -586,7 +598,7 @@ hipError_t launch_tile(const Problem &p, int variant, hipStream_t stream) {
   a.slope = p.slope;
   a.out_bf16 = p.out_bf16;
   a.tiles_m = (int32_t)((p.M + BM - 1) / BM);
-  a.tiles_n = (int32_t)(p.N / BN);
+  a.tiles_n = (int32_t)((p.N + BN - 1) / BN);
   switch (variant) {
     case 0:
       return launch_mi<32, false, 1>(p, a, stream);
