@@ -164,6 +164,51 @@ def test_kernel_selection_by_layout_and_shape():
     assert tsm.tsm_gemm_kernel_name(256, 256, 8192, A0, 8192, 0, 0, B0, 256, 0, 0, C0, 256, 0, 1, 0).startswith("splitk_")
 
 
+def test_skinny_selection():
+    """Up to 128 rows of row-major operands go to the streaming kernel: 256-column workgroups when those fill the
+    256 CUs, 64-column ones otherwise; row blocks follow M.  K not a multiple of 64, N not a multiple of 64 or a
+    column-major operand go elsewhere."""
+    B0 = 0x7E0000000000
+    N, K = 16384, 8192
+
+    def pick(M, N=N, K=K, batch=1, lb=0, ldb=None):
+        ldb = ldb if ldb is not None else (K if lb else N)
+        return tsm.tsm_gemm_kernel_name(M, N, K, A0, K, 0, M * K, B0, ldb, lb, K * N, C0, N, M * N, batch, 0)
+
+    assert pick(16, batch=8) == "skinny_m16_n256_k64"  # 64 x 8 = 512 workgroups of 256 columns
+    assert pick(16) == "skinny_m16_n64_k64"  # 64 workgroups of 256 columns would leave most CUs idle
+    assert pick(1) == "skinny_m16_n64_k64"
+    assert pick(17) == "skinny_m32_n64_k64"
+    assert pick(32, batch=4) == "skinny_m32_n256_k64"
+    assert pick(48) == "skinny_m64_n64_k64"
+    assert pick(64, batch=4) == "skinny_m64_n256_k64"
+    assert pick(16, N=16448) == "skinny_m16_n64_k64"  # N % 256 != 0
+    assert pick(65) == "skinny_m128_n64_k64"
+    assert pick(128) == "skinny_m128_n64_k64"
+    assert not pick(129).startswith("skinny_")
+    # few streaming workgroups times few 16-row tiles: split-K spreads the passes over B wider
+    assert pick(16, N=4096, K=4096).startswith("splitk_")
+    assert pick(32, N=4096, K=4096) == "skinny_m32_n64_k64"
+    assert pick(48, N=128, K=4096).startswith("splitk_")
+    assert not pick(16, K=8200).startswith("skinny_")
+    assert not pick(16, N=16400).startswith("skinny_")
+    assert not pick(16, lb=1).startswith("skinny_")
+
+
+def test_skinny_forced_width(monkeypatch):
+    B0 = 0x7E0000000000
+    args = (100, 512, 512, A0, 512, 0, 0, B0, 512, 0, 0, C0, 512, 0, 1, 0)
+    monkeypatch.setenv("TSM_GEMM_KERNEL", "skinny_m128_n64_k64")
+    assert tsm.tsm_gemm_kernel_name(*args) == "skinny_m128_n64_k64"
+    # a name whose row blocks do not match M, or 256 columns with 128 rows, cannot run the problem
+    for bad in ("skinny_m64_n64_k64", "skinny_m128_n256_k64", "skinny_m16_n128_k64"):
+        monkeypatch.setenv("TSM_GEMM_KERNEL", bad)
+        assert tsm.tsm_gemm_kernel_name(*args) is None
+        with pytest.raises(tsm.TsmError) as ei:
+            tsm.gemm(100, 512, 512, A0, 512, B0, 512, C0, 512, 0, 0)
+        assert ei.value.status == 2
+
+
 R0 = 0x7F3000000000  # fake device address of the row counts
 
 

@@ -28,6 +28,8 @@ FAMILIES = [
     ("tile_256x256x32_mi16_nn", (512, 256, 256, 1), "row", "row"),
     ("tile_256x256x64_mi16_nn", (256, 256, 256, 2), "row", "row"),
     ("skinny_m16_n256_k64", (13, 512, 512, 2), "row", "row"),
+    ("skinny_m64_n64_k64", (40, 320, 192, 2), "row", "row"),
+    ("skinny_m128_n64_k64", (100, 128, 128, 1), "row", "row"),
     ("splitk_16x16_w16", (48, 32, 4096, 1), "row", "row"),
 ]
 ACTS = [(tsm.TSM_ACT_NONE, 0.0), (tsm.TSM_ACT_RELU, 0.0), (tsm.TSM_ACT_LEAKY_RELU, 0.1),

@@ -85,19 +85,22 @@ def test_grouped_masked(orc, a_layout, b_layout, shape):
     check_grouped(orc, C, A, B, M, N, K, F16, "f32", rows, a_layout=a_layout, b_layout=b_layout, what="masked")
 
 
-def test_grouped_skinny(orc):
-    """Up to 16 rows per group on the streaming kernel."""
-    M, N, K = 16, 512, 512
-    rows = [0, 1, 7, 16, 20, -3, 15]
-    A, B = make_operands(43, len(rows), M, N, K, F16, ("uniform", -0.5, 0.5))
-    say(f"[gpu] grouped skinny rows={rows}")
-    C = run_grouped(A, B, M, N, K, F16, "f32", rows, kernel="skinny_")
-    check_grouped(orc, C, A, B, M, N, K, F16, "f32", rows, what="skinny")
+@pytest.mark.parametrize("M,variant", [(16, "skinny_m16_n64_k64"), (64, "skinny_m64_n64_k64"),
+                                       (128, "skinny_m128_n64_k64"), (32, "skinny_m32_n256_k64")])
+def test_grouped_skinny(orc, monkeypatch, M, variant):
+    """Grouped rows on the streaming kernel: counts past M, zero and negative, ragged inside a 16-row block."""
+    monkeypatch.setenv("TSM_GEMM_KERNEL", variant)
+    N, K = 512, 512
+    rows = [0, 1, 7, M, M + 20, -3, M - 1, 17]
+    A, B = make_operands(43 + M, len(rows), M, N, K, F16, ("uniform", -0.5, 0.5))
+    say(f"[gpu] grouped {variant} rows={rows}")
+    C = run_grouped(A, B, M, N, K, F16, "f32", rows, kernel=variant)
+    check_grouped(orc, C, A, B, M, N, K, F16, "f32", rows, what=variant)
 
 
 def test_grouped_deep_k_avoids_split_k(orc):
-    M, N, K = 64, 64, 4096
-    rows = [64, 17, 0]
+    M, N, K = 160, 64, 4096
+    rows = [160, 17, 0]
     A, B = make_operands(44, len(rows), M, N, K, F16, ("uniform", -1.0, 1.0))
     say("[gpu] grouped deep K")
     C = run_grouped(A, B, M, N, K, F16, "f32", rows, kernel="masked_")

@@ -239,10 +239,16 @@ SKINNY = "skinny_"
 SKINNY_SHAPES = [(16, 256, 256, 1), (1, 512, 256, 1), (5, 256, 512, 3), (16, 768, 1024, 2), (12, 256, 256, 2)]
 
 
+def skinny_variant(M, width):
+    """Kernel name of the skinny variant for M rows at the given workgroup width."""
+    mb = 1 if M <= 16 else 2 if M <= 32 else 4 if M <= 64 else 8
+    return f"skinny_m{16 * mb}_n{width}_k64"
+
+
 @pytest.mark.parametrize("shape", SKINNY_SHAPES, ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("in_fmt,out_fmt", [(F16, "f32"), (BF16, "f16"), (F16, "f16"), (BF16, "f32")])
 def test_skinny_kernel(orc, shape, in_fmt, out_fmt):
-    """The M <= 16 streaming kernel (row-major A and B) against the oracle, rows past M masked."""
+    """The streaming kernel for few rows (row-major A and B) against the oracle, rows past M masked."""
     M, N, K, batch = shape
     A, B = make_operands(M * 1000 + N + K + batch, batch, M, N, K, in_fmt, ("uniform", -1.0, 1.0))
     say(f"[gpu] skinny kernel {shape} {in_fmt}->{out_fmt}")
@@ -251,27 +257,68 @@ def test_skinny_kernel(orc, shape, in_fmt, out_fmt):
     check(C, Cr, S, K, out_fmt, f"skinny {shape}")
 
 
-def test_skinny_kernel_padded_and_sentinel(orc):
-    """Padded lda/ldb/ldc with C prefilled: rows of C past M and the ld padding keep their bits."""
-    M, N, K, batch = 7, 512, 256, 2
+# every row-block count at both widths (256 only up to 64 rows); M ragged inside its last 16-row block; K from
+# one 64-deep slice (the rest of the ring's first round loads zeros) to several rounds plus a partial one
+SKINNY_VARIANT_SHAPES = [(1, 64), (13, 64), (16, 256), (17, 64), (30, 256), (32, 64), (33, 64), (47, 256), (64, 64),
+                         (65, 64), (100, 64), (128, 64)]
+SKINNY_K = [64, 192, 576, 1344]
+
+
+@pytest.mark.parametrize("M,width", SKINNY_VARIANT_SHAPES, ids=lambda v: str(v))
+@pytest.mark.parametrize("K", SKINNY_K)
+def test_skinny_variants(orc, monkeypatch, M, width, K):
+    """Each skinny variant (16, 32, 64 or 128 rows; 64 or 256 columns per workgroup) forced, against the oracle."""
+    variant = skinny_variant(M, width)
+    N, batch = (512, 2) if width == 256 else (320, 3)
+    monkeypatch.setenv("TSM_GEMM_KERNEL", variant)
+    in_fmt, out_fmt = [(F16, "f32"), (BF16, "f16"), (BF16, "bf16"), (F16, "f16")][(M + K) % 4]
+    A, B = make_operands(M * 7 + K + width, batch, M, N, K, in_fmt, ("uniform", -1.0, 1.0))
+    say(f"[gpu] {variant} M={M} N={N} K={K} batch={batch} {in_fmt}->{out_fmt}")
+    C = run(A, B, M, N, K, in_fmt, out_fmt, batch=batch, kernel=variant)
+    Cr, S = orc.gemm_rows(A, B, M, N, K, in_fmt, batch=batch)
+    check(C, Cr, S, K, out_fmt, f"{variant} K={K}")
+
+
+@pytest.mark.parametrize("M,width", [(7, 256), (7, 64), (40, 64), (90, 64)], ids=lambda v: str(v))
+def test_skinny_kernel_padded_and_sentinel(orc, monkeypatch, M, width):
+    """Padded lda/ldb/ldc holding NaN, C prefilled: the padding is never read, and rows of C past M and the ld
+    padding keep their bits."""
+    variant = skinny_variant(M, width)
+    monkeypatch.setenv("TSM_GEMM_KERNEL", variant)
+    N, K, batch = 512, 256, 2
     lda, ldb, ldc = K + 24, N + 64, N + 8
-    A, B = make_operands(77, batch, M, N, K, F16, ("uniform", -1.0, 1.0))
-    Ap = np.zeros((batch, M, lda), np.uint16)
+    A, B = make_operands(77 + M, batch, M, N, K, F16, ("uniform", -1.0, 1.0))
+    nan16 = np.uint16(0x7E00)
+    Ap = np.full((batch, M, lda), nan16, np.uint16)
     Ap[:, :, :K] = A
-    Bp = np.zeros((batch, K, ldb), np.uint16)
+    Bp = np.full((batch, K, ldb), nan16, np.uint16)
     Bp[:, :, :N] = B
-    sC = 16 * ldc
-    say("[gpu] skinny padded + sentinel")
+    rows_c = M + 3
+    sC = rows_c * ldc
+    say(f"[gpu] {variant} padded + sentinel M={M}")
     C, raw = run(Ap, Bp, M, N, K, F16, "f32", batch=batch, lda=lda, ldb=ldb, ldc=ldc, sC=sC, fill=100.0, keep=True,
-                 kernel=SKINNY)
+                 kernel=variant)
     Cr, S = orc.gemm_rows(A, B, M, N, K, F16, batch=batch)
-    check(C, Cr, S, K, "f32", "skinny padded")
+    check(C, Cr, S, K, "f32", f"{variant} padded")
     host = raw.cpu().numpy()
     for z in range(batch):
         for i in range(M):
             o = z * sC + i * ldc
             assert np.all(host[o + N:o + ldc] == 100.0)
-        assert np.all(host[z * sC + M * ldc:z * sC + 16 * ldc][: (16 - M) * ldc] == 100.0) if z < batch - 1 else True
+        if z < batch - 1:
+            assert np.all(host[z * sC + M * ldc:(z + 1) * sC] == 100.0)
+
+
+def test_skinny_decode_sampled(orc):
+    """A decode-sized product, 48 x 16384 x 8192 (one problem: the 64-column workgroups), on sampled cells."""
+    M, N, K = 48, 16384, 8192
+    A, B = make_operands(4242, 1, M, N, K, F16, ("uniform", -0.5, 0.5))
+    say("[gpu] skinny decode 48x16384x8192 sampled")
+    C = run(A, B, M, N, K, F16, "f32", kernel="skinny_m64_n64_k64")
+    rng = np.random.default_rng(12)
+    z, i, j = _sample_cells(rng, 1, M, N, 3000)
+    Cp, Sp = orc.gemm_points(A, B, M, N, K, F16, z, i, j)
+    check(C[z, i, j], Cp, Sp, K, "f32", "skinny decode sampled")
 
 
 SPLITK = "splitk_"

@@ -45,7 +45,7 @@ bool ranges_overlap(const void *p, int64_t pbytes, const void *q, int64_t qbytes
 
 enum class Kernel { None, Masked8, Masked1, Small8, Small1, Tile32, Tile16, Tile16NN, TileW, TileWNN, Skinny, SplitK };
 
-const char *kernel_name(Kernel k) {
+const char *kernel_name(Kernel k, const Problem &p) {
   switch (k) {
     case Kernel::Masked8:
       return masked_name(8, 128);
@@ -66,7 +66,7 @@ const char *kernel_name(Kernel k) {
     case Kernel::TileWNN:
       return tile_name(4);
     case Kernel::Skinny:
-      return skinny_name();
+      return skinny_name(p);
     case Kernel::SplitK:
       return splitk_name();
     default:
@@ -203,7 +203,16 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
   const bool many = ((M + TileInfo::BM - 1) / TileInfo::BM) * ((N + TileInfo::BN - 1) / TileInfo::BN) * batch >= 256;
   if (K > 0 && many && tile_supports(p, false)) out->kernel = Kernel::TileW;
   if (K > 0 && many && tile_supports(p, true)) out->kernel = Kernel::Tile16NN;
-  if (K > 0 && skinny_supports(p)) out->kernel = Kernel::Skinny;
+  // up to 128 rows: the streaming kernel reads B once, where split-K reads
+  // it once per 16-row tile and the 256-row tiles waste most of their MFMA
+  // work.  Its rate grows with its grid (about 6.7 TB/s at 256 workgroups,
+  // one per CU); split-K's falls with the row tiles (about 3 TB/s over one).
+  // Split-K keeps the problem while grid x row tiles < 128.
+  if (K > 0) {
+    const SkinnyPlan sp = skinny_plan(p);
+    const bool narrow = sp.mb && (N / sp.w) * batch * ((M + 15) / 16) < 128;
+    if (sp.mb && !(narrow && out->kernel == Kernel::SplitK)) out->kernel = Kernel::Skinny;
+  }
 
   // TSM_GEMM_KERNEL=<name> forces a kernel variant (tests and tuning); a
   // variant that cannot run this problem is an error, never a silent fallback.
@@ -212,7 +221,16 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
     const Kernel all[] = {Kernel::Masked8, Kernel::Masked1, Kernel::Small8, Kernel::Small1, Kernel::Tile32, Kernel::Tile16, Kernel::Tile16NN, Kernel::TileW, Kernel::TileWNN, Kernel::Skinny, Kernel::SplitK};
     Kernel want = Kernel::None;
     for (Kernel k : all)
-      if (strcmp(force, kernel_name(k)) == 0) want = k;
+      if (k != Kernel::Skinny && strcmp(force, kernel_name(k, p)) == 0) want = k;
+    // a skinny name fixes the workgroup width (its row blocks follow from M)
+    if (strncmp(force, "skinny_", 7) == 0) {
+      want = Kernel::Skinny;
+      const char *w = strstr(force, "_n");
+      p.skinny_w = w ? atoi(w + 2) : -1;
+      const char *nm = skinny_name(p);
+      if (!nm || strcmp(nm, force) != 0)
+        return fail(TSM_ERROR_NOT_SUPPORTED, "TSM_GEMM_KERNEL=%s cannot run this problem", force);
+    }
     if (want == Kernel::None) return fail(TSM_ERROR_INVALID_VALUE, "TSM_GEMM_KERNEL=%s names no kernel", force);
     const bool ok = want == Kernel::Masked1 || want == Kernel::Small1 ||
                     ((want == Kernel::Masked8 || want == Kernel::Small8) && a8 && b8) ||
@@ -392,7 +410,7 @@ const char *tsm_gemm_kernel_name(int64_t M, int64_t N, int64_t K, const void *A,
   if (tsm::plan(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, strideB, C, ldc, strideC, batch, dtype, nullptr,
                 false, TSM_ACT_NONE, 0.f, &pl) != TSM_SUCCESS)
     return nullptr;
-  return tsm::kernel_name(pl.kernel);
+  return tsm::kernel_name(pl.kernel, pl.p);
 }
 
 const char *tsm_gemm_grouped_kernel_name(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a,
@@ -403,7 +421,7 @@ const char *tsm_gemm_grouped_kernel_name(int64_t M, int64_t N, int64_t K, const 
   if (tsm::plan(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, strideB, C, ldc, strideC, groups, dtype, rows,
                 true, TSM_ACT_NONE, 0.f, &pl) != TSM_SUCCESS)
     return nullptr;
-  return tsm::kernel_name(pl.kernel);
+  return tsm::kernel_name(pl.kernel, pl.p);
 }
 
 }  // extern "C"

@@ -24,6 +24,7 @@ struct Problem {
   int act;        // epilogue activation: 0 none, 1 ReLU, 2 leaky ReLU
   float slope;    // leaky ReLU slope
   const int32_t *rows;  // grouped products: device array of per-problem row counts (else null)
+  int skinny_w;         // skinny kernel: workgroup width forced (64 or 256), or 0 to choose by the grid
 };
 
 // Kernel arguments, passed by value.  Offsets are 64-bit throughout.
@@ -76,11 +77,17 @@ struct TileInfo {
 };
 bool tile_supports(const Problem &p, bool b_row);
 
-// Skinny kernel: M <= 16, row-major A and B, N a multiple of 256, K a
-// multiple of 256, 16-byte aligned rows.
+// Skinny kernel: M <= 128 (in 1, 2, 4 or 8 blocks of 16 rows), row-major A
+// and B, N a multiple of the workgroup width (256 columns when that grid fills
+// the chip, else 64), K a multiple of 64, 16-byte aligned rows.
 struct SkinnyInfo {
-  static constexpr int BN = 256, BK = 64;
+  static constexpr int BK = 64;
 };
+struct SkinnyPlan {
+  int mb = 0;  // 16-row blocks (0: the kernel cannot run the problem)
+  int w = 0;   // columns per workgroup
+};
+SkinnyPlan skinny_plan(const Problem &p);
 bool skinny_supports(const Problem &p);
 
 // Split-K kernel for small M x N and deep K: 16 x 16 tiles, K split across the
@@ -93,7 +100,7 @@ bool splitk_supports(const Problem &p);
 hipError_t launch_splitk(const Problem &p, hipStream_t stream);
 const char *splitk_name();
 hipError_t launch_skinny(const Problem &p, hipStream_t stream);
-const char *skinny_name();
+const char *skinny_name(const Problem &p);
 hipError_t launch_tile(const Problem &p, int variant, hipStream_t stream);
 const char *tile_name(int variant);
 
