@@ -96,6 +96,7 @@ def workload_args(argv):
                 out.append(next(it, ""))
     return " ".join(out)
 KERNEL_SYMBOL = {"tile_": "gemm_tile_kernel", "skinny_": "gemm_skinny_kernel", "splitk_": "gemm_splitk_kernel",
+                 "ksplit_": "gemm_skinny_kernel",  # the K-split pass; its reduction is the short second kernel
                  "masked_": "gemm_masked_kernel", "rowsum_wave": "rowsum_wave_kernel",
                  "rowsum_block": "rowsum_block_kernel"}
 
@@ -209,7 +210,7 @@ def summarize(run_dir):
 class Setup:
     """Inputs of one workload uploaded to the GPU, and a closure that runs one step."""
 
-    def __init__(self, w, torch, tsm, act=0, slope=0.0):
+    def __init__(self, w, torch, tsm, act=0, slope=0.0, workspace=True):
         self.w = w
         self.act, self.slope = act, slope
         log(f"generating {w.name} inputs on the host")
@@ -245,7 +246,14 @@ class Setup:
                          self.c, self.ldc, self.sC, w.batch, self.code)
             self.kernel = tsm.tsm_gemm_kernel_name(*self.args)
             self.call = tsm.gemm_strided_batched_ex
-            if act:  # the same product with an activation fused into the epilogue
+            # few output tiles and deep K: split K through a workspace allocated here, outside the timed steps
+            self.ws_bytes = tsm.gemm_workspace_bytes(w.M, w.N, w.K, w.batch) if workspace else 0
+            if self.ws_bytes:
+                self.ws = torch.empty(self.ws_bytes // 4, dtype=torch.float32, device="cuda")
+                self.kernel = tsm.tsm_gemm_ws_kernel_name(*self.args, self.ws, self.ws_bytes)
+                self.args = self.args + (act, slope, self.ws, self.ws_bytes)
+                self.call = tsm.gemm_strided_batched_ws
+            elif act:  # the same product with an activation fused into the epilogue
                 self.args = self.args + (act, slope)
                 self.call = tsm.gemm_strided_batched_act
 
@@ -389,6 +397,9 @@ def main():
     ap.add_argument("--activation", choices=["none", "relu", "leaky_relu"], default="none",
                     help="fuse an activation into the epilogue (the result is checked through it)")
     ap.add_argument("--slope", type=float, default=0.01, help="leaky ReLU slope")
+    ap.add_argument("--no-workspace", action="store_true",
+                    help="never split K through a workspace (shapes with few output tiles then use split-K inside "
+                         "a workgroup)")
     ap.add_argument("--summarize", metavar="RUN_DIR",
                     help="no GPU: write profiles/ from the rocprofv3 output of the commands in PROFILE_COMMANDS")
     args = ap.parse_args()
@@ -426,7 +437,7 @@ def main():
         print(json.dumps(rowsum_bench(args, w, torch, tsm)), flush=True)
         return
     act = {"none": 0, "relu": 1, "leaky_relu": 2}[args.activation]
-    s = Setup(w, torch, tsm, act, args.slope if act == 2 else 0.0)
+    s = Setup(w, torch, tsm, act, args.slope if act == 2 else 0.0, workspace=not args.no_workspace)
     log(f"kernel {s.kernel}; warm-up {args.warmup}")
     for _ in range(args.warmup):
         s.step()

@@ -189,6 +189,43 @@ int gemm_strided_batched_act(int64_t M, int64_t N, int64_t K, const void *A, int
                              int64_t ldc, int64_t strideC, int64_t batch, int dtype, int activation, float slope,
                              void *stream);
 
+/*
+ * gemm_workspace_bytes -- bytes of workspace with which gemm_strided_batched_ws
+ * splits K for a problem of this shape: batch * S * M * N * 4 for S chunks of
+ * K, or 0 when the shape does not split (its output tiles already occupy the
+ * chip, K is below 512 or not a multiple of 64, or N is not a multiple of 64).
+ * Depends on the sizes only.  Negative sizes give 0.
+ */
+int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t batch);
+
+/*
+ * gemm_strided_batched_ws -- gemm_strided_batched_act that may split K through
+ * a caller's workspace, for products with few output tiles and deep K (e.g.
+ * 256 x 256 x 8192, sixteen 64 x 64 tiles for 256 CUs).  The two-pass,
+ * deterministic form of the split: pass 1 gives each workgroup one output tile
+ * and one K chunk of 512 or more and stores its float32 partial sums into the
+ * workspace; pass 2 adds the chunks of every output element in a fixed order,
+ * applies the activation and the output conversion, and stores C once.  No
+ * atomics, no zeroed memory: the store-once rule of "A Dumb Triton Runtime
+ * Error" (section "The Takeaway and the Final Fix") holds across the split.
+ *   workspace       : device memory owned by the caller, 16-byte aligned, not
+ *                     overlapping A, B or C; its contents on entry do not
+ *                     matter and on return are unspecified.  May be NULL
+ *                     (with workspace_bytes = 0): the call then never splits.
+ *   workspace_bytes : its size.  Below gemm_workspace_bytes(M, N, K, batch),
+ *                     or for operands the split pass cannot read (it needs
+ *                     row-major A and B, 16-byte aligned rows and bases), the
+ *                     call runs exactly as gemm_strided_batched_act.
+ * Two calls in flight at once must not share a workspace.  Other arguments,
+ * rules and errors as for gemm_strided_batched_act; additionally
+ * TSM_ERROR_INVALID_VALUE for negative workspace_bytes, a NULL workspace with
+ * workspace_bytes > 0, a misaligned workspace or one overlapping an operand.
+ */
+int gemm_strided_batched_ws(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a,
+                            int64_t strideA, const void *B, int64_t ldb, int layout_b, int64_t strideB, void *C,
+                            int64_t ldc, int64_t strideC, int64_t batch, int dtype, int activation, float slope,
+                            void *workspace, int64_t workspace_bytes, void *stream);
+
 /* Static text for a status code ("success", "invalid value", ...). */
 const char *tsm_status_string(int status);
 
@@ -206,6 +243,13 @@ const char *tsm_last_error_detail(void);
 const char *tsm_gemm_kernel_name(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a,
                                  int64_t strideA, const void *B, int64_t ldb, int layout_b, int64_t strideB,
                                  void *C, int64_t ldc, int64_t strideC, int64_t batch, int dtype);
+
+/* tsm_gemm_ws_kernel_name -- the same for a gemm_strided_batched_ws call (a
+ * split names its pass-1 kernel followed by "+reduce"). */
+const char *tsm_gemm_ws_kernel_name(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a,
+                                    int64_t strideA, const void *B, int64_t ldb, int layout_b, int64_t strideB,
+                                    void *C, int64_t ldc, int64_t strideC, int64_t batch, int dtype,
+                                    const void *workspace, int64_t workspace_bytes);
 
 /* tsm_gemm_grouped_kernel_name -- the same for a gemm_grouped call. */
 const char *tsm_gemm_grouped_kernel_name(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a,

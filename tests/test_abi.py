@@ -209,6 +209,56 @@ def test_skinny_forced_width(monkeypatch):
         assert ei.value.status == 2
 
 
+W0 = 0x7F4000000000  # fake device address of a workspace
+
+
+def test_workspace_bytes():
+    """The K split's workspace depends on the shape only: batch * chunks * M * N * 4 bytes, or 0."""
+    assert tsm.gemm_workspace_bytes(256, 256, 8192, 1) == 16 * 256 * 256 * 4  # sixteen 512-deep chunks
+    assert tsm.gemm_workspace_bytes(16, 4096, 4096, 1) == 4 * 16 * 4096 * 4
+    assert tsm.gemm_workspace_bytes(100, 192, 1344, 1) == 5 * 100 * 192 * 4  # chunks of 320, the last 64 deep
+    assert tsm.gemm_workspace_bytes(8192, 8192, 8192, 1) == 0  # enough output tiles
+    assert tsm.gemm_workspace_bytes(16, 16384, 8192, 1) == 0  # 256 workgroups of 64 columns already
+    assert tsm.gemm_workspace_bytes(256, 256, 8200, 1) == 0  # K % 64
+    assert tsm.gemm_workspace_bytes(256, 250, 8192, 1) == 0  # N % 64
+    assert tsm.gemm_workspace_bytes(256, 256, 448, 1) == 0  # K below 512
+    assert tsm.gemm_workspace_bytes(-1, 256, 8192, 1) == 0
+
+
+def _ws_args(M=256, N=256, K=8192, ws=W0, nbytes=None, lb=0):
+    nbytes = tsm.gemm_workspace_bytes(M, N, K, 1) if nbytes is None else nbytes
+    ldb = K if lb else N
+    return (M, N, K, A0, K, 0, 0, 0x7E0000000000, ldb, lb, 0, C0, N, 0, 1, 0, ws, nbytes)
+
+
+def test_workspace_routing(monkeypatch):
+    assert tsm.tsm_gemm_ws_kernel_name(*_ws_args()) == "ksplit_skinny_m64_n64_k64+reduce"
+    assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(M=16, N=4096, K=4096)) == "ksplit_skinny_m16_n64_k64+reduce"
+    assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(M=24, N=4096, K=4096)) == "ksplit_skinny_m32_n64_k64+reduce"
+    # too little workspace, none, a column-major B or a forced kernel: the kernel that needs none
+    assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(nbytes=16 * 256 * 256 * 4 - 4)).startswith("splitk_")
+    assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(ws=0, nbytes=0)).startswith("splitk_")
+    assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(lb=1, nbytes=1 << 30)).startswith("masked_")
+    monkeypatch.setenv("TSM_GEMM_KERNEL", "masked_64x64x32_vec8")
+    assert tsm.tsm_gemm_ws_kernel_name(*_ws_args()) == "masked_64x64x32_vec8"
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(nbytes=-1), "negative workspace_bytes"),
+    (dict(ws=0, nbytes=64), "workspace is NULL"),
+    (dict(ws=W0 + 8), "not 16-byte aligned"),
+    (dict(ws=C0 + 1024), "workspace overlaps C"),
+    (dict(ws=A0 + 4096), "workspace overlaps A"),
+])
+def test_workspace_errors(kw, needle):
+    args = list(_ws_args(**kw))
+    with pytest.raises(tsm.TsmError) as ei:
+        tsm.gemm_strided_batched_ws(*args[:16], 0, 0.0, args[16], args[17], 0)
+    assert ei.value.status == 1
+    assert needle in ei.value.detail
+    assert tsm.tsm_gemm_ws_kernel_name(*args) is None
+
+
 R0 = 0x7F3000000000  # fake device address of the row counts
 
 

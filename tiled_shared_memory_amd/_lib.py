@@ -60,6 +60,11 @@ SIGNATURES = {
     "gemm_strided_batched_act": ([_I64, _I64, _I64, _PTR, _I64, _INT, _I64, _PTR, _I64, _INT, _I64, _PTR, _I64, _I64,
                                   _I64, _INT, _INT, ctypes.c_float, _PTR], _INT),
     "tsm_rowsum_kernel_name": ([_I64, _I64, _PTR, _I64, _I64, _INT, _PTR], ctypes.c_char_p),
+    "gemm_workspace_bytes": ([_I64, _I64, _I64, _I64], _I64),
+    "gemm_strided_batched_ws": ([_I64, _I64, _I64, _PTR, _I64, _INT, _I64, _PTR, _I64, _INT, _I64, _PTR, _I64, _I64,
+                                 _I64, _INT, _INT, ctypes.c_float, _PTR, _I64, _PTR], _INT),
+    "tsm_gemm_ws_kernel_name": ([_I64, _I64, _I64, _PTR, _I64, _INT, _I64, _PTR, _I64, _INT, _I64, _PTR, _I64, _I64,
+                                 _I64, _INT, _PTR, _I64], ctypes.c_char_p),
 }
 
 
@@ -152,6 +157,25 @@ def gemm_strided_batched_act(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_
     return _check(lib, lib.gemm_strided_batched_act(M, N, K, _ptr(A), lda, layout_a, strideA, _ptr(B), ldb, layout_b,
                                                     strideB, _ptr(C), ldc, strideC, batch, dtype, activation, slope,
                                                     _stream(stream)))
+
+
+def gemm_workspace_bytes(M, N, K, batch):
+    return int(load().gemm_workspace_bytes(M, N, K, batch))
+
+
+def gemm_strided_batched_ws(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, strideB, C, ldc, strideC, batch,
+                            dtype, activation, slope, workspace, workspace_bytes, stream=None):
+    lib = load()
+    return _check(lib, lib.gemm_strided_batched_ws(M, N, K, _ptr(A), lda, layout_a, strideA, _ptr(B), ldb, layout_b,
+                                                   strideB, _ptr(C), ldc, strideC, batch, dtype, activation, slope,
+                                                   _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def tsm_gemm_ws_kernel_name(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, strideB, C, ldc, strideC, batch,
+                            dtype, workspace, workspace_bytes):
+    r = load().tsm_gemm_ws_kernel_name(M, N, K, _ptr(A), lda, layout_a, strideA, _ptr(B), ldb, layout_b, strideB,
+                                       _ptr(C), ldc, strideC, batch, dtype, _ptr(workspace), workspace_bytes)
+    return r.decode() if r else None
 
 
 def gemm_grouped(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, strideB, C, ldc, strideC, rows, groups, dtype,

@@ -77,6 +77,8 @@ const char *kernel_name(Kernel k, const Problem &p) {
 struct Plan {
   Problem p;
   Kernel kernel = Kernel::None;
+  bool forced = false;                      // TSM_GEMM_KERNEL named the kernel
+  int64_t a_bytes = 0, b_bytes = 0, c_bytes = 0;  // operand extents (A and B only when K > 0)
 };
 
 // Can an operand be read with 16-byte vectors along its contiguous dimension?
@@ -109,8 +111,8 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
                                            (long long)M, (long long)N, (long long)K);
   if (batch < 0) return fail(TSM_ERROR_INVALID_VALUE, "negative batch %lld", (long long)batch);
 
+  *out = Plan{};
   Problem &p = out->p;
-  p = Problem{};
   p.A = (const uint16_t *)A;
   p.B = (const uint16_t *)B;
   p.C = C;
@@ -162,6 +164,7 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
   int64_t c_elems, c_bytes;
   if (!extent(batch, strideC, M, ldc, N, &c_elems) || !mul_ok(c_elems, csize, &c_bytes))
     return fail(TSM_ERROR_NOT_SUPPORTED, "C extent overflows int64");
+  out->c_bytes = c_bytes;
 
   // ---- A and B (only read when K > 0)
   if (K > 0) {
@@ -182,6 +185,8 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
       return fail(TSM_ERROR_NOT_SUPPORTED, "operand extent overflows int64");
     if (ranges_overlap(C, c_bytes, A, a_bytes)) return fail(TSM_ERROR_INVALID_VALUE, "C overlaps A");
     if (ranges_overlap(C, c_bytes, B, b_bytes)) return fail(TSM_ERROR_INVALID_VALUE, "C overlaps B");
+    out->a_bytes = a_bytes;
+    out->b_bytes = b_bytes;
   }
   if (batch == 1) {
     p.sA = p.sB = p.sC = 0;
@@ -241,6 +246,7 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
                     (want == Kernel::SplitK && K > 0 && splitk_supports(p));
     if (!ok) return fail(TSM_ERROR_NOT_SUPPORTED, "TSM_GEMM_KERNEL=%s cannot run this problem", force);
     out->kernel = want;
+    out->forced = true;
   }
   return TSM_SUCCESS;
 }
@@ -285,6 +291,31 @@ int run(const Plan &pl, void *stream) {
       e = launch_splitk(pl.p, s);
       break;
   }
+  if (e != hipSuccess) return fail(TSM_ERROR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return TSM_SUCCESS;
+}
+
+// Workspace of a K-split call: validated on the host; `ks` gets the split to
+// run (none when the problem does not split, the workspace is too small, or
+// a kernel is forced).
+int ws_check(const Plan &pl, const void *ws, int64_t ws_bytes, KSplit *ks) {
+  *ks = KSplit{};
+  if (ws_bytes < 0) return fail(TSM_ERROR_INVALID_VALUE, "negative workspace_bytes");
+  if (!ws && ws_bytes > 0) return fail(TSM_ERROR_INVALID_VALUE, "workspace is NULL with workspace_bytes > 0");
+  if (!ws || pl.kernel == Kernel::None || pl.forced) return TSM_SUCCESS;
+  if ((uintptr_t)ws & 15) return fail(TSM_ERROR_INVALID_VALUE, "workspace not 16-byte aligned");
+  if (ranges_overlap(ws, ws_bytes, pl.p.C, pl.c_bytes)) return fail(TSM_ERROR_INVALID_VALUE, "workspace overlaps C");
+  if (ranges_overlap(ws, ws_bytes, pl.p.A, pl.a_bytes)) return fail(TSM_ERROR_INVALID_VALUE, "workspace overlaps A");
+  if (ranges_overlap(ws, ws_bytes, pl.p.B, pl.b_bytes)) return fail(TSM_ERROR_INVALID_VALUE, "workspace overlaps B");
+  const KSplit k = ksplit_plan(pl.p);
+  if (!k.splits || pl.p.batch * k.splits * pl.p.M * pl.p.N * 4 > ws_bytes) return TSM_SUCCESS;
+  *ks = k;
+  return TSM_SUCCESS;
+}
+
+int run_ws(const Plan &pl, const KSplit &ks, void *ws, void *stream) {
+  if (!ks.splits) return run(pl, stream);
+  const hipError_t e = launch_ksplit(pl.p, ks, (float *)ws, (hipStream_t)stream);
   if (e != hipSuccess) return fail(TSM_ERROR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   return TSM_SUCCESS;
 }
@@ -357,6 +388,38 @@ int gemm_strided_batched_act(int64_t M, int64_t N, int64_t K, const void *A, int
                      nullptr, false, activation, slope, &pl);
   if (st != TSM_SUCCESS) return st;
   return tsm::run(pl, stream);
+}
+
+int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t batch) {
+  const tsm::KSplit ks = tsm::ksplit_shape(M, N, K, batch);
+  return ks.splits ? batch * ks.splits * M * N * 4 : 0;
+}
+
+int gemm_strided_batched_ws(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a,
+                            int64_t strideA, const void *B, int64_t ldb, int layout_b, int64_t strideB, void *C,
+                            int64_t ldc, int64_t strideC, int64_t batch, int dtype, int activation, float slope,
+                            void *workspace, int64_t workspace_bytes, void *stream) {
+  tsm::Plan pl;
+  int st = tsm::plan(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, strideB, C, ldc, strideC, batch, dtype,
+                     nullptr, false, activation, slope, &pl);
+  if (st != TSM_SUCCESS) return st;
+  tsm::KSplit ks;
+  st = tsm::ws_check(pl, workspace, workspace_bytes, &ks);
+  if (st != TSM_SUCCESS) return st;
+  return tsm::run_ws(pl, ks, workspace, stream);
+}
+
+const char *tsm_gemm_ws_kernel_name(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a,
+                                    int64_t strideA, const void *B, int64_t ldb, int layout_b, int64_t strideB,
+                                    void *C, int64_t ldc, int64_t strideC, int64_t batch, int dtype,
+                                    const void *workspace, int64_t workspace_bytes) {
+  tsm::Plan pl;
+  if (tsm::plan(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, strideB, C, ldc, strideC, batch, dtype, nullptr,
+                false, TSM_ACT_NONE, 0.f, &pl) != TSM_SUCCESS)
+    return nullptr;
+  tsm::KSplit ks;
+  if (tsm::ws_check(pl, workspace, workspace_bytes, &ks) != TSM_SUCCESS) return nullptr;
+  return ks.splits ? tsm::ksplit_name(ks) : tsm::kernel_name(pl.kernel, pl.p);
 }
 
 int gemm_grouped(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a, int64_t strideA,

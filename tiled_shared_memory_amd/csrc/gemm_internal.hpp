@@ -42,6 +42,10 @@ struct KernelArgs {
   int32_t act;             // epilogue: 0 none, 1 ReLU, 2 leaky ReLU
   float slope;             // leaky ReLU slope
   int32_t out_bf16;        // 16-bit output is bf16 (else f16)
+  // skinny kernel, K-split pass: grid.y enumerates (problem, row block, K chunk);
+  // 0 splits means a plain launch
+  int32_t splits, row_blocks;
+  int64_t kchunk;  // K depth of every chunk but the last (a multiple of 64)
 };
 
 // Rows of problem z: M, or for a grouped product the caller's count for z
@@ -89,6 +93,24 @@ struct SkinnyPlan {
 };
 SkinnyPlan skinny_plan(const Problem &p);
 bool skinny_supports(const Problem &p);
+
+// K split through a caller's workspace, for problems whose tiles cannot fill
+// the chip: pass 1 runs the skinny kernel (64 columns per workgroup, row
+// blocks of 16 * mb rows) on each K chunk and writes float32 partial sums,
+// one M x N slab per (problem, chunk); pass 2 adds the slabs in chunk order
+// and applies the epilogue.
+struct KSplit {
+  int splits = 0;  // K chunks (0: no split)
+  int64_t kchunk = 0;
+  int mb = 0, row_blocks = 0;
+};
+// Depends on the shape only; workspace bytes = batch * splits * M * N * 4.
+KSplit ksplit_shape(int64_t M, int64_t N, int64_t K, int64_t batch);
+// The shape's split, if the operands' layouts and alignment allow it.
+KSplit ksplit_plan(const Problem &p);
+hipError_t launch_ksplit(const Problem &p, const KSplit &ks, float *ws, hipStream_t stream);
+hipError_t launch_ksplit_pass1(const Problem &p, const KSplit &ks, float *ws, hipStream_t stream);
+const char *ksplit_name(const KSplit &ks);
 
 // Split-K kernel for small M x N and deep K: 16 x 16 tiles, K split across the
 // 16 waves of a workgroup; row-major A and B, M, N multiples of 16, K a

@@ -1,0 +1,88 @@
+// K split through a caller's workspace: the fixed-order reduction (pass 2).
+//
+// Problems with few output tiles and deep K (256 x 256 x 8192 has sixteen
+// 64 x 64 tiles) cannot occupy 256 CUs by tiling M and N.  Pass 1 (the skinny
+// kernel in its K-split mode) gives each workgroup one 64-column panel, one
+// row block and one K chunk, and writes float32 partial sums: one M x N slab
+// per (problem, chunk).  This pass adds the slabs of each problem in chunk
+// order and applies the epilogue, so C is overwritten with a deterministic
+// result and no atomics or zeroed memory are involved ("A Dumb Triton Runtime
+// Error", section "The Takeaway and the Final Fix": reduce, then store once,
+// rather than accumulate across blocks with atomics).
+//
+// HBM-bound: each thread owns 4 consecutive columns of one row, loads the
+// 16-byte partials of every chunk (all issued before the first add) and
+// stores 16 bytes of float32 or 8 bytes of 16-bit output.
+#include "gemm_internal.hpp"
+#include "mfma.hpp"
+
+namespace tsm {
+namespace {
+
+struct ReduceArgs {
+  const float *ws;  // slabs [batch][splits][M][N]
+  void *C;
+  int64_t M, N, ldc, sC;
+  int64_t groups;  // batch * M * N / 4
+  int32_t splits;
+  int32_t act;
+  float slope;
+  int32_t out_bf16;
+};
+
+template <bool OUT16>
+__global__ __launch_bounds__(256) void ksplit_reduce_kernel(ReduceArgs r) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;  // group of 4 columns
+  if (g >= r.groups) return;
+  const int64_t q = r.N / 4;
+  const int64_t per_problem = r.M * q;
+  const int64_t z = g / per_problem;
+  const int64_t rem = g - z * per_problem;
+  const int64_t m = rem / q;
+  const int64_t n = (rem - m * q) * 4;
+  const int64_t slab = r.M * r.N;
+  const f32x4 *w = reinterpret_cast<const f32x4 *>(r.ws + (z * r.splits * r.M + m) * r.N + n);
+  const int64_t step = slab / 4;
+  // eight chunks in flight, added in chunk order
+  f32x4 acc = w[0];
+  int s = 1;
+  for (; s + 8 <= r.splits; s += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(&w[(s + u) * step]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  for (; s < r.splits; ++s) acc += __builtin_nontemporal_load(&w[s * step]);
+  const Epilogue ep{r.act, r.slope, r.out_bf16 != 0};
+  const int64_t at = z * r.sC + m * r.ldc + n;
+  store4<OUT16>(OUT16 ? (void *)((uint16_t *)r.C + at) : (void *)((float *)r.C + at), ep, acc[0], acc[1], acc[2],
+                acc[3]);
+}
+
+}  // namespace
+
+hipError_t launch_ksplit(const Problem &p, const KSplit &ks, float *ws, hipStream_t stream) {
+  hipError_t e = launch_ksplit_pass1(p, ks, ws, stream);
+  if (e != hipSuccess) return e;
+  ReduceArgs r;
+  r.ws = ws;
+  r.C = p.C;
+  r.M = p.M;
+  r.N = p.N;
+  r.ldc = p.ldc;
+  r.sC = p.sC;
+  r.groups = p.batch * p.M * (p.N / 4);
+  r.splits = ks.splits;
+  r.act = p.act;
+  r.slope = p.slope;
+  r.out_bf16 = p.out_bf16;
+  const int64_t blocks = (r.groups + 255) / 256;
+  if (p.out16)
+    hipLaunchKernelGGL((ksplit_reduce_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, stream, r);
+  else
+    hipLaunchKernelGGL((ksplit_reduce_kernel<false>), dim3((unsigned)blocks), dim3(256), 0, stream, r);
+  return hipGetLastError();
+}
+
+}  // namespace tsm

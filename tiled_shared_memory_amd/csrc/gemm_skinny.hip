@@ -230,17 +230,29 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(KernelArgs p) {
   const int lane = c.lane;
 
   const int64_t n0 = (int64_t)blockIdx.x * W;
-  const int64_t z = (int64_t)p.z0 + blockIdx.y;
-  const int64_t M = rows_of(p, z);  // this problem's rows (<= 16 * MB)
-  if (M == 0) return;               // uniform: nothing to compute or store
-  const uint16_t *A = p.A + z * p.sA;
-  const uint16_t *B = p.B + z * p.sB + n0;
+  const int64_t zz = (int64_t)p.z0 + blockIdx.y;
+  // K-split pass: grid.y enumerates (problem z, row block, K chunk s), and the
+  // workgroup computes rows r0 .. r0+16*MB-1 over k0 .. k0+K-1
+  int64_t z = zz, s = 0, r0 = 0;
+  if (p.splits) {
+    s = zz % p.splits;
+    const int64_t t = zz / p.splits;
+    r0 = (t % p.row_blocks) * (16 * MB);
+    z = t / p.row_blocks;
+  }
+  int64_t M = rows_of(p, z) - r0;  // this workgroup's rows (<= 16 * MB)
+  if (M > 16 * MB) M = 16 * MB;
+  if (M <= 0) return;  // uniform: nothing to compute or store
+  const int64_t k0 = s * p.kchunk;
+  const int64_t K = p.splits ? (p.K - k0 < p.kchunk ? p.K - k0 : p.kchunk) : p.K;  // a positive multiple of 64
+  const uint16_t *A = p.A + z * p.sA + r0 * p.lda + k0;
+  const uint16_t *B = p.B + z * p.sB + k0 * p.ldb + n0;
 
   c.ldb_bytes = (uint32_t)(p.ldb * 2);
   // B resource: K rows of the W-column panel (host keeps it below 1 GiB)
-  c.rb = make_rsrc(B, (uint32_t)(((p.K - 1) * p.ldb + W) * 2));
+  c.rb = make_rsrc(B, (uint32_t)(((K - 1) * p.ldb + W) * 2));
   // A resource: the M rows of A; rows at or past M point outside it
-  c.ra = make_rsrc(A, (uint32_t)(((M - 1) * p.lda + p.K) * 2));
+  c.ra = make_rsrc(A, (uint32_t)(((M - 1) * p.lda + K) * 2));
   // A chunks: block q = 8 rows; lane l fills row 8q + l/8 at position l%8
 #pragma unroll
   for (int g = 0; g < SH::A_LOADS; ++g) {
@@ -256,7 +268,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(KernelArgs p) {
     const int chunk = swz_b<W>(r, lane % SH::CHUNKS);  // the swizzle is an involution in the chunk
     c.offB[g] = (uint32_t)r * c.ldb_bytes + (uint32_t)chunk * 16u;
   }
-  c.nk = (int)(p.K / BK);  // the host guarantees K is a positive multiple of BK
+  c.nk = (int)(K / BK);  // the host guarantees K is a positive multiple of BK
 
   f32x4 acc[MB][SH::CB];
 #pragma unroll
@@ -269,8 +281,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(KernelArgs p) {
   for (int j = 0; j < c.nk; j += SH::NS) round_from<BF16, MB, W, 0>(c, j, acc);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the loads issued past the end
 
-  // ---- epilogue: lane holds C[16 mb + lane % 16][n .. n+3]
+  // ---- epilogue: lane holds C[r0 + 16 mb + lane % 16][n .. n+3]; a K-split
+  // pass stores raw float32 sums into slab z * splits + s (its ldc is N)
   const Epilogue ep = epilogue_of(p);
+  const int64_t zc = p.splits ? z * p.splits + s : z;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int64_t m = mb * 16 + (lane & 15);
@@ -278,7 +292,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(KernelArgs p) {
 #pragma unroll
     for (int cb = 0; cb < SH::CB; ++cb) {
       const int64_t n = n0 + c.wave * SH::CPW + cb * 16 + 4 * (lane >> 4);
-      const int64_t at = z * p.sC + m * p.ldc + n;
+      const int64_t at = zc * p.sC + (r0 + m) * p.ldc + n;
       store4<OUT16>(OUT16 ? (void *)((uint16_t *)p.C + at) : (void *)((float *)p.C + at), ep, acc[mb][cb][0],
                     acc[mb][cb][1], acc[mb][cb][2], acc[mb][cb][3]);
     }
@@ -362,6 +376,72 @@ hipError_t launch_skinny(const Problem &p, hipStream_t stream) {
   if (pl.mb == 2) return launch_shape<2, 64>(p, a, stream);
   if (pl.mb == 4) return launch_shape<4, 64>(p, a, stream);
   return launch_shape<8, 64>(p, a, stream);
+}
+
+KSplit ksplit_shape(int64_t M, int64_t N, int64_t K, int64_t batch) {
+  KSplit ks;
+  if (M < 1 || N < 64 || N % 64 || K % BK || K < 512 || batch < 1) return ks;
+  const int mb = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+  const int64_t row_blocks = (M + 16 * mb - 1) / (16 * mb);
+  const int64_t base = batch * (N / 64) * row_blocks;  // workgroups without a split
+  if (base >= 128) return ks;                          // enough to keep most CUs busy
+  int64_t splits = 256 / base;                         // about one workgroup per CU
+  if (splits > K / 256) splits = K / 256;              // chunks at least 256 deep
+  if (splits > 64) splits = 64;
+  if (splits < 2) return ks;
+  const int64_t kchunk = ((K + splits - 1) / splits + BK - 1) / BK * BK;
+  splits = (K + kchunk - 1) / kchunk;
+  if (splits < 2 || batch * splits * row_blocks > 0x7fffffffLL) return ks;
+  ks.splits = (int)splits;
+  ks.kchunk = kchunk;
+  ks.mb = mb;
+  ks.row_blocks = (int)row_blocks;
+  return ks;
+}
+
+KSplit ksplit_plan(const Problem &p) {
+  const KSplit ks = ksplit_shape(p.M, p.N, p.K, p.batch);
+  if (!ks.splits || p.a_col || p.b_col || p.rows) return KSplit{};
+  if (((uintptr_t)p.A & 15) || ((uintptr_t)p.B & 15) || ((uintptr_t)p.C & 15)) return KSplit{};
+  if (p.lda % 8 || p.ldb % 8 || p.ldc % 4) return KSplit{};
+  if (p.batch > 1 && (p.sA % 8 || p.sB % 8 || p.sC % 4)) return KSplit{};
+  // 32-bit buffer offsets within one chunk: B's kchunk rows, A's row block
+  if ((ks.kchunk - 1) * p.ldb + 64 >= ((int64_t)1 << 29)) return KSplit{};
+  if ((16 * ks.mb - 1) * p.lda + ks.kchunk >= ((int64_t)1 << 29)) return KSplit{};
+  return ks;
+}
+
+hipError_t launch_ksplit_pass1(const Problem &p, const KSplit &ks, float *ws, hipStream_t stream) {
+  KernelArgs a{};
+  a.A = p.A;
+  a.B = p.B;
+  a.C = ws;
+  a.M = p.M;
+  a.N = p.N;
+  a.K = p.K;
+  a.lda = p.lda;
+  a.ldb = p.ldb;
+  a.ldc = p.N;
+  a.sA = p.sA;
+  a.sB = p.sB;
+  a.sC = p.M * p.N;
+  a.splits = ks.splits;
+  a.row_blocks = ks.row_blocks;
+  a.kchunk = ks.kchunk;
+  a.tiles_m = 1;
+  a.tiles_n = (int32_t)(p.N / 64);
+  const int64_t launches = p.batch * ks.row_blocks * ks.splits;  // grid.y entries
+  if (ks.mb == 1)
+    return p.in_bf16 ? launch_t<true, false, 1, 64>(a, launches, stream) : launch_t<false, false, 1, 64>(a, launches, stream);
+  if (ks.mb == 2)
+    return p.in_bf16 ? launch_t<true, false, 2, 64>(a, launches, stream) : launch_t<false, false, 2, 64>(a, launches, stream);
+  return p.in_bf16 ? launch_t<true, false, 4, 64>(a, launches, stream) : launch_t<false, false, 4, 64>(a, launches, stream);
+}
+
+const char *ksplit_name(const KSplit &ks) {
+  if (!ks.splits) return nullptr;
+  return ks.mb == 1 ? "ksplit_skinny_m16_n64_k64+reduce"
+                    : ks.mb == 2 ? "ksplit_skinny_m32_n64_k64+reduce" : "ksplit_skinny_m64_n64_k64+reduce";
 }
 
 const char *skinny_name(const Problem &p) {
