@@ -10,9 +10,9 @@
 // Error", section "The Takeaway and the Final Fix": reduce, then store once,
 // rather than accumulate across blocks with atomics).
 //
-// HBM-bound: each thread owns 4 consecutive columns of one row, loads the
-// 16-byte partials of every chunk (all issued before the first add) and
-// stores 16 bytes of float32 or 8 bytes of 16-bit output.
+// Memory-bound: each thread owns 4 consecutive columns of one row, loads the
+// 16-byte partials of sixteen chunks at a time (all issued before the first
+// add) and stores 16 bytes of float32 or 8 bytes of 16-bit output.
 #include "gemm_internal.hpp"
 #include "mfma.hpp"
 
@@ -43,17 +43,15 @@ __global__ __launch_bounds__(256) void ksplit_reduce_kernel(ReduceArgs r) {
   const int64_t slab = r.M * r.N;
   const f32x4 *w = reinterpret_cast<const f32x4 *>(r.ws + (z * r.splits * r.M + m) * r.N + n);
   const int64_t step = slab / 4;
-  // eight chunks in flight, added in chunk order
-  f32x4 acc = w[0];
-  int s = 1;
-  for (; s + 8 <= r.splits; s += 8) {
-    f32x4 v[8];
+  // sixteen chunks in flight, added in chunk order (missing ones add +0)
+  f32x4 acc = f32x4{};
+  for (int s0 = 0; s0 < r.splits; s0 += 16) {
+    f32x4 v[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(&w[(s + u) * step]);
+    for (int u = 0; u < 16; ++u) v[u] = s0 + u < r.splits ? __builtin_nontemporal_load(&w[(s0 + u) * step]) : f32x4{};
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc += v[u];
+    for (int u = 0; u < 16; ++u) acc += v[u];
   }
-  for (; s < r.splits; ++s) acc += __builtin_nontemporal_load(&w[s * step]);
   const Epilogue ep{r.act, r.slope, r.out_bf16 != 0};
   const int64_t at = z * r.sC + m * r.ldc + n;
   store4<OUT16>(OUT16 ? (void *)((uint16_t *)r.C + at) : (void *)((float *)r.C + at), ep, acc[0], acc[1], acc[2],

@@ -229,16 +229,25 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(KernelArgs p) {
   c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = c.lane;
 
-  const int64_t n0 = (int64_t)blockIdx.x * W;
-  const int64_t zz = (int64_t)p.z0 + blockIdx.y;
-  // K-split pass: grid.y enumerates (problem z, row block, K chunk s), and the
-  // workgroup computes rows r0 .. r0+16*MB-1 over k0 .. k0+K-1
+  int64_t n0 = (int64_t)blockIdx.x * W;
+  int64_t zz = (int64_t)p.z0 + blockIdx.y;
+  // K-split pass: grid.y enumerates (problem z, K chunk s, row block), and
+  // the workgroup computes rows r0 .. r0+16*MB-1 over k0 .. k0+K-1.
+  // Workgroup i of a launch runs on XCD i % 8; numbering the work so that
+  // each XCD's share is contiguous (column block fastest, then row block,
+  // then chunk) lets the workgroups on one XCD share their chunk's A and B
+  // panels in its L2.
   int64_t z = zz, s = 0, r0 = 0;
   if (p.splits) {
-    s = zz % p.splits;
-    const int64_t t = zz / p.splits;
-    r0 = (t % p.row_blocks) * (16 * MB);
-    z = t / p.row_blocks;
+    const int64_t gx = gridDim.x, total = gx * gridDim.y;
+    int64_t id = blockIdx.x + (int64_t)blockIdx.y * gx;
+    if (total % 8 == 0) id = (id % 8) * (total / 8) + id / 8;
+    n0 = (id % gx) * W;
+    zz = p.z0 + id / gx;
+    r0 = (zz % p.row_blocks) * (16 * MB);
+    const int64_t t = zz / p.row_blocks;
+    s = t % p.splits;
+    z = t / p.splits;
   }
   int64_t M = rows_of(p, z) - r0;  // this workgroup's rows (<= 16 * MB)
   if (M > 16 * MB) M = 16 * MB;
