@@ -218,7 +218,8 @@ def test_workspace_bytes():
     assert tsm.gemm_workspace_bytes(16, 4096, 4096, 1) == 4 * 16 * 4096 * 4
     assert tsm.gemm_workspace_bytes(100, 192, 1344, 1) == 5 * 100 * 192 * 4  # chunks of 320, the last 64 deep
     assert tsm.gemm_workspace_bytes(8192, 8192, 8192, 1) == 0  # enough output tiles
-    assert tsm.gemm_workspace_bytes(16, 16384, 8192, 1) == 0  # 256 workgroups of 64 columns already
+    assert tsm.gemm_workspace_bytes(16, 16384, 8192, 1) == 4 * 16 * 16384 * 4  # 64 panels of 256 columns, 4 chunks
+    assert tsm.gemm_workspace_bytes(16, 16384, 8192, 8) == 0  # 512 panels of 256 columns already
     assert tsm.gemm_workspace_bytes(256, 256, 8200, 1) == 0  # K % 64
     assert tsm.gemm_workspace_bytes(256, 250, 8192, 1) == 0  # N % 64
     assert tsm.gemm_workspace_bytes(256, 256, 448, 1) == 0  # K below 512
@@ -235,6 +236,9 @@ def test_workspace_routing(monkeypatch):
     assert tsm.tsm_gemm_ws_kernel_name(*_ws_args()) == "ksplit_skinny_m64_n64_k64+reduce"
     assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(M=16, N=4096, K=4096)) == "ksplit_skinny_m16_n64_k64+reduce"
     assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(M=24, N=4096, K=4096)) == "ksplit_skinny_m32_n64_k64+reduce"
+    # 32 to 127 panels of 256 columns: split those (512-byte row segments of B)
+    assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(M=16, N=16384, K=8192)) == "ksplit_skinny_m16_n256_k64+reduce"
+    assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(M=64, N=8192, K=8192)) == "ksplit_skinny_m64_n256_k64+reduce"
     # too little workspace, none, a column-major B or a forced kernel: the kernel that needs none
     assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(nbytes=16 * 256 * 256 * 4 - 4)).startswith("splitk_")
     assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(ws=0, nbytes=0)).startswith("splitk_")

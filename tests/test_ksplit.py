@@ -47,14 +47,16 @@ def run_ws(A, B, M, N, K, in_fmt, out_fmt, *, batch=1, lda=None, ldb=None, ldc=N
 
 SPLIT = "ksplit_"
 SHAPES = [(256, 256, 8192, 1), (16, 4096, 4096, 1), (100, 192, 1344, 1), (48, 128, 2048, 3), (1, 64, 512, 2),
-          (200, 320, 960, 1)]
+          (200, 320, 960, 1),
+          # 256-column panels
+          (16, 8192, 1024, 1), (40, 8192, 2048, 1), (8, 4096, 1088, 2)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("in_fmt,out_fmt", [(F16, "f32"), (BF16, "f16"), (BF16, "bf16")])
 def test_ksplit_parity(orc, shape, in_fmt, out_fmt):
-    """Chunks of 256 or more (the last one ragged where K allows), row blocks ragged in M, batches; the workspace
-    starts as NaN and none of it leaks."""
+    """Chunks of 256 or more (the last one ragged where K allows), row blocks ragged in M, batches, 64- and
+    256-column panels; the workspace starts as NaN and none of it leaks."""
     M, N, K, batch = shape
     assert tsm.gemm_workspace_bytes(M, N, K, batch) > 0
     A, B = make_operands(M + 3 * N + K + batch, batch, M, N, K, in_fmt, ("uniform", -1.0, 1.0))

@@ -95,14 +95,15 @@ SkinnyPlan skinny_plan(const Problem &p);
 bool skinny_supports(const Problem &p);
 
 // K split through a caller's workspace, for problems whose tiles cannot fill
-// the chip: pass 1 runs the skinny kernel (64 columns per workgroup, row
-// blocks of 16 * mb rows) on each K chunk and writes float32 partial sums,
+// the chip: pass 1 runs the skinny kernel (64 or 256 columns per workgroup,
+// row blocks of 16 * mb rows) on each K chunk and writes float32 partial sums,
 // one M x N slab per (problem, chunk); pass 2 adds the slabs in chunk order
 // and applies the epilogue.
 struct KSplit {
   int splits = 0;  // K chunks (0: no split)
   int64_t kchunk = 0;
   int mb = 0, row_blocks = 0;
+  int w = 64;  // columns per pass-1 workgroup (64 or 256)
 };
 // Depends on the shape only; workspace bytes = batch * splits * M * N * 4.
 KSplit ksplit_shape(int64_t M, int64_t N, int64_t K, int64_t batch);

@@ -392,7 +392,19 @@ KSplit ksplit_shape(int64_t M, int64_t N, int64_t K, int64_t batch) {
   if (M < 1 || N < 64 || N % 64 || K % BK || K < 512 || batch < 1) return ks;
   const int mb = M <= 16 ? 1 : M <= 32 ? 2 : 4;
   const int64_t row_blocks = (M + 16 * mb - 1) / (16 * mb);
-  const int64_t base = batch * (N / 64) * row_blocks;  // workgroups without a split
+  // workgroups without a split: 64-column panels, or 256-column panels when
+  // there are enough of them for a split of at most 8 (each workgroup then
+  // streams 512-byte row segments of B, which HBM serves faster than the
+  // 128-byte segments of 64-column panels)
+  int w = 64;
+  int64_t base = batch * (N / 64) * row_blocks;
+  if (N % 256 == 0) {
+    const int64_t base256 = batch * (N / 256) * row_blocks;
+    if (base256 >= 32 && base256 < 128) {
+      w = 256;
+      base = base256;
+    }
+  }
   if (base >= 128) return ks;                          // enough to keep most CUs busy
   int64_t splits = 256 / base;                         // about one workgroup per CU
   if (splits > K / 256) splits = K / 256;              // chunks at least 256 deep
@@ -405,6 +417,7 @@ KSplit ksplit_shape(int64_t M, int64_t N, int64_t K, int64_t batch) {
   ks.kchunk = kchunk;
   ks.mb = mb;
   ks.row_blocks = (int)row_blocks;
+  ks.w = w;
   return ks;
 }
 
@@ -415,9 +428,19 @@ KSplit ksplit_plan(const Problem &p) {
   if (p.lda % 8 || p.ldb % 8 || p.ldc % 4) return KSplit{};
   if (p.batch > 1 && (p.sA % 8 || p.sB % 8 || p.sC % 4)) return KSplit{};
   // 32-bit buffer offsets within one chunk: B's kchunk rows, A's row block
-  if ((ks.kchunk - 1) * p.ldb + 64 >= ((int64_t)1 << 29)) return KSplit{};
+  if ((ks.kchunk - 1) * p.ldb + ks.w >= ((int64_t)1 << 29)) return KSplit{};
   if ((16 * ks.mb - 1) * p.lda + ks.kchunk >= ((int64_t)1 << 29)) return KSplit{};
   return ks;
+}
+
+template <int W>
+hipError_t launch_split_w(const Problem &p, const KSplit &ks, const KernelArgs &a, int64_t launches,
+                          hipStream_t stream) {
+  if (ks.mb == 1)
+    return p.in_bf16 ? launch_t<true, false, 1, W>(a, launches, stream) : launch_t<false, false, 1, W>(a, launches, stream);
+  if (ks.mb == 2)
+    return p.in_bf16 ? launch_t<true, false, 2, W>(a, launches, stream) : launch_t<false, false, 2, W>(a, launches, stream);
+  return p.in_bf16 ? launch_t<true, false, 4, W>(a, launches, stream) : launch_t<false, false, 4, W>(a, launches, stream);
 }
 
 hipError_t launch_ksplit_pass1(const Problem &p, const KSplit &ks, float *ws, hipStream_t stream) {
@@ -438,19 +461,18 @@ hipError_t launch_ksplit_pass1(const Problem &p, const KSplit &ks, float *ws, hi
   a.row_blocks = ks.row_blocks;
   a.kchunk = ks.kchunk;
   a.tiles_m = 1;
-  a.tiles_n = (int32_t)(p.N / 64);
+  a.tiles_n = (int32_t)(p.N / ks.w);
   const int64_t launches = p.batch * ks.row_blocks * ks.splits;  // grid.y entries
-  if (ks.mb == 1)
-    return p.in_bf16 ? launch_t<true, false, 1, 64>(a, launches, stream) : launch_t<false, false, 1, 64>(a, launches, stream);
-  if (ks.mb == 2)
-    return p.in_bf16 ? launch_t<true, false, 2, 64>(a, launches, stream) : launch_t<false, false, 2, 64>(a, launches, stream);
-  return p.in_bf16 ? launch_t<true, false, 4, 64>(a, launches, stream) : launch_t<false, false, 4, 64>(a, launches, stream);
+  return ks.w == 256 ? launch_split_w<256>(p, ks, a, launches, stream) : launch_split_w<64>(p, ks, a, launches, stream);
 }
 
 const char *ksplit_name(const KSplit &ks) {
+  static const char *const names[2][3] = {
+      {"ksplit_skinny_m16_n64_k64+reduce", "ksplit_skinny_m32_n64_k64+reduce", "ksplit_skinny_m64_n64_k64+reduce"},
+      {"ksplit_skinny_m16_n256_k64+reduce", "ksplit_skinny_m32_n256_k64+reduce",
+       "ksplit_skinny_m64_n256_k64+reduce"}};
   if (!ks.splits) return nullptr;
-  return ks.mb == 1 ? "ksplit_skinny_m16_n64_k64+reduce"
-                    : ks.mb == 2 ? "ksplit_skinny_m32_n64_k64+reduce" : "ksplit_skinny_m64_n64_k64+reduce";
+  return names[ks.w == 256][ks.mb == 1 ? 0 : ks.mb == 2 ? 1 : 2];
 }
 
 const char *skinny_name(const Problem &p) {
