@@ -8,14 +8,17 @@
 // Tile K": one K slice live at a time, float32 accumulators carried across the
 // loop).  Two shapes:
 //  * W = 256 (each wave 64 columns): 32 KiB B slices, one workgroup per CU;
-//  * W = 64 (each wave 16 columns): 8 KiB B slices, several workgroups per CU,
-//    four times the workgroups, for problems whose W = 256 grid cannot fill
-//    the chip (a single 16 x 16384 x 8192 product has only 64 such columns
-//    blocks).
+//  * W = 64 (each wave 16 columns): 8 KiB B slices, four times the
+//    workgroups, for problems whose W = 256 grid cannot fill the chip (a
+//    single 16 x 16384 x 8192 product has only 64 such column blocks).
 // Rows come in MB blocks of 16 (MB = 1, 2, 4 or 8; 8 only with W = 64).
 //
 //  * B slices go HBM -> LDS with non-temporal buffer loads that write LDS
-//    directly, through a ring of 4 stages, three slices ahead.
+//    directly, through a ring of NS stages, NS - 1 slices ahead (NS = 4 for
+//    W = 256; 8, or 6 for MB = 8, for W = 64).
+//  * K-split mode (pass 1 of the workspace path): grid.y also enumerates row
+//    blocks and K chunks; each workgroup covers one chunk of one row block
+//    and stores raw float32 partial sums, which a second kernel adds.
 //  * The MFMA wants 8 consecutive k per lane for one column, while row-major
 //    B is contiguous along n.  ds_read_b64_tr_b16 transposes on the way out
 //    of LDS: in each group of 16 lanes, lane j points at row k0 + j/4, columns
