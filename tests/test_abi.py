@@ -164,6 +164,26 @@ def test_kernel_selection_by_layout_and_shape():
     assert tsm.tsm_gemm_kernel_name(256, 256, 8192, A0, 8192, 0, 0, B0, 256, 0, 0, C0, 256, 0, 1, 0).startswith("splitk_")
 
 
+def test_mid_size_selection():
+    """Below 256 tiles the 256 x 256 kernels still win: with row-major B from 32 tiles (9 once K >= 4096), with
+    K-contiguous B from 128 tiles (48 once K >= 2048)."""
+    B0 = 0x7E0000000000
+
+    def pick(n, K, lb, m=None):
+        m = m or n
+        return tsm.tsm_gemm_kernel_name(m, n, K, A0, K, 0, 0, B0, K if lb else n, lb, 0, C0, n, 0, 1, 3)
+
+    assert pick(2048, 8192, 1) == "tile_256x256x64_mi16"  # 64 tiles
+    assert pick(2048, 1024, 1).startswith("masked_")  # 64 tiles, shallow
+    assert pick(3072, 1024, 1) == "tile_256x256x64_mi16"  # 144 tiles
+    assert pick(1536, 8192, 1).startswith("masked_64x64")  # 36 tiles
+    assert pick(768, 8192, 0) == "tile_256x256x32_mi16_nn"  # 9 tiles, deep
+    assert not pick(768, 2048, 0).startswith("tile_")  # 9 tiles, shallow
+    assert pick(4096, 4096, 0, m=512) == "tile_256x256x32_mi16_nn"  # 32 tiles
+    assert pick(3072, 8192, 0) == "tile_256x256x32_mi16_nn"
+    assert pick(512, 8192, 0).startswith("splitk_")  # 4 tiles
+
+
 def test_skinny_selection():
     """Up to 128 rows of row-major operands go to the streaming kernel: 256-column workgroups when those fill the
     256 CUs, 64-column ones otherwise; row blocks follow M.  K not a multiple of 64, N not a multiple of 64 or a

@@ -203,11 +203,21 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
   const int64_t masked_tiles = tiles * batch;
   // few 128 x 128 tiles otherwise: 64 x 64 tiles, four times the workgroups
   if (masked_tiles < 256) out->kernel = (a8 && b8) ? Kernel::Small8 : Kernel::Small1;
-  if (K > 0 && masked_tiles < 256 && splitk_supports(p)) out->kernel = Kernel::SplitK;
-  // the 256 x 256 kernels once their tiles (one workgroup per CU) fill the chip
-  const bool many = ((M + TileInfo::BM - 1) / TileInfo::BM) * ((N + TileInfo::BN - 1) / TileInfo::BN) * batch >= 256;
-  if (K > 0 && many && tile_supports(p, false)) out->kernel = Kernel::TileW;
-  if (K > 0 && many && tile_supports(p, true)) out->kernel = Kernel::Tile16NN;
+  const bool splitk_ok = K > 0 && masked_tiles < 256 && splitk_supports(p);
+  if (splitk_ok) out->kernel = Kernel::SplitK;
+  // The 256 x 256 kernels take about the same time per round of up to 256
+  // tiles (one workgroup per CU) whatever the tile count, about 8 TFLOP/s
+  // per tile, plus a fixed start-up that weighs more at small K.  Measured on
+  // squares and rectangles from 512 to 4096 with K from 512 to 8192, they
+  // overtake the masked kernels (which transpose a row-major B element by
+  // element into LDS) from 32 tiles with row-major B (9 tiles once K >= 4096),
+  // and from 128 tiles with K-contiguous B (48 tiles once K >= 2048).
+  const int64_t tiles256 =
+      ((M + TileInfo::BM - 1) / TileInfo::BM) * ((N + TileInfo::BN - 1) / TileInfo::BN) * batch;
+  const bool tile_col = tiles256 >= 128 || (tiles256 >= 48 && K >= 2048);
+  const bool tile_row = tiles256 >= 32 || (tiles256 >= 9 && K >= 4096);
+  if (K > 0 && tile_col && tile_supports(p, false)) out->kernel = Kernel::TileW;
+  if (K > 0 && tile_row && tile_supports(p, true)) out->kernel = Kernel::Tile16NN;
   // up to 128 rows: the streaming kernel reads B once, where split-K reads
   // it once per 16-row tile and the 256-row tiles waste most of their MFMA
   // work.  Its rate grows with its grid (about 6.7 TB/s at 256 workgroups,
@@ -216,7 +226,7 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
   if (K > 0) {
     const SkinnyPlan sp = skinny_plan(p);
     const bool narrow = sp.mb && (N / sp.w) * batch * ((M + 15) / 16) < 128;
-    if (sp.mb && !(narrow && out->kernel == Kernel::SplitK)) out->kernel = Kernel::Skinny;
+    if (sp.mb) out->kernel = narrow && splitk_ok ? Kernel::SplitK : Kernel::Skinny;
   }
 
   // TSM_GEMM_KERNEL=<name> forces a kernel variant (tests and tuning); a
