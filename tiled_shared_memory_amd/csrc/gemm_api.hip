@@ -317,7 +317,8 @@ int ws_check(const Plan &pl, const void *ws, int64_t ws_bytes, KSplit *ks) {
   if (ranges_overlap(ws, ws_bytes, pl.p.C, pl.c_bytes)) return fail(TSM_ERROR_INVALID_VALUE, "workspace overlaps C");
   if (ranges_overlap(ws, ws_bytes, pl.p.A, pl.a_bytes)) return fail(TSM_ERROR_INVALID_VALUE, "workspace overlaps A");
   if (ranges_overlap(ws, ws_bytes, pl.p.B, pl.b_bytes)) return fail(TSM_ERROR_INVALID_VALUE, "workspace overlaps B");
-  const KSplit k = ksplit_plan(pl.p);
+  KSplit k = ksplit_plan(pl.p);
+  if (!k.splits) k = tsplit_plan(pl.p);
   if (!k.splits || pl.p.batch * k.splits * pl.p.M * pl.p.N * 4 > ws_bytes) return TSM_SUCCESS;
   *ks = k;
   return TSM_SUCCESS;
@@ -401,8 +402,10 @@ int gemm_strided_batched_act(int64_t M, int64_t N, int64_t K, const void *A, int
 }
 
 int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t batch) {
-  const tsm::KSplit ks = tsm::ksplit_shape(M, N, K, batch);
-  return ks.splits ? batch * ks.splits * M * N * 4 : 0;
+  const tsm::KSplit ks = tsm::ksplit_shape(M, N, K, batch), ts = tsm::tsplit_shape(M, N, K, batch);
+  const int64_t a = ks.splits ? batch * ks.splits * M * N * 4 : 0;
+  const int64_t b = ts.splits ? batch * ts.splits * M * N * 4 : 0;
+  return a > b ? a : b;
 }
 
 int gemm_strided_batched_ws(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a,

@@ -104,6 +104,7 @@ struct KSplit {
   int64_t kchunk = 0;
   int mb = 0, row_blocks = 0;
   int w = 64;  // columns per pass-1 workgroup (64 or 256)
+  int tile_variant = -1;  // >= 0: pass 1 is that 256 x 256 kernel (a batch of the K chunks), not the skinny one
 };
 // Depends on the shape only; workspace bytes = batch * splits * M * N * 4.
 KSplit ksplit_shape(int64_t M, int64_t N, int64_t K, int64_t batch);
@@ -111,6 +112,10 @@ KSplit ksplit_shape(int64_t M, int64_t N, int64_t K, int64_t batch);
 KSplit ksplit_plan(const Problem &p);
 hipError_t launch_ksplit(const Problem &p, const KSplit &ks, float *ws, hipStream_t stream);
 hipError_t launch_ksplit_pass1(const Problem &p, const KSplit &ks, float *ws, hipStream_t stream);
+// The 256 x 256 kernels' split, for single products of 8-127 such tiles:
+// pass 1 runs the K chunks as a strided batch of products into the workspace.
+KSplit tsplit_shape(int64_t M, int64_t N, int64_t K, int64_t batch);
+KSplit tsplit_plan(const Problem &p);
 const char *ksplit_name(const KSplit &ks);
 
 // Split-K kernel for small M x N and deep K: 16 x 16 tiles, K split across the

@@ -1,4 +1,5 @@
-// K split through a caller's workspace: the fixed-order reduction (pass 2).
+// K split through a caller's workspace: the split of the 256 x 256 kernels
+// and the fixed-order reduction (pass 2).
 //
 // Problems with few output tiles and deep K (256 x 256 x 8192 has sixteen
 // 64 x 64 tiles) cannot occupy 256 CUs by tiling M and N.  Pass 1 (the skinny
@@ -60,8 +61,58 @@ __global__ __launch_bounds__(256) void ksplit_reduce_kernel(ReduceArgs r) {
 
 }  // namespace
 
+KSplit tsplit_shape(int64_t M, int64_t N, int64_t K, int64_t batch) {
+  KSplit ks;
+  // up to 128 rows the skinny kernel's split fits better than 256-row tiles
+  if (batch != 1 || M <= 128 || N < 8 || K % 128 || K < 1024) return ks;
+  const int64_t tiles = ((M + TileInfo::BM - 1) / TileInfo::BM) * ((N + TileInfo::BN - 1) / TileInfo::BN);
+  if (tiles < 8 || tiles >= 128) return ks;
+  // about one workgroup per CU, chunks of 512 or more that divide K into
+  // equal multiples of 128 (the chunks run as one strided batch)
+  int64_t splits = 256 / tiles;
+  if (splits > K / 512) splits = K / 512;
+  while (splits >= 2 && (K / 128) % splits) --splits;
+  if (splits < 2) return ks;
+  ks.splits = (int)splits;
+  ks.kchunk = K / splits;
+  ks.tile_variant = 0;  // chosen by tsplit_plan from B's layout
+  return ks;
+}
+
+namespace {
+// Pass 1 of the tile split: the K chunks as a strided batch of products whose
+// float32 results are the workspace slabs.
+Problem tsplit_pass1_problem(const Problem &p, const KSplit &ks, float *ws) {
+  Problem q = p;
+  q.C = ws;
+  q.ldc = p.N;
+  q.sC = p.M * p.N;
+  q.out16 = false;
+  q.out_bf16 = false;
+  q.act = 0;
+  q.slope = 0.f;
+  q.rows = nullptr;
+  q.K = ks.kchunk;
+  q.batch = ks.splits;
+  q.sA = ks.kchunk;                             // A row-major: the next chunk starts kchunk columns on
+  q.sB = p.b_col ? ks.kchunk : ks.kchunk * p.ldb;  // B: kchunk columns (K-contiguous) or rows on
+  return q;
+}
+}  // namespace
+
+KSplit tsplit_plan(const Problem &p) {
+  KSplit ks = tsplit_shape(p.M, p.N, p.K, p.batch);
+  if (!ks.splits || p.a_col || p.rows) return KSplit{};
+  if ((uintptr_t)p.C & 15) return KSplit{};
+  const Problem q = tsplit_pass1_problem(p, ks, (float *)p.C);  // alignment of the workspace is checked apart
+  if (!tile_supports(q, !p.b_col)) return KSplit{};
+  ks.tile_variant = p.b_col ? 3 : 2;  // the default large-tile kernel for B's layout
+  return ks;
+}
+
 hipError_t launch_ksplit(const Problem &p, const KSplit &ks, float *ws, hipStream_t stream) {
-  hipError_t e = launch_ksplit_pass1(p, ks, ws, stream);
+  hipError_t e = ks.tile_variant >= 0 ? launch_tile(tsplit_pass1_problem(p, ks, ws), ks.tile_variant, stream)
+                                      : launch_ksplit_pass1(p, ks, ws, stream);
   if (e != hipSuccess) return e;
   ReduceArgs r;
   r.ws = ws;

@@ -395,6 +395,9 @@ KSplit ksplit_shape(int64_t M, int64_t N, int64_t K, int64_t batch) {
   if (M < 1 || N < 64 || N % 64 || K % BK || K < 512 || batch < 1) return ks;
   const int mb = M <= 16 ? 1 : M <= 32 ? 2 : 4;
   const int64_t row_blocks = (M + 16 * mb - 1) / (16 * mb);
+  // every row block reads all of B again: beyond 512 rows the 256 x 256
+  // kernels' split (tsplit_shape) reads less
+  if (row_blocks > 8) return ks;
   // workgroups without a split: 64-column panels, or 256-column panels when
   // there are enough of them for a split of at most 8 (each workgroup then
   // streams 512-byte row segments of B, which HBM serves faster than the
@@ -470,6 +473,8 @@ hipError_t launch_ksplit_pass1(const Problem &p, const KSplit &ks, float *ws, hi
 }
 
 const char *ksplit_name(const KSplit &ks) {
+  if (ks.splits && ks.tile_variant == 3) return "ksplit_tile_256x256x64_mi16+reduce";
+  if (ks.splits && ks.tile_variant == 2) return "ksplit_tile_256x256x32_mi16_nn+reduce";
   static const char *const names[2][3] = {
       {"ksplit_skinny_m16_n64_k64+reduce", "ksplit_skinny_m32_n64_k64+reduce", "ksplit_skinny_m64_n64_k64+reduce"},
       {"ksplit_skinny_m16_n256_k64+reduce", "ksplit_skinny_m32_n256_k64+reduce",
