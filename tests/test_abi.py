@@ -181,6 +181,12 @@ def test_mid_size_selection():
     assert not pick(768, 2048, 0).startswith("tile_")  # 9 tiles, shallow
     assert pick(4096, 4096, 0, m=512) == "tile_256x256x32_mi16_nn"  # 32 tiles
     assert pick(3072, 8192, 0) == "tile_256x256x32_mi16_nn"
+    # column-major A (M-contiguous): the transposing variants
+    n, K = 2048, 8192
+    for lb, name in ((0, "tile_256x256x32_mi16_tn"), (1, "tile_256x256x32_mi16_tt")):
+        assert tsm.tsm_gemm_kernel_name(n, n, K, A0, n, 1, 0, B0, K if lb else n, lb, 0, C0, n, 0, 1, 3) == name
+    # M not a multiple of 8: the general kernel
+    assert tsm.tsm_gemm_kernel_name(n - 4, n, K, A0, n, 1, 0, B0, n, 0, 0, C0, n, 0, 1, 3).startswith("masked_")
     assert pick(512, 8192, 0).startswith("splitk_")  # 4 tiles
 
 

@@ -17,12 +17,13 @@ pytestmark = pytest.mark.gpu
 
 def run_ws(A, B, M, N, K, in_fmt, out_fmt, *, batch=1, lda=None, ldb=None, ldc=None, sA=None, sB=None, sC=None,
            act=tsm.TSM_ACT_NONE, slope=0.0, ws_bytes=None, ws_fill=float("nan"), fill=None, keep=False,
-           expect=None, b_layout="row"):
+           expect=None, a_layout="row", b_layout="row"):
     """C = act(A.B) through gemm_strided_batched_ws with a workspace of ws_bytes (default: what the shape needs)."""
     import torch
 
+    la = 1 if a_layout == "col" else 0
     lb = 1 if b_layout == "col" else 0
-    lda = lda if lda is not None else K
+    lda = lda if lda is not None else (M if la else K)
     ldb = ldb if ldb is not None else (K if lb else N)
     ldc = ldc if ldc is not None else N
     sA = sA if sA is not None else A.size // batch
@@ -35,11 +36,11 @@ def run_ws(A, B, M, N, K, in_fmt, out_fmt, *, batch=1, lda=None, ldb=None, ldc=N
     b_buf, b_ptr = to_device(B)
     c = alloc_c(batch, M, N, ldc, sC, out_fmt, fill)
     code = DTYPE[(in_fmt, out_fmt)]
-    name = tsm.tsm_gemm_ws_kernel_name(M, N, K, a_ptr, lda, 0, sA, b_ptr, ldb, lb, sB, c, ldc, sC, batch, code, ws,
+    name = tsm.tsm_gemm_ws_kernel_name(M, N, K, a_ptr, lda, la, sA, b_ptr, ldb, lb, sB, c, ldc, sC, batch, code, ws,
                                        ws_bytes)
     if expect is not None:
         assert name is not None and name.startswith(expect), f"routed to {name}, expected {expect}"
-    tsm.gemm_strided_batched_ws(M, N, K, a_ptr, lda, 0, sA, b_ptr, ldb, lb, sB, c, ldc, sC, batch, code, act, slope,
+    tsm.gemm_strided_batched_ws(M, N, K, a_ptr, lda, la, sA, b_ptr, ldb, lb, sB, c, ldc, sC, batch, code, act, slope,
                                 ws, ws_bytes, 0)
     torch.cuda.synchronize()
     res = c_view(c, batch, M, N, ldc, sC, out_fmt)
@@ -68,7 +69,8 @@ def test_ksplit_parity(orc, shape, in_fmt, out_fmt):
     say(f"[gpu] ksplit {shape}: max err/bound = {ratio:.3e}")
 
 
-TILE_SPLIT = [(640, 768, 1536, "col"), (600, 520, 1024, "row"), (1000, 512, 2048, "row"), (300, 2304, 1024, "col")]
+TILE_SPLIT = [(640, 768, 1536, "row", "col"), (600, 520, 1024, "row", "row"), (1000, 512, 2048, "row", "row"),
+              (300, 2304, 1024, "row", "col"), (520, 1024, 2048, "col", "row"), (768, 1024, 1024, "col", "col")]
 
 
 @pytest.mark.parametrize("shape", TILE_SPLIT, ids=lambda s: "x".join(map(str, s)))
@@ -76,11 +78,11 @@ TILE_SPLIT = [(640, 768, 1536, "col"), (600, 520, 1024, "row"), (1000, 512, 2048
 def test_tile_split_parity(orc, shape, in_fmt, out_fmt):
     """The 256 x 256 kernels' split (products of 8-127 such tiles, more than 128 rows): the K chunks run as a
     strided batch into the workspace, ragged M and N, both B layouts."""
-    M, N, K, b_layout = shape
-    A, B = make_operands(M + N + K, 1, M, N, K, in_fmt, ("uniform", -1.0, 1.0), "row", b_layout)
+    M, N, K, a_layout, b_layout = shape
+    A, B = make_operands(M + N + K, 1, M, N, K, in_fmt, ("uniform", -1.0, 1.0), a_layout, b_layout)
     say(f"[gpu] tile split {shape} {in_fmt}->{out_fmt}")
-    C = run_ws(A, B, M, N, K, in_fmt, out_fmt, expect="ksplit_tile_", b_layout=b_layout)
-    Cr, S = orc.gemm_rows(A, B, M, N, K, in_fmt, b_layout=b_layout)
+    C = run_ws(A, B, M, N, K, in_fmt, out_fmt, expect="ksplit_tile_", a_layout=a_layout, b_layout=b_layout)
+    Cr, S = orc.gemm_rows(A, B, M, N, K, in_fmt, a_layout=a_layout, b_layout=b_layout)
     ratio = check(C, Cr, S, K, out_fmt, f"tile split {shape}")
     say(f"[gpu] tile split {shape}: max err/bound = {ratio:.3e}")
 

@@ -405,6 +405,30 @@ def test_subnormal_f16_operands(orc):
     check(C, Cr, S, K, "f32", "subnormal")
 
 
+COL_A_VARIANTS = [("tile_256x256x32_mi16_tn", "row"), ("tile_256x256x32_mi16_tt", "col")]
+COL_A_SHAPES = [(256, 256, 128, 1), (512, 768, 384, 1), (264, 520, 256, 2), (1000, 256, 512, 1)]
+
+
+@pytest.mark.parametrize("shape", COL_A_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("in_fmt,out_fmt", [(BF16, "f16"), (F16, "f32")])
+@pytest.mark.parametrize("variant,b_layout", COL_A_VARIANTS, ids=[v for v, _ in COL_A_VARIANTS])
+def test_tile_col_a(orc, monkeypatch, shape, in_fmt, out_fmt, variant, b_layout):
+    """Column-major A (M-contiguous, as in a product with a transposed operand) on the large-tile kernel: its
+    slices are transposed out of LDS like a row-major B.  M is a multiple of 8 but not always of 256; A is stored
+    with padding rows of NaN beyond M, which must not leak."""
+    monkeypatch.setenv("TSM_GEMM_KERNEL", variant)
+    M, N, K, batch = shape
+    A, B = make_operands(M + 2 * N + K + batch, batch, M, N, K, in_fmt, ("uniform", -1.0, 1.0), "col", b_layout)
+    lda = M + 24
+    Ap = np.full((batch, K, lda), 0x7E00 if in_fmt == F16 else 0x7FC0, np.uint16)
+    Ap[:, :, :M] = A
+    say(f"[gpu] {variant} {shape} {in_fmt}->{out_fmt}")
+    C = run(Ap, B, M, N, K, in_fmt, out_fmt, batch=batch, a_layout="col", b_layout=b_layout, lda=lda,
+            ldc=N + 4, fill=float("nan"), kernel=variant)
+    Cr, S = orc.gemm_rows(A, B, M, N, K, in_fmt, batch=batch, a_layout="col", b_layout=b_layout)
+    check(C, Cr, S, K, out_fmt, f"{variant} {shape}")
+
+
 RAGGED_N = [(600, 1000, 256, 1), (256, 8, 128, 2), (300, 264, 384, 1), (512, 1304, 128, 1)]
 
 

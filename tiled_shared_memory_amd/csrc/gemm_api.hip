@@ -43,7 +43,9 @@ bool ranges_overlap(const void *p, int64_t pbytes, const void *q, int64_t qbytes
   return a < b + (uintptr_t)qbytes && b < a + (uintptr_t)pbytes;
 }
 
-enum class Kernel { None, Masked8, Masked1, Small8, Small1, Tile32, Tile16, Tile16NN, TileW, TileWNN, Skinny, SplitK };
+enum class Kernel {
+  None, Masked8, Masked1, Small8, Small1, Tile32, Tile16, Tile16NN, TileW, TileWNN, Tile16TN, Tile16TT, Skinny, SplitK
+};
 
 const char *kernel_name(Kernel k, const Problem &p) {
   switch (k) {
@@ -65,6 +67,10 @@ const char *kernel_name(Kernel k, const Problem &p) {
       return tile_name(3);
     case Kernel::TileWNN:
       return tile_name(4);
+    case Kernel::Tile16TN:
+      return tile_name(5);
+    case Kernel::Tile16TT:
+      return tile_name(6);
     case Kernel::Skinny:
       return skinny_name(p);
     case Kernel::SplitK:
@@ -216,8 +222,11 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
       ((M + TileInfo::BM - 1) / TileInfo::BM) * ((N + TileInfo::BN - 1) / TileInfo::BN) * batch;
   const bool tile_col = tiles256 >= 128 || (tiles256 >= 48 && K >= 2048);
   const bool tile_row = tiles256 >= 32 || (tiles256 >= 9 && K >= 4096);
-  if (K > 0 && tile_col && tile_supports(p, false)) out->kernel = Kernel::TileW;
-  if (K > 0 && tile_row && tile_supports(p, true)) out->kernel = Kernel::Tile16NN;
+  if (K > 0 && tile_col && tile_supports(p, false, false)) out->kernel = Kernel::TileW;
+  if (K > 0 && tile_row && tile_supports(p, false, true)) out->kernel = Kernel::Tile16NN;
+  // column-major A: the masked kernels transpose it element by element, like a row-major B
+  if (K > 0 && tile_row && tile_supports(p, true, true)) out->kernel = Kernel::Tile16TN;
+  if (K > 0 && tile_row && tile_supports(p, true, false)) out->kernel = Kernel::Tile16TT;
   // up to 128 rows: the streaming kernel reads B once, where split-K reads
   // it once per 16-row tile and the 256-row tiles waste most of their MFMA
   // work.  Its rate grows with its grid (about 6.7 TB/s at 256 workgroups,
@@ -233,7 +242,9 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
   // variant that cannot run this problem is an error, never a silent fallback.
   const char *force = getenv("TSM_GEMM_KERNEL");
   if (force && *force) {
-    const Kernel all[] = {Kernel::Masked8, Kernel::Masked1, Kernel::Small8, Kernel::Small1, Kernel::Tile32, Kernel::Tile16, Kernel::Tile16NN, Kernel::TileW, Kernel::TileWNN, Kernel::Skinny, Kernel::SplitK};
+    const Kernel all[] = {Kernel::Masked8,  Kernel::Masked1,  Kernel::Small8,   Kernel::Small1,  Kernel::Tile32,
+                          Kernel::Tile16,   Kernel::Tile16NN, Kernel::TileW,    Kernel::TileWNN, Kernel::Tile16TN,
+                          Kernel::Tile16TT, Kernel::Skinny,   Kernel::SplitK};
     Kernel want = Kernel::None;
     for (Kernel k : all)
       if (k != Kernel::Skinny && strcmp(force, kernel_name(k, p)) == 0) want = k;
@@ -250,8 +261,10 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
     const bool ok = want == Kernel::Masked1 || want == Kernel::Small1 ||
                     ((want == Kernel::Masked8 || want == Kernel::Small8) && a8 && b8) ||
                     ((want == Kernel::Tile32 || want == Kernel::Tile16 || want == Kernel::TileW) && K > 0 &&
-                     tile_supports(p, false)) ||
-                    ((want == Kernel::Tile16NN || want == Kernel::TileWNN) && K > 0 && tile_supports(p, true)) ||
+                     tile_supports(p, false, false)) ||
+                    ((want == Kernel::Tile16NN || want == Kernel::TileWNN) && K > 0 && tile_supports(p, false, true)) ||
+                    (want == Kernel::Tile16TN && K > 0 && tile_supports(p, true, true)) ||
+                    (want == Kernel::Tile16TT && K > 0 && tile_supports(p, true, false)) ||
                     (want == Kernel::Skinny && K > 0 && skinny_supports(p)) ||
                     (want == Kernel::SplitK && K > 0 && splitk_supports(p));
     if (!ok) return fail(TSM_ERROR_NOT_SUPPORTED, "TSM_GEMM_KERNEL=%s cannot run this problem", force);
@@ -293,6 +306,12 @@ int run(const Plan &pl, void *stream) {
       break;
     case Kernel::TileWNN:
       e = launch_tile(pl.p, 4, s);
+      break;
+    case Kernel::Tile16TN:
+      e = launch_tile(pl.p, 5, s);
+      break;
+    case Kernel::Tile16TT:
+      e = launch_tile(pl.p, 6, s);
       break;
     case Kernel::Skinny:
       e = launch_skinny(pl.p, s);

@@ -73,13 +73,14 @@ const char *masked_name(int vec, int tile);
 // Large-tile kernel: A row-major, B either layout, N a multiple of 8, K a
 // multiple of 128, 16-byte aligned rows; any M (rows past M or N, or past a
 // grouped problem's count, read as zero and are not stored).
-// Variants (K slab depth, MFMA shape, B layout): 0 = 32-deep, 32x32x16,
-// column-major B; 1 = 32-deep, 16x16x32, column-major; 2 = 32-deep, 16x16x32,
-// row-major B (transposed out of LDS); 3, 4 = as 1, 2 with 64-deep slabs.
+// Variants (K slab depth, MFMA shape, A and B layouts): 0 = 32-deep, 32x32x16,
+// column-major B; 1 = 32-deep, 16x16x32, column-major B; 2 = 32-deep,
+// 16x16x32, row-major B (transposed out of LDS); 3, 4 = as 1, 2 with 64-deep
+// slabs; 5, 6 = as 2, 1 with column-major A (also transposed out of LDS).
 struct TileInfo {
   static constexpr int BM = 256, BN = 256, BK = 32, STAGES = 4;
 };
-bool tile_supports(const Problem &p, bool b_row);
+bool tile_supports(const Problem &p, bool a_col, bool b_row);
 
 // Skinny kernel: M <= 128 (in 1, 2, 4 or 8 blocks of 16 rows), row-major A
 // and B, N a multiple of the workgroup width (256 columns when that grid fills

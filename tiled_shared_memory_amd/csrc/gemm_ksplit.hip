@@ -94,7 +94,7 @@ Problem tsplit_pass1_problem(const Problem &p, const KSplit &ks, float *ws) {
   q.rows = nullptr;
   q.K = ks.kchunk;
   q.batch = ks.splits;
-  q.sA = ks.kchunk;                             // A row-major: the next chunk starts kchunk columns on
+  q.sA = p.a_col ? ks.kchunk * p.lda : ks.kchunk;  // A: the next chunk starts kchunk columns (rows) on
   q.sB = p.b_col ? ks.kchunk : ks.kchunk * p.ldb;  // B: kchunk columns (K-contiguous) or rows on
   return q;
 }
@@ -102,11 +102,12 @@ Problem tsplit_pass1_problem(const Problem &p, const KSplit &ks, float *ws) {
 
 KSplit tsplit_plan(const Problem &p) {
   KSplit ks = tsplit_shape(p.M, p.N, p.K, p.batch);
-  if (!ks.splits || p.a_col || p.rows) return KSplit{};
+  if (!ks.splits || p.rows) return KSplit{};
   if ((uintptr_t)p.C & 15) return KSplit{};
   const Problem q = tsplit_pass1_problem(p, ks, (float *)p.C);  // alignment of the workspace is checked apart
-  if (!tile_supports(q, !p.b_col)) return KSplit{};
-  ks.tile_variant = p.b_col ? 3 : 2;  // the default large-tile kernel for B's layout
+  if (!tile_supports(q, p.a_col, !p.b_col)) return KSplit{};
+  // the default large-tile kernel for the operands' layouts
+  ks.tile_variant = p.a_col ? (p.b_col ? 6 : 5) : (p.b_col ? 3 : 2);
   return ks;
 }
 

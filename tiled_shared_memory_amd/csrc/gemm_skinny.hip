@@ -475,6 +475,8 @@ hipError_t launch_ksplit_pass1(const Problem &p, const KSplit &ks, float *ws, hi
 const char *ksplit_name(const KSplit &ks) {
   if (ks.splits && ks.tile_variant == 3) return "ksplit_tile_256x256x64_mi16+reduce";
   if (ks.splits && ks.tile_variant == 2) return "ksplit_tile_256x256x32_mi16_nn+reduce";
+  if (ks.splits && ks.tile_variant == 5) return "ksplit_tile_256x256x32_mi16_tn+reduce";
+  if (ks.splits && ks.tile_variant == 6) return "ksplit_tile_256x256x32_mi16_tt+reduce";
   static const char *const names[2][3] = {
       {"ksplit_skinny_m16_n64_k64+reduce", "ksplit_skinny_m32_n64_k64+reduce", "ksplit_skinny_m64_n64_k64+reduce"},
       {"ksplit_skinny_m16_n256_k64+reduce", "ksplit_skinny_m32_n256_k64+reduce",

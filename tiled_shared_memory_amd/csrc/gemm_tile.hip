@@ -193,12 +193,36 @@ struct Frags {
   u32x4 a[NSTEP][NA], b[NSTEP][NA];
 };
 
+// A 16x16x32 operand from a slice stored k-row by k-row (512-byte rows of
+// 256 columns, swizzled by swz_row): lane needs X[8*(lane/16) .. +7][column
+// col0 + lane % 16]; two ds_read_b64_tr_b16, each 4 rows deep (in each 16-lane
+// group, lane j points at row 4h + j/4 of the group's 8 rows, columns
+// 4*(j%4) .. +3).  Sub-slice U of the slab is a constant offset of 32 rows.
+template <int U>
+__device__ __forceinline__ u32x4 read_tr_operand(const char *s, int col0, int lane) {
+  u32x4 f;
+  const int col = col0 + 4 * (lane & 3);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = 8 * (lane >> 4) + 4 * h + ((lane & 15) >> 2);
+    const int off = (32 * U + r) * 512 + swz_row(r, col >> 3) * 16 + (col & 7) * 2;
+    const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)((lds_char *)s + off));
+    const u32x2 d = __builtin_bit_cast(u32x2, v);
+    f[2 * h] = d[0];
+    f[2 * h + 1] = d[1];
+  }
+  return f;
+}
+
 // Fragments of sub-slice U (k = 32U .. 32U + 31) of a slab of depth 32 KB.
-template <int MI, bool BROW, int KB, int U>
+// ACOL: A is column-major (its slices are k rows of 256 m); BROW: B is
+// row-major (k rows of 256 n).  Both are transposed on the way out of LDS.
+template <int MI, bool ACOL, bool BROW, int KB, int U>
 __device__ __forceinline__ void read_frags(const char *sa, const char *sb, Frags<MI> &f, int wm, int wn, int lane) {
   constexpr int NA = Frags<MI>::NA;
   constexpr int RB = 64 * KB;  // bytes per K-contiguous row
   static_assert(!BROW || MI == 16, "row-major B is read with 16x16x32 operands");
+  static_assert(!ACOL || (MI == 16 && KB == 1), "column-major A is read with 16x16x32 operands, 32-deep slices");
   static_assert(KB == 1 || MI == 16, "64-deep slabs are read with 16x16x32 operands");
   // lane reads row (lane % MI) of each block, K chunk (lane / MI) of the step;
   // block rows are multiples of 16, so the swizzle sees row % 16 == lane % 16
@@ -206,31 +230,22 @@ __device__ __forceinline__ void read_frags(const char *sa, const char *sb, Frags
 #pragma unroll
   for (int s = 0; s < Frags<MI>::NSTEP; ++s) {
     const int chunk = swz<KB>(lane, 4 * U + s * (4 / Frags<MI>::NSTEP) + lane / MI) * 16;
+    if constexpr (!ACOL) {
 #pragma unroll
-    for (int i = 0; i < NA; ++i)
-      f.a[s][i] = *reinterpret_cast<const u32x4 *>(sa + (wm * 128 + i * MI + row) * RB + chunk);
+      for (int i = 0; i < NA; ++i)
+        f.a[s][i] = *reinterpret_cast<const u32x4 *>(sa + (wm * 128 + i * MI + row) * RB + chunk);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NA; ++i) f.a[s][i] = read_tr_operand<U>(sa, wm * 128 + i * 16, lane);
+    }
     if constexpr (!BROW) {
 #pragma unroll
       for (int j = 0; j < NA; ++j)
         f.b[s][j] = *reinterpret_cast<const u32x4 *>(sb + (wn * 128 + j * MI + row) * RB + chunk);
     } else {
-      // B operand of 16x16x32 from row-major B: lane needs B[8*(lane/16) .. +7][column lane % 16]
-      // of its block; two ds_read_b64_tr_b16, each 4 rows deep (in each 16-lane group,
-      // lane j points at row 4h + j/4 of the group's 8 rows, columns 4*(j%4) .. +3)
+      // B operand of 16x16x32 from row-major B: column lane % 16 of its block
 #pragma unroll
-      for (int j = 0; j < NA; ++j) {
-        const int col = wn * 128 + j * 16 + 4 * (lane & 3);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          // the swizzle sees the row within the 32-row sub-slice, so sub-slice U is a constant offset
-          const int r = 8 * (lane >> 4) + 4 * h + ((lane & 15) >> 2);
-          const int off = (32 * U + r) * 512 + swz_row(r, col >> 3) * 16 + (col & 7) * 2;
-          const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)((lds_char *)sb + off));
-          const u32x2 d = __builtin_bit_cast(u32x2, v);
-          f.b[s][j][2 * h] = d[0];
-          f.b[s][j][2 * h + 1] = d[1];
-        }
-      }
+      for (int j = 0; j < NA; ++j) f.b[s][j] = read_tr_operand<U>(sb, wn * 128 + j * 16, lane);
     }
   }
 }
@@ -273,6 +288,7 @@ template <int L>
 struct CtxT {
   __amdgpu_buffer_rsrc_t ra, rb;
   uint32_t offA[L], offB[L];
+  uint32_t kstepA;  // bytes between consecutive slabs of A (row bytes if K-contiguous, 32 KB rows if column-major)
   uint32_t kstepB;  // bytes between consecutive slabs of B (row bytes if K-contiguous, 32 KB rows if row-major)
   int nk, wave, wm, wn, lane;
 };
@@ -282,7 +298,7 @@ using CtxW = CtxT<2 * LOADS>;
 // Slice j, resident in stage S: after its barrier, read all of its fragments
 // into one register set while the MFMAs of slice j-1 run from the other set,
 // and refill the stage that slice j-1 freed with slice j+3.
-template <bool BF16, int MI, bool BROW, int S>
+template <bool BF16, int MI, bool ACOL, bool BROW, int S>
 __device__ __forceinline__ void slice(Ctx &c, int j, Frags<MI> (&fr)[2], Acc<MI> &acc) {
   // Keep every MFMA of the previous slice above this point: sinking them past
   // the fragment reads below would need a third fragment register set.
@@ -293,10 +309,10 @@ __device__ __forceinline__ void slice(Ctx &c, int j, Frags<MI> (&fr)[2], Acc<MI>
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * 2 * LOADS) : "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  read_frags<MI, BROW, 1, 0>(Ring<S>::a(), Ring<S>::b(), fr[S & 1], c.wm, c.wn, c.lane);
+  read_frags<MI, ACOL, BROW, 1, 0>(Ring<S>::a(), Ring<S>::b(), fr[S & 1], c.wm, c.wn, c.lane);
   // the last slice again near the end keeps the load count per slice uniform
   const int next = min(j + NS - 1, c.nk - 1);
-  issue<LOADS>(c.ra, c.offA, (uint32_t)next * ROW_BYTES, Ring<(S + NS - 1) % NS>::a(), c.wave);
+  issue<LOADS>(c.ra, c.offA, (uint32_t)next * c.kstepA, Ring<(S + NS - 1) % NS>::a(), c.wave);
   issue<LOADS>(c.rb, c.offB, (uint32_t)next * c.kstepB, Ring<(S + NS - 1) % NS>::b(), c.wave);
   mma<BF16, MI>(fr[(S & 1) ^ 1], acc);  // slice j-1
   // schedule: one fragment read or load after every other MFMA, spread over
@@ -304,7 +320,8 @@ __device__ __forceinline__ void slice(Ctx &c, int j, Frags<MI> (&fr)[2], Acc<MI>
   // and with it the MFMA pipe)
   constexpr int NMFMA = MI == 32 ? 32 : 64;
   constexpr int G = NMFMA / 8;          // MFMAs per group of reads + 1 load
-  constexpr int R = BROW ? 3 : 2;       // reads per group: 8 A reads + (16 or 8) B reads over 8 groups
+  // reads per group: (16 or 8) A reads + (16 or 8) B reads over 8 groups
+  constexpr int R = ((ACOL ? 16 : 8) + (BROW ? 16 : 8)) / 8;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, G / 4, 0);
@@ -352,11 +369,11 @@ __device__ __forceinline__ void substep_w(CtxW &c, int j, Frags<16> (&fr)[2], Ac
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   }
-  read_frags<16, BROW, 2, U>(WRing<S>::a(), WRing<S>::b(), fr[U], c.wm, c.wn, c.lane);
+  read_frags<16, false, BROW, 2, U>(WRing<S>::a(), WRing<S>::b(), fr[U], c.wm, c.wn, c.lane);
   if constexpr (U == 0) {
     // the last slab again at the end keeps the load count per slab uniform
     const int next = min(j + 1, c.nk - 1);
-    issue<2 * LOADS>(c.ra, c.offA, (uint32_t)next * WROW_BYTES, WRing<S ^ 1>::a(), c.wave);
+    issue<2 * LOADS>(c.ra, c.offA, (uint32_t)next * c.kstepA, WRing<S ^ 1>::a(), c.wave);
     issue<2 * LOADS>(c.rb, c.offB, (uint32_t)next * c.kstepB, WRing<S ^ 1>::b(), c.wave);
   }
   mma<BF16, 16>(fr[U ^ 1], acc);  // the previous sub-slice
@@ -374,9 +391,10 @@ __device__ __forceinline__ void substep_w(CtxW &c, int j, Frags<16> (&fr)[2], Ac
   }
 }
 
-template <bool BF16, bool OUT16, int MI, bool BROW, int KB>
+template <bool BF16, bool OUT16, int MI, bool ACOL, bool BROW, int KB>
 __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
   static_assert(KB == 1 || MI == 16, "64-deep slabs use 16x16x32 operands");
+  static_assert(!ACOL || KB == 1, "column-major A uses the 32-deep ring");
   CtxT<LOADS * KB> c;
   const int tid = threadIdx.x;
   c.lane = tid & 63;
@@ -416,7 +434,8 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
   if (m0 >= M) return;              // the whole tile lies past them (uniform)
   const int64_t vrows = M - m0 < BM ? M - m0 : BM;
   const int vcols = (int)(p.N - n0 < BN ? p.N - n0 : BN);  // valid columns of this tile (N is a multiple of 8)
-  const uint16_t *A = p.A + z * p.sA + m0 * p.lda;  // row m0, k = 0 (row-major A)
+  // row m0, k = 0: row-major A starts its panel at row m0, column-major A at column m0
+  const uint16_t *A = p.A + z * p.sA + (ACOL ? m0 : m0 * p.lda);
   // column n0, k = 0: column-major B starts its panel at row n0, row-major B at column n0
   const uint16_t *B = p.B + z * p.sB + (BROW ? n0 : n0 * p.ldb);
 
@@ -436,9 +455,15 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
   // Buffer resources cover exactly the operand panels: the tile's valid rows
   // of A (rows past M load as zero) and 256 rows, or K rows x 256 columns, of
   // B.  The host keeps each extent below 1 GiB, so all offsets are 32-bit.
-  c.ra = make_rsrc(A, (uint32_t)(((vrows - 1) * p.lda + p.K) * 2));
+  c.ra = make_rsrc(A, (uint32_t)((ACOL ? (p.K - 1) * p.lda + vrows : (vrows - 1) * p.lda + p.K) * 2));
   c.rb = make_rsrc(B, (uint32_t)((BROW ? (p.K - 1) * p.ldb + vcols : (vcols - 1) * p.ldb + p.K) * 2));
-  slice_offsets<LOADS * KB, KB>(c.offA, p.lda, c.wave, lane);
+  if constexpr (ACOL) {
+    slice_offsets_row<LOADS * KB>(c.offA, p.lda, c.wave, lane, (int)vrows);
+    c.kstepA = (uint32_t)(32 * KB * p.lda * 2);
+  } else {
+    slice_offsets<LOADS * KB, KB>(c.offA, p.lda, c.wave, lane);
+    c.kstepA = 64 * KB;
+  }
   if constexpr (BROW) {
     slice_offsets_row<LOADS * KB>(c.offB, p.ldb, c.wave, lane, vcols);
     c.kstepB = (uint32_t)(32 * KB * p.ldb * 2);
@@ -466,11 +491,11 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the duplicate tail loads
   } else {
   // prologue: slices 0 .. NS-2 in flight
-  issue<LOADS>(c.ra, c.offA, 0 * ROW_BYTES, Ring<0>::a(), c.wave);
+  issue<LOADS>(c.ra, c.offA, 0 * c.kstepA, Ring<0>::a(), c.wave);
   issue<LOADS>(c.rb, c.offB, 0 * c.kstepB, Ring<0>::b(), c.wave);
-  issue<LOADS>(c.ra, c.offA, 1 * ROW_BYTES, Ring<1>::a(), c.wave);
+  issue<LOADS>(c.ra, c.offA, 1 * c.kstepA, Ring<1>::a(), c.wave);
   issue<LOADS>(c.rb, c.offB, 1 * c.kstepB, Ring<1>::b(), c.wave);
-  issue<LOADS>(c.ra, c.offA, 2 * ROW_BYTES, Ring<2>::a(), c.wave);
+  issue<LOADS>(c.ra, c.offA, 2 * c.kstepA, Ring<2>::a(), c.wave);
   issue<LOADS>(c.rb, c.offB, 2 * c.kstepB, Ring<2>::b(), c.wave);
 
   // Before slice 0 there is no previous slice: zero fragments add exactly 0.
@@ -483,10 +508,10 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
   // The steady-state loop has no data-dependent branches, which keeps the
   // 256 accumulators of each lane in place across iterations.
   for (int j = 0; j < c.nk; j += NS) {
-    slice<BF16, MI, BROW, 0>(c, j + 0, fr, acc);
-    slice<BF16, MI, BROW, 1>(c, j + 1, fr, acc);
-    slice<BF16, MI, BROW, 2>(c, j + 2, fr, acc);
-    slice<BF16, MI, BROW, 3>(c, j + 3, fr, acc);
+    slice<BF16, MI, ACOL, BROW, 0>(c, j + 0, fr, acc);
+    slice<BF16, MI, ACOL, BROW, 1>(c, j + 1, fr, acc);
+    slice<BF16, MI, ACOL, BROW, 2>(c, j + 2, fr, acc);
+    slice<BF16, MI, ACOL, BROW, 3>(c, j + 3, fr, acc);
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   mma<BF16, MI>(fr[1], acc);  // the last slice (nk is a multiple of 4, so it sits in set 1)
@@ -526,7 +551,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
   }
 }
 
-template <bool BF16, bool OUT16, int MI, bool BROW, int KB>
+template <bool BF16, bool OUT16, int MI, bool ACOL, bool BROW, int KB>
 hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
   const int64_t tiles = (int64_t)base.tiles_m * base.tiles_n;
   if (base.rows && batch <= kMaxCompactGroups && tiles * batch <= 0x7fffffffLL) {
@@ -535,7 +560,7 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
     KernelArgs a = base;
     a.z0 = 0;
     a.compact_groups = (int32_t)batch;
-    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT16, MI, BROW, KB>), dim3((unsigned)(tiles * batch)), dim3(256), 0,
+    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT16, MI, ACOL, BROW, KB>), dim3((unsigned)(tiles * batch)), dim3(256), 0,
                        stream, a);
     return hipGetLastError();
   }
@@ -543,7 +568,7 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
     KernelArgs a = base;
     a.z0 = (int32_t)z0;
     const int64_t nz = batch - z0 < kMaxGridY ? batch - z0 : kMaxGridY;
-    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT16, MI, BROW, KB>), dim3((unsigned)tiles, (unsigned)nz), dim3(256), 0,
+    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT16, MI, ACOL, BROW, KB>), dim3((unsigned)tiles, (unsigned)nz), dim3(256), 0,
                        stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -551,26 +576,27 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
   return hipSuccess;
 }
 
-template <int MI, bool BROW, int KB>
+template <int MI, bool ACOL, bool BROW, int KB>
 hipError_t launch_mi(const Problem &p, const KernelArgs &a, hipStream_t stream) {
   if (p.in_bf16)
-    return p.out16 ? launch_t<true, true, MI, BROW, KB>(a, p.batch, stream)
-                     : launch_t<true, false, MI, BROW, KB>(a, p.batch, stream);
-  return p.out16 ? launch_t<false, true, MI, BROW, KB>(a, p.batch, stream)
-                   : launch_t<false, false, MI, BROW, KB>(a, p.batch, stream);
+    return p.out16 ? launch_t<true, true, MI, ACOL, BROW, KB>(a, p.batch, stream)
+                     : launch_t<true, false, MI, ACOL, BROW, KB>(a, p.batch, stream);
+  return p.out16 ? launch_t<false, true, MI, ACOL, BROW, KB>(a, p.batch, stream)
+                   : launch_t<false, false, MI, ACOL, BROW, KB>(a, p.batch, stream);
 }
 
 }  // namespace
 
-bool tile_supports(const Problem &p, bool b_row) {
-  if (p.a_col) return false;              // A must be K-contiguous
-  if (p.b_col == b_row) return false;     // the requested B layout
+bool tile_supports(const Problem &p, bool a_col, bool b_row) {
+  if (p.a_col != a_col || p.b_col == b_row) return false;  // the requested layouts
   // any M and any N that is a multiple of 8: rows and columns past them load
-  // as zero and are not stored
+  // as zero and are not stored; a column-major A needs M % 8 too (its chunks
+  // of 8 rows lie wholly inside or outside) and no grouped row counts
   if (p.N % 8 || p.K % (NS * BK) || p.K == 0) return false;
-  // 32-bit buffer offsets: an A panel (up to 256 rows) and a B panel (256 rows
-  // or K rows x 256 columns) must span less than 1 GiB
-  if (255 * p.lda + p.K >= (int64_t)1 << 29) return false;
+  if (a_col && (p.M % 8 || p.rows)) return false;
+  // 32-bit buffer offsets: an A panel (256 rows, or K rows x 256 columns) and
+  // a B panel (256 rows, or K rows x 256 columns) must span less than 1 GiB
+  if ((a_col ? (p.K - 1) * p.lda + 256 : 255 * p.lda + p.K) >= (int64_t)1 << 29) return false;
   if ((b_row ? (p.K - 1) * p.ldb + 256 : 255 * p.ldb + p.K) >= (int64_t)1 << 29) return false;
   if (((uintptr_t)p.A & 15) || ((uintptr_t)p.B & 15) || ((uintptr_t)p.C & 15)) return false;
   if (p.lda % 8 || p.ldb % 8) return false;
@@ -601,21 +627,28 @@ hipError_t launch_tile(const Problem &p, int variant, hipStream_t stream) {
   a.tiles_n = (int32_t)((p.N + BN - 1) / BN);
   switch (variant) {
     case 0:
-      return launch_mi<32, false, 1>(p, a, stream);
+      return launch_mi<32, false, false, 1>(p, a, stream);
     case 1:
-      return launch_mi<16, false, 1>(p, a, stream);
+      return launch_mi<16, false, false, 1>(p, a, stream);
     case 2:
-      return launch_mi<16, true, 1>(p, a, stream);
+      return launch_mi<16, false, true, 1>(p, a, stream);
     case 3:
-      return launch_mi<16, false, 2>(p, a, stream);
+      return launch_mi<16, false, false, 2>(p, a, stream);
+    case 4:
+      return launch_mi<16, false, true, 2>(p, a, stream);
+    case 5:
+      return launch_mi<16, true, true, 1>(p, a, stream);
     default:
-      return launch_mi<16, true, 2>(p, a, stream);
+      return launch_mi<16, true, false, 1>(p, a, stream);
   }
 }
 
 const char *tile_name(int variant) {
-  static const char *const names[] = {"tile_256x256x32_mi32", "tile_256x256x32_mi16", "tile_256x256x32_mi16_nn",
-                                      "tile_256x256x64_mi16", "tile_256x256x64_mi16_nn"};
+  // suffix: n = stored as used (A row-major, B row-major), t = transposed storage;
+  // no suffix = A row-major, B column-major
+  static const char *const names[] = {"tile_256x256x32_mi32",    "tile_256x256x32_mi16",   "tile_256x256x32_mi16_nn",
+                                      "tile_256x256x64_mi16",    "tile_256x256x64_mi16_nn", "tile_256x256x32_mi16_tn",
+                                      "tile_256x256x32_mi16_tt"};
   return names[variant];
 }
 
