@@ -29,6 +29,7 @@ FAMILIES = [
     ("tile_256x256x64_mi16_nn", (256, 256, 256, 2), "row", "row"),
     ("tile_256x256x32_mi16_tn", (264, 256, 256, 2), "col", "row"),
     ("tile_256x256x32_mi16_tt", (256, 264, 128, 1), "col", "col"),
+    ("tile_256x256x64_mi16_tt", (520, 256, 256, 2), "col", "col"),
     ("skinny_m16_n256_k64", (13, 512, 512, 2), "row", "row"),
     ("skinny_m64_n64_k64", (40, 320, 192, 2), "row", "row"),
     ("skinny_m128_n64_k64", (100, 128, 128, 1), "row", "row"),

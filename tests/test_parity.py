@@ -405,7 +405,8 @@ def test_subnormal_f16_operands(orc):
     check(C, Cr, S, K, "f32", "subnormal")
 
 
-COL_A_VARIANTS = [("tile_256x256x32_mi16_tn", "row"), ("tile_256x256x32_mi16_tt", "col")]
+COL_A_VARIANTS = [("tile_256x256x32_mi16_tn", "row"), ("tile_256x256x32_mi16_tt", "col"),
+                  ("tile_256x256x64_mi16_tt", "col")]
 COL_A_SHAPES = [(256, 256, 128, 1), (512, 768, 384, 1), (264, 520, 256, 2), (1000, 256, 512, 1)]
 
 

@@ -44,7 +44,8 @@ bool ranges_overlap(const void *p, int64_t pbytes, const void *q, int64_t qbytes
 }
 
 enum class Kernel {
-  None, Masked8, Masked1, Small8, Small1, Tile32, Tile16, Tile16NN, TileW, TileWNN, Tile16TN, Tile16TT, Skinny, SplitK
+  None, Masked8, Masked1, Small8, Small1, Tile32, Tile16, Tile16NN, TileW, TileWNN, Tile16TN, Tile16TT, TileWTT, Skinny,
+  SplitK
 };
 
 const char *kernel_name(Kernel k, const Problem &p) {
@@ -71,6 +72,8 @@ const char *kernel_name(Kernel k, const Problem &p) {
       return tile_name(5);
     case Kernel::Tile16TT:
       return tile_name(6);
+    case Kernel::TileWTT:
+      return tile_name(7);
     case Kernel::Skinny:
       return skinny_name(p);
     case Kernel::SplitK:
@@ -244,7 +247,7 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
   if (force && *force) {
     const Kernel all[] = {Kernel::Masked8,  Kernel::Masked1,  Kernel::Small8,   Kernel::Small1,  Kernel::Tile32,
                           Kernel::Tile16,   Kernel::Tile16NN, Kernel::TileW,    Kernel::TileWNN, Kernel::Tile16TN,
-                          Kernel::Tile16TT, Kernel::Skinny,   Kernel::SplitK};
+                          Kernel::Tile16TT, Kernel::TileWTT,  Kernel::Skinny,   Kernel::SplitK};
     Kernel want = Kernel::None;
     for (Kernel k : all)
       if (k != Kernel::Skinny && strcmp(force, kernel_name(k, p)) == 0) want = k;
@@ -264,7 +267,7 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
                      tile_supports(p, false, false)) ||
                     ((want == Kernel::Tile16NN || want == Kernel::TileWNN) && K > 0 && tile_supports(p, false, true)) ||
                     (want == Kernel::Tile16TN && K > 0 && tile_supports(p, true, true)) ||
-                    (want == Kernel::Tile16TT && K > 0 && tile_supports(p, true, false)) ||
+                    ((want == Kernel::Tile16TT || want == Kernel::TileWTT) && K > 0 && tile_supports(p, true, false)) ||
                     (want == Kernel::Skinny && K > 0 && skinny_supports(p)) ||
                     (want == Kernel::SplitK && K > 0 && splitk_supports(p));
     if (!ok) return fail(TSM_ERROR_NOT_SUPPORTED, "TSM_GEMM_KERNEL=%s cannot run this problem", force);
@@ -312,6 +315,9 @@ int run(const Plan &pl, void *stream) {
       break;
     case Kernel::Tile16TT:
       e = launch_tile(pl.p, 6, s);
+      break;
+    case Kernel::TileWTT:
+      e = launch_tile(pl.p, 7, s);
       break;
     case Kernel::Skinny:
       e = launch_skinny(pl.p, s);

@@ -222,7 +222,7 @@ __device__ __forceinline__ void read_frags(const char *sa, const char *sb, Frags
   constexpr int NA = Frags<MI>::NA;
   constexpr int RB = 64 * KB;  // bytes per K-contiguous row
   static_assert(!BROW || MI == 16, "row-major B is read with 16x16x32 operands");
-  static_assert(!ACOL || (MI == 16 && KB == 1), "column-major A is read with 16x16x32 operands, 32-deep slices");
+  static_assert(!ACOL || MI == 16, "column-major A is read with 16x16x32 operands");
   static_assert(KB == 1 || MI == 16, "64-deep slabs are read with 16x16x32 operands");
   // lane reads row (lane % MI) of each block, K chunk (lane / MI) of the step;
   // block rows are multiples of 16, so the swizzle sees row % 16 == lane % 16
@@ -361,7 +361,7 @@ __device__ __forceinline__ void tile_order(int pid, int tiles_m, int tiles_n, in
 // other stage (freed by that barrier) with slab j+1 while the previous
 // sub-slice's MFMAs run; U = 1 only reads and multiplies.  A slab is thus
 // requested one slab (two sub-slices) before it is used.
-template <bool BF16, bool BROW, int S, int U>
+template <bool BF16, bool ACOL, bool BROW, int S, int U>
 __device__ __forceinline__ void substep_w(CtxW &c, int j, Frags<16> (&fr)[2], Acc<16> &acc) {
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (U == 0) {
@@ -369,7 +369,7 @@ __device__ __forceinline__ void substep_w(CtxW &c, int j, Frags<16> (&fr)[2], Ac
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   }
-  read_frags<16, false, BROW, 2, U>(WRing<S>::a(), WRing<S>::b(), fr[U], c.wm, c.wn, c.lane);
+  read_frags<16, ACOL, BROW, 2, U>(WRing<S>::a(), WRing<S>::b(), fr[U], c.wm, c.wn, c.lane);
   if constexpr (U == 0) {
     // the last slab again at the end keeps the load count per slab uniform
     const int next = min(j + 1, c.nk - 1);
@@ -377,7 +377,7 @@ __device__ __forceinline__ void substep_w(CtxW &c, int j, Frags<16> (&fr)[2], Ac
     issue<2 * LOADS>(c.rb, c.offB, (uint32_t)next * c.kstepB, WRing<S ^ 1>::b(), c.wave);
   }
   mma<BF16, 16>(fr[U ^ 1], acc);  // the previous sub-slice
-  constexpr int R = BROW ? 3 : 2;  // fragment reads per group of 8 MFMAs
+  constexpr int R = ((ACOL ? 16 : 8) + (BROW ? 16 : 8)) / 8;  // fragment reads per group of 8 MFMAs
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);
@@ -394,7 +394,6 @@ __device__ __forceinline__ void substep_w(CtxW &c, int j, Frags<16> (&fr)[2], Ac
 template <bool BF16, bool OUT16, int MI, bool ACOL, bool BROW, int KB>
 __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
   static_assert(KB == 1 || MI == 16, "64-deep slabs use 16x16x32 operands");
-  static_assert(!ACOL || KB == 1, "column-major A uses the 32-deep ring");
   CtxT<LOADS * KB> c;
   const int tid = threadIdx.x;
   c.lane = tid & 63;
@@ -481,10 +480,10 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
 #pragma unroll
     for (int i = 0; i < Frags<16>::NA; ++i) fr[1].a[0][i] = fr[1].b[0][i] = u32x4{0, 0, 0, 0};
     for (int j = 0; j < c.nk; j += 2) {
-      substep_w<BF16, BROW, 0, 0>(c, j, fr, acc);
-      substep_w<BF16, BROW, 0, 1>(c, j, fr, acc);
-      substep_w<BF16, BROW, 1, 0>(c, j + 1, fr, acc);
-      substep_w<BF16, BROW, 1, 1>(c, j + 1, fr, acc);
+      substep_w<BF16, ACOL, BROW, 0, 0>(c, j, fr, acc);
+      substep_w<BF16, ACOL, BROW, 0, 1>(c, j, fr, acc);
+      substep_w<BF16, ACOL, BROW, 1, 0>(c, j + 1, fr, acc);
+      substep_w<BF16, ACOL, BROW, 1, 1>(c, j + 1, fr, acc);
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     mma<BF16, 16>(fr[1], acc);  // the last sub-slice
@@ -638,8 +637,10 @@ hipError_t launch_tile(const Problem &p, int variant, hipStream_t stream) {
       return launch_mi<16, false, true, 2>(p, a, stream);
     case 5:
       return launch_mi<16, true, true, 1>(p, a, stream);
-    default:
+    case 6:
       return launch_mi<16, true, false, 1>(p, a, stream);
+    default:
+      return launch_mi<16, true, false, 2>(p, a, stream);
   }
 }
 
@@ -648,7 +649,7 @@ const char *tile_name(int variant) {
   // no suffix = A row-major, B column-major
   static const char *const names[] = {"tile_256x256x32_mi32",    "tile_256x256x32_mi16",   "tile_256x256x32_mi16_nn",
                                       "tile_256x256x64_mi16",    "tile_256x256x64_mi16_nn", "tile_256x256x32_mi16_tn",
-                                      "tile_256x256x32_mi16_tt"};
+                                      "tile_256x256x32_mi16_tt", "tile_256x256x64_mi16_tt"};
   return names[variant];
 }
 
