@@ -192,9 +192,10 @@ int gemm_strided_batched_act(int64_t M, int64_t N, int64_t K, const void *A, int
 /*
  * gemm_workspace_bytes -- bytes of workspace with which gemm_strided_batched_ws
  * splits K for a problem of this shape: batch * S * M * N * 4 for S chunks of
- * K, or 0 when the shape does not split (its output tiles already occupy the
- * chip, K is below 512 or not a multiple of 64, or N is not a multiple of 64).
- * Depends on the sizes only.  Negative sizes give 0.
+ * K (the largest S the operands' layouts may lead to), or 0 when the shape
+ * does not split (its output tiles already occupy the chip, K is below 512 or
+ * not a multiple of 64, or N is not a multiple of 64 or 8).  Depends on the
+ * sizes only.  Negative sizes give 0.
  */
 int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t batch);
 

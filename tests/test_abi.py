@@ -192,8 +192,8 @@ def test_mid_size_selection():
 
 def test_skinny_selection():
     """Up to 128 rows of row-major operands go to the streaming kernel: 256-column workgroups when those fill the
-    256 CUs, 64-column ones otherwise; row blocks follow M.  K not a multiple of 64, N not a multiple of 64 or a
-    column-major operand go elsewhere."""
+    256 CUs, 64-column ones otherwise; row blocks follow M; B either way.  K not a multiple of 64 or N not a
+    multiple of 64 go elsewhere."""
     B0 = 0x7E0000000000
     N, K = 16384, 8192
 
@@ -218,7 +218,9 @@ def test_skinny_selection():
     assert pick(48, N=128, K=4096).startswith("splitk_")
     assert not pick(16, K=8200).startswith("skinny_")
     assert not pick(16, N=16400).startswith("skinny_")
-    assert not pick(16, lb=1).startswith("skinny_")
+    # K-contiguous B (a weight stored output feature by output feature): the same kernel, B staged like A
+    assert pick(16, lb=1) == "skinny_m16_n64_k64_t"
+    assert pick(16, batch=8, lb=1) == "skinny_m16_n256_k64_t"
 
 
 def test_skinny_forced_width(monkeypatch):
@@ -265,10 +267,11 @@ def test_workspace_routing(monkeypatch):
     # 32 to 127 panels of 256 columns: split those (512-byte row segments of B)
     assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(M=16, N=16384, K=8192)) == "ksplit_skinny_m16_n256_k64+reduce"
     assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(M=64, N=8192, K=8192)) == "ksplit_skinny_m64_n256_k64+reduce"
-    # too little workspace, none, a column-major B or a forced kernel: the kernel that needs none
+    # a K-contiguous B splits the same way
+    assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(lb=1, nbytes=1 << 30)) == "ksplit_skinny_m64_n64_k64_t+reduce"
+    # too little workspace, none or a forced kernel: the kernel that needs none
     assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(nbytes=16 * 256 * 256 * 4 - 4)).startswith("splitk_")
     assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(ws=0, nbytes=0)).startswith("splitk_")
-    assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(lb=1, nbytes=1 << 30)).startswith("masked_")
     monkeypatch.setenv("TSM_GEMM_KERNEL", "masked_64x64x32_vec8")
     assert tsm.tsm_gemm_ws_kernel_name(*_ws_args()) == "masked_64x64x32_vec8"
 

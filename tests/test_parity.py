@@ -239,10 +239,10 @@ SKINNY = "skinny_"
 SKINNY_SHAPES = [(16, 256, 256, 1), (1, 512, 256, 1), (5, 256, 512, 3), (16, 768, 1024, 2), (12, 256, 256, 2)]
 
 
-def skinny_variant(M, width):
-    """Kernel name of the skinny variant for M rows at the given workgroup width."""
+def skinny_variant(M, width, b_layout="row"):
+    """Kernel name of the skinny variant for M rows at the given workgroup width (suffix _t: K-contiguous B)."""
     mb = 1 if M <= 16 else 2 if M <= 32 else 4 if M <= 64 else 8
-    return f"skinny_m{16 * mb}_n{width}_k64"
+    return f"skinny_m{16 * mb}_n{width}_k64" + ("_t" if b_layout == "col" else "")
 
 
 @pytest.mark.parametrize("shape", SKINNY_SHAPES, ids=lambda s: "x".join(map(str, s)))
@@ -266,16 +266,18 @@ SKINNY_K = [64, 192, 576, 1344]
 
 @pytest.mark.parametrize("M,width", SKINNY_VARIANT_SHAPES, ids=lambda v: str(v))
 @pytest.mark.parametrize("K", SKINNY_K)
-def test_skinny_variants(orc, monkeypatch, M, width, K):
-    """Each skinny variant (16, 32, 64 or 128 rows; 64 or 256 columns per workgroup) forced, against the oracle."""
-    variant = skinny_variant(M, width)
+@pytest.mark.parametrize("b_layout", ["row", "col"])
+def test_skinny_variants(orc, monkeypatch, M, width, K, b_layout):
+    """Each skinny variant (16, 32, 64 or 128 rows; 64 or 256 columns per workgroup; row-major or K-contiguous
+    B) forced, against the oracle."""
+    variant = skinny_variant(M, width, b_layout)
     N, batch = (512, 2) if width == 256 else (320, 3)
     monkeypatch.setenv("TSM_GEMM_KERNEL", variant)
     in_fmt, out_fmt = [(F16, "f32"), (BF16, "f16"), (BF16, "bf16"), (F16, "f16")][(M + K) % 4]
-    A, B = make_operands(M * 7 + K + width, batch, M, N, K, in_fmt, ("uniform", -1.0, 1.0))
+    A, B = make_operands(M * 7 + K + width, batch, M, N, K, in_fmt, ("uniform", -1.0, 1.0), "row", b_layout)
     say(f"[gpu] {variant} M={M} N={N} K={K} batch={batch} {in_fmt}->{out_fmt}")
-    C = run(A, B, M, N, K, in_fmt, out_fmt, batch=batch, kernel=variant)
-    Cr, S = orc.gemm_rows(A, B, M, N, K, in_fmt, batch=batch)
+    C = run(A, B, M, N, K, in_fmt, out_fmt, batch=batch, b_layout=b_layout, kernel=variant)
+    Cr, S = orc.gemm_rows(A, B, M, N, K, in_fmt, batch=batch, b_layout=b_layout)
     check(C, Cr, S, K, out_fmt, f"{variant} K={K}")
 
 
@@ -307,6 +309,21 @@ def test_skinny_kernel_padded_and_sentinel(orc, monkeypatch, M, width):
             assert np.all(host[o + N:o + ldc] == 100.0)
         if z < batch - 1:
             assert np.all(host[z * sC + M * ldc:(z + 1) * sC] == 100.0)
+
+
+def test_skinny_col_b_padded(orc, monkeypatch):
+    """K-contiguous B with padded ldb holding NaN past K: the padding is never read."""
+    variant = "skinny_m32_n64_k64_t"
+    monkeypatch.setenv("TSM_GEMM_KERNEL", variant)
+    M, N, K, batch = 24, 192, 640, 2
+    ldb = K + 40
+    A, B = make_operands(78, batch, M, N, K, F16, ("uniform", -1.0, 1.0), "row", "col")
+    Bp = np.full((batch, N, ldb), np.uint16(0x7E00), np.uint16)
+    Bp[:, :, :K] = B
+    say("[gpu] skinny col-B padded")
+    C = run(A, Bp, M, N, K, F16, "f32", batch=batch, b_layout="col", ldb=ldb, kernel=variant)
+    Cr, S = orc.gemm_rows(A, B, M, N, K, F16, batch=batch, b_layout="col")
+    check(C, Cr, S, K, "f32", "skinny col-B padded")
 
 
 def test_skinny_decode_sampled(orc):

@@ -427,10 +427,13 @@ int gemm_strided_batched_act(int64_t M, int64_t N, int64_t K, const void *A, int
 }
 
 int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t batch) {
-  const tsm::KSplit ks = tsm::ksplit_shape(M, N, K, batch), ts = tsm::tsplit_shape(M, N, K, batch);
-  const int64_t a = ks.splits ? batch * ks.splits * M * N * 4 : 0;
-  const int64_t b = ts.splits ? batch * ts.splits * M * N * 4 : 0;
-  return a > b ? a : b;
+  // the largest need over the splits a problem of this shape may take
+  int64_t most = 0;
+  const tsm::KSplit cand[3] = {tsm::ksplit_shape(M, N, K, batch, true), tsm::ksplit_shape(M, N, K, batch, false),
+                               tsm::tsplit_shape(M, N, K, batch)};
+  for (const tsm::KSplit &ks : cand)
+    if (ks.splits && batch * ks.splits * M * N * 4 > most) most = batch * ks.splits * M * N * 4;
+  return most;
 }
 
 int gemm_strided_batched_ws(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a,
@@ -457,7 +460,7 @@ const char *tsm_gemm_ws_kernel_name(int64_t M, int64_t N, int64_t K, const void 
     return nullptr;
   tsm::KSplit ks;
   if (tsm::ws_check(pl, workspace, workspace_bytes, &ks) != TSM_SUCCESS) return nullptr;
-  return ks.splits ? tsm::ksplit_name(ks) : tsm::kernel_name(pl.kernel, pl.p);
+  return ks.splits ? tsm::ksplit_name(ks, pl.p.b_col) : tsm::kernel_name(pl.kernel, pl.p);
 }
 
 int gemm_grouped(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a, int64_t strideA,

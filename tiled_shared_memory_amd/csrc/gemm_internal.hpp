@@ -82,9 +82,9 @@ struct TileInfo {
 };
 bool tile_supports(const Problem &p, bool a_col, bool b_row);
 
-// Skinny kernel: M <= 128 (in 1, 2, 4 or 8 blocks of 16 rows), row-major A
-// and B, N a multiple of the workgroup width (256 columns when that grid fills
-// the chip, else 64), K a multiple of 64, 16-byte aligned rows.
+// Skinny kernel: M <= 128 (in 1, 2, 4 or 8 blocks of 16 rows), row-major A,
+// B either way, N a multiple of the workgroup width (256 columns when that
+// grid fills the chip, else 64), K a multiple of 64, 16-byte aligned rows.
 struct SkinnyInfo {
   static constexpr int BK = 64;
 };
@@ -107,8 +107,9 @@ struct KSplit {
   int w = 64;  // columns per pass-1 workgroup (64 or 256)
   int tile_variant = -1;  // >= 0: pass 1 is that 256 x 256 kernel (a batch of the K chunks), not the skinny one
 };
-// Depends on the shape only; workspace bytes = batch * splits * M * N * 4.
-KSplit ksplit_shape(int64_t M, int64_t N, int64_t K, int64_t batch);
+// Depends on the shape (and, through `wide`, on whether B is row-major);
+// workspace bytes = batch * splits * M * N * 4.
+KSplit ksplit_shape(int64_t M, int64_t N, int64_t K, int64_t batch, bool wide);
 // The shape's split, if the operands' layouts and alignment allow it.
 KSplit ksplit_plan(const Problem &p);
 hipError_t launch_ksplit(const Problem &p, const KSplit &ks, float *ws, hipStream_t stream);
@@ -117,7 +118,7 @@ hipError_t launch_ksplit_pass1(const Problem &p, const KSplit &ks, float *ws, hi
 // pass 1 runs the K chunks as a strided batch of products into the workspace.
 KSplit tsplit_shape(int64_t M, int64_t N, int64_t K, int64_t batch);
 KSplit tsplit_plan(const Problem &p);
-const char *ksplit_name(const KSplit &ks);
+const char *ksplit_name(const KSplit &ks, bool b_col);
 
 // Split-K kernel for small M x N and deep K: 16 x 16 tiles, K split across the
 // 16 waves of a workgroup; row-major A and B, M, N multiples of 16, K a

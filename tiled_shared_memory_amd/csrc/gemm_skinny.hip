@@ -108,13 +108,13 @@ __device__ __forceinline__ int swz_b(int r, int c) {
 // swizzle measured conflict-free for 16x16x32 operand reads of 128-byte rows.
 __device__ __forceinline__ int swz_a(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-template <int MB, int W>
+template <int MB, int W, bool BCOL>
 struct Ctx {
   using SH = Shape<MB, W>;
   __amdgpu_buffer_rsrc_t rb, ra;
   uint32_t offB[SH::LOADS];    // per-lane byte offsets of this wave's B chunks within a slice
   uint32_t offA[SH::A_LOADS];  // per-lane byte offsets of this wave's A chunks (k = 0); outside past M
-  uint32_t ldb_bytes;          // bytes between consecutive k rows of B
+  uint32_t kstep_b;            // bytes between consecutive slices of B (64 rows, or 128 bytes if K-contiguous)
   int nk, wave, lane;
 };
 
@@ -143,12 +143,12 @@ __device__ __forceinline__ u32x2 read_tr(const char *p) {
 // panel, then the matching A slice behind it.  Slices at or past the end of K
 // (the loop runs whole rounds of the ring) get per-lane offsets outside both
 // buffer resources, so they load as zero and add nothing.
-template <int MB, int W>
-__device__ __forceinline__ void issue(const Ctx<MB, W> &c, int k, char *s) {
+template <int MB, int W, bool BCOL>
+__device__ __forceinline__ void issue(const Ctx<MB, W, BCOL> &c, int k, char *s) {
   using SH = Shape<MB, W>;
   const bool in = k < c.nk;
-  const uint32_t past = in ? 0u : kOutside;                     // per-lane offsets stay below 1 GiB
-  const uint32_t krow = in ? (uint32_t)k * BK * c.ldb_bytes : 0u;  // byte offset of the slice's first row
+  const uint32_t past = in ? 0u : kOutside;              // per-lane offsets stay below 1 GiB
+  const uint32_t krow = in ? (uint32_t)k * c.kstep_b : 0u;  // byte offset of the slice's first k
 #pragma unroll
   for (int g = 0; g < SH::LOADS; ++g) dma16_nt(c.rb, s + (c.wave * SH::LOADS + g) * 1024, c.offB[g] | past, krow);
   const uint32_t kbytes = in ? (uint32_t)k * A_ROW_BYTES : 0u;
@@ -163,15 +163,15 @@ __device__ __forceinline__ void issue(const Ctx<MB, W> &c, int k, char *s) {
 // 16-column block two transpose reads and MB MFMAs.  The MFMA takes B as its
 // first operand, so each lane's 4 accumulators are 4 consecutive columns of
 // one row of C.
-template <bool BF16, int MB, int W, int S>
-__device__ __forceinline__ void slice(Ctx<MB, W> &c, int j, f32x4 (&acc)[MB][Shape<MB, W>::CB]) {
+template <bool BF16, int MB, int W, bool BCOL, int S>
+__device__ __forceinline__ void slice(Ctx<MB, W, BCOL> &c, int j, f32x4 (&acc)[MB][Shape<MB, W>::CB]) {
   using SH = Shape<MB, W>;
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(SH::IN_FLIGHT) : "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   // refill the stage freed by slice j-1 with slice j+NS-1
   constexpr int NS = SH::NS;
-  issue<MB, W>(c, j + NS - 1, ring_stage<SH::STAGE_BYTES, (S + NS - 1) % NS>());
+  issue<MB, W, BCOL>(c, j + NS - 1, ring_stage<SH::STAGE_BYTES, (S + NS - 1) % NS>());
 
   const char *s = ring_stage<SH::STAGE_BYTES, S>();
   const char *sa = s + SH::SLICE_BYTES;
@@ -189,15 +189,22 @@ __device__ __forceinline__ void slice(Ctx<MB, W> &c, int j, f32x4 (&acc)[MB][Sha
     }
 #pragma unroll
     for (int cb = 0; cb < SH::CB; ++cb) {
-      const int col = c.wave * SH::CPW + cb * 16 + 4 * (g16 & 3);  // first of the 4 columns this lane points at
       u32x4 bf;
+      if constexpr (BCOL) {
+        // K-contiguous B: column n = wave*CPW + 16 cb + lane % 16 is LDS row n,
+        // laid out like an A row: one 16-byte read
+        const int r = c.wave * SH::CPW + cb * 16 + g16;
+        bf = *reinterpret_cast<const u32x4 *>(s + r * A_ROW_BYTES + swz_a(r, t * 4 + kq) * 16);
+      } else {
+        const int col = c.wave * SH::CPW + cb * 16 + 4 * (g16 & 3);  // first of the 4 columns this lane points at
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int r = t * 32 + kq * 8 + h * 4 + rin;  // k row inside the slice
-        const int off = r * SH::ROW_BYTES + swz_b<W>(r, col >> 3) * 16 + (col & 7) * 2;
-        const u32x2 w = read_tr(s + off);
-        bf[2 * h] = w[0];
-        bf[2 * h + 1] = w[1];
+        for (int h = 0; h < 2; ++h) {
+          const int r = t * 32 + kq * 8 + h * 4 + rin;  // k row inside the slice
+          const int off = r * SH::ROW_BYTES + swz_b<W>(r, col >> 3) * 16 + (col & 7) * 2;
+          const u32x2 w = read_tr(s + off);
+          bf[2 * h] = w[0];
+          bf[2 * h + 1] = w[1];
+        }
       }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) acc[mb][cb] = mfma_16x16x32<BF16>(bf, af[mb], acc[mb][cb]);
@@ -206,27 +213,30 @@ __device__ __forceinline__ void slice(Ctx<MB, W> &c, int j, f32x4 (&acc)[MB][Sha
 }
 
 // Fill stages 0 .. NS-2 with slices 0 .. NS-2.
-template <int MB, int W, int S>
-__device__ __forceinline__ void prologue(const Ctx<MB, W> &c) {
+template <int MB, int W, bool BCOL, int S>
+__device__ __forceinline__ void prologue(const Ctx<MB, W, BCOL> &c) {
   if constexpr (S < Shape<MB, W>::NS - 1) {
-    issue<MB, W>(c, S, ring_stage<Shape<MB, W>::STAGE_BYTES, S>());
-    prologue<MB, W, S + 1>(c);
+    issue<MB, W, BCOL>(c, S, ring_stage<Shape<MB, W>::STAGE_BYTES, S>());
+    prologue<MB, W, BCOL, S + 1>(c);
   }
 }
 
 // One round of the ring: slices j+S .. j+NS-1 from stages S .. NS-1.
-template <bool BF16, int MB, int W, int S>
-__device__ __forceinline__ void round_from(Ctx<MB, W> &c, int j, f32x4 (&acc)[MB][Shape<MB, W>::CB]) {
+template <bool BF16, int MB, int W, bool BCOL, int S>
+__device__ __forceinline__ void round_from(Ctx<MB, W, BCOL> &c, int j, f32x4 (&acc)[MB][Shape<MB, W>::CB]) {
   if constexpr (S < Shape<MB, W>::NS) {
-    slice<BF16, MB, W, S>(c, j + S, acc);
-    round_from<BF16, MB, W, S + 1>(c, j, acc);
+    slice<BF16, MB, W, BCOL, S>(c, j + S, acc);
+    round_from<BF16, MB, W, BCOL, S + 1>(c, j, acc);
   }
 }
 
-template <bool BF16, bool OUT16, int MB, int W>
+// BCOL: B is K-contiguous (column-major, element (k, n) at B[n*ldb + k], the
+// layout of a weight stored output-feature by output-feature); its slices are
+// W rows of 64 k, staged and read like A.
+template <bool BF16, bool OUT16, int MB, int W, bool BCOL>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(KernelArgs p) {
   using SH = Shape<MB, W>;
-  Ctx<MB, W> c;
+  Ctx<MB, W, BCOL> c;
   const int tid = threadIdx.x;
   c.lane = tid & 63;
   c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -258,11 +268,12 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(KernelArgs p) {
   const int64_t k0 = s * p.kchunk;
   const int64_t K = p.splits ? (p.K - k0 < p.kchunk ? p.K - k0 : p.kchunk) : p.K;  // a positive multiple of 64
   const uint16_t *A = p.A + z * p.sA + r0 * p.lda + k0;
-  const uint16_t *B = p.B + z * p.sB + k0 * p.ldb + n0;
+  const uint16_t *B = p.B + z * p.sB + (BCOL ? n0 * p.ldb + k0 : k0 * p.ldb + n0);
 
-  c.ldb_bytes = (uint32_t)(p.ldb * 2);
-  // B resource: K rows of the W-column panel (host keeps it below 1 GiB)
-  c.rb = make_rsrc(B, (uint32_t)(((K - 1) * p.ldb + W) * 2));
+  // B resource: the W-column panel over this K range, K rows of W columns or
+  // W rows of K (host keeps it below 1 GiB)
+  c.rb = make_rsrc(B, (uint32_t)((BCOL ? (W - 1) * p.ldb + K : (K - 1) * p.ldb + W) * 2));
+  c.kstep_b = BCOL ? (uint32_t)A_ROW_BYTES : (uint32_t)(BK * p.ldb * 2);
   // A resource: the M rows of A; rows at or past M point outside it
   c.ra = make_rsrc(A, (uint32_t)(((M - 1) * p.lda + K) * 2));
   // A chunks: block q = 8 rows; lane l fills row 8q + l/8 at position l%8
@@ -276,9 +287,15 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(KernelArgs p) {
   // i.e. rows ROWS_PER_LOAD*(wave*LOADS+g) + lane/CHUNKS, position lane%CHUNKS
 #pragma unroll
   for (int g = 0; g < SH::LOADS; ++g) {
-    const int r = SH::ROWS_PER_LOAD * (c.wave * SH::LOADS + g) + lane / SH::CHUNKS;
-    const int chunk = swz_b<W>(r, lane % SH::CHUNKS);  // the swizzle is an involution in the chunk
-    c.offB[g] = (uint32_t)r * c.ldb_bytes + (uint32_t)chunk * 16u;
+    if constexpr (BCOL) {
+      // column-major B: 128-byte rows (one per column), 8 per wave-load, like A
+      const int r = 8 * (c.wave * SH::LOADS + g) + (lane >> 3);
+      c.offB[g] = (uint32_t)(r * p.ldb + swz_a(r, lane & 7) * 8) * 2u;
+    } else {
+      const int r = SH::ROWS_PER_LOAD * (c.wave * SH::LOADS + g) + lane / SH::CHUNKS;
+      const int chunk = swz_b<W>(r, lane % SH::CHUNKS);  // the swizzle is an involution in the chunk
+      c.offB[g] = (uint32_t)(r * p.ldb * 2) + (uint32_t)chunk * 16u;
+    }
   }
   c.nk = (int)(K / BK);  // the host guarantees K is a positive multiple of BK
 
@@ -288,9 +305,9 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(KernelArgs p) {
 #pragma unroll
     for (int cb = 0; cb < SH::CB; ++cb) acc[mb][cb] = f32x4{};
 
-  prologue<MB, W, 0>(c);
+  prologue<MB, W, BCOL, 0>(c);
   // whole rounds; the slices past K in the last one are zero
-  for (int j = 0; j < c.nk; j += SH::NS) round_from<BF16, MB, W, 0>(c, j, acc);
+  for (int j = 0; j < c.nk; j += SH::NS) round_from<BF16, MB, W, BCOL, 0>(c, j, acc);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the loads issued past the end
 
   // ---- epilogue: lane holds C[r0 + 16 mb + lane % 16][n .. n+3]; a K-split
@@ -311,13 +328,13 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(KernelArgs p) {
   }
 }
 
-template <bool BF16, bool OUT16, int MB, int W>
+template <bool BF16, bool OUT16, int MB, int W, bool BCOL>
 hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
   for (int64_t z0 = 0; z0 < batch; z0 += kMaxGridY) {
     KernelArgs a = base;
     a.z0 = (int32_t)z0;
     const int64_t nz = batch - z0 < kMaxGridY ? batch - z0 : kMaxGridY;
-    hipLaunchKernelGGL((gemm_skinny_kernel<BF16, OUT16, MB, W>), dim3((unsigned)(base.N / W), (unsigned)nz),
+    hipLaunchKernelGGL((gemm_skinny_kernel<BF16, OUT16, MB, W, BCOL>), dim3((unsigned)(base.N / W), (unsigned)nz),
                        dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -325,18 +342,25 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
   return hipSuccess;
 }
 
+template <int MB, int W, bool BCOL>
+hipError_t launch_layout(const Problem &p, const KernelArgs &a, hipStream_t stream) {
+  if (p.in_bf16)
+    return p.out16 ? launch_t<true, true, MB, W, BCOL>(a, p.batch, stream)
+                   : launch_t<true, false, MB, W, BCOL>(a, p.batch, stream);
+  return p.out16 ? launch_t<false, true, MB, W, BCOL>(a, p.batch, stream)
+                 : launch_t<false, false, MB, W, BCOL>(a, p.batch, stream);
+}
+
 template <int MB, int W>
 hipError_t launch_shape(const Problem &p, const KernelArgs &a, hipStream_t stream) {
-  if (p.in_bf16)
-    return p.out16 ? launch_t<true, true, MB, W>(a, p.batch, stream) : launch_t<true, false, MB, W>(a, p.batch, stream);
-  return p.out16 ? launch_t<false, true, MB, W>(a, p.batch, stream) : launch_t<false, false, MB, W>(a, p.batch, stream);
+  return p.b_col ? launch_layout<MB, W, true>(p, a, stream) : launch_layout<MB, W, false>(p, a, stream);
 }
 
 }  // namespace
 
 SkinnyPlan skinny_plan(const Problem &p) {
   SkinnyPlan pl{};
-  if (p.a_col || p.b_col) return pl;  // row-major A and B
+  if (p.a_col) return pl;  // row-major A; B either way
   if (p.M < 1 || p.M > 128) return pl;
   pl.mb = p.M <= 16 ? 1 : p.M <= 32 ? 2 : p.M <= 64 ? 4 : 8;
   // W = 256 when its grid fills the chip (one workgroup per CU), else W = 64;
@@ -350,8 +374,8 @@ SkinnyPlan skinny_plan(const Problem &p) {
   if (((uintptr_t)p.A & 15) || ((uintptr_t)p.B & 15) || ((uintptr_t)p.C & 15)) return SkinnyPlan{};
   if (p.lda % 8 || p.ldb % 8 || p.ldc % 4) return SkinnyPlan{};
   if (p.batch > 1 && (p.sA % 8 || p.sB % 8 || p.sC % 4)) return SkinnyPlan{};
-  // 32-bit buffer offsets: one B panel (K rows) and A's M rows below 1 GiB
-  if ((p.K - 1) * p.ldb + pl.w >= ((int64_t)1 << 29)) return SkinnyPlan{};
+  // 32-bit buffer offsets: one B panel (K rows of W, or W rows of K) and A's M rows below 1 GiB
+  if ((p.b_col ? (pl.w - 1) * p.ldb + p.K : (p.K - 1) * p.ldb + pl.w) >= ((int64_t)1 << 29)) return SkinnyPlan{};
   if ((p.M - 1) * p.lda + p.K >= ((int64_t)1 << 29)) return SkinnyPlan{};
   return pl;
 }
@@ -390,7 +414,7 @@ hipError_t launch_skinny(const Problem &p, hipStream_t stream) {
   return launch_shape<8, 64>(p, a, stream);
 }
 
-KSplit ksplit_shape(int64_t M, int64_t N, int64_t K, int64_t batch) {
+KSplit ksplit_shape(int64_t M, int64_t N, int64_t K, int64_t batch, bool wide) {
   KSplit ks;
   if (M < 1 || N < 64 || N % 64 || K % BK || K < 512 || batch < 1) return ks;
   const int mb = M <= 16 ? 1 : M <= 32 ? 2 : 4;
@@ -398,13 +422,15 @@ KSplit ksplit_shape(int64_t M, int64_t N, int64_t K, int64_t batch) {
   // every row block reads all of B again: beyond 512 rows the 256 x 256
   // kernels' split (tsplit_shape) reads less
   if (row_blocks > 8) return ks;
-  // workgroups without a split: 64-column panels, or 256-column panels when
-  // there are enough of them for a split of at most 8 (each workgroup then
-  // streams 512-byte row segments of B, which HBM serves faster than the
-  // 128-byte segments of 64-column panels)
+  // workgroups without a split: 64-column panels, or (wide: row-major B)
+  // 256-column panels when there are enough of them for a split of at most 8
+  // (each workgroup then streams 512-byte row segments of B, which HBM serves
+  // faster than the 128-byte segments of 64-column panels; a K-contiguous B
+  // is read in 128-byte row segments at either width, and the wider split
+  // measured slower there)
   int w = 64;
   int64_t base = batch * (N / 64) * row_blocks;
-  if (N % 256 == 0) {
+  if (wide && N % 256 == 0) {
     const int64_t base256 = batch * (N / 256) * row_blocks;
     if (base256 >= 32 && base256 < 128) {
       w = 256;
@@ -428,25 +454,37 @@ KSplit ksplit_shape(int64_t M, int64_t N, int64_t K, int64_t batch) {
 }
 
 KSplit ksplit_plan(const Problem &p) {
-  const KSplit ks = ksplit_shape(p.M, p.N, p.K, p.batch);
-  if (!ks.splits || p.a_col || p.b_col || p.rows) return KSplit{};
+  const KSplit ks = ksplit_shape(p.M, p.N, p.K, p.batch, !p.b_col);
+  if (!ks.splits || p.a_col || p.rows) return KSplit{};
   if (((uintptr_t)p.A & 15) || ((uintptr_t)p.B & 15) || ((uintptr_t)p.C & 15)) return KSplit{};
   if (p.lda % 8 || p.ldb % 8 || p.ldc % 4) return KSplit{};
   if (p.batch > 1 && (p.sA % 8 || p.sB % 8 || p.sC % 4)) return KSplit{};
-  // 32-bit buffer offsets within one chunk: B's kchunk rows, A's row block
-  if ((ks.kchunk - 1) * p.ldb + ks.w >= ((int64_t)1 << 29)) return KSplit{};
+  // 32-bit buffer offsets within one chunk: B's panel, A's row block
+  if ((p.b_col ? (ks.w - 1) * p.ldb + ks.kchunk : (ks.kchunk - 1) * p.ldb + ks.w) >= ((int64_t)1 << 29))
+    return KSplit{};
   if ((16 * ks.mb - 1) * p.lda + ks.kchunk >= ((int64_t)1 << 29)) return KSplit{};
   return ks;
+}
+
+template <int MB, int W, bool BCOL>
+hipError_t launch_split_mb(const Problem &p, const KernelArgs &a, int64_t launches, hipStream_t stream) {
+  return p.in_bf16 ? launch_t<true, false, MB, W, BCOL>(a, launches, stream)
+                   : launch_t<false, false, MB, W, BCOL>(a, launches, stream);
+}
+
+template <int W, bool BCOL>
+hipError_t launch_split_layout(const Problem &p, const KSplit &ks, const KernelArgs &a, int64_t launches,
+                               hipStream_t stream) {
+  if (ks.mb == 1) return launch_split_mb<1, W, BCOL>(p, a, launches, stream);
+  if (ks.mb == 2) return launch_split_mb<2, W, BCOL>(p, a, launches, stream);
+  return launch_split_mb<4, W, BCOL>(p, a, launches, stream);
 }
 
 template <int W>
 hipError_t launch_split_w(const Problem &p, const KSplit &ks, const KernelArgs &a, int64_t launches,
                           hipStream_t stream) {
-  if (ks.mb == 1)
-    return p.in_bf16 ? launch_t<true, false, 1, W>(a, launches, stream) : launch_t<false, false, 1, W>(a, launches, stream);
-  if (ks.mb == 2)
-    return p.in_bf16 ? launch_t<true, false, 2, W>(a, launches, stream) : launch_t<false, false, 2, W>(a, launches, stream);
-  return p.in_bf16 ? launch_t<true, false, 4, W>(a, launches, stream) : launch_t<false, false, 4, W>(a, launches, stream);
+  return p.b_col ? launch_split_layout<W, true>(p, ks, a, launches, stream)
+                 : launch_split_layout<W, false>(p, ks, a, launches, stream);
 }
 
 hipError_t launch_ksplit_pass1(const Problem &p, const KSplit &ks, float *ws, hipStream_t stream) {
@@ -472,27 +510,34 @@ hipError_t launch_ksplit_pass1(const Problem &p, const KSplit &ks, float *ws, hi
   return ks.w == 256 ? launch_split_w<256>(p, ks, a, launches, stream) : launch_split_w<64>(p, ks, a, launches, stream);
 }
 
-const char *ksplit_name(const KSplit &ks) {
+const char *ksplit_name(const KSplit &ks, bool b_col) {
   if (ks.splits && ks.tile_variant == 3) return "ksplit_tile_256x256x64_mi16+reduce";
   if (ks.splits && ks.tile_variant == 2) return "ksplit_tile_256x256x32_mi16_nn+reduce";
   if (ks.splits && ks.tile_variant == 5) return "ksplit_tile_256x256x32_mi16_tn+reduce";
   if (ks.splits && ks.tile_variant == 6) return "ksplit_tile_256x256x32_mi16_tt+reduce";
-  static const char *const names[2][3] = {
-      {"ksplit_skinny_m16_n64_k64+reduce", "ksplit_skinny_m32_n64_k64+reduce", "ksplit_skinny_m64_n64_k64+reduce"},
-      {"ksplit_skinny_m16_n256_k64+reduce", "ksplit_skinny_m32_n256_k64+reduce",
-       "ksplit_skinny_m64_n256_k64+reduce"}};
+  static const char *const names[2][2][3] = {
+      {{"ksplit_skinny_m16_n64_k64+reduce", "ksplit_skinny_m32_n64_k64+reduce", "ksplit_skinny_m64_n64_k64+reduce"},
+       {"ksplit_skinny_m16_n256_k64+reduce", "ksplit_skinny_m32_n256_k64+reduce",
+        "ksplit_skinny_m64_n256_k64+reduce"}},
+      {{"ksplit_skinny_m16_n64_k64_t+reduce", "ksplit_skinny_m32_n64_k64_t+reduce",
+        "ksplit_skinny_m64_n64_k64_t+reduce"},
+       {"ksplit_skinny_m16_n256_k64_t+reduce", "ksplit_skinny_m32_n256_k64_t+reduce",
+        "ksplit_skinny_m64_n256_k64_t+reduce"}}};
   if (!ks.splits) return nullptr;
-  return names[ks.w == 256][ks.mb == 1 ? 0 : ks.mb == 2 ? 1 : 2];
+  return names[b_col][ks.w == 256][ks.mb == 1 ? 0 : ks.mb == 2 ? 1 : 2];
 }
 
 const char *skinny_name(const Problem &p) {
-  static const char *const names[2][4] = {
-      {"skinny_m16_n64_k64", "skinny_m32_n64_k64", "skinny_m64_n64_k64", "skinny_m128_n64_k64"},
-      {"skinny_m16_n256_k64", "skinny_m32_n256_k64", "skinny_m64_n256_k64", nullptr}};
+  // suffix _t: B stored transposed (column-major, K-contiguous)
+  static const char *const names[2][2][4] = {
+      {{"skinny_m16_n64_k64", "skinny_m32_n64_k64", "skinny_m64_n64_k64", "skinny_m128_n64_k64"},
+       {"skinny_m16_n256_k64", "skinny_m32_n256_k64", "skinny_m64_n256_k64", nullptr}},
+      {{"skinny_m16_n64_k64_t", "skinny_m32_n64_k64_t", "skinny_m64_n64_k64_t", "skinny_m128_n64_k64_t"},
+       {"skinny_m16_n256_k64_t", "skinny_m32_n256_k64_t", "skinny_m64_n256_k64_t", nullptr}}};
   const SkinnyPlan pl = skinny_plan(p);
   if (!pl.mb) return nullptr;
   const int i = pl.mb == 1 ? 0 : pl.mb == 2 ? 1 : pl.mb == 4 ? 2 : 3;
-  return names[pl.w == 256][i];
+  return names[p.b_col][pl.w == 256][i];
 }
 
 }  // namespace tsm
