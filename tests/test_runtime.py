@@ -91,6 +91,31 @@ def test_matmul_wrapper_reads_layouts_from_views(orc):
     check(c.cpu().numpy().astype(np.float64)[None], Cr, S, K, "f32", "matmul wrapper")
 
 
+def test_matmul_wrapper_activation_and_workspace(orc):
+    """The torch-level wrapper with a fused leaky ReLU, bf16 output and a workspace that splits K."""
+    import torch
+
+    import oracle
+    import tiled_shared_memory_amd as tsm
+
+    M, N, K = 256, 256, 2048
+    A, B = make_operands(9, 1, M, N, K, F16, ("uniform", -1.0, 1.0))
+    a = torch.from_numpy(A[0].view(np.int16)).cuda().view(torch.float16)
+    b = torch.from_numpy(B[0].view(np.int16)).cuda().view(torch.float16)
+    ws = tsm.workspace_for(a, b)
+    assert ws is not None
+    say("[gpu] matmul wrapper with activation and workspace")
+    c = tsm.matmul(a, b, out_dtype=torch.bfloat16, activation="leaky_relu", slope=0.25, workspace=ws)
+    torch.cuda.synchronize()
+    Cr, S = orc.gemm_rows(A, B, M, N, K, F16)
+    from gpu_util import check
+
+    check(c.float().cpu().numpy().astype(np.float64)[None], Cr, S, K, "bf16", "matmul ws",
+          act=oracle.ACT_LEAKY_RELU, slope=0.25)
+    with pytest.raises(tsm.TsmError):
+        tsm.matmul(a, b, activation="gelu")
+
+
 def test_launch_error_is_not_raised_for_valid_calls():
     # a valid call after many invalid ones still launches (no sticky error state)
     import tiled_shared_memory_amd as tsm

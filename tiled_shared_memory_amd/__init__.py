@@ -45,13 +45,30 @@ def _layout(t, rows_dim_size, cols_dim_size):
     raise TsmError(TSM_ERROR_INVALID_VALUE, "operand must be row- or column-major in its last two dims")
 
 
-def matmul(a, b, *, out=None, out_dtype=None, stream=None):
-    """C = A.B for CUDA tensors ``a`` (..., M, K) and ``b`` (..., K, N) in float16 or bfloat16.
+_ACTIVATIONS = {None: TSM_ACT_NONE, "relu": TSM_ACT_RELU, "leaky_relu": TSM_ACT_LEAKY_RELU}
+
+
+def workspace_for(a, b):
+    """A float32 CUDA tensor big enough for ``matmul(a, b, workspace=...)`` to split K, or None when the shape
+    does not split.  Allocate it once and reuse it across calls of that shape on one stream."""
+    import torch
+
+    M, K, N = a.shape[-2], a.shape[-1], b.shape[-1]
+    batch = max(a.shape[0] if a.dim() == 3 else 1, b.shape[0] if b.dim() == 3 else 1)
+    nbytes = gemm_workspace_bytes(M, N, K, batch)
+    return torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=a.device) if nbytes else None
+
+
+def matmul(a, b, *, out=None, out_dtype=None, activation=None, slope=0.01, workspace=None, stream=None):
+    """C = act(A.B) for CUDA tensors ``a`` (..., M, K) and ``b`` (..., K, N) in float16 or bfloat16.
 
     2-D operands give one product, 3-D ones a strided batch (a batch dim of
     size 1 or stride 0 broadcasts).  Each operand may be row-major or
     column-major in its last two dims (e.g. ``w.t()``); the result is row-major
-    float32 (default) or float16.
+    float32 (default), float16 or bfloat16.  ``activation`` is None, "relu" or
+    "leaky_relu" (with ``slope``), fused into the kernels' epilogue.  With a
+    ``workspace`` (see ``workspace_for``) products with few output tiles and
+    deep K split K through it.
     """
     import torch
 
@@ -76,6 +93,10 @@ def matmul(a, b, *, out=None, out_dtype=None, stream=None):
     def bstride(t):
         return 0 if t.dim() == 2 or t.shape[0] == 1 else t.stride(0)
 
-    gemm_strided_batched_ex(M, N, K, a, lda, la, bstride(a), b, ldb, lb, bstride(b), out, ldc,
-                            out.stride(0) if out.dim() == 3 else 0, batch, code, stream)
+    if activation not in _ACTIVATIONS:
+        raise TsmError(TSM_ERROR_INVALID_VALUE, f"unknown activation {activation!r}")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    gemm_strided_batched_ws(M, N, K, a, lda, la, bstride(a), b, ldb, lb, bstride(b), out, ldc,
+                            out.stride(0) if out.dim() == 3 else 0, batch, code, _ACTIVATIONS[activation], slope,
+                            workspace, ws_bytes, stream)
     return out
