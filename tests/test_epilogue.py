@@ -34,6 +34,8 @@ FAMILIES = [
     ("skinny_m64_n64_k64", (40, 320, 192, 2), "row", "row"),
     ("skinny_m128_n64_k64", (100, 128, 128, 1), "row", "row"),
     ("splitk_16x16_w16", (48, 32, 4096, 1), "row", "row"),
+    ("splitk_16x16_w16_t", (32, 48, 2048, 2), "row", "col"),
+    ("skinny_m32_n64_k64_t", (20, 192, 320, 2), "row", "col"),
 ]
 ACTS = [(tsm.TSM_ACT_NONE, 0.0), (tsm.TSM_ACT_RELU, 0.0), (tsm.TSM_ACT_LEAKY_RELU, 0.1),
         (tsm.TSM_ACT_LEAKY_RELU, -1.5)]

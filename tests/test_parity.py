@@ -344,16 +344,18 @@ SPLITK_SHAPES = [(16, 16, 2048, 1), (256, 256, 8192, 1), (48, 80, 4096, 2), (128
 
 @pytest.mark.parametrize("shape", SPLITK_SHAPES, ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("in_fmt,out_fmt", [(F16, "f32"), (BF16, "f16"), (BF16, "f32")])
-def test_splitk_kernel(orc, shape, in_fmt, out_fmt):
-    """The deep-K kernel (16 x 16 tiles, K split over 16 waves, fixed-order LDS reduction) against the oracle."""
+@pytest.mark.parametrize("b_layout", ["row", "col"])
+def test_splitk_kernel(orc, shape, in_fmt, out_fmt, b_layout):
+    """The deep-K kernel (16 x 16 tiles, K split over 16 waves, fixed-order LDS reduction) against the oracle,
+    with B row-major (transposed out of LDS) or K-contiguous."""
     M, N, K, batch = shape
-    A, B = make_operands(M + 7 * N + K + batch, batch, M, N, K, in_fmt, ("uniform", -1.0, 1.0))
-    say(f"[gpu] splitk kernel {shape} {in_fmt}->{out_fmt}")
-    C = run(A, B, M, N, K, in_fmt, out_fmt, batch=batch, kernel=SPLITK)
-    Cr, S = orc.gemm_rows(A, B, M, N, K, in_fmt, batch=batch)
+    A, B = make_operands(M + 7 * N + K + batch, batch, M, N, K, in_fmt, ("uniform", -1.0, 1.0), "row", b_layout)
+    say(f"[gpu] splitk kernel {shape} {in_fmt}->{out_fmt} B {b_layout}")
+    C = run(A, B, M, N, K, in_fmt, out_fmt, batch=batch, b_layout=b_layout, kernel=SPLITK)
+    Cr, S = orc.gemm_rows(A, B, M, N, K, in_fmt, batch=batch, b_layout=b_layout)
     check(C, Cr, S, K, out_fmt, f"splitk {shape}")
     # deterministic: the reduction order is fixed
-    assert np.array_equal(run(A, B, M, N, K, in_fmt, out_fmt, batch=batch, kernel=SPLITK), C)
+    assert np.array_equal(run(A, B, M, N, K, in_fmt, out_fmt, batch=batch, b_layout=b_layout, kernel=SPLITK), C)
 
 
 def test_k_zero_writes_zeros():

@@ -77,7 +77,7 @@ const char *kernel_name(Kernel k, const Problem &p) {
     case Kernel::Skinny:
       return skinny_name(p);
     case Kernel::SplitK:
-      return splitk_name();
+      return splitk_name(p.b_col);
     default:
       return nullptr;
   }
@@ -212,7 +212,11 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
   const int64_t masked_tiles = tiles * batch;
   // few 128 x 128 tiles otherwise: 64 x 64 tiles, four times the workgroups
   if (masked_tiles < 256) out->kernel = (a8 && b8) ? Kernel::Small8 : Kernel::Small1;
-  const bool splitk_ok = K > 0 && masked_tiles < 256 && splitk_supports(p);
+  // split-K reads B in 16-column pieces, 64-byte rows when B is K-contiguous
+  // (then it loses to the 64 x 64 masked tiles from 48 tiles of 128 x 128:
+  // 1024 x 1024 x 8192 took 144 us against 96 us) and 32-byte rows when B is
+  // row-major (where the masked kernel is slow too)
+  const bool splitk_ok = K > 0 && masked_tiles < (p.b_col ? 48 : 256) && splitk_supports(p);
   if (splitk_ok) out->kernel = Kernel::SplitK;
   // The 256 x 256 kernels take about the same time per round of up to 256
   // tiles (one workgroup per CU) whatever the tile count, about 8 TFLOP/s

@@ -121,14 +121,14 @@ KSplit tsplit_plan(const Problem &p);
 const char *ksplit_name(const KSplit &ks, bool b_col);
 
 // Split-K kernel for small M x N and deep K: 16 x 16 tiles, K split across the
-// 16 waves of a workgroup; row-major A and B, M, N multiples of 16, K a
-// multiple of 2048.
+// 16 waves of a workgroup; row-major A, B either way, M, N multiples of 16, K
+// a multiple of 2048.
 struct SplitKInfo {
   static constexpr int WAVES = 16;
 };
 bool splitk_supports(const Problem &p);
 hipError_t launch_splitk(const Problem &p, hipStream_t stream);
-const char *splitk_name();
+const char *splitk_name(bool b_col);
 hipError_t launch_skinny(const Problem &p, hipStream_t stream);
 const char *skinny_name(const Problem &p);
 hipError_t launch_tile(const Problem &p, int variant, hipStream_t stream);

@@ -70,7 +70,7 @@ __device__ __forceinline__ void issue(const Ctx &c, int t, char *s) {
                                            0);
 }
 
-template <bool BF16, int S>
+template <bool BF16, bool BCOL, int S>
 __device__ __forceinline__ void step(Ctx &c, int t, f32x4 &acc) {
   // step t has landed once only the two younger steps' loads (2 each) are
   // pending; the previous step's LDS reads are complete before its stage is
@@ -81,21 +81,29 @@ __device__ __forceinline__ void step(Ctx &c, int t, f32x4 &acc) {
   const int lane = c.lane;
   // A operand: row lane % 16 (64 bytes), k 8*(lane/16) .. +7
   const u32x4 af = *reinterpret_cast<const u32x4 *>(w + (lane & 15) * 64 + (lane >> 4) * 16);
-  // B operand: two transpose reads of rows 8*(lane/16) + 4h + (lane%16)/4, columns 4*(lane%4)
   u32x4 bf;
+  if constexpr (BCOL) {
+    // K-contiguous B: staged like A, column lane % 16 (64 bytes), k 8*(lane/16) .. +7
+    bf = *reinterpret_cast<const u32x4 *>(w + 1024 + (lane & 15) * 64 + (lane >> 4) * 16);
+  } else {
+    // row-major B: two transpose reads of rows 8*(lane/16) + 4h + (lane%16)/4, columns 4*(lane%4)
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int row = 8 * (lane >> 4) + 4 * h + ((lane & 15) >> 2);
-    const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)((lds_char *)(w + 1024) + row * 32 + (lane & 3) * 8));
-    const u32x2 d = __builtin_bit_cast(u32x2, v);
-    bf[2 * h] = d[0];
-    bf[2 * h + 1] = d[1];
+    for (int h = 0; h < 2; ++h) {
+      const int row = 8 * (lane >> 4) + 4 * h + ((lane & 15) >> 2);
+      const v4s v =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)((lds_char *)(w + 1024) + row * 32 + (lane & 3) * 8));
+      const u32x2 d = __builtin_bit_cast(u32x2, v);
+      bf[2 * h] = d[0];
+      bf[2 * h + 1] = d[1];
+    }
   }
   issue(c, next, stage<(S + NS - 1) % NS>());  // stage S-1 was read in step t-1
   acc = mfma_16x16x32<BF16>(bf, af, acc);
 }
 
-template <bool BF16, bool OUT16>
+// BCOL: B is K-contiguous (column-major); its 16 x 32 slice per step is staged
+// and read like A's.
+template <bool BF16, bool OUT16, bool BCOL>
 __global__ __launch_bounds__(WAVES * 64, 1) void gemm_splitk_kernel(KernelArgs p) {
   Ctx c;
   const int tid = threadIdx.x;
@@ -120,22 +128,28 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_splitk_kernel(KernelArgs p
   c.nsteps = (int)(p.K / (32 * WAVES));
   const int64_t k0 = (int64_t)c.wave * c.nsteps * 32;
   const uint16_t *A = p.A + z * p.sA + m0 * p.lda + k0;
-  const uint16_t *B = p.B + z * p.sB + k0 * p.ldb + n0;
+  const uint16_t *B = p.B + z * p.sB + (BCOL ? n0 * p.ldb + k0 : k0 * p.ldb + n0);
   c.ra = make_rsrc(A, (uint32_t)((15 * p.lda + (int64_t)c.nsteps * 32) * 2));
-  c.rb = make_rsrc(B, (uint32_t)((((int64_t)c.nsteps * 32 - 1) * p.ldb + 16) * 2));
   c.offA = (uint32_t)((lane >> 2) * p.lda + 8 * (lane & 3)) * 2u;
-  c.offB = (uint32_t)((lane >> 1) * p.ldb + 8 * (lane & 1)) * 2u;
-  c.kstepB = (uint32_t)(32 * p.ldb * 2);
+  if constexpr (BCOL) {
+    c.rb = make_rsrc(B, (uint32_t)((15 * p.ldb + (int64_t)c.nsteps * 32) * 2));
+    c.offB = (uint32_t)((lane >> 2) * p.ldb + 8 * (lane & 3)) * 2u;
+    c.kstepB = 64;
+  } else {
+    c.rb = make_rsrc(B, (uint32_t)((((int64_t)c.nsteps * 32 - 1) * p.ldb + 16) * 2));
+    c.offB = (uint32_t)((lane >> 1) * p.ldb + 8 * (lane & 1)) * 2u;
+    c.kstepB = (uint32_t)(32 * p.ldb * 2);
+  }
 
   f32x4 acc = f32x4{};
   issue(c, 0, stage<0>());
   issue(c, min(1, c.nsteps - 1), stage<1>());
   issue(c, min(2, c.nsteps - 1), stage<2>());
   for (int t = 0; t < c.nsteps; t += NS) {
-    step<BF16, 0>(c, t + 0, acc);
-    step<BF16, 1>(c, t + 1, acc);
-    step<BF16, 2>(c, t + 2, acc);
-    step<BF16, 3>(c, t + 3, acc);
+    step<BF16, BCOL, 0>(c, t + 0, acc);
+    step<BF16, BCOL, 1>(c, t + 1, acc);
+    step<BF16, BCOL, 2>(c, t + 2, acc);
+    step<BF16, BCOL, 3>(c, t + 3, acc);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the duplicate tail loads
 
@@ -157,14 +171,14 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_splitk_kernel(KernelArgs p
   }
 }
 
-template <bool BF16, bool OUT16>
+template <bool BF16, bool OUT16, bool BCOL>
 hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
   const int64_t tiles = (int64_t)base.tiles_m * base.tiles_n;
   for (int64_t z0 = 0; z0 < batch; z0 += kMaxGridY) {
     KernelArgs a = base;
     a.z0 = (int32_t)z0;
     const int64_t nz = batch - z0 < kMaxGridY ? batch - z0 : kMaxGridY;
-    hipLaunchKernelGGL((gemm_splitk_kernel<BF16, OUT16>), dim3((unsigned)tiles, (unsigned)nz), dim3(WAVES * 64), 0,
+    hipLaunchKernelGGL((gemm_splitk_kernel<BF16, OUT16, BCOL>), dim3((unsigned)tiles, (unsigned)nz), dim3(WAVES * 64), 0,
                        stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -175,14 +189,15 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
 }  // namespace
 
 bool splitk_supports(const Problem &p) {
-  if (p.a_col || p.b_col) return false;  // row-major A and B
+  if (p.a_col) return false;  // row-major A; B either way
   if (p.rows) return false;  // stores whole 16 x 16 tiles: no per-problem row counts
   if (p.M % 16 || p.N % 16 || p.K % (32 * WAVES * NS) || p.K == 0) return false;
   if (((uintptr_t)p.A & 15) || ((uintptr_t)p.B & 15) || ((uintptr_t)p.C & 15)) return false;
   if (p.lda % 8 || p.ldb % 8 || p.ldc % 4) return false;
   if (p.batch > 1 && (p.sA % 8 || p.sB % 8 || p.sC % 4)) return false;
-  // a wave's B range (K / 16 rows) and A rows must span less than 2 GiB
-  if ((p.K / WAVES) * p.ldb >= ((int64_t)1 << 30) || 16 * p.lda >= ((int64_t)1 << 30)) return false;
+  // a wave's B range (K / 16 rows, or 16 columns) and A rows must span less than 2 GiB
+  if ((p.b_col ? 16 * p.ldb : (p.K / WAVES) * p.ldb) >= ((int64_t)1 << 30) || 16 * p.lda >= ((int64_t)1 << 30))
+    return false;
   if ((p.M / 16) * (p.N / 16) > 0x7fffffff / 2) return false;
   return true;
 }
@@ -207,11 +222,16 @@ hipError_t launch_splitk(const Problem &p, hipStream_t stream) {
   a.out_bf16 = p.out_bf16;
   a.tiles_m = (int32_t)(p.M / 16);
   a.tiles_n = (int32_t)(p.N / 16);
+  if (p.b_col) {
+    if (p.in_bf16)
+      return p.out16 ? launch_t<true, true, true>(a, p.batch, stream) : launch_t<true, false, true>(a, p.batch, stream);
+    return p.out16 ? launch_t<false, true, true>(a, p.batch, stream) : launch_t<false, false, true>(a, p.batch, stream);
+  }
   if (p.in_bf16)
-    return p.out16 ? launch_t<true, true>(a, p.batch, stream) : launch_t<true, false>(a, p.batch, stream);
-  return p.out16 ? launch_t<false, true>(a, p.batch, stream) : launch_t<false, false>(a, p.batch, stream);
+    return p.out16 ? launch_t<true, true, false>(a, p.batch, stream) : launch_t<true, false, false>(a, p.batch, stream);
+  return p.out16 ? launch_t<false, true, false>(a, p.batch, stream) : launch_t<false, false, false>(a, p.batch, stream);
 }
 
-const char *splitk_name() { return "splitk_16x16_w16"; }
+const char *splitk_name(bool b_col) { return b_col ? "splitk_16x16_w16_t" : "splitk_16x16_w16"; }
 
 }  // namespace tsm
