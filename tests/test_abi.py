@@ -267,6 +267,11 @@ def test_workspace_routing(monkeypatch):
     # 32 to 127 panels of 256 columns: split those (512-byte row segments of B)
     assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(M=16, N=16384, K=8192)) == "ksplit_skinny_m16_n256_k64+reduce"
     assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(M=64, N=8192, K=8192)) == "ksplit_skinny_m64_n256_k64+reduce"
+    # C rows that are not 16-byte multiples: the reduction's 4-column stores would not be aligned
+    args = list(_ws_args(M=1024, N=1024, K=8192, nbytes=1 << 30))
+    assert tsm.tsm_gemm_ws_kernel_name(*args).startswith("ksplit_tile_")
+    args[12] = 1026  # ldc
+    assert not tsm.tsm_gemm_ws_kernel_name(*args).startswith("ksplit_")
     # a K-contiguous B splits the same way
     assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(lb=1, nbytes=1 << 30)) == "ksplit_skinny_m64_n64_k64_t+reduce"
     # too little workspace, none or a forced kernel: the kernel that needs none

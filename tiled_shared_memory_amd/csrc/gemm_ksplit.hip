@@ -103,7 +103,8 @@ Problem tsplit_pass1_problem(const Problem &p, const KSplit &ks, float *ws) {
 KSplit tsplit_plan(const Problem &p) {
   KSplit ks = tsplit_shape(p.M, p.N, p.K, p.batch);
   if (!ks.splits || p.rows) return KSplit{};
-  if ((uintptr_t)p.C & 15) return KSplit{};
+  // pass 2 stores 4 consecutive columns of C at once
+  if (((uintptr_t)p.C & 15) || p.ldc % 4) return KSplit{};
   const Problem q = tsplit_pass1_problem(p, ks, (float *)p.C);  // alignment of the workspace is checked apart
   if (!tile_supports(q, p.a_col, !p.b_col)) return KSplit{};
   // the default large-tile kernel for the operands' layouts
