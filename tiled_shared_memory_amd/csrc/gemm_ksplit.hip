@@ -2,14 +2,16 @@
 // and the fixed-order reduction (pass 2).
 //
 // Problems with few output tiles and deep K (256 x 256 x 8192 has sixteen
-// 64 x 64 tiles) cannot occupy 256 CUs by tiling M and N.  Pass 1 (the skinny
-// kernel in its K-split mode) gives each workgroup one 64-column panel, one
-// row block and one K chunk, and writes float32 partial sums: one M x N slab
-// per (problem, chunk).  This pass adds the slabs of each problem in chunk
-// order and applies the epilogue, so C is overwritten with a deterministic
-// result and no atomics or zeroed memory are involved ("A Dumb Triton Runtime
-// Error", section "The Takeaway and the Final Fix": reduce, then store once,
-// rather than accumulate across blocks with atomics).
+// 64 x 64 tiles) cannot occupy 256 CUs by tiling M and N.  Pass 1 gives each
+// workgroup one output tile and one K chunk and writes float32 partial sums,
+// one M x N slab per (problem, chunk): the skinny kernel in its K-split mode
+// (a 64- or 256-column panel and a row block of up to 64 rows), or, for 8-127
+// tiles of 256 x 256, the large-tile kernel run over the chunks as a strided
+// batch.  Pass 2 adds the slabs of each problem in chunk order and applies
+// the epilogue, so C is overwritten with a deterministic result and no atomics
+// or zeroed memory are involved ("A Dumb Triton Runtime Error", section "The
+// Takeaway and the Final Fix": reduce, then store once, rather than
+// accumulate across blocks with atomics).
 //
 // Memory-bound: each thread owns 4 consecutive columns of one row, loads the
 // 16-byte partials of sixteen chunks at a time (all issued before the first
