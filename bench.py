@@ -40,13 +40,26 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
+# Sources that define each kernel family's device code (with the shared headers
+# below): a counter record stays valid while these are unchanged.
+KERNEL_FILES = {"tile_": ("gemm_tile.hip",), "skinny_": ("gemm_skinny.hip",),
+                "ksplit_": ("gemm_skinny.hip", "gemm_ksplit.hip", "gemm_tile.hip"),
+                "splitk_": ("gemm_splitk.hip",), "masked_": ("gemm_masked.hip",), "rowsum_": ("rowsum.hip",)}
+SHARED_FILES = ("gemm_internal.hpp", "mfma.hpp")
+
+
+def kernel_source_hash(kernel=None):
+    """Hash of the kernel sources: of every file under csrc/, or, given a kernel name, of its family's files."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tiled_shared_memory_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp", ".h")):
-            h.update(f.encode())
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    if kernel is None:
+        files = [f for f in sorted(os.listdir(csrc)) if f.endswith((".hip", ".hpp", ".h"))]
+    else:
+        fam = next(v for k, v in KERNEL_FILES.items() if kernel.startswith(k))
+        files = sorted(set(fam) | set(SHARED_FILES))
+    for f in files:
+        h.update(f.encode())
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -59,7 +72,7 @@ def traffic_from_profiles(workload, kernel):
         rec = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if rec.get("source_hash") != kernel_source_hash() or rec.get("kernel") != kernel:
+    if rec.get("source_hash") != kernel_source_hash(kernel) or rec.get("kernel") != kernel:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -138,9 +151,11 @@ def summarize(run_dir):
     if "secondary" in bench:
         jobs.append((bench["secondary"]["workload"], bench["secondary"]["kernel"], bench["secondary"]["ms_per_step"]))
     src = bench.get("kernel_source_hash")
-    if src != kernel_source_hash():
-        print(f"--summarize: the run measured kernel source {src}, the tree now holds {kernel_source_hash()}; "
-              "the traffic records will not be used by bench.py", file=sys.stderr)
+    per_kernel = bench.get("kernel_source_hashes", {})
+    for _, kern, _ in jobs:
+        if per_kernel.get(kern) != kernel_source_hash(kern):
+            print(f"--summarize: the run measured {kern} from source {per_kernel.get(kern)}, the tree now holds "
+                  f"{kernel_source_hash(kern)}; its traffic record will not be used by bench.py", file=sys.stderr)
     wargs = workload_args(bench.get("argv", []))
     cmd = lambda k: " ".join(("cd /tmp && " + PROFILE_COMMANDS[k].replace("WORKLOAD_ARGS", wargs)).split())  # noqa: E731
     stats = _csv(os.path.join(run_dir, "trace", "*kernel_stats.csv"))
@@ -177,7 +192,7 @@ def summarize(run_dir):
         mops = c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0) + c.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0)
         lds = c.get("SQ_LDS_IDX_ACTIVE", 0)
         txt = [f"# rocprofv3 counters for {kern} on {wl}, averages per dispatch, one MI355X",
-               f"# kernel source hash: {src}",
+               f"# kernel source hash: {per_kernel.get(kern)} ({kern}'s sources); {src} (all of csrc/)",
                f"# SQ counters: {cmd('sq')}",
                f"# FETCH_SIZE: {cmd('fetch')}",
                f"# WRITE_SIZE: {cmd('write')}",
@@ -196,7 +211,7 @@ def summarize(run_dir):
                 f"# kernel-trace average {float(trace_row['AverageNs']) / 1e6:.4f} ms over {trace_row['Calls']} "
                 f"calls; bench.py ms_per_step in the same run {ms:.4f} ms"]
         open(os.path.join(out, f"counters__{kern}__{wl}.txt"), "w").write("\n".join(txt) + "\n")
-        rec = {"kernel": kern, "workload": wl, "source_hash": src, "hbm_bytes_per_launch": hbm_r + hbm_w,
+        rec = {"kernel": kern, "workload": wl, "source_hash": per_kernel.get(kern), "hbm_bytes_per_launch": hbm_r + hbm_w,
                "hbm_read_bytes_per_launch": hbm_r, "hbm_write_bytes_per_launch": hbm_w,
                "algorithmic_bytes_per_launch": w.bytes, "fetch_size_kib": f_kib, "write_size_kib": w_kib,
                "fetch_scale": fscale, "write_scale": wscale, "avg_duration_ns": float(trace_row["AverageNs"]),
@@ -378,7 +393,8 @@ def rowsum_bench(args, w, torch, tsm):
                      "algorithmic_bytes_per_launch": w.bytes, "algorithmic_flops_per_launch": w.flops},
         "cpu_baseline": {"value": w.bytes / cpu_s / 1e9, "unit": "GB/s", "cores": orc.threads(), "kind": "oracle",
                          "sample": f"all {w.R} rows, {cpu_s:.2f} s"},
-        "kernel_source_hash": kernel_source_hash(), "argv": sys.argv[1:],
+        "kernel_source_hash": kernel_source_hash(), "kernel_source_hashes": {kernel: kernel_source_hash(kernel)},
+        "argv": sys.argv[1:],
     }
 
 
@@ -488,6 +504,7 @@ def main():
         "check": check,
         "roofline": roof,
         "kernel_source_hash": kernel_source_hash(),
+        "kernel_source_hashes": {s.kernel: kernel_source_hash(s.kernel)},
         "argv": sys.argv[1:],
     }
     if s.rows is not None:
@@ -518,6 +535,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": gbs2, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs2 / HBM_PEAK_GBS, "traffic": traffic_from_profiles(w2.name, s2.kernel)},
         }
+        result["kernel_source_hashes"][s2.kernel] = kernel_source_hash(s2.kernel)
         log(f"secondary {w2.name}: {ms2:.4f} ms, {gbs2:.0f} GB/s")
         del s2
 
