@@ -240,6 +240,17 @@ def test_skinny_forced_width(monkeypatch):
 W0 = 0x7F4000000000  # fake device address of a workspace
 
 
+def test_general_kernel_leading_dimension_limit():
+    """The general kernel addresses operand slices with 32-bit offsets: a leading dimension of 2^23 elements or
+    more is reported, not truncated."""
+    B0 = 0x7E0000000000
+    big = 1 << 23
+    with pytest.raises(tsm.TsmError) as ei:
+        tsm.gemm_ex(100, 100, 100, A0, big, 0, B0, 100, 0, C0, 100, 0, 0)
+    assert ei.value.status == 2 and "general kernel" in ei.value.detail
+    assert tsm.tsm_gemm_kernel_name(100, 100, 100, A0, big - 8, 0, 0, B0, 100, 0, 0, C0, 100, 0, 1, 0) is not None
+
+
 def test_workspace_bytes():
     """The K split's workspace depends on the shape only: batch * chunks * M * N * 4 bytes, or 0."""
     assert tsm.gemm_workspace_bytes(256, 256, 8192, 1) == 16 * 256 * 256 * 4  # sixteen 512-deep chunks

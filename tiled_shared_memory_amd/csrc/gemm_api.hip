@@ -278,6 +278,13 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
     out->kernel = want;
     out->forced = true;
   }
+  // the masked kernels address each 32-deep operand slice with 32-bit
+  // offsets from its corner: up to 127 rows of a leading dimension
+  const bool masked = out->kernel == Kernel::Masked8 || out->kernel == Kernel::Masked1 ||
+                      out->kernel == Kernel::Small8 || out->kernel == Kernel::Small1;
+  if (masked && K > 0 && (lda >= MaskedInfo::kMaxLd || ldb >= MaskedInfo::kMaxLd))
+    return fail(TSM_ERROR_NOT_SUPPORTED, "lda=%lld or ldb=%lld >= %lld on the general kernel", (long long)lda,
+                (long long)ldb, (long long)MaskedInfo::kMaxLd);
   return TSM_SUCCESS;
 }
 

@@ -65,6 +65,9 @@ constexpr int64_t kMaxGridY = 65535;
 // operands; vec = 1 accepts anything 2-byte aligned.
 struct MaskedInfo {
   static constexpr int BM = 128, BN = 128, BK = 32, THREADS = 256;
+  // largest leading dimension (elements, exclusive): a slice spans at most
+  // 127 of them plus 32 elements, below 2^30 bytes
+  static constexpr int64_t kMaxLd = (int64_t)1 << 23;
 };
 // tile: 128 (128 x 128) or 64 (64 x 64, for problems with few 128-tiles).
 hipError_t launch_masked(const Problem &p, int vec, int tile, hipStream_t stream);

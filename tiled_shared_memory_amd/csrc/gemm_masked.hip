@@ -38,6 +38,7 @@ namespace tsm {
 namespace {
 
 constexpr int BK = MaskedInfo::BK;
+constexpr uint32_t kOutside = 0x80000000u;  // a per-lane offset past every buffer resource
 constexpr int THREADS = MaskedInfo::THREADS;
 constexpr int PITCH = BK + 8;  // LDS row pitch in 16-bit elements (80 bytes)
 
@@ -52,31 +53,42 @@ struct Stage {
 // Fetch the OUTER x BK slice starting at (o0, k0) of an operand.
 //   KMAJ: element (o, k) at X[o*ld + k]   (K contiguous)
 //  !KMAJ: element (o, k) at X[k*ld + o]   (outer contiguous)
+// Buffer loads relative to the slice's corner, with 32-bit offsets (the host
+// keeps a slice's span below 1 GiB): elements outside the matrix get an
+// offset past the buffer resource and load as zero, without a branch.
 template <int T, bool KMAJ, int VEC>
 __device__ __forceinline__ void fetch(Stage<T, VEC> &st, const uint16_t *X, int64_t ld, int64_t outer_total,
                                       int64_t K, int64_t o0, int64_t k0, int tid) {
+  const uint16_t *corner = X + (KMAJ ? o0 * ld + k0 : k0 * ld + o0);
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(corner), (short)0, 0x7fffffff, 0x00020000);
+  // rows (outer) and k still inside the matrix from the corner (clamped to the slice)
+  const int o_left = (int)(outer_total - o0 < T ? outer_total - o0 : T);
+  const int k_left = (int)(K - k0 < BK ? K - k0 : BK);
+  // load r of a thread covers (o, k) = (o_t + r * o_step, k_t) (KMAJ) or
+  // (o_t, k_t + r * k_step): its offset advances by a fixed stride, kept in a
+  // vector register (hoisting one scalar product per load would run the
+  // 128-tile element-load kernels out of scalar registers)
+  constexpr int PER_ROW = KMAJ ? BK / VEC : T / VEC;  // vectors per row of the contiguous dimension
+  constexpr int STEP = THREADS / PER_ROW;             // rows advanced per load
+  const int row_t = tid / PER_ROW, col_t = (tid % PER_ROW) * VEC;
+  const int o_t = KMAJ ? row_t : col_t, k_t = KMAJ ? col_t : row_t;
+  uint32_t stride;
+  asm("v_mov_b32 %0, %1" : "=v"(stride) : "s"((uint32_t)(STEP * ld * 2)));
+  uint32_t off = (KMAJ ? (uint32_t)o_t * (uint32_t)ld + (uint32_t)k_t : (uint32_t)k_t * (uint32_t)ld + (uint32_t)o_t) * 2u;
 #pragma unroll
-  for (int r = 0; r < Stage<T, VEC>::kLoads; ++r) {
-    const int v = tid + r * THREADS;
-    int o, k;
-    if constexpr (KMAJ) {
-      constexpr int PER_ROW = BK / VEC;  // vectors per outer row
-      o = v / PER_ROW;
-      k = (v % PER_ROW) * VEC;
-    } else {
-      constexpr int PER_ROW = T / VEC;  // vectors per k row
-      k = v / PER_ROW;
-      o = (v % PER_ROW) * VEC;
-    }
-    const int64_t go = o0 + o, gk = k0 + k;
+  for (int r = 0; r < Stage<T, VEC>::kLoads; ++r, off += stride) {
     // With VEC = 8 the host guarantees the contiguous extent is a multiple of 8,
     // so a vector is either wholly inside or wholly outside the matrix.
-    const bool ok = go < outer_total && gk < K;
-    const int64_t off = KMAJ ? go * ld + gk : gk * ld + go;
+    // outside the matrix: set bit 31 of the offset (past the resource), in
+    // arithmetic rather than with a per-load lane mask
+    const int o = KMAJ ? o_t + r * STEP : o_t, k = KMAJ ? k_t : k_t + r * STEP;
+    const uint32_t outside = ((uint32_t)(o_left - 1 - o) | (uint32_t)(k_left - 1 - k)) & kOutside;
+    const uint32_t voff = off | outside;
     if constexpr (VEC == 8) {
-      st.v[r] = ok ? *reinterpret_cast<const u32x4 *>(X + off) : u32x4{0, 0, 0, 0};
+      st.v[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, 0, 0));
     } else {
-      st.v[r] = ok ? X[off] : (uint16_t)0;
+      st.v[r] = __builtin_amdgcn_raw_buffer_load_b16(rsrc, voff, 0, 0);
     }
   }
 }
