@@ -42,6 +42,13 @@ constexpr uint32_t kOutside = 0x80000000u;  // a per-lane offset past every buff
 constexpr int THREADS = MaskedInfo::THREADS;
 constexpr int PITCH = BK + 8;  // LDS row pitch in 16-bit elements (80 bytes)
 
+// Slices in flight in registers (even: the LDS buffers alternate): four, or
+// two for 128-tiles of single-element loads (32 staging registers a slice).
+template <int T, int VEC>
+constexpr int depth() {
+  return (T == 128 && VEC == 1) ? 2 : 4;
+}
+
 // Staging registers for one operand tile (T x BK elements).
 template <int T, int VEC>
 struct Stage {
@@ -148,44 +155,58 @@ __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
 
+  // Software pipeline: registers hold the next D slices in flight while LDS
+  // holds the current one (double-buffered), so a slice's loads have D slices
+  // of work to land behind instead of one.  The loop runs whole rounds of D
+  // slices; slices past K load as zeros (no memory access) and add nothing.
+  constexpr int D = depth<T, VEC>();
   const int64_t nk = (p.K + BK - 1) / BK;
-  Stage<T, VEC> ra, rb;
+  Stage<T, VEC> ra[D], rb[D];
   if (nk > 0) {
-    fetch<T, A_KMAJ, VEC>(ra, A, p.lda, M, p.K, m0, 0, tid);
-    fetch<T, B_KMAJ, VEC>(rb, B, p.ldb, p.N, p.K, n0, 0, tid);
-    commit<T, A_KMAJ, VEC>(ra, sA[0], tid);
-    commit<T, B_KMAJ, VEC>(rb, sB[0], tid);
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      fetch<T, A_KMAJ, VEC>(ra[u], A, p.lda, M, p.K, m0, u * BK, tid);
+      fetch<T, B_KMAJ, VEC>(rb[u], B, p.ldb, p.N, p.K, n0, u * BK, tid);
+    }
+    commit<T, A_KMAJ, VEC>(ra[0], sA[0], tid);
+    commit<T, B_KMAJ, VEC>(rb[0], sB[0], tid);
+    // registers then hold slices 1 .. D: slice D goes where slice 0 was
+    fetch<T, A_KMAJ, VEC>(ra[0], A, p.lda, M, p.K, m0, D * BK, tid);
+    fetch<T, B_KMAJ, VEC>(rb[0], B, p.ldb, p.N, p.K, n0, D * BK, tid);
   }
   __syncthreads();
 
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {  // next slice in flight while this one is multiplied
-      fetch<T, A_KMAJ, VEC>(ra, A, p.lda, M, p.K, m0, (kt + 1) * BK, tid);
-      fetch<T, B_KMAJ, VEC>(rb, B, p.ldb, p.N, p.K, n0, (kt + 1) * BK, tid);
-    }
-    const uint16_t *a_s = sA[cur];
-    const uint16_t *b_s = sB[cur];
+  // at slice t: LDS buffer t % 2 holds slice t, registers slices t+1 .. t+D
+  for (int64_t kt = 0; kt < nk; kt += D) {
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int kk = ks * 16 + (lane >> 5) * 8;
-      u32x4 af[NB], bf[NB];
+    for (int u = 0; u < D; ++u) {  // slice kt + u (D is even, so its buffer is u % 2)
+      const uint16_t *a_s = sA[u & 1];
+      const uint16_t *b_s = sB[u & 1];
 #pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        af[i] = *reinterpret_cast<const u32x4 *>(a_s + (wm * W + i * 32 + (lane & 31)) * PITCH + kk);
-        bf[i] = *reinterpret_cast<const u32x4 *>(b_s + (wn * W + i * 32 + (lane & 31)) * PITCH + kk);
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        const int kk = ks * 16 + (lane >> 5) * 8;
+        u32x4 af[NB], bf[NB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          af[i] = *reinterpret_cast<const u32x4 *>(a_s + (wm * W + i * 32 + (lane & 31)) * PITCH + kk);
+          bf[i] = *reinterpret_cast<const u32x4 *>(b_s + (wn * W + i * 32 + (lane & 31)) * PITCH + kk);
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+          for (int j = 0; j < NB; ++j) acc[i][j] = mfma_32x32x16<BF16>(af[i], bf[j], acc[i][j]);
       }
-#pragma unroll
-      for (int i = 0; i < NB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = mfma_32x32x16<BF16>(af[i], bf[j], acc[i][j]);
+      // slice kt+u+1 (fetched D slices ago) into the other LDS buffer, whose
+      // last readers passed the previous barrier; then refill its registers
+      // with slice kt+u+1+D
+      const int nx = (u + 1) % D;  // a constant once the loop is unrolled
+      commit<T, A_KMAJ, VEC>(ra[nx], sA[(u + 1) & 1], tid);
+      commit<T, B_KMAJ, VEC>(rb[nx], sB[(u + 1) & 1], tid);
+      const int64_t kf = (kt + u + 1 + D) * BK;
+      fetch<T, A_KMAJ, VEC>(ra[nx], A, p.lda, M, p.K, m0, kf, tid);
+      fetch<T, B_KMAJ, VEC>(rb[nx], B, p.ldb, p.N, p.K, n0, kf, tid);
+      __syncthreads();
     }
-    if (more) {
-      commit<T, A_KMAJ, VEC>(ra, sA[cur ^ 1], tid);
-      commit<T, B_KMAJ, VEC>(rb, sB[cur ^ 1], tid);
-    }
-    __syncthreads();
   }
 
   void *C = OUT16 ? (void *)((uint16_t *)p.C + z * p.sC) : (void *)((float *)p.C + z * p.sC);
