@@ -165,22 +165,25 @@ def test_kernel_selection_by_layout_and_shape():
 
 
 def test_mid_size_selection():
-    """Below 256 tiles the 256 x 256 kernels still win: with row-major B from 32 tiles (9 once K >= 4096), with
-    K-contiguous B from 128 tiles (48 once K >= 2048)."""
+    """Below 256 tiles the 256 x 256 kernels still win from 32 tiles when an operand must be transposed (row-major
+    B, column-major A) and from 128 tiles with both operands K-contiguous; below that the masked kernels (64 x 64
+    tiles under 144 tiles of 128 x 128), and split-K under 16 tiles of 128 x 128."""
     B0 = 0x7E0000000000
 
     def pick(n, K, lb, m=None):
         m = m or n
         return tsm.tsm_gemm_kernel_name(m, n, K, A0, K, 0, 0, B0, K if lb else n, lb, 0, C0, n, 0, 1, 3)
 
-    assert pick(2048, 8192, 1) == "tile_256x256x64_mi16"  # 64 tiles
-    assert pick(2048, 1024, 1).startswith("masked_")  # 64 tiles, shallow
     assert pick(3072, 1024, 1) == "tile_256x256x64_mi16"  # 144 tiles
-    assert pick(1536, 8192, 1).startswith("masked_64x64")  # 36 tiles
-    assert pick(768, 8192, 0) == "tile_256x256x32_mi16_nn"  # 9 tiles, deep
-    assert not pick(768, 2048, 0).startswith("tile_")  # 9 tiles, shallow
+    assert pick(2048, 8192, 1) == "masked_128x128x32_vec8"  # 64 tiles, 256 of 128 x 128
+    assert pick(1536, 8192, 1) == "masked_128x128x32_vec8"  # 144 of 128 x 128
+    assert pick(1024, 8192, 1) == "masked_64x64x32_vec8"  # 64 of 128 x 128
+    assert pick(1536, 8192, 0) == "tile_256x256x32_mi16_nn"  # 36 tiles
+    assert pick(1024, 8192, 0) == "masked_64x64x32_vec8"  # 16 tiles
     assert pick(4096, 4096, 0, m=512) == "tile_256x256x32_mi16_nn"  # 32 tiles
-    assert pick(3072, 8192, 0) == "tile_256x256x32_mi16_nn"
+    assert pick(384, 8192, 1) == "splitk_16x16_w16_t"  # 9 of 128 x 128
+    assert pick(384, 8192, 0) == "splitk_16x16_w16"
+    assert pick(640, 8192, 0) == "masked_64x64x32_vec8"  # 25 of 128 x 128
     # column-major A (M-contiguous): the transposing variants
     n, K = 2048, 8192
     for lb, name in ((0, "tile_256x256x32_mi16_tn"), (1, "tile_256x256x32_mi16_tt")):

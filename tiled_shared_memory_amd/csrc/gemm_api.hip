@@ -208,27 +208,28 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
   const bool a8 = K == 0 || vec8_ok(A, p.a_col ? M : K, lda, p.sA, batch);
   const bool b8 = K == 0 || vec8_ok(B, p.b_col ? K : N, ldb, p.sB, batch);
   out->kernel = (a8 && b8) ? Kernel::Masked8 : Kernel::Masked1;
-  // few output tiles and deep K: take the parallelism from K
   const int64_t masked_tiles = tiles * batch;
-  // few 128 x 128 tiles otherwise: 64 x 64 tiles, four times the workgroups
-  if (masked_tiles < 256) out->kernel = (a8 && b8) ? Kernel::Small8 : Kernel::Small1;
-  // split-K reads B in 16-column pieces, 64-byte rows when B is K-contiguous
-  // (then it loses to the 64 x 64 masked tiles from 48 tiles of 128 x 128:
-  // 1024 x 1024 x 8192 took 144 us against 96 us) and 32-byte rows when B is
-  // row-major (where the masked kernel is slow too)
-  const bool splitk_ok = K > 0 && masked_tiles < (p.b_col ? 48 : 256) && splitk_supports(p);
-  if (splitk_ok) out->kernel = Kernel::SplitK;
+  // fewer than 144 tiles of 128 x 128: 64 x 64 tiles, four times the
+  // workgroups (measured: 128 tiles 36 us against 43; 144 tiles 99 against 83)
+  if (masked_tiles < 144) out->kernel = (a8 && b8) ? Kernel::Small8 : Kernel::Small1;
+  // few output tiles and deep K: take the parallelism from K.  The 64 x 64
+  // masked tiles walk K at a fixed pace per workgroup (about 38 us for 8192
+  // with K-contiguous B, 80 us with row-major B, for any grid below the CU
+  // count), split-K at about 70-120 TFLOP/s: split-K up to 16 such tiles
+  // (512 x 512; 256 x 256 x 8192 takes 9.3 us against 38)
+  const bool splitk_ok = K > 0 && splitk_supports(p);
+  if (splitk_ok && masked_tiles <= 16) out->kernel = Kernel::SplitK;
   // The 256 x 256 kernels take about the same time per round of up to 256
   // tiles (one workgroup per CU) whatever the tile count, about 8 TFLOP/s
-  // per tile, plus a fixed start-up that weighs more at small K.  Measured on
-  // squares and rectangles from 512 to 4096 with K from 512 to 8192, they
-  // overtake the masked kernels (which transpose a row-major B element by
-  // element into LDS) from 32 tiles with row-major B (9 tiles once K >= 4096),
-  // and from 128 tiles with K-contiguous B (48 tiles once K >= 2048).
+  // per tile.  Measured on squares and rectangles from 512 to 4096 with K
+  // from 512 to 8192, they overtake the masked kernels from 32 tiles when an
+  // operand must be transposed (row-major B, column-major A: the masked
+  // kernels write those into LDS element by element) and from 128 tiles with
+  // both operands K-contiguous.
   const int64_t tiles256 =
       ((M + TileInfo::BM - 1) / TileInfo::BM) * ((N + TileInfo::BN - 1) / TileInfo::BN) * batch;
-  const bool tile_col = tiles256 >= 128 || (tiles256 >= 48 && K >= 2048);
-  const bool tile_row = tiles256 >= 32 || (tiles256 >= 9 && K >= 4096);
+  const bool tile_col = tiles256 >= 128;
+  const bool tile_row = tiles256 >= 32;
   if (K > 0 && tile_col && tile_supports(p, false, false)) out->kernel = Kernel::TileW;
   if (K > 0 && tile_row && tile_supports(p, false, true)) out->kernel = Kernel::Tile16NN;
   // column-major A: the masked kernels transpose it element by element, like a row-major B
@@ -242,7 +243,7 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
   if (K > 0) {
     const SkinnyPlan sp = skinny_plan(p);
     const bool narrow = sp.mb && (N / sp.w) * batch * ((M + 15) / 16) < 128;
-    if (sp.mb) out->kernel = narrow && splitk_ok ? Kernel::SplitK : Kernel::Skinny;
+    if (sp.mb) out->kernel = narrow && splitk_ok && masked_tiles < 256 ? Kernel::SplitK : Kernel::Skinny;
   }
 
   // TSM_GEMM_KERNEL=<name> forces a kernel variant (tests and tuning); a
