@@ -18,10 +18,13 @@
 // sum); the masked K loop of the Intel XPU Triton README ("Use Tensor
 // Descriptors ...", the pointer-based loop) zero-fills the same way.
 //
-// LDS layout: both operand tiles are stored K-contiguous, [outer][BK + 8]
-// 16-bit elements (row pitch 80 bytes, so every 16-byte fragment read stays
-// aligned and consecutive rows start on different banks).  An operand that is
-// contiguous along M or N is transposed element by element on its way into LDS.
+// LDS layout: an operand contiguous along K is stored as it comes, [outer][BK
+// + 8] 16-bit elements (row pitch 80 bytes, so every 16-byte fragment read
+// stays aligned and consecutive rows start on different banks).  An operand
+// contiguous along M or N (row-major B, column-major A) is also stored as it
+// comes, [BK][T] with its 16-byte chunks XOR-swizzled by the k row, and
+// ds_read_b64_tr_b16 transposes it on the way out of LDS into the
+// 8-consecutive-k fragments of v_mfma_f32_32x32x16.
 //
 // Compute: 4 waves in a 2 x 2 grid, each owning (T/2) x (T/2) of the tile as
 // blocks of v_mfma_f32_32x32x16 (2 x 2 blocks, 64 accumulator registers per
@@ -41,6 +44,38 @@ constexpr int BK = MaskedInfo::BK;
 constexpr uint32_t kOutside = 0x80000000u;  // a per-lane offset past every buffer resource
 constexpr int THREADS = MaskedInfo::THREADS;
 constexpr int PITCH = BK + 8;  // LDS row pitch in 16-bit elements (80 bytes)
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Byte offset of element (k, o) in a [BK][T] tile contiguous along o.  The
+// 16-byte chunk index is XORed with the row: the transposing reads of one
+// half-wave cover 4 rows x 64 bytes, which then fall on 64 distinct banks
+// (rows of 128 bytes sit 32 banks apart, rows of 256 bytes on the same ones).
+template <int T>
+__device__ __forceinline__ int omaj_off(int k, int o) {
+  constexpr int SW = T == 64 ? 2 : 4;
+  return k * (T * 2) + (((o >> 3) ^ (SW * (k & 3))) << 4) + (o & 7) * 2;
+}
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane j gives the address of
+// 4 elements (row j / 4 of a 4 x 16 block) and receives column j of the block.
+__device__ __forceinline__ u32x2 read_tr(const char *p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(lds_char *)p));
+}
+
+// The 32x32x16 operand of block column cb from a [BK][T] tile: lane holds
+// k = 16 ks + 8 (lane / 32) .. +7 of column cb + lane % 32, read as two 4-row
+// transposes.
+template <int T>
+__device__ __forceinline__ u32x4 read_omaj(const uint16_t *s, int cb, int ks, int lane) {
+  const int o = cb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int k = ks * 16 + 8 * (lane >> 5) + ((lane & 15) >> 2);
+  const u32x2 lo = read_tr(reinterpret_cast<const char *>(s) + omaj_off<T>(k, o));
+  const u32x2 hi = read_tr(reinterpret_cast<const char *>(s) + omaj_off<T>(k + 4, o));
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
 
 // Slices in flight in registers (even: the LDS buffers alternate): four, or
 // two for 128-tiles of single-element loads (32 staging registers a slice).
@@ -100,7 +135,8 @@ __device__ __forceinline__ void fetch(Stage<T, VEC> &st, const uint16_t *X, int6
   }
 }
 
-// Write the staged slice into an LDS tile laid out [outer][PITCH], K contiguous.
+// Write the staged slice into its LDS tile: [outer][PITCH] when K is the
+// contiguous dimension, [BK][T] (swizzled) otherwise.
 template <int T, bool KMAJ, int VEC>
 __device__ __forceinline__ void commit(const Stage<T, VEC> &st, uint16_t *s, int tid) {
 #pragma unroll
@@ -116,13 +152,11 @@ __device__ __forceinline__ void commit(const Stage<T, VEC> &st, uint16_t *s, int
     } else {
       constexpr int PER_ROW = T / VEC;
       const int k = v / PER_ROW, o = (v % PER_ROW) * VEC;
-      if constexpr (VEC == 8) {
-        const u32x4 w = st.v[r];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s[(o + e) * PITCH + k] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-      } else {
-        s[o * PITCH + k] = st.v[r];
-      }
+      char *at = reinterpret_cast<char *>(s) + omaj_off<T>(k, o);
+      if constexpr (VEC == 8)
+        *reinterpret_cast<u32x4 *>(at) = st.v[r];
+      else
+        *reinterpret_cast<uint16_t *>(at) = st.v[r];
     }
   }
 }
@@ -131,6 +165,7 @@ template <int T, bool BF16, bool OUT16, bool A_KMAJ, bool B_KMAJ, int VEC>
 __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
   constexpr int W = T / 2;    // wave tile
   constexpr int NB = W / 32;  // 32 x 32 MFMA blocks per wave and dimension
+  static_assert(BK * T <= T * PITCH, "a [BK][T] tile fits the buffer of a [T][PITCH] one");
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][T * PITCH];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][T * PITCH];
 
@@ -188,8 +223,14 @@ __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
         u32x4 af[NB], bf[NB];
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-          af[i] = *reinterpret_cast<const u32x4 *>(a_s + (wm * W + i * 32 + (lane & 31)) * PITCH + kk);
-          bf[i] = *reinterpret_cast<const u32x4 *>(b_s + (wn * W + i * 32 + (lane & 31)) * PITCH + kk);
+          if constexpr (A_KMAJ)
+            af[i] = *reinterpret_cast<const u32x4 *>(a_s + (wm * W + i * 32 + (lane & 31)) * PITCH + kk);
+          else
+            af[i] = read_omaj<T>(a_s, wm * W + i * 32, ks, lane);
+          if constexpr (B_KMAJ)
+            bf[i] = *reinterpret_cast<const u32x4 *>(b_s + (wn * W + i * 32 + (lane & 31)) * PITCH + kk);
+          else
+            bf[i] = read_omaj<T>(b_s, wn * W + i * 32, ks, lane);
         }
 #pragma unroll
         for (int i = 0; i < NB; ++i)
