@@ -138,7 +138,7 @@ def test_kernel_selection_for_the_workloads():
                                                w.batch, code)
         assert picks[name] is not None, name
     # the ragged workload has K = 777, so rows of A are only 2-byte aligned
-    assert picks["ragged_f16_1000x1500x777"].endswith("vec1")
+    assert picks["ragged_f16_1000x1500x777"].endswith("vecu")
 
 
 def test_kernel_selection_by_layout_and_shape():
@@ -165,9 +165,9 @@ def test_kernel_selection_by_layout_and_shape():
 
 
 def test_mid_size_selection():
-    """Below 256 tiles the 256 x 256 kernels still win from 32 tiles when an operand must be transposed (row-major
-    B, column-major A) and from 128 tiles with both operands K-contiguous; below that the masked kernels (64 x 64
-    tiles under 144 tiles of 128 x 128), and split-K under 16 tiles of 128 x 128."""
+    """The 256 x 256 kernels from 128 tiles (96 once K >= 4096), whatever the layouts; below that the masked
+    kernels (64 x 64 tiles under 256 tiles of 128 x 128), and split-K up to 9 such tiles with K-contiguous B, 4
+    with row-major B."""
     B0 = 0x7E0000000000
 
     def pick(n, K, lb, m=None):
@@ -175,22 +175,23 @@ def test_mid_size_selection():
         return tsm.tsm_gemm_kernel_name(m, n, K, A0, K, 0, 0, B0, K if lb else n, lb, 0, C0, n, 0, 1, 3)
 
     assert pick(3072, 1024, 1) == "tile_256x256x64_mi16"  # 144 tiles
+    assert pick(3072, 1024, 0) == "tile_256x256x32_mi16_nn"
+    assert pick(2560, 8192, 0) == "tile_256x256x32_mi16_nn"  # 100 tiles, deep K
+    assert pick(2560, 2048, 0) == "masked_128x128x32_vec8"  # 100 tiles, 400 of 128 x 128
     assert pick(2048, 8192, 1) == "masked_128x128x32_vec8"  # 64 tiles, 256 of 128 x 128
-    assert pick(1536, 8192, 1) == "masked_128x128x32_vec8"  # 144 of 128 x 128
-    assert pick(1024, 8192, 1) == "masked_64x64x32_vec8"  # 64 of 128 x 128
-    assert pick(1536, 8192, 0) == "tile_256x256x32_mi16_nn"  # 36 tiles
-    assert pick(1024, 8192, 0) == "masked_64x64x32_vec8"  # 16 tiles
-    assert pick(4096, 4096, 0, m=512) == "tile_256x256x32_mi16_nn"  # 32 tiles
+    assert pick(2048, 8192, 0) == "masked_128x128x32_vec8"
+    assert pick(1536, 8192, 1) == "masked_64x64x64_vec8"  # 144 of 128 x 128
+    assert pick(1024, 8192, 0) == "masked_64x64x64_vec8"
     assert pick(384, 8192, 1) == "splitk_16x16_w16_t"  # 9 of 128 x 128
-    assert pick(384, 8192, 0) == "splitk_16x16_w16"
-    assert pick(640, 8192, 0) == "masked_64x64x32_vec8"  # 25 of 128 x 128
+    assert pick(512, 8192, 1) == "masked_64x64x64_vec8"  # 16
+    assert pick(256, 8192, 0) == "splitk_16x16_w16"  # 4
+    assert pick(384, 8192, 0) == "masked_64x64x64_vec8"  # 9
     # column-major A (M-contiguous): the transposing variants
-    n, K = 2048, 8192
+    n, K = 3072, 8192
     for lb, name in ((0, "tile_256x256x32_mi16_tn"), (1, "tile_256x256x32_mi16_tt")):
         assert tsm.tsm_gemm_kernel_name(n, n, K, A0, n, 1, 0, B0, K if lb else n, lb, 0, C0, n, 0, 1, 3) == name
     # M not a multiple of 8: the general kernel
     assert tsm.tsm_gemm_kernel_name(n - 4, n, K, A0, n, 1, 0, B0, n, 0, 0, C0, n, 0, 1, 3).startswith("masked_")
-    assert pick(512, 8192, 0).startswith("splitk_")  # 4 tiles
 
 
 def test_skinny_selection():
@@ -291,8 +292,8 @@ def test_workspace_routing(monkeypatch):
     # too little workspace, none or a forced kernel: the kernel that needs none
     assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(nbytes=16 * 256 * 256 * 4 - 4)).startswith("splitk_")
     assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(ws=0, nbytes=0)).startswith("splitk_")
-    monkeypatch.setenv("TSM_GEMM_KERNEL", "masked_64x64x32_vec8")
-    assert tsm.tsm_gemm_ws_kernel_name(*_ws_args()) == "masked_64x64x32_vec8"
+    monkeypatch.setenv("TSM_GEMM_KERNEL", "masked_64x64x64_vec8")
+    assert tsm.tsm_gemm_ws_kernel_name(*_ws_args()) == "masked_64x64x64_vec8"
 
 
 @pytest.mark.parametrize("kw,needle", [

@@ -18,10 +18,10 @@ pytestmark = pytest.mark.gpu
 
 # (kernel, shape M x N x K x batch, A layout, B layout) that the kernel accepts
 FAMILIES = [
-    ("masked_128x128x32_vec1", (130, 257, 100, 2), "col", "row"),
+    ("masked_128x128x32_vecu", (130, 257, 100, 2), "col", "row"),
     ("masked_128x128x32_vec8", (200, 136, 96, 1), "row", "col"),
-    ("masked_64x64x32_vec1", (65, 63, 33, 3), "row", "row"),
-    ("masked_64x64x32_vec8", (72, 80, 64, 1), "col", "col"),
+    ("masked_64x64x64_vecu", (65, 63, 33, 3), "row", "row"),
+    ("masked_64x64x64_vec8", (72, 80, 64, 1), "col", "col"),
     ("tile_256x256x64_mi16", (600, 512, 256, 2), "row", "col"),
     ("tile_256x256x32_mi16", (256, 512, 384, 1), "row", "col"),
     ("tile_256x256x32_mi32", (256, 256, 128, 1), "row", "col"),

@@ -86,8 +86,8 @@ EDGE_SHAPES = [(1, 1, 1), (1, 2, 3), (2, 3, 1), (3, 1, 2), (15, 17, 16), (16, 16
                (255, 1, 64), (1, 300, 257), (64, 128, 128), (200, 8, 8), (8, 200, 1000)]
 
 
-MASKED_VARIANTS = ["masked_128x128x32_vec1", "masked_64x64x32_vec1", "masked_128x128x32_vec8",
-                   "masked_64x64x32_vec8"]
+MASKED_VARIANTS = ["masked_128x128x32_vecu", "masked_64x64x64_vecu", "masked_128x128x32_vec8",
+                   "masked_64x64x64_vec8"]
 
 
 @pytest.mark.parametrize("variant", MASKED_VARIANTS)

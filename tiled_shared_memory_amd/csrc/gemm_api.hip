@@ -44,7 +44,7 @@ bool ranges_overlap(const void *p, int64_t pbytes, const void *q, int64_t qbytes
 }
 
 enum class Kernel {
-  None, Masked8, Masked1, Small8, Small1, Tile32, Tile16, Tile16NN, TileW, TileWNN, Tile16TN, Tile16TT, TileWTT, Skinny,
+  None, Masked8, MaskedU, Small8, SmallU, Tile32, Tile16, Tile16NN, TileW, TileWNN, Tile16TN, Tile16TT, TileWTT, Skinny,
   SplitK
 };
 
@@ -52,11 +52,11 @@ const char *kernel_name(Kernel k, const Problem &p) {
   switch (k) {
     case Kernel::Masked8:
       return masked_name(8, 128);
-    case Kernel::Masked1:
+    case Kernel::MaskedU:
       return masked_name(1, 128);
     case Kernel::Small8:
       return masked_name(8, 64);
-    case Kernel::Small1:
+    case Kernel::SmallU:
       return masked_name(1, 64);
     case Kernel::Tile32:
       return tile_name(0);
@@ -207,34 +207,35 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
     return fail(TSM_ERROR_NOT_SUPPORTED, "tile grid too large (%lld tiles)", (long long)tiles);
   const bool a8 = K == 0 || vec8_ok(A, p.a_col ? M : K, lda, p.sA, batch);
   const bool b8 = K == 0 || vec8_ok(B, p.b_col ? K : N, ldb, p.sB, batch);
-  out->kernel = (a8 && b8) ? Kernel::Masked8 : Kernel::Masked1;
+  out->kernel = (a8 && b8) ? Kernel::Masked8 : Kernel::MaskedU;
   const int64_t masked_tiles = tiles * batch;
-  // fewer than 144 tiles of 128 x 128: 64 x 64 tiles, four times the
-  // workgroups (measured: 128 tiles 36 us against 43; 144 tiles 99 against 83)
-  if (masked_tiles < 144) out->kernel = (a8 && b8) ? Kernel::Small8 : Kernel::Small1;
+  // fewer than 256 tiles of 128 x 128 (one round of workgroups): 64 x 64
+  // tiles, four times the workgroups (1536 x 1536 x 2048: 25 us against 28;
+  // 2048 x 2048 x 2048: 35 against 31)
+  if (masked_tiles < 256) out->kernel = (a8 && b8) ? Kernel::Small8 : Kernel::SmallU;
   // few output tiles and deep K: take the parallelism from K.  The 64 x 64
-  // masked tiles walk K at a fixed pace per workgroup (about 38 us for 8192
-  // with K-contiguous B, 80 us with row-major B, for any grid below the CU
-  // count), split-K at about 70-120 TFLOP/s: split-K up to 16 such tiles
-  // (512 x 512; 256 x 256 x 8192 takes 9.3 us against 38)
+  // masked tiles walk K at a fixed pace per workgroup for any grid below the
+  // CU count (about 36 us for K = 8192 with K-contiguous B, 40 us with
+  // row-major B); split-K beats that up to 9 such tiles with K-contiguous B
+  // (384 x 384 x 8192: 27 us against 36) and up to 4 with row-major B, whose
+  // 16-column slices it reads as 32-byte rows (256 x 256 x 8192: 16 us
+  // against 41; 384 x 384: 47 against 40)
   const bool splitk_ok = K > 0 && splitk_supports(p);
-  if (splitk_ok && masked_tiles <= 16) out->kernel = Kernel::SplitK;
+  if (splitk_ok && masked_tiles <= (p.b_col ? 9 : 4)) out->kernel = Kernel::SplitK;
   // The 256 x 256 kernels take about the same time per round of up to 256
   // tiles (one workgroup per CU) whatever the tile count, about 8 TFLOP/s
-  // per tile.  Measured on squares and rectangles from 512 to 4096 with K
-  // from 512 to 8192, they overtake the masked kernels from 32 tiles when an
-  // operand must be transposed (row-major B, column-major A: the masked
-  // kernels write those into LDS element by element) and from 128 tiles with
-  // both operands K-contiguous.
+  // per tile.  Measured on squares from 256 to 4096 with K from 512 to 8192
+  // and every layout, they overtake the masked kernels from 128 tiles, or
+  // from 96 once K >= 4096 (2560 x 2560 x 8192: 146 us against 167; at
+  // 2048 x 2048 x 8192, 64 tiles, the masked kernels take 93-110 us against
+  // 138-148).
   const int64_t tiles256 =
       ((M + TileInfo::BM - 1) / TileInfo::BM) * ((N + TileInfo::BN - 1) / TileInfo::BN) * batch;
-  const bool tile_col = tiles256 >= 128;
-  const bool tile_row = tiles256 >= 32;
-  if (K > 0 && tile_col && tile_supports(p, false, false)) out->kernel = Kernel::TileW;
-  if (K > 0 && tile_row && tile_supports(p, false, true)) out->kernel = Kernel::Tile16NN;
-  // column-major A: the masked kernels transpose it element by element, like a row-major B
-  if (K > 0 && tile_row && tile_supports(p, true, true)) out->kernel = Kernel::Tile16TN;
-  if (K > 0 && tile_row && tile_supports(p, true, false)) out->kernel = Kernel::Tile16TT;
+  const bool tile_ok = K > 0 && (tiles256 >= 128 || (tiles256 >= 96 && K >= 4096));
+  if (tile_ok && tile_supports(p, false, false)) out->kernel = Kernel::TileW;
+  if (tile_ok && tile_supports(p, false, true)) out->kernel = Kernel::Tile16NN;
+  if (tile_ok && tile_supports(p, true, true)) out->kernel = Kernel::Tile16TN;
+  if (tile_ok && tile_supports(p, true, false)) out->kernel = Kernel::Tile16TT;
   // up to 128 rows: the streaming kernel reads B once, where split-K reads
   // it once per 16-row tile and the 256-row tiles waste most of their MFMA
   // work.  Its rate grows with its grid (about 6.7 TB/s at 256 workgroups,
@@ -250,7 +251,7 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
   // variant that cannot run this problem is an error, never a silent fallback.
   const char *force = getenv("TSM_GEMM_KERNEL");
   if (force && *force) {
-    const Kernel all[] = {Kernel::Masked8,  Kernel::Masked1,  Kernel::Small8,   Kernel::Small1,  Kernel::Tile32,
+    const Kernel all[] = {Kernel::Masked8,  Kernel::MaskedU,  Kernel::Small8,   Kernel::SmallU,  Kernel::Tile32,
                           Kernel::Tile16,   Kernel::Tile16NN, Kernel::TileW,    Kernel::TileWNN, Kernel::Tile16TN,
                           Kernel::Tile16TT, Kernel::TileWTT,  Kernel::Skinny,   Kernel::SplitK};
     Kernel want = Kernel::None;
@@ -266,7 +267,7 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
         return fail(TSM_ERROR_NOT_SUPPORTED, "TSM_GEMM_KERNEL=%s cannot run this problem", force);
     }
     if (want == Kernel::None) return fail(TSM_ERROR_INVALID_VALUE, "TSM_GEMM_KERNEL=%s names no kernel", force);
-    const bool ok = want == Kernel::Masked1 || want == Kernel::Small1 ||
+    const bool ok = want == Kernel::MaskedU || want == Kernel::SmallU ||
                     ((want == Kernel::Masked8 || want == Kernel::Small8) && a8 && b8) ||
                     ((want == Kernel::Tile32 || want == Kernel::Tile16 || want == Kernel::TileW) && K > 0 &&
                      tile_supports(p, false, false)) ||
@@ -281,8 +282,8 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
   }
   // the masked kernels address each 32-deep operand slice with 32-bit
   // offsets from its corner: up to 127 rows of a leading dimension
-  const bool masked = out->kernel == Kernel::Masked8 || out->kernel == Kernel::Masked1 ||
-                      out->kernel == Kernel::Small8 || out->kernel == Kernel::Small1;
+  const bool masked = out->kernel == Kernel::Masked8 || out->kernel == Kernel::MaskedU ||
+                      out->kernel == Kernel::Small8 || out->kernel == Kernel::SmallU;
   if (masked && K > 0 && (lda >= MaskedInfo::kMaxLd || ldb >= MaskedInfo::kMaxLd))
     return fail(TSM_ERROR_NOT_SUPPORTED, "lda=%lld or ldb=%lld >= %lld on the general kernel", (long long)lda,
                 (long long)ldb, (long long)MaskedInfo::kMaxLd);
@@ -298,13 +299,13 @@ int run(const Plan &pl, void *stream) {
     case Kernel::Masked8:
       e = launch_masked(pl.p, 8, 128, s);
       break;
-    case Kernel::Masked1:
+    case Kernel::MaskedU:
       e = launch_masked(pl.p, 1, 128, s);
       break;
     case Kernel::Small8:
       e = launch_masked(pl.p, 8, 64, s);
       break;
-    case Kernel::Small1:
+    case Kernel::SmallU:
       e = launch_masked(pl.p, 1, 64, s);
       break;
     case Kernel::Tile32:

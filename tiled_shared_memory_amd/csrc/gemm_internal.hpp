@@ -64,12 +64,14 @@ constexpr int64_t kMaxGridY = 65535;
 // vec = 8 needs 16-byte aligned rows along the contiguous dimension of both
 // operands; vec = 1 accepts anything 2-byte aligned.
 struct MaskedInfo {
-  static constexpr int BM = 128, BN = 128, BK = 32, THREADS = 256;
+  static constexpr int BM = 128, BN = 128, THREADS = 256;  // K slices of 32 (64 on 64 x 64 tiles)
   // largest leading dimension (elements, exclusive): a slice spans at most
-  // 127 of them plus 32 elements, below 2^30 bytes
+  // 127 of them plus under 80 elements, below 2^31 bytes (bit 31 of a load's offset
+  // marks an element outside the matrix)
   static constexpr int64_t kMaxLd = (int64_t)1 << 23;
 };
-// tile: 128 (128 x 128) or 64 (64 x 64, for problems with few 128-tiles).
+// vec: 8 (16-byte aligned vectors) or any other value (vectors at any 2-byte
+// alignment); tile: 128 (128 x 128) or 64 (64 x 64, for problems with few 128-tiles).
 hipError_t launch_masked(const Problem &p, int vec, int tile, hipStream_t stream);
 const char *masked_name(int vec, int tile);
 

@@ -10,9 +10,13 @@
 // is fetched from global memory while the previous one feeds the matrix cores
 // (double-buffered LDS, one barrier per slice).
 //
-// Loads: each thread fetches `VEC` contiguous 16-bit elements of an operand
-// (VEC = 8: one 16-byte load; VEC = 1: single elements) along the operand's
-// contiguous dimension.  Elements outside M, N or K read as zero in both
+// Loads: each thread fetches vectors of 8 contiguous 16-bit elements of an
+// operand along its contiguous dimension.  VEC = 8: one 16-byte load, when the
+// base, the leading dimension, the batch stride and the contiguous extent
+// allow it.  VEC = 0 (any 2-byte alignment, e.g. rows of 777 elements): one
+// dword-aligned 16-byte load and one 4-byte load cover the vector; a 16-bit
+// funnel shift (v_alignbit_b32) realigns it and a mask clears the elements
+// past the contiguous extent.  Elements outside M, N or K read as zero in both
 // operands: "A Dumb Triton Runtime Error", Step 2 on masked loads, where the
 // padding must be the additive identity (a -inf or garbage pad would poison the
 // sum); the masked K loop of the Intel XPU Triton README ("Use Tensor
@@ -40,10 +44,22 @@
 namespace tsm {
 namespace {
 
-constexpr int BK = MaskedInfo::BK;
 constexpr uint32_t kOutside = 0x80000000u;  // a per-lane offset past every buffer resource
 constexpr int THREADS = MaskedInfo::THREADS;
-constexpr int PITCH = BK + 8;  // LDS row pitch in 16-bit elements (80 bytes)
+// K slice depth: 32 for 128-tiles, 64 for 64-tiles (whose waves have one
+// 32 x 32 block each: a deeper slice gives them twice the matrix-core work per
+// barrier).
+template <int T>
+constexpr int bk() {
+  return T == 64 ? 64 : 32;
+}
+// LDS row pitch of a K-contiguous tile, in 16-bit elements (80 or 144 bytes:
+// 16-byte aligned, and the 16 rows one 16-lane group reads fall on distinct
+// banks)
+template <int T>
+constexpr int pitch() {
+  return bk<T>() + 8;
+}
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
@@ -77,61 +93,134 @@ __device__ __forceinline__ u32x4 read_omaj(const uint16_t *s, int cb, int ks, in
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
-// Slices in flight in registers (even: the LDS buffers alternate): four, or
-// two for 128-tiles of single-element loads (32 staging registers a slice).
+// Slices in flight in registers (even: the LDS buffers alternate): 4 x 32 k
+// on 128-tiles, 2 x 64 k on 64-tiles (the same k distance ahead).
 template <int T, int VEC>
 constexpr int depth() {
-  return (T == 128 && VEC == 1) ? 2 : 4;
+  return T == 64 ? 2 : 4;
 }
 
-// Staging registers for one operand tile (T x BK elements).
+// Staging registers for one operand tile (T x BK elements): 8-element vectors,
+// and with VEC = 0 the dword after each 16-byte load, the thread's funnel
+// shift (0 or 16 bits: the stride between a thread's vectors is even, so it is
+// one for all of them) and its count of elements inside the contiguous extent
+// (the same for all of a thread's vectors too).
 template <int T, int VEC>
 struct Stage {
-  static constexpr int kLoads = (T * BK) / (THREADS * VEC);  // loads per thread
-  using Vec = typename std::conditional<VEC == 8, u32x4, uint16_t>::type;
-  Vec v[kLoads];
+  static constexpr int kLoads = (T * bk<T>()) / (THREADS * 8);  // vectors per thread
+  u32x4 v[kLoads];
+  uint32_t tail[VEC == 0 ? kLoads : 1];
+  uint32_t shift;
+  int valid;
 };
+
+// One operand of one tile, fixed for the whole K loop.
+struct Src {
+  const uint16_t *base;  // element (o0, k = 0) of the tile, one element lower when that sits at 2 mod 4 bytes
+  int64_t ld;
+  int64_t rest;          // elements from base to the operand's last element + 1 (VEC = 0)
+  int o_left;            // rows (outer) of the tile inside the matrix, at most T
+  uint32_t delta;        // 1 when base was moved down one element
+};
+
+// Slice k0 of a tile starts k0 (KMAJ) or k0 * ld (outer contiguous) elements
+// after the tile's corner: an even count (k0 is a multiple of BK), so the
+// corner's alignment, and delta, hold for every slice.
+template <int T, bool KMAJ, int VEC>
+__device__ __forceinline__ Src make_src(const uint16_t *X, int64_t ld, int64_t outer_total, int64_t K, int64_t o0) {
+  const int64_t at = KMAJ ? o0 * ld : o0;
+  const uint16_t *p = X + at;
+  const uint32_t delta = VEC == 0 ? (uint32_t)(((uintptr_t)p >> 1) & 1) : 0u;
+  // the operand's storage ends after row outer_total - 1 (K contiguous) or k row K - 1
+  const int64_t end = KMAJ ? (outer_total - 1) * ld + K : (K - 1) * ld + outer_total;
+  return Src{p - delta, ld, end - at + delta, (int)(outer_total - o0 < T ? outer_total - o0 : T), delta};
+}
+
+__device__ __forceinline__ uint32_t funnel(uint32_t hi, uint32_t lo, uint32_t shift) {
+  return __builtin_amdgcn_alignbit(hi, lo, shift);
+}
 
 // Fetch the OUTER x BK slice starting at (o0, k0) of an operand.
 //   KMAJ: element (o, k) at X[o*ld + k]   (K contiguous)
 //  !KMAJ: element (o, k) at X[k*ld + o]   (outer contiguous)
 // Buffer loads relative to the slice's corner, with 32-bit offsets (the host
-// keeps a slice's span below 1 GiB): elements outside the matrix get an
-// offset past the buffer resource and load as zero, without a branch.
+// keeps a slice's span below 2^31 bytes): elements outside the matrix get an
+// offset with bit 31 set, past the buffer resource, and load as zero without a
+// branch.
 template <int T, bool KMAJ, int VEC>
-__device__ __forceinline__ void fetch(Stage<T, VEC> &st, const uint16_t *X, int64_t ld, int64_t outer_total,
-                                      int64_t K, int64_t o0, int64_t k0, int tid) {
-  const uint16_t *corner = X + (KMAJ ? o0 * ld + k0 : k0 * ld + o0);
-  const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(corner), (short)0, 0x7fffffff, 0x00020000);
-  // rows (outer) and k still inside the matrix from the corner (clamped to the slice)
-  const int o_left = (int)(outer_total - o0 < T ? outer_total - o0 : T);
-  const int k_left = (int)(K - k0 < BK ? K - k0 : BK);
-  // load r of a thread covers (o, k) = (o_t + r * o_step, k_t) (KMAJ) or
-  // (o_t, k_t + r * k_step): its offset advances by a fixed stride, kept in a
-  // vector register (hoisting one scalar product per load would run the
-  // 128-tile element-load kernels out of scalar registers)
-  constexpr int PER_ROW = KMAJ ? BK / VEC : T / VEC;  // vectors per row of the contiguous dimension
-  constexpr int STEP = THREADS / PER_ROW;             // rows advanced per load
-  const int row_t = tid / PER_ROW, col_t = (tid % PER_ROW) * VEC;
+__device__ __forceinline__ void fetch(Stage<T, VEC> &st, const Src &src, int64_t K, int64_t k0, int tid) {
+  constexpr int BK = bk<T>();
+  const int64_t koff = KMAJ ? k0 : k0 * src.ld;
+  // VEC = 0: the resource starts at the dword holding the slice's corner and
+  // ends at the dword holding the operand's last element, so the dwords a
+  // vector's cover reads past that end load as zero instead of touching
+  // memory (the range check is per dword).  Every dword inside lies in a page
+  // the operand uses.
+  int64_t records = 0x7fffffff;
+  if constexpr (VEC == 0) {
+    const int64_t bytes = ((src.rest - koff) * 2 + 3) & ~(int64_t)3;
+    records = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
+  }
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(src.base + koff),
+                                                                        (short)0, (int)records, 0x00020000);
+  const int o_left = src.o_left;
+  const int k_left = (int)(K - k0 < BK ? K - k0 : BK);  // k still inside the matrix (clamped to the slice)
+  // vector r of a thread covers (o, k) = (o_t + r * o_step, k_t .. +7) (KMAJ)
+  // or (o_t .. +7, k_t + r * k_step): its offset advances by a fixed stride,
+  // kept in a vector register (hoisting one scalar product per load would run
+  // the 128-tile kernels out of scalar registers)
+  constexpr int PER_ROW = KMAJ ? BK / 8 : T / 8;  // vectors per row of the contiguous dimension
+  constexpr int STEP = THREADS / PER_ROW;         // rows advanced per vector (even)
+  const int row_t = tid / PER_ROW, col_t = (tid % PER_ROW) * 8;
   const int o_t = KMAJ ? row_t : col_t, k_t = KMAJ ? col_t : row_t;
+  const uint32_t ld = (uint32_t)src.ld;
   uint32_t stride;
-  asm("v_mov_b32 %0, %1" : "=v"(stride) : "s"((uint32_t)(STEP * ld * 2)));
-  uint32_t off = (KMAJ ? (uint32_t)o_t * (uint32_t)ld + (uint32_t)k_t : (uint32_t)k_t * (uint32_t)ld + (uint32_t)o_t) * 2u;
+  asm("v_mov_b32 %0, %1" : "=v"(stride) : "s"(STEP * ld * 2u));
+  uint32_t off = (KMAJ ? (uint32_t)o_t * ld + (uint32_t)k_t : (uint32_t)k_t * ld + (uint32_t)o_t);
+  off = (off + src.delta) * 2u;
+  if constexpr (VEC == 0) {
+    // the element offset's parity picks the funnel shift; the loads start at
+    // the dword below
+    st.shift = (off & 2u) * 8u;
+    off &= ~3u;
+    // elements of the vector inside the contiguous extent (K, or M / N)
+    st.valid = KMAJ ? k_left - k_t : o_left - o_t;
+  }
 #pragma unroll
   for (int r = 0; r < Stage<T, VEC>::kLoads; ++r, off += stride) {
-    // With VEC = 8 the host guarantees the contiguous extent is a multiple of 8,
-    // so a vector is either wholly inside or wholly outside the matrix.
-    // outside the matrix: set bit 31 of the offset (past the resource), in
-    // arithmetic rather than with a per-load lane mask
+    // A vector wholly outside the matrix (past the other dimension, or
+    // starting past the contiguous extent) sets bit 31 of its offsets (past the
+    // resource), in arithmetic rather than with a per-load lane mask.  With
+    // VEC = 8 the host guarantees the contiguous extent is a multiple of 8, so
+    // no vector is partly outside.
     const int o = KMAJ ? o_t + r * STEP : o_t, k = KMAJ ? k_t : k_t + r * STEP;
     const uint32_t outside = ((uint32_t)(o_left - 1 - o) | (uint32_t)(k_left - 1 - k)) & kOutside;
     const uint32_t voff = off | outside;
-    if constexpr (VEC == 8) {
-      st.v[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, 0, 0));
-    } else {
-      st.v[r] = __builtin_amdgcn_raw_buffer_load_b16(rsrc, voff, 0, 0);
+    st.v[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, 0, 0));
+    if constexpr (VEC == 0) {
+      // the fifth dword only matters when the vector is shifted
+      const uint32_t unshifted = st.shift ? 0u : kOutside;
+      st.tail[r] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (voff + 16u) | unshifted, 0, 0);
     }
+  }
+}
+
+// Vector r of a stage as 8 elements: realigned and masked for VEC = 0.
+template <int T, int VEC>
+__device__ __forceinline__ u32x4 vector_of(const Stage<T, VEC> &st, int r) {
+  if constexpr (VEC == 8) {
+    return st.v[r];
+  } else {
+    const u32x4 w = st.v[r];
+    const uint32_t s = st.shift;
+    u32x4 e{funnel(w[1], w[0], s), funnel(w[2], w[1], s), funnel(w[3], w[2], s), funnel(st.tail[r], w[3], s)};
+    // keep elements 0 .. valid-1
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t m = st.valid >= 2 * j + 2 ? 0xffffffffu : (st.valid == 2 * j + 1 ? 0x0000ffffu : 0u);
+      e[j] &= m;
+    }
+    return e;
   }
 }
 
@@ -139,24 +228,19 @@ __device__ __forceinline__ void fetch(Stage<T, VEC> &st, const uint16_t *X, int6
 // contiguous dimension, [BK][T] (swizzled) otherwise.
 template <int T, bool KMAJ, int VEC>
 __device__ __forceinline__ void commit(const Stage<T, VEC> &st, uint16_t *s, int tid) {
+  constexpr int BK = bk<T>(), PITCH = pitch<T>();
 #pragma unroll
   for (int r = 0; r < Stage<T, VEC>::kLoads; ++r) {
     const int v = tid + r * THREADS;
+    const u32x4 e = vector_of<T, VEC>(st, r);
     if constexpr (KMAJ) {
-      constexpr int PER_ROW = BK / VEC;
-      const int o = v / PER_ROW, k = (v % PER_ROW) * VEC;
-      if constexpr (VEC == 8)
-        *reinterpret_cast<u32x4 *>(s + o * PITCH + k) = st.v[r];
-      else
-        s[o * PITCH + k] = st.v[r];
+      constexpr int PER_ROW = BK / 8;
+      const int o = v / PER_ROW, k = (v % PER_ROW) * 8;
+      *reinterpret_cast<u32x4 *>(s + o * PITCH + k) = e;
     } else {
-      constexpr int PER_ROW = T / VEC;
-      const int k = v / PER_ROW, o = (v % PER_ROW) * VEC;
-      char *at = reinterpret_cast<char *>(s) + omaj_off<T>(k, o);
-      if constexpr (VEC == 8)
-        *reinterpret_cast<u32x4 *>(at) = st.v[r];
-      else
-        *reinterpret_cast<uint16_t *>(at) = st.v[r];
+      constexpr int PER_ROW = T / 8;
+      const int k = v / PER_ROW, o = (v % PER_ROW) * 8;
+      *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(s) + omaj_off<T>(k, o)) = e;
     }
   }
 }
@@ -165,6 +249,7 @@ template <int T, bool BF16, bool OUT16, bool A_KMAJ, bool B_KMAJ, int VEC>
 __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
   constexpr int W = T / 2;    // wave tile
   constexpr int NB = W / 32;  // 32 x 32 MFMA blocks per wave and dimension
+  constexpr int BK = bk<T>(), PITCH = pitch<T>();
   static_assert(BK * T <= T * PITCH, "a [BK][T] tile fits the buffer of a [T][PITCH] one");
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][T * PITCH];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][T * PITCH];
@@ -183,6 +268,8 @@ __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
   const Epilogue ep = epilogue_in_vgprs(p);  // kept out of the scalar registers the loop needs
   const uint16_t *A = p.A + z * p.sA;
   const uint16_t *B = p.B + z * p.sB;
+  const Src src_a = make_src<T, A_KMAJ, VEC>(A, p.lda, M, p.K, m0);
+  const Src src_b = make_src<T, B_KMAJ, VEC>(B, p.ldb, p.N, p.K, n0);
 
   f32x16 acc[NB][NB];
 #pragma unroll
@@ -200,14 +287,14 @@ __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
   if (nk > 0) {
 #pragma unroll
     for (int u = 0; u < D; ++u) {
-      fetch<T, A_KMAJ, VEC>(ra[u], A, p.lda, M, p.K, m0, u * BK, tid);
-      fetch<T, B_KMAJ, VEC>(rb[u], B, p.ldb, p.N, p.K, n0, u * BK, tid);
+      fetch<T, A_KMAJ, VEC>(ra[u], src_a, p.K, u * BK, tid);
+      fetch<T, B_KMAJ, VEC>(rb[u], src_b, p.K, u * BK, tid);
     }
     commit<T, A_KMAJ, VEC>(ra[0], sA[0], tid);
     commit<T, B_KMAJ, VEC>(rb[0], sB[0], tid);
     // registers then hold slices 1 .. D: slice D goes where slice 0 was
-    fetch<T, A_KMAJ, VEC>(ra[0], A, p.lda, M, p.K, m0, D * BK, tid);
-    fetch<T, B_KMAJ, VEC>(rb[0], B, p.ldb, p.N, p.K, n0, D * BK, tid);
+    fetch<T, A_KMAJ, VEC>(ra[0], src_a, p.K, D * BK, tid);
+    fetch<T, B_KMAJ, VEC>(rb[0], src_b, p.K, D * BK, tid);
   }
   __syncthreads();
 
@@ -244,8 +331,8 @@ __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
       commit<T, A_KMAJ, VEC>(ra[nx], sA[(u + 1) & 1], tid);
       commit<T, B_KMAJ, VEC>(rb[nx], sB[(u + 1) & 1], tid);
       const int64_t kf = (kt + u + 1 + D) * BK;
-      fetch<T, A_KMAJ, VEC>(ra[nx], A, p.lda, M, p.K, m0, kf, tid);
-      fetch<T, B_KMAJ, VEC>(rb[nx], B, p.ldb, p.N, p.K, n0, kf, tid);
+      fetch<T, A_KMAJ, VEC>(ra[nx], src_a, p.K, kf, tid);
+      fetch<T, B_KMAJ, VEC>(rb[nx], src_b, p.K, kf, tid);
       __syncthreads();
     }
   }
@@ -316,13 +403,13 @@ hipError_t launch_masked(const Problem &p, int vec, int tile, hipStream_t stream
   a.out_bf16 = p.out_bf16;
   a.tiles_m = (int32_t)((p.M + tile - 1) / tile);
   a.tiles_n = (int32_t)((p.N + tile - 1) / tile);
-  if (tile == 64) return vec == 8 ? dispatch_types<64, 8>(p, a, stream) : dispatch_types<64, 1>(p, a, stream);
-  return vec == 8 ? dispatch_types<128, 8>(p, a, stream) : dispatch_types<128, 1>(p, a, stream);
+  if (tile == 64) return vec == 8 ? dispatch_types<64, 8>(p, a, stream) : dispatch_types<64, 0>(p, a, stream);
+  return vec == 8 ? dispatch_types<128, 8>(p, a, stream) : dispatch_types<128, 0>(p, a, stream);
 }
 
 const char *masked_name(int vec, int tile) {
-  if (tile == 64) return vec == 8 ? "masked_64x64x32_vec8" : "masked_64x64x32_vec1";
-  return vec == 8 ? "masked_128x128x32_vec8" : "masked_128x128x32_vec1";
+  if (tile == 64) return vec == 8 ? "masked_64x64x64_vec8" : "masked_64x64x64_vecu";
+  return vec == 8 ? "masked_128x128x32_vec8" : "masked_128x128x32_vecu";
 }
 
 }  // namespace tsm
