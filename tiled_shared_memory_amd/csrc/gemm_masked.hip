@@ -39,8 +39,6 @@
 #include "gemm_internal.hpp"
 #include "mfma.hpp"
 
-#include <type_traits>
-
 namespace tsm {
 namespace {
 
