@@ -195,9 +195,9 @@ def test_mid_size_selection():
 
 
 def test_skinny_selection():
-    """Up to 128 rows of row-major operands go to the streaming kernel: 256-column workgroups when those fill the
-    256 CUs, 64-column ones otherwise; row blocks follow M; B either way.  K not a multiple of 64 or N not a
-    multiple of 64 go elsewhere."""
+    """Up to 128 rows of row-major A go to the streaming kernel: the widest panel whose grid fills the 256 CUs
+    (256 columns up to 64 rows; 128 columns with row-major B or 65-128 rows), 64 columns otherwise; row blocks
+    follow M; B either way.  K not a multiple of 64 or N not a multiple of 64 go elsewhere."""
     B0 = 0x7E0000000000
     N, K = 16384, 8192
 
@@ -225,13 +225,21 @@ def test_skinny_selection():
     # K-contiguous B (a weight stored output feature by output feature): the same kernel, B staged like A
     assert pick(16, lb=1) == "skinny_m16_n64_k64_t"
     assert pick(16, batch=8, lb=1) == "skinny_m16_n256_k64_t"
+    # 128-column panels: 256 of them over a batch of 2, or 128 rows (no 256-column variant)
+    assert pick(16, batch=2) == "skinny_m16_n128_k64"
+    assert pick(128, batch=2) == "skinny_m128_n128_k64"
+    assert pick(128, batch=8) == "skinny_m128_n128_k64"
+    assert pick(128, batch=8, lb=1) == "skinny_m128_n128_k64_t"
+    assert pick(16, batch=2, lb=1) == "skinny_m16_n64_k64_t"
+    assert pick(16, N=16448, batch=2) == "skinny_m16_n64_k64"  # N % 128 != 0
 
 
 def test_skinny_forced_width(monkeypatch):
     B0 = 0x7E0000000000
     args = (100, 512, 512, A0, 512, 0, 0, B0, 512, 0, 0, C0, 512, 0, 1, 0)
-    monkeypatch.setenv("TSM_GEMM_KERNEL", "skinny_m128_n64_k64")
-    assert tsm.tsm_gemm_kernel_name(*args) == "skinny_m128_n64_k64"
+    for good in ("skinny_m128_n64_k64", "skinny_m128_n128_k64"):
+        monkeypatch.setenv("TSM_GEMM_KERNEL", good)
+        assert tsm.tsm_gemm_kernel_name(*args) == good
     # a name whose row blocks do not match M, or 256 columns with 128 rows, cannot run the problem
     for bad in ("skinny_m64_n64_k64", "skinny_m128_n256_k64", "skinny_m16_n128_k64"):
         monkeypatch.setenv("TSM_GEMM_KERNEL", bad)

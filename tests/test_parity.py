@@ -287,7 +287,8 @@ def test_skinny_kernel(orc, shape, in_fmt, out_fmt):
 # every row-block count at both widths (256 only up to 64 rows); M ragged inside its last 16-row block; K from
 # one 64-deep slice (the rest of the ring's first round loads zeros) to several rounds plus a partial one
 SKINNY_VARIANT_SHAPES = [(1, 64), (13, 64), (16, 256), (17, 64), (30, 256), (32, 64), (33, 64), (47, 256), (64, 64),
-                         (65, 64), (100, 64), (128, 64)]
+                         (65, 64), (100, 64), (128, 64), (5, 128), (32, 128), (49, 128), (64, 128), (97, 128),
+                         (128, 128)]
 SKINNY_K = [64, 192, 576, 1344]
 
 
@@ -295,10 +296,10 @@ SKINNY_K = [64, 192, 576, 1344]
 @pytest.mark.parametrize("K", SKINNY_K)
 @pytest.mark.parametrize("b_layout", ["row", "col"])
 def test_skinny_variants(orc, monkeypatch, M, width, K, b_layout):
-    """Each skinny variant (16, 32, 64 or 128 rows; 64 or 256 columns per workgroup; row-major or K-contiguous
-    B) forced, against the oracle."""
+    """Each skinny variant (16, 32, 64 or 128 rows; 64, 128 or 256 columns per workgroup; row-major or
+    K-contiguous B) forced, against the oracle."""
     variant = skinny_variant(M, width, b_layout)
-    N, batch = (512, 2) if width == 256 else (320, 3)
+    N, batch = {256: (512, 2), 128: (384, 2), 64: (320, 3)}[width]
     monkeypatch.setenv("TSM_GEMM_KERNEL", variant)
     in_fmt, out_fmt = [(F16, "f32"), (BF16, "f16"), (BF16, "bf16"), (F16, "f16")][(M + K) % 4]
     A, B = make_operands(M * 7 + K + width, batch, M, N, K, in_fmt, ("uniform", -1.0, 1.0), "row", b_layout)

@@ -6,16 +6,19 @@
 // Each 256-thread workgroup owns W columns of C for all M rows and walks all
 // of K in slices of 64 ("The PTSS Cliff", section "The Idea: Stage in SLM,
 // Tile K": one K slice live at a time, float32 accumulators carried across the
-// loop).  Two shapes:
+// loop).  Three shapes:
 //  * W = 256 (each wave 64 columns): 32 KiB B slices, one workgroup per CU;
 //  * W = 64 (each wave 16 columns): 8 KiB B slices, four times the
 //    workgroups, for problems whose W = 256 grid cannot fill the chip (a
-//    single 16 x 16384 x 8192 product has only 64 such column blocks).
-// Rows come in MB blocks of 16 (MB = 1, 2, 4 or 8; 8 only with W = 64).
+//    single 16 x 16384 x 8192 product has only 64 such column blocks);
+//  * W = 128 (each wave 32 columns): 16 KiB B slices, for 64 and 128 rows,
+//    where every workgroup reading all of A (1-2 MiB) from L2 costs as much
+//    as streaming its share of B: half the A traffic of W = 64.
+// Rows come in MB blocks of 16 (MB = 1, 2, 4 or 8; 8 not with W = 256).
 //
 //  * B slices go HBM -> LDS with non-temporal buffer loads that write LDS
 //    directly, through a ring of NS stages, NS - 1 slices ahead (NS = 4 for
-//    W = 256; 8, or 6 for MB = 8, for W = 64).
+//    W = 256; 6, or 4 for MB = 8, for W = 128; 8, or 6 for MB = 8, for W = 64).
 //  * K-split mode (pass 1 of the workspace path): grid.y also enumerates row
 //    blocks and K chunks; each workgroup covers one chunk of one row block
 //    and stores raw float32 partial sums, which a second kernel adds.
@@ -47,8 +50,8 @@ constexpr uint32_t kOutside = 0x80000000u;  // a per-lane offset past every buff
 // Compile-time shape of one variant.
 template <int MB, int W>
 struct Shape {
-  static_assert(W == 256 || W == 64, "workgroup widths");
-  static_assert(MB == 1 || MB == 2 || MB == 4 || (MB == 8 && W == 64), "row blocks");
+  static_assert(W == 256 || W == 128 || W == 64, "workgroup widths");
+  static_assert(MB == 1 || MB == 2 || MB == 4 || (MB == 8 && W != 256), "row blocks");
   static constexpr int CPW = W / 4;                   // columns per wave
   static constexpr int CB = CPW / 16;                 // 16-column MFMA blocks per wave
   static constexpr int ROW_BYTES = W * 2;             // one k row of the B slice
@@ -61,10 +64,11 @@ struct Shape {
   static constexpr int A_LOADS = A_BLOCKS < 4 ? 1 : A_BLOCKS / 4;  // per wave (MB = 1: two waves repeat a block)
   static constexpr int STAGE_BYTES = SLICE_BYTES + A_BYTES;
   // Ring depth: the bytes of B in flight per CU are (NS - 1) slices.  W = 256
-  // runs one workgroup per CU with 3 x 32 KiB ahead; W = 64 is chosen when
-  // there are about as many workgroups as CUs, so its ring is deeper to keep
-  // 40-56 KiB of B in flight (and stays within the 160 KiB of LDS).
-  static constexpr int NS = W == 256 ? 4 : (MB == 8 ? 6 : 8);
+  // runs one workgroup per CU with 3 x 32 KiB ahead; W = 64 and 128 are
+  // chosen when there are about as many workgroups as CUs, so their rings are
+  // deeper to keep 40-80 KiB of B in flight (and stay within the 160 KiB of
+  // LDS).
+  static constexpr int NS = W == 256 ? 4 : W == 128 ? (MB == 8 ? 4 : 6) : (MB == 8 ? 6 : 8);
   static_assert(NS * STAGE_BYTES <= 160 * 1024, "LDS");
   // loads a wave may leave outstanding at the wait for a slice: those of the
   // NS - 2 slices issued after it
@@ -96,11 +100,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 // column block (chunks 2b, 2b+1).
 //  W = 256 (32 chunks): the XOR sends those 16 rows to 16 distinct even
 //    offsets, so the 32 chunks read land on 32 distinct positions;
+//  W = 128 (16 chunks, rows 64 banks apart): the XOR sends the 8 rows a
+//    half-wave reads (r % 4 and bit 3 of r) to 8 distinct even offsets, so
+//    its 16 chunks fall on 64 distinct banks;
 //  W = 64 (8 chunks): the XOR moves the block of the rows that share a
 //    512-byte window (equal r % 4) to 4 distinct positions.
 template <int W>
 __device__ __forceinline__ int swz_b(int r, int c) {
   if constexpr (W == 256) return c ^ (2 * ((r & 3) | ((r >> 1) & 12)));
+  else if constexpr (W == 128) return c ^ (2 * ((r & 3) | ((r >> 1) & 4)));
   else return c ^ (2 * ((r >> 3) & 3));
 }
 
@@ -363,11 +371,21 @@ SkinnyPlan skinny_plan(const Problem &p) {
   if (p.a_col) return pl;  // row-major A; B either way
   if (p.M < 1 || p.M > 128) return pl;
   pl.mb = p.M <= 16 ? 1 : p.M <= 32 ? 2 : p.M <= 64 ? 4 : 8;
-  // W = 256 when its grid fills the chip (one workgroup per CU), else W = 64;
-  // a forced width must fit the problem
-  const bool fills = (p.N / 256) * p.batch >= 256;
-  pl.w = p.skinny_w ? p.skinny_w : (p.N % 256 == 0 && pl.mb <= 4 && fills) ? 256 : 64;
-  if (pl.w != 64 && pl.w != 256) return SkinnyPlan{};
+  // The widest panel whose grid fills the chip (one workgroup per CU): wider
+  // panels re-read A fewer times.  W = 256 up to 64 rows; W = 128 with
+  // row-major B, or with 65-128 rows (with K-contiguous B and fewer rows it
+  // measured slower than W = 64: 16 x 16384 x 8192, batch 2, 119 us against
+  // 105); else W = 64, whose grid is four times that of W = 256 (a single
+  // decode product: 49.5 us against 56.1 for W = 128 at 16 rows, 70.5 against
+  // 82.3 at 128 rows).  A forced width must fit the problem.
+  const bool fills256 = (p.N / 256) * p.batch >= 256, fills128 = (p.N / 128) * p.batch >= 256;
+  int w = 64;
+  if (p.N % 256 == 0 && pl.mb <= 4 && fills256)
+    w = 256;
+  else if (p.N % 128 == 0 && fills128 && (!p.b_col || pl.mb == 8))
+    w = 128;
+  pl.w = p.skinny_w ? p.skinny_w : w;
+  if (pl.w != 64 && pl.w != 128 && pl.w != 256) return SkinnyPlan{};
   if (pl.w == 256 && pl.mb > 4) return SkinnyPlan{};
   if (p.N % pl.w) return SkinnyPlan{};
   if (p.K % BK || p.K == 0) return SkinnyPlan{};
@@ -407,6 +425,12 @@ hipError_t launch_skinny(const Problem &p, hipStream_t stream) {
     if (pl.mb == 1) return launch_shape<1, 256>(p, a, stream);
     if (pl.mb == 2) return launch_shape<2, 256>(p, a, stream);
     return launch_shape<4, 256>(p, a, stream);
+  }
+  if (pl.w == 128) {
+    if (pl.mb == 1) return launch_shape<1, 128>(p, a, stream);
+    if (pl.mb == 2) return launch_shape<2, 128>(p, a, stream);
+    if (pl.mb == 4) return launch_shape<4, 128>(p, a, stream);
+    return launch_shape<8, 128>(p, a, stream);
   }
   if (pl.mb == 1) return launch_shape<1, 64>(p, a, stream);
   if (pl.mb == 2) return launch_shape<2, 64>(p, a, stream);
@@ -529,15 +553,17 @@ const char *ksplit_name(const KSplit &ks, bool b_col) {
 
 const char *skinny_name(const Problem &p) {
   // suffix _t: B stored transposed (column-major, K-contiguous)
-  static const char *const names[2][2][4] = {
+  static const char *const names[2][3][4] = {
       {{"skinny_m16_n64_k64", "skinny_m32_n64_k64", "skinny_m64_n64_k64", "skinny_m128_n64_k64"},
+       {"skinny_m16_n128_k64", "skinny_m32_n128_k64", "skinny_m64_n128_k64", "skinny_m128_n128_k64"},
        {"skinny_m16_n256_k64", "skinny_m32_n256_k64", "skinny_m64_n256_k64", nullptr}},
       {{"skinny_m16_n64_k64_t", "skinny_m32_n64_k64_t", "skinny_m64_n64_k64_t", "skinny_m128_n64_k64_t"},
+       {"skinny_m16_n128_k64_t", "skinny_m32_n128_k64_t", "skinny_m64_n128_k64_t", "skinny_m128_n128_k64_t"},
        {"skinny_m16_n256_k64_t", "skinny_m32_n256_k64_t", "skinny_m64_n256_k64_t", nullptr}}};
   const SkinnyPlan pl = skinny_plan(p);
   if (!pl.mb) return nullptr;
   const int i = pl.mb == 1 ? 0 : pl.mb == 2 ? 1 : pl.mb == 4 ? 2 : 3;
-  return names[p.b_col][pl.w == 256][i];
+  return names[p.b_col][pl.w == 64 ? 0 : pl.w == 128 ? 1 : 2][i];
 }
 
 }  // namespace tsm
