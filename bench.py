@@ -425,8 +425,8 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the data-parallel sharding across GPUs is described in DESIGN.md, not built)", file=sys.stderr)
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
+              "(sharding the product across GPUs by output slabs is not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import torch
