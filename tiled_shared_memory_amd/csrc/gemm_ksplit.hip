@@ -35,7 +35,7 @@ struct ReduceArgs {
 
 template <bool OUT16>
 __global__ __launch_bounds__(256) void ksplit_reduce_kernel(ReduceArgs r) {
-  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;  // group of 4 columns
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // group of 4 columns
   if (g >= r.groups) return;
   const int64_t q = r.N / 4;
   const int64_t per_problem = r.M * q;
@@ -130,11 +130,16 @@ hipError_t launch_ksplit(const Problem &p, const KSplit &ks, float *ws, hipStrea
   r.act = p.act;
   r.slope = p.slope;
   r.out_bf16 = p.out_bf16;
-  const int64_t blocks = (r.groups + 255) / 256;
+  // one wave per workgroup while 256-thread workgroups would leave CUs idle:
+  // each thread's loads are all issued at once, so the reduction takes about
+  // one memory latency wherever the threads run, and spreading them over more
+  // CUs adds request slots
+  const int threads = r.groups >= 256 * 256 ? 256 : 64;
+  const int64_t blocks = (r.groups + threads - 1) / threads;
   if (p.out16)
-    hipLaunchKernelGGL((ksplit_reduce_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, stream, r);
+    hipLaunchKernelGGL((ksplit_reduce_kernel<true>), dim3((unsigned)blocks), dim3(threads), 0, stream, r);
   else
-    hipLaunchKernelGGL((ksplit_reduce_kernel<false>), dim3((unsigned)blocks), dim3(256), 0, stream, r);
+    hipLaunchKernelGGL((ksplit_reduce_kernel<false>), dim3((unsigned)blocks), dim3(threads), 0, stream, r);
   return hipGetLastError();
 }
 
