@@ -57,7 +57,7 @@ def run_case(orc, c, kernel=None):
     check(C, Cr, S, K, c["out_fmt"], str(c), act=c["act"], slope=c["slope"])
 
 
-@pytest.mark.parametrize("i", range(80))
+@pytest.mark.parametrize("i", range(160))
 def test_random_call(orc, i):
     c = draw_case(i)
     say(f"[gpu] fuzz {i}: {c}")

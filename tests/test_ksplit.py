@@ -81,6 +81,21 @@ def test_ksplit_parity(orc, shape, in_fmt, out_fmt):
     say(f"[gpu] ksplit {shape}: max err/bound = {ratio:.3e}")
 
 
+def test_largek_workload_through_the_workspace(orc):
+    """The 256 x 256 x 8192 workload with its own seeded operands, through the workspace route that the
+    benchmark times (pass 1 of the skinny kernel's split, then the reduction), against the oracle everywhere."""
+    from workloads import WORKLOADS
+
+    w = WORKLOADS["largek_f16_256x256x8192"]
+    A, B = w.operands()
+    say(f"[gpu] {w.name} through the workspace")
+    C = run_ws(A, B, w.M, w.N, w.K, w.in_fmt, w.out_fmt, batch=w.batch, fill=float("nan"),
+               expect="ksplit_skinny_m64_n64_k64+reduce")
+    Cr, S = orc.gemm_rows(A, B, w.M, w.N, w.K, w.in_fmt, batch=w.batch)
+    ratio = check(C, Cr, S, w.K, w.out_fmt, w.name)
+    say(f"[gpu] {w.name} workspace: max err/bound = {ratio:.3e}")
+
+
 TILE_SPLIT = [(640, 768, 1536, "row", "col"), (600, 520, 1024, "row", "row"), (1000, 512, 2048, "row", "row"),
               (600, 2304, 1024, "row", "col"), (520, 1024, 2048, "col", "row"), (768, 1024, 1024, "col", "col")]
 
