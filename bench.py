@@ -398,6 +398,37 @@ def rowsum_bench(args, w, torch, tsm):
     }
 
 
+def torch_reference(args, w, torch, tsm):
+    """torch.matmul (hipBLASLt on ROCm) on the same seeded operands and layouts, timed like the benchmark's steps:
+    a reference point for the library's number, never the reported value.  torch's product keeps the operand
+    dtype (no float32 or cross-dtype output) and a batch runs as one batched product."""
+    s = Setup(w, torch, tsm, workspace=False)
+    dt = torch.bfloat16 if w.in_fmt == "bf16" else torch.float16
+
+    def view(flat, layout, rows, cols, ld):
+        # the logical rows x cols operand of each problem, as stored (row- or column-major)
+        t = flat.view(dt).view(w.batch, -1)[:, :(cols if layout == "col" else rows) * ld]
+        if layout == "col":
+            return t.reshape(w.batch, cols, ld)[:, :, :rows].transpose(1, 2)
+        return t.reshape(w.batch, rows, ld)[:, :, :cols]
+
+    a = view(s.a, w.a_layout, w.M, w.K, s.lda)
+    b = view(s.b, w.b_layout, w.K, w.N, s.ldb)
+    if w.batch == 1:
+        a, b = a[0], b[0]
+    else:  # batched products in 16-bit with a transposed right operand: made contiguous first
+        a, b = a.contiguous(), b.contiguous()
+    s.step = lambda: torch.matmul(a, b)
+    for _ in range(args.warmup):
+        s.step()
+    torch.cuda.synchronize()
+    ms = s.time_steps(args.steps) / args.steps
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    return {"reference": "torch.matmul", "torch": torch.__version__, "workload": w.name, "steps": args.steps,
+            "ms_per_step": ms, "ms_per_step_interleaved_median": s.interleaved_ms(), "tflops": tflops,
+            "pct_of_mfma_peak": 100.0 * tflops / MFMA_PEAK_TFLOPS, "out_dtype": str(dt).replace("torch.", "")}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -408,6 +439,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--torch-reference", action="store_true",
+                    help="time torch.matmul on the workload's operands instead (a reference line, not the benchmark)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (to scale HBM counters)")
     ap.add_argument("--activation", choices=["none", "relu", "leaky_relu"], default="none",
@@ -451,6 +484,9 @@ def main():
     w = lookup(args.workload)
     if hasattr(w, "operand"):  # a row-sum workload
         print(json.dumps(rowsum_bench(args, w, torch, tsm)), flush=True)
+        return
+    if args.torch_reference:
+        print(json.dumps(torch_reference(args, w, torch, tsm)), flush=True)
         return
     act = {"none": 0, "relu": 1, "leaky_relu": 2}[args.activation]
     s = Setup(w, torch, tsm, act, args.slope if act == 2 else 0.0, workspace=not args.no_workspace)
