@@ -39,6 +39,7 @@ struct KernelArgs {
   int32_t z0;  // first problem index covered by this launch
   const int32_t *rows;  // per-problem row counts in device memory, or null (every problem has M rows)
   int32_t compact_groups;  // large-tile kernel, grouped call: number of groups, tiles numbered over valid ones only
+  int32_t flat_batch;      // large-tile kernel, strided batch: number of problems, tiles numbered over all of them
   int32_t act;             // epilogue: 0 none, 1 ReLU, 2 leaky ReLU
   float slope;             // leaky ReLU slope
   int32_t out_bf16;        // 16-bit output is bf16 (else f16)

@@ -423,6 +423,16 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
     }
     tile_order(pid, work_rows(p, g), p.tiles_n, tm, tn);
     z = g;
+  } else if (p.flat_batch) {
+    // Strided batch: one 1-D grid over every tile of every problem, so the
+    // per-XCD regrouping gives each XCD a run of tiles of one problem (a
+    // 2-D grid would regroup within each problem only, and the 32 tiles
+    // resident on an XCD would come from several problems' panels:
+    // 8 x 2048 x 2048 x 4096 took 0.261 ms that way against 0.217 ms)
+    const int T = p.tiles_m * p.tiles_n;
+    const int pid = xcd_remap(blockIdx.x, T * p.flat_batch);
+    z = pid / T;
+    tile_order(pid - (int)z * T, p.tiles_m, p.tiles_n, tm, tn);
   } else {
     tile_order(xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n), p.tiles_m, p.tiles_n, tm, tn);
     z = (int64_t)p.z0 + blockIdx.y;
@@ -559,6 +569,14 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
     KernelArgs a = base;
     a.z0 = 0;
     a.compact_groups = (int32_t)batch;
+    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT16, MI, ACOL, BROW, KB>), dim3((unsigned)(tiles * batch)), dim3(256), 0,
+                       stream, a);
+    return hipGetLastError();
+  }
+  if (!base.rows && batch > 1 && tiles * batch <= 0x7fffffffLL) {
+    KernelArgs a = base;
+    a.z0 = 0;
+    a.flat_batch = (int32_t)batch;
     hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT16, MI, ACOL, BROW, KB>), dim3((unsigned)(tiles * batch)), dim3(256), 0,
                        stream, a);
     return hipGetLastError();
