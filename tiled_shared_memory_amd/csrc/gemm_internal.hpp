@@ -39,7 +39,7 @@ struct KernelArgs {
   int32_t z0;  // first problem index covered by this launch
   const int32_t *rows;  // per-problem row counts in device memory, or null (every problem has M rows)
   int32_t compact_groups;  // large-tile kernel, grouped call: number of groups, tiles numbered over valid ones only
-  int32_t flat_batch;      // large-tile kernel, strided batch: number of problems, tiles numbered over all of them
+  int32_t flat_batch;      // large-tile and masked kernels, strided batch: number of problems, tiles numbered over all of them
   int32_t act;             // epilogue: 0 none, 1 ReLU, 2 leaky ReLU
   float slope;             // leaky ReLU slope
   int32_t out_bf16;        // 16-bit output is bf16 (else f16)
@@ -55,6 +55,27 @@ __device__ __forceinline__ int64_t rows_of(const KernelArgs &p, int64_t z) {
   if (!p.rows) return p.M;
   const int64_t r = p.rows[z];
   return r < 0 ? 0 : (r > p.M ? p.M : r);
+}
+
+// The 8 XCDs take workgroups round-robin; re-deal index b of T so that each
+// XCD gets a contiguous run of tiles (the last T % 8 keep their index).
+__device__ __forceinline__ int xcd_remap(int b, int T) {
+  const int T8 = T & ~7;
+  return b < T8 ? (b & 7) * (T8 >> 3) + (b >> 3) : b;
+}
+
+// Tile (tm, tn) of run index pid over a tiles_m x tiles_n grid: groups of
+// group_m tile rows, walked column by column (the grouped ordering of the
+// Intel XPU Triton README's matmul signature, GROUP_SIZE_M), so consecutive
+// tiles share A and B panels.
+__device__ __forceinline__ void tile_order(int pid, int tiles_m, int tiles_n, int group_m, int &tm, int &tn) {
+  const int per_group = group_m * tiles_n;
+  const int group = pid / per_group;
+  const int first_m = group * group_m;
+  const int gm = min(tiles_m - first_m, group_m);
+  const int in_group = pid - group * per_group;
+  tm = first_m + in_group % gm;
+  tn = in_group / gm;
 }
 
 // Largest grid.y a launch uses for the batch; bigger batches are split.

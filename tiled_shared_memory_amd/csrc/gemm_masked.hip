@@ -257,10 +257,24 @@ __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  const int tile = blockIdx.x;
-  const int64_t m0 = (int64_t)(tile / p.tiles_n) * T;
-  const int64_t n0 = (int64_t)(tile % p.tiles_n) * T;
-  const int64_t z = (int64_t)p.z0 + blockIdx.y;
+  // tile order: per-XCD regrouping, then groups of 8 tile rows column by
+  // column, so the tiles resident on one XCD share A and B panels in its L2;
+  // a strided batch runs as one 1-D grid over every problem's tiles
+  const int ntiles = p.tiles_m * p.tiles_n;
+  int pid;
+  int64_t z;
+  if (p.flat_batch) {
+    pid = xcd_remap(blockIdx.x, ntiles * p.flat_batch);
+    z = pid / ntiles;
+    pid -= (int)z * ntiles;
+  } else {
+    pid = xcd_remap(blockIdx.x, ntiles);
+    z = (int64_t)p.z0 + blockIdx.y;
+  }
+  int tm, tn;
+  tile_order(pid, p.tiles_m, p.tiles_n, 8, tm, tn);
+  const int64_t m0 = (int64_t)tm * T;
+  const int64_t n0 = (int64_t)tn * T;
   const int64_t M = rows_of(p, z);  // this problem's rows
   if (m0 >= M) return;              // the whole tile lies past them (uniform)
   const Epilogue ep = epilogue_in_vgprs(p);  // kept out of the scalar registers the loop needs
@@ -351,6 +365,14 @@ __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
 template <int T, bool BF16, bool OUT16, bool A_KMAJ, bool B_KMAJ, int VEC>
 hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
   const int64_t tiles = (int64_t)base.tiles_m * base.tiles_n;
+  if (batch > 1 && tiles * batch <= 0x7fffffffLL) {
+    KernelArgs a = base;
+    a.z0 = 0;
+    a.flat_batch = (int32_t)batch;
+    hipLaunchKernelGGL((gemm_masked_kernel<T, BF16, OUT16, A_KMAJ, B_KMAJ, VEC>), dim3((unsigned)(tiles * batch)),
+                       dim3(THREADS), 0, stream, a);
+    return hipGetLastError();
+  }
   for (int64_t z0 = 0; z0 < batch; z0 += kMaxGridY) {
     KernelArgs a = base;
     a.z0 = (int32_t)z0;

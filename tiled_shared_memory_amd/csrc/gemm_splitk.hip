@@ -112,16 +112,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_splitk_kernel(KernelArgs p
   const int lane = c.lane;
 
   // ---- tile order: per-XCD regrouping, then GROUP_M tile rows column by column
-  const int T = p.tiles_m * p.tiles_n;
-  int pid = blockIdx.x;
-  if ((T & 7) == 0) pid = (pid & 7) * (T >> 3) + (pid >> 3);
-  const int per_group = GROUP_M * p.tiles_n;
-  const int group = pid / per_group;
-  const int first_m = group * GROUP_M;
-  const int gm = min(p.tiles_m - first_m, GROUP_M);
-  const int in_group = pid - group * per_group;
-  const int64_t m0 = (int64_t)(first_m + in_group % gm) * 16;
-  const int64_t n0 = (int64_t)(in_group / gm) * 16;
+  int tm, tn;
+  tile_order(xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n), p.tiles_m, p.tiles_n, GROUP_M, tm, tn);
+  const int64_t m0 = (int64_t)tm * 16;
+  const int64_t n0 = (int64_t)tn * 16;
   const int64_t z = (int64_t)p.z0 + blockIdx.y;
 
   // this wave's K range: nsteps steps of 32 starting at k0

@@ -337,25 +337,6 @@ __device__ __forceinline__ void slice(Ctx &c, int j, Frags<MI> (&fr)[2], Acc<MI>
 // Tile-rows of 256 that hold rows of problem g of a grouped call.
 __device__ __forceinline__ int work_rows(const KernelArgs &p, int g) { return (int)((rows_of(p, g) + BM - 1) / BM); }
 
-// The 8 XCDs take workgroups round-robin; re-deal index b of T so that each
-// XCD gets a contiguous run of tiles (the last T % 8 keep their index).
-__device__ __forceinline__ int xcd_remap(int b, int T) {
-  const int T8 = T & ~7;
-  return b < T8 ? (b & 7) * (T8 >> 3) + (b >> 3) : b;
-}
-
-// Tile (tm, tn) of run index pid over a tiles_m x tiles_n grid: groups of
-// GROUP_M tile rows, walked column by column.
-__device__ __forceinline__ void tile_order(int pid, int tiles_m, int tiles_n, int &tm, int &tn) {
-  const int per_group = GROUP_M * tiles_n;
-  const int group = pid / per_group;
-  const int first_m = group * GROUP_M;
-  const int gm = min(tiles_m - first_m, GROUP_M);
-  const int in_group = pid - group * per_group;
-  tm = first_m + in_group % gm;
-  tn = in_group / gm;
-}
-
 // Wide variant, sub-slice U of slab j (resident in stage S): U = 0 waits for
 // the slab and the barrier, reads sub-slice 0's fragments and refills the
 // other stage (freed by that barrier) with slab j+1 while the previous
@@ -421,7 +402,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
       if (pid < t) break;
       pid -= t;
     }
-    tile_order(pid, work_rows(p, g), p.tiles_n, tm, tn);
+    tile_order(pid, work_rows(p, g), p.tiles_n, GROUP_M, tm, tn);
     z = g;
   } else if (p.flat_batch) {
     // Strided batch: one 1-D grid over every tile of every problem, so the
@@ -432,9 +413,9 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
     const int T = p.tiles_m * p.tiles_n;
     const int pid = xcd_remap(blockIdx.x, T * p.flat_batch);
     z = pid / T;
-    tile_order(pid - (int)z * T, p.tiles_m, p.tiles_n, tm, tn);
+    tile_order(pid - (int)z * T, p.tiles_m, p.tiles_n, GROUP_M, tm, tn);
   } else {
-    tile_order(xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n), p.tiles_m, p.tiles_n, tm, tn);
+    tile_order(xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n), p.tiles_m, p.tiles_n, GROUP_M, tm, tn);
     z = (int64_t)p.z0 + blockIdx.y;
   }
 
