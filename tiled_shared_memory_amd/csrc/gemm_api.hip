@@ -53,11 +53,11 @@ const char *kernel_name(Kernel k, const Problem &p) {
     case Kernel::Masked8:
       return masked_name(8, 128);
     case Kernel::MaskedU:
-      return masked_name(1, 128);
+      return masked_name(0, 128);
     case Kernel::Small8:
       return masked_name(8, 64);
     case Kernel::SmallU:
-      return masked_name(1, 64);
+      return masked_name(0, 64);
     case Kernel::Tile32:
       return tile_name(0);
     case Kernel::Tile16:
@@ -280,8 +280,8 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
     out->kernel = want;
     out->forced = true;
   }
-  // the masked kernels address each 32-deep operand slice with 32-bit
-  // offsets from its corner: up to 127 rows of a leading dimension
+  // the masked kernels address each operand slice (32 or 64 deep) with
+  // 32-bit offsets from its corner: up to 127 rows of a leading dimension
   const bool masked = out->kernel == Kernel::Masked8 || out->kernel == Kernel::MaskedU ||
                       out->kernel == Kernel::Small8 || out->kernel == Kernel::SmallU;
   if (masked && K > 0 && (lda >= MaskedInfo::kMaxLd || ldb >= MaskedInfo::kMaxLd))
@@ -300,13 +300,13 @@ int run(const Plan &pl, void *stream) {
       e = launch_masked(pl.p, 8, 128, s);
       break;
     case Kernel::MaskedU:
-      e = launch_masked(pl.p, 1, 128, s);
+      e = launch_masked(pl.p, 0, 128, s);
       break;
     case Kernel::Small8:
       e = launch_masked(pl.p, 8, 64, s);
       break;
     case Kernel::SmallU:
-      e = launch_masked(pl.p, 1, 64, s);
+      e = launch_masked(pl.p, 0, 64, s);
       break;
     case Kernel::Tile32:
       e = launch_tile(pl.p, 0, s);

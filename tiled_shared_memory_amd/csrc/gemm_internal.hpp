@@ -92,7 +92,7 @@ struct MaskedInfo {
   // marks an element outside the matrix)
   static constexpr int64_t kMaxLd = (int64_t)1 << 23;
 };
-// vec: 8 (16-byte aligned vectors) or any other value (vectors at any 2-byte
+// vec: 8 (16-byte aligned vectors) or 0 (realigned vectors at any 2-byte
 // alignment); tile: 128 (128 x 128) or 64 (64 x 64, for problems with few 128-tiles).
 hipError_t launch_masked(const Problem &p, int vec, int tile, hipStream_t stream);
 const char *masked_name(int vec, int tile);

@@ -11,9 +11,10 @@
 //  * W = 64 (each wave 16 columns): 8 KiB B slices, four times the
 //    workgroups, for problems whose W = 256 grid cannot fill the chip (a
 //    single 16 x 16384 x 8192 product has only 64 such column blocks);
-//  * W = 128 (each wave 32 columns): 16 KiB B slices, for 64 and 128 rows,
-//    where every workgroup reading all of A (1-2 MiB) from L2 costs as much
-//    as streaming its share of B: half the A traffic of W = 64.
+//  * W = 128 (each wave 32 columns): 16 KiB B slices, when its grid fills
+//    the chip and W = 256 does not apply (65-128 rows, or a batch of two
+//    16384-column weights): every workgroup reads all of A from L2, so it
+//    moves half the A bytes of W = 64.
 // Rows come in MB blocks of 16 (MB = 1, 2, 4 or 8; 8 not with W = 256).
 //
 //  * B slices go HBM -> LDS with non-temporal buffer loads that write LDS
