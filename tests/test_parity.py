@@ -389,13 +389,18 @@ def test_splitk_kernel(orc, shape, in_fmt, out_fmt, b_layout):
     assert np.array_equal(run(A, B, M, N, K, in_fmt, out_fmt, batch=batch, b_layout=b_layout, kernel=SPLITK), C)
 
 
-def test_k_zero_writes_zeros():
-    M, N = 33, 65
-    A = np.zeros((1, M, 0), np.uint16)
-    B = np.zeros((1, 0, N), np.uint16)
-    say("[gpu] K=0")
-    C = run(A, B, M, N, 0, F16, "f32", lda=1, ldb=N, fill=float("nan"))
+@pytest.mark.parametrize("M,N,batch", [(33, 65, 1), (33, 65, 3), (300, 520, 2)])
+def test_k_zero_writes_zeros(M, N, batch):
+    """K = 0: C is the empty sum, zeros in every problem of a batch (the batch runs as one flat grid), and the
+    ld padding stays untouched."""
+    A = np.zeros((batch, M, 0), np.uint16)
+    B = np.zeros((batch, 0, N), np.uint16)
+    say(f"[gpu] K=0 {M}x{N} batch {batch}")
+    C, raw = run(A, B, M, N, 0, F16, "f32", batch=batch, lda=1, ldb=N, ldc=N + 3, sA=0, sB=0, fill=float("nan"),
+                 keep=True)
     assert np.all(C == 0.0)
+    host = raw.cpu().numpy()[:batch * M * (N + 3)].reshape(batch, M, N + 3)
+    assert np.all(np.isnan(host[:, :, N:])), "ld padding written"
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
