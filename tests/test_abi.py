@@ -232,6 +232,11 @@ def test_skinny_selection():
     assert pick(128, batch=8, lb=1) == "skinny_m128_n128_k64_t"
     assert pick(16, batch=2, lb=1) == "skinny_m16_n64_k64_t"
     assert pick(16, N=16448, batch=2) == "skinny_m16_n64_k64"  # N % 128 != 0
+    # 33-128 rows with fewer K slices than one round of the ring: the 64 x 64 masked tiles
+    assert pick(64, N=128, K=128) == "masked_64x64x64_vec8"
+    assert pick(128, N=8192, K=256) == "masked_64x64x64_vec8"
+    assert pick(128, N=8192, K=384) == "skinny_m128_n64_k64"  # 6 slices: one round of its ring
+    assert pick(16, N=4096, K=128) == "skinny_m16_n64_k64"  # up to 32 rows the streaming kernel keeps them
 
 
 def test_skinny_forced_width(monkeypatch):

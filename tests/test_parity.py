@@ -57,7 +57,7 @@ def _sample_cells(rng, batch, M, N, n):
 # with the K split)
 EXPECTED_KERNEL = {"square_bf16_8192": "tile_256x256x64_mi16", "skinny_f16_16x16384x8192_b8": "skinny_m16_n256_k64",
                    "largek_f16_256x256x8192": "splitk_", "ragged_f16_1000x1500x777": "masked_64x64x64_vecu",
-                   "single_f16_64x128x128": "skinny_m64_n64_k64"}
+                   "single_f16_64x128x128": "masked_64x64x64_vec8"}
 
 
 @pytest.mark.parametrize("name", ["square_bf16_8192", "skinny_f16_16x16384x8192_b8"])

@@ -241,10 +241,15 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
   // work.  Its rate grows with its grid (about 6.7 TB/s at 256 workgroups,
   // one per CU); split-K's falls with the row tiles (about 3 TB/s over one).
   // Split-K keeps the problem while grid x row tiles < 128.
+  // The streaming kernel runs whole rounds of its ring: with 33-128 rows and
+  // fewer K slices than one round, the 64 x 64 masked tiles win (64 x 128 x
+  // 128: 3.7 us against 4.2; 128 x 8192 x 256: 5.6 against 6.6); with up to
+  // 32 rows it keeps them (16 x 16384 x 448: 4.2 against 6.2).
   if (K > 0) {
     const SkinnyPlan sp = skinny_plan(p);
     const bool narrow = sp.mb && (N / sp.w) * batch * ((M + 15) / 16) < 128;
-    if (sp.mb) out->kernel = narrow && splitk_ok && masked_tiles < 256 ? Kernel::SplitK : Kernel::Skinny;
+    const bool short_k = sp.mb > 2 && K < 64 * (int64_t)skinny_ring_slices(sp);
+    if (sp.mb && !short_k) out->kernel = narrow && splitk_ok && masked_tiles < 256 ? Kernel::SplitK : Kernel::Skinny;
   }
 
   // TSM_GEMM_KERNEL=<name> forces a kernel variant (tests and tuning); a

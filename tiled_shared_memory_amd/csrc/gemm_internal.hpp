@@ -120,6 +120,8 @@ struct SkinnyPlan {
   int w = 0;   // columns per workgroup
 };
 SkinnyPlan skinny_plan(const Problem &p);
+// slices in one round of the kernel's LDS ring (it always runs whole rounds)
+int skinny_ring_slices(const SkinnyPlan &pl);
 bool skinny_supports(const Problem &p);
 
 // K split through a caller's workspace, for problems whose tiles cannot fill

@@ -401,6 +401,12 @@ SkinnyPlan skinny_plan(const Problem &p) {
 
 bool skinny_supports(const Problem &p) { return skinny_plan(p).mb != 0; }
 
+int skinny_ring_slices(const SkinnyPlan &pl) {
+  if (pl.w == 256) return Shape<1, 256>::NS;
+  if (pl.w == 128) return pl.mb == 8 ? Shape<8, 128>::NS : Shape<1, 128>::NS;
+  return pl.mb == 8 ? Shape<8, 64>::NS : Shape<1, 64>::NS;
+}
+
 hipError_t launch_skinny(const Problem &p, hipStream_t stream) {
   const SkinnyPlan pl = skinny_plan(p);
   KernelArgs a{};
