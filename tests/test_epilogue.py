@@ -33,6 +33,8 @@ FAMILIES = [
     ("skinny_m16_n256_k64", (13, 512, 512, 2), "row", "row"),
     ("skinny_m64_n64_k64", (40, 320, 192, 2), "row", "row"),
     ("skinny_m128_n64_k64", (100, 128, 128, 1), "row", "row"),
+    ("skinny_m128_n128_k64", (100, 384, 192, 2), "row", "row"),
+    ("skinny_m32_n128_k64", (20, 256, 320, 1), "row", "row"),
     ("splitk_16x16_w16", (48, 32, 4096, 1), "row", "row"),
     ("splitk_16x16_w16_t", (32, 48, 2048, 2), "row", "col"),
     ("skinny_m32_n64_k64_t", (20, 192, 320, 2), "row", "col"),

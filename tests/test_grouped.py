@@ -86,7 +86,8 @@ def test_grouped_masked(orc, a_layout, b_layout, shape):
 
 
 @pytest.mark.parametrize("M,variant", [(16, "skinny_m16_n64_k64"), (64, "skinny_m64_n64_k64"),
-                                       (128, "skinny_m128_n64_k64"), (32, "skinny_m32_n256_k64")])
+                                       (128, "skinny_m128_n64_k64"), (32, "skinny_m32_n256_k64"),
+                                       (32, "skinny_m32_n128_k64"), (128, "skinny_m128_n128_k64")])
 def test_grouped_skinny(orc, monkeypatch, M, variant):
     """Grouped rows on the streaming kernel: counts past M, zero and negative, ragged inside a 16-row block."""
     monkeypatch.setenv("TSM_GEMM_KERNEL", variant)
