@@ -3,12 +3,14 @@
 // It handles every layout, every alignment and ragged M, N and K.  Each
 // 256-thread workgroup owns a T x T tile of C (T = 128, or 64 when the
 // 128-tile grid is too small to occupy the chip) and walks K in slices of
-// BK = 32 ("The PTSS Cliff", section "The Idea: Stage in SLM, Tile K": only one
-// K slice is live in registers, the float32 accumulator is carried across the
-// loop).  Unlike the page's pass, which stages whole operands once, the slices
-// are streamed: at large K a whole operand panel cannot fit LDS, so each slice
-// is fetched from global memory while the previous one feeds the matrix cores
-// (double-buffered LDS, one barrier per slice).
+// BK = 32 (T = 128) or 64 (T = 64) ("The PTSS Cliff", section "The Idea:
+// Stage in SLM, Tile K": only a bounded K slice is live, the float32
+// accumulator is carried across the loop).  Unlike the page's pass, which
+// stages whole operands once, the slices are streamed: at large K a whole
+// operand panel cannot fit LDS, so registers hold the next slices in flight
+// while the current one, in LDS, feeds the matrix cores (double-buffered LDS,
+// one barrier per slice).  Tiles are regrouped per XCD and walked in groups of
+// 8 tile rows; a strided batch or grouped call is one 1-D grid.
 //
 // Loads: each thread fetches vectors of 8 contiguous 16-bit elements of an
 // operand along its contiguous dimension.  VEC = 8: one 16-byte load, when the
@@ -23,8 +25,9 @@
 // Descriptors ...", the pointer-based loop) zero-fills the same way.
 //
 // LDS layout: an operand contiguous along K is stored as it comes, [outer][BK
-// + 8] 16-bit elements (row pitch 80 bytes, so every 16-byte fragment read
-// stays aligned and consecutive rows start on different banks).  An operand
+// + 8] 16-bit elements (row pitch 80 or 144 bytes, so every 16-byte fragment
+// read stays aligned and the rows one 16-lane group reads fall on distinct
+// banks).  An operand
 // contiguous along M or N (row-major B, column-major A) is also stored as it
 // comes, [BK][T] with its 16-byte chunks XOR-swizzled by the k row, and
 // ds_read_b64_tr_b16 transposes it on the way out of LDS into the
