@@ -214,9 +214,12 @@ int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t batch);
  *                     matter and on return are unspecified.  May be NULL
  *                     (with workspace_bytes = 0): the call then never splits.
  *   workspace_bytes : its size.  Below gemm_workspace_bytes(M, N, K, batch),
- *                     or for operands the split pass cannot read (it needs
- *                     row-major A and B, 16-byte aligned rows and bases), the
- *                     call runs exactly as gemm_strided_batched_act.
+ *                     or for operands the split passes cannot read, the call
+ *                     runs exactly as gemm_strided_batched_act.  The split
+ *                     needs 16-byte aligned bases and rows (lda, ldb multiples
+ *                     of 8, ldc of 4) and no grouped counts; up to 128 rows
+ *                     (skinny split) A row-major and B either way; above that
+ *                     (256 x 256 tiles, one problem) any layout.
  * Two calls in flight at once must not share a workspace.  Other arguments,
  * rules and errors as for gemm_strided_batched_act; additionally
  * TSM_ERROR_INVALID_VALUE for negative workspace_bytes, a NULL workspace with
