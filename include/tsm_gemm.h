@@ -217,9 +217,10 @@ int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t batch);
  *                     or for operands the split passes cannot read, the call
  *                     runs exactly as gemm_strided_batched_act.  The split
  *                     needs 16-byte aligned bases and rows (lda, ldb multiples
- *                     of 8, ldc of 4) and no grouped counts; up to 128 rows
- *                     (skinny split) A row-major and B either way; above that
- *                     (256 x 256 tiles, one problem) any layout.
+ *                     of 8, ldc of 4) and no grouped counts.  The streaming
+ *                     kernel's split (up to 512 rows) needs row-major A, B
+ *                     either way; the 256 x 256 tiles' split (above 128 rows,
+ *                     one problem) takes any layout.
  * Two calls in flight at once must not share a workspace.  Other arguments,
  * rules and errors as for gemm_strided_batched_act; additionally
  * TSM_ERROR_INVALID_VALUE for negative workspace_bytes, a NULL workspace with
