@@ -340,10 +340,24 @@ def cpu_baseline(orc, w, A, B, target_s):
     rows = max(1, min(w.M, int((target_s - fixed) / per_row)))
     t = run(rows)
     flops = 2.0 * rows * w.N * w.K
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": orc.threads(), "kind": "oracle",
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": orc.threads(), "cpu": cpu_model(), "kind": "oracle",
             "sample": f"rows 0..{rows - 1} of problem 0 ({rows} x {w.N} x {w.K} fp64 multiply-adds, "
                       f"{t:.1f} s including the decode of B)",
             "seconds": t}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name, reported beside the oracle's thread count."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
 
 
 def rowsum_bench(args, w, torch, tsm):
@@ -391,8 +405,8 @@ def rowsum_bench(args, w, torch, tsm):
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                      "traffic": traffic_from_profiles(w.name, kernel), "kernel": kernel,
                      "algorithmic_bytes_per_launch": w.bytes, "algorithmic_flops_per_launch": w.flops},
-        "cpu_baseline": {"value": w.bytes / cpu_s / 1e9, "unit": "GB/s", "cores": orc.threads(), "kind": "oracle",
-                         "sample": f"all {w.R} rows, {cpu_s:.2f} s"},
+        "cpu_baseline": {"value": w.bytes / cpu_s / 1e9, "unit": "GB/s", "cores": orc.threads(), "cpu": cpu_model(),
+                         "kind": "oracle", "sample": f"all {w.R} rows, {cpu_s:.2f} s"},
         "kernel_source_hash": kernel_source_hash(), "kernel_source_hashes": {kernel: kernel_source_hash(kernel)},
         "argv": sys.argv[1:],
     }

@@ -50,3 +50,7 @@ def test_profile_summaries_name_their_commands():
             assert key in rec, f"{os.path.basename(path)}: {key}"
         assert all("rocprofv3 --pmc" in c for c in rec["commands"])
         assert os.path.basename(path) == f"traffic_{rec['workload']}.json"
+
+
+def test_cpu_model_is_named():
+    assert bench.cpu_model() and "\n" not in bench.cpu_model()

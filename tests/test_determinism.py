@@ -1,0 +1,47 @@
+"""Run-to-run determinism: every kernel variant, forced, gives the same bits on a second call with the same
+inputs (each variant's accumulation order is fixed; results may differ between variants, within the
+oracle's bound).  The second call's output starts as NaN, so an element either call left unwritten fails."""
+
+import numpy as np
+import pytest
+
+from gpu_util import check, run, say
+from workloads.inputs import F16, BF16, make_operands
+
+pytestmark = pytest.mark.gpu
+
+# (variant, A layout, B layout, (M, N, K, batch), operand format, output format); a variant ending in "_" is
+# matched as a prefix of the routed kernel and not forced
+CASES = [
+    ("tile_256x256x64_mi16", "row", "col", (512, 512, 1024, 1), BF16, "f16"),
+    ("tile_256x256x32_mi16", "row", "col", (256, 512, 384, 2), F16, "f32"),
+    ("tile_256x256x32_mi32", "row", "col", (512, 256, 256, 1), BF16, "f32"),
+    ("tile_256x256x32_mi16_nn", "row", "row", (512, 520, 256, 1), BF16, "f16"),
+    ("tile_256x256x32_mi16_tn", "col", "row", (264, 512, 256, 1), F16, "f16"),
+    ("tile_256x256x32_mi16_tt", "col", "col", (256, 256, 512, 2), BF16, "f32"),
+    ("masked_128x128x32_vecu", "row", "row", (130, 257, 100, 1), F16, "f32"),
+    ("masked_128x128x32_vec8", "row", "col", (200, 72, 1000, 1), BF16, "f16"),
+    ("masked_64x64x64_vecu", "col", "col", (65, 63, 33, 2), F16, "f16"),
+    ("masked_64x64x64_vec8", "row", "row", (200, 72, 1000, 1), F16, "f32"),
+    ("skinny_m16_n256_k64", "row", "row", (16, 512, 576, 1), F16, "f32"),
+    ("skinny_m64_n64_k64_t", "row", "col", (50, 256, 192, 2), BF16, "f16"),
+    ("skinny_m128_n128_k64", "row", "row", (100, 512, 384, 1), F16, "f16"),
+    ("splitk_", "row", "row", (48, 80, 4096, 2), F16, "f32"),
+    ("splitk_", "row", "col", (16, 16, 2048, 1), BF16, "f16"),
+]
+
+
+@pytest.mark.parametrize("variant,a_layout,b_layout,shape,in_fmt,out_fmt", CASES,
+                         ids=[f"{c[0]}{c[1][0]}{c[2][0]}" for c in CASES])
+def test_second_call_same_bits(orc, monkeypatch, variant, a_layout, b_layout, shape, in_fmt, out_fmt):
+    M, N, K, batch = shape
+    if not variant.endswith("_"):
+        monkeypatch.setenv("TSM_GEMM_KERNEL", variant)
+    A, B = make_operands(M + 3 * N + 5 * K + batch, batch, M, N, K, in_fmt, ("normal", 1.0), a_layout, b_layout)
+    say(f"[gpu] determinism {variant} {shape} A:{a_layout} B:{b_layout} {in_fmt}->{out_fmt}")
+    kw = dict(batch=batch, a_layout=a_layout, b_layout=b_layout, kernel=variant)
+    first = run(A, B, M, N, K, in_fmt, out_fmt, **kw)
+    second = run(A, B, M, N, K, in_fmt, out_fmt, fill=float("nan"), **kw)
+    assert np.array_equal(first.view(np.uint8), second.view(np.uint8)), f"{variant}: bits differ between calls"
+    Cr, S = orc.gemm_rows(A, B, M, N, K, in_fmt, batch=batch, a_layout=a_layout, b_layout=b_layout)
+    check(first, Cr, S, K, out_fmt, f"{variant} {shape}")
