@@ -149,11 +149,11 @@ def test_kernel_selection_by_layout_and_shape():
     n = 4096
     col = tsm.tsm_gemm_kernel_name(n, n, n, A0, n, 0, 0, B0, n, 1, 0, C0, n, 0, 1, 2)
     row = tsm.tsm_gemm_kernel_name(n, n, n, A0, n, 0, 0, B0, n, 0, 0, C0, n, 0, 1, 2)
-    assert col == "tile_256x256x64_mi16"
+    assert col == "tile_256x256x64_mi16_st"
     assert row == "tile_256x256x32_mi16_nn"
     # 16 tiles of 256 x 256 but a batch of 16: 256 workgroups
     assert tsm.tsm_gemm_kernel_name(1024, 1024, 1024, A0, 1024, 0, 1 << 20, B0, 1024, 1, 1 << 20, C0, 1024, 1 << 20,
-                                    16, 2) == "tile_256x256x64_mi16"
+                                    16, 2) == "tile_256x256x64_mi16_st"
     # 16 tiles, one problem: the 128 x 128 kernel spreads over more CUs
     assert tsm.tsm_gemm_kernel_name(1024, 1024, 1024, A0, 1024, 0, 0, B0, 1024, 1, 0, C0, 1024, 0, 1,
                                     2).startswith("masked_")
@@ -174,7 +174,7 @@ def test_mid_size_selection():
         m = m or n
         return tsm.tsm_gemm_kernel_name(m, n, K, A0, K, 0, 0, B0, K if lb else n, lb, 0, C0, n, 0, 1, 3)
 
-    assert pick(3072, 1024, 1) == "tile_256x256x64_mi16"  # 144 tiles
+    assert pick(3072, 1024, 1) == "tile_256x256x64_mi16_st"  # 144 tiles
     assert pick(3072, 1024, 0) == "tile_256x256x32_mi16_nn"
     assert pick(2560, 8192, 0) == "tile_256x256x32_mi16_nn"  # 100 tiles, deep K
     assert pick(2560, 2048, 0) == "masked_128x128x32_vec8"  # 100 tiles, 400 of 128 x 128
@@ -361,7 +361,7 @@ def test_grouped_kernel_selection():
     # MoE-like: 8 experts, up to 2048 tokens, 1024 x 1024 weights stored K-contiguous
     big = _grouped(M=2048, N=1024, K=1024, lda=1024, sA=2048 * 1024, ldb=1024, lb=1, sB=1024 * 1024, ldc=1024,
                    sC=2048 * 1024, groups=8, dtype=3)
-    assert tsm.tsm_gemm_grouped_kernel_name(*big) == "tile_256x256x64_mi16"
+    assert tsm.tsm_gemm_grouped_kernel_name(*big) == "tile_256x256x64_mi16_st"
     big[9] = 0  # row-major weights
     assert tsm.tsm_gemm_grouped_kernel_name(*big) == "tile_256x256x32_mi16_nn"
     # up to 16 rows per group: the skinny kernel
@@ -377,7 +377,7 @@ def test_grouped_kernel_selection():
 def test_plain_products_with_ragged_m_use_the_tile_kernel():
     """M need not be a multiple of 256 for the large-tile kernels: rows past M load as zero and are not stored."""
     assert tsm.tsm_gemm_kernel_name(8000, 8192, 8192, A0, 8192, 0, 0, B0, 8192, 1, 0, C0, 8192, 0, 1,
-                                    3) == "tile_256x256x64_mi16"
+                                    3) == "tile_256x256x64_mi16_st"
 
 
 X0, O0 = 0x7F4000000000, 0x7F5000000000
@@ -421,7 +421,7 @@ def test_rowsum_kernel_selection():
 def test_ragged_n_routes_to_the_tile_kernel():
     """N a multiple of 8 (not of 256) stays on the large-tile kernels; N not a multiple of 8 does not."""
     assert tsm.tsm_gemm_kernel_name(4096, 50256, 4096, A0, 4096, 0, 0, B0, 4096, 1, 0, C0, 50256, 0, 1,
-                                    3) == "tile_256x256x64_mi16"
+                                    3) == "tile_256x256x64_mi16_st"
     assert tsm.tsm_gemm_kernel_name(4096, 50256, 4096, A0, 4096, 0, 0, B0, 50256, 0, 0, C0, 50256, 0, 1,
                                     3) == "tile_256x256x32_mi16_nn"
     assert tsm.tsm_gemm_kernel_name(4096, 50257, 4096, A0, 4096, 0, 0, B0, 4096, 1, 0, C0, 50260, 0, 1,

@@ -14,6 +14,7 @@ pytestmark = pytest.mark.gpu
 # matched as a prefix of the routed kernel and not forced
 CASES = [
     ("tile_256x256x64_mi16", "row", "col", (512, 512, 1024, 1), BF16, "f16"),
+    ("tile_256x256x64_mi16_st", "row", "col", (512, 512, 1280, 1), BF16, "f16"),
     ("tile_256x256x32_mi16", "row", "col", (256, 512, 384, 2), F16, "f32"),
     ("tile_256x256x32_mi32", "row", "col", (512, 256, 256, 1), BF16, "f32"),
     ("tile_256x256x32_mi16_nn", "row", "row", (512, 520, 256, 1), BF16, "f16"),

@@ -23,6 +23,7 @@ FAMILIES = [
     ("masked_64x64x64_vecu", (65, 63, 33, 3), "row", "row"),
     ("masked_64x64x64_vec8", (72, 80, 64, 1), "col", "col"),
     ("tile_256x256x64_mi16", (600, 512, 256, 2), "row", "col"),
+    ("tile_256x256x64_mi16_st", (600, 512, 768, 2), "row", "col"),
     ("tile_256x256x32_mi16", (256, 512, 384, 1), "row", "col"),
     ("tile_256x256x32_mi32", (256, 256, 128, 1), "row", "col"),
     ("tile_256x256x32_mi16_nn", (512, 256, 256, 1), "row", "row"),

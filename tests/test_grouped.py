@@ -58,7 +58,8 @@ def check_grouped(orc, C, A, B, M, N, K, fmt, out_fmt, rows, *, a_layout="row", 
 EDGE_ROWS = [600, 0, 257, 1, -7, 700, 256, 255]
 
 
-@pytest.mark.parametrize("variant,b_layout", [("tile_256x256x64_mi16", "col"), ("tile_256x256x32_mi16", "col"),
+@pytest.mark.parametrize("variant,b_layout", [("tile_256x256x64_mi16_st", "col"), ("tile_256x256x64_mi16", "col"),
+                                              ("tile_256x256x32_mi16", "col"),
                                               ("tile_256x256x32_mi16_nn", "row"), ("tile_256x256x64_mi16_nn", "row"),
                                               ("tile_256x256x32_mi32", "col")])
 @pytest.mark.parametrize("in_fmt,out_fmt", [(BF16, "f16"), (F16, "f32")])

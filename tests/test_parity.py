@@ -55,7 +55,7 @@ def _sample_cells(rng, batch, M, N, n):
 
 # the kernels the benchmark times (the large-K workload: without a workspace; its workspace route is tested
 # with the K split)
-EXPECTED_KERNEL = {"square_bf16_8192": "tile_256x256x64_mi16", "skinny_f16_16x16384x8192_b8": "skinny_m16_n256_k64",
+EXPECTED_KERNEL = {"square_bf16_8192": "tile_256x256x64_mi16_st", "skinny_f16_16x16384x8192_b8": "skinny_m16_n256_k64",
                    "largek_f16_256x256x8192": "splitk_", "ragged_f16_1000x1500x777": "masked_64x64x64_vecu",
                    "single_f16_64x128x128": "masked_64x64x64_vec8"}
 
@@ -200,7 +200,7 @@ TILE = "tile_256x256x"
 TILE_SHAPES = [(256, 256, 128, 1), (512, 768, 384, 1), (256, 512, 1024, 3), (768, 256, 256, 2)]
 # every large-tile variant with the B layout it reads
 TILE_VARIANTS = [("tile_256x256x32_mi32", "col"), ("tile_256x256x32_mi16", "col"), ("tile_256x256x32_mi16_nn", "row"),
-                 ("tile_256x256x64_mi16", "col"), ("tile_256x256x64_mi16_nn", "row")]
+                 ("tile_256x256x64_mi16", "col"), ("tile_256x256x64_mi16_nn", "row"), ("tile_256x256x64_mi16_st", "col")]
 
 
 @pytest.mark.parametrize("shape", TILE_SHAPES, ids=lambda s: "x".join(map(str, s)))
@@ -247,7 +247,7 @@ def test_tile_nn_large_sampled(orc):
     check(C[z, i, j], Cp, Sp, K, "f32", "tile nn 4096 sampled")
 
 
-@pytest.mark.parametrize("variant", ["tile_256x256x32_mi16", "tile_256x256x64_mi16"])
+@pytest.mark.parametrize("variant", ["tile_256x256x32_mi16", "tile_256x256x64_mi16", "tile_256x256x64_mi16_st"])
 def test_tile_kernel_padded_ld_and_strides(orc, monkeypatch, variant):
     """Padded lda/ldb/ldc and batch strides larger than the matrices, still on the tile kernel."""
     monkeypatch.setenv("TSM_GEMM_KERNEL", variant)

@@ -45,7 +45,7 @@ bool ranges_overlap(const void *p, int64_t pbytes, const void *q, int64_t qbytes
 
 enum class Kernel {
   None, Masked8, MaskedU, Small8, SmallU, Tile32, Tile16, Tile16NN, TileW, TileWNN, Tile16TN, Tile16TT, TileWTT, Skinny,
-  SplitK
+  SplitK, TileST
 };
 
 const char *kernel_name(Kernel k, const Problem &p) {
@@ -74,6 +74,8 @@ const char *kernel_name(Kernel k, const Problem &p) {
       return tile_name(6);
     case Kernel::TileWTT:
       return tile_name(7);
+    case Kernel::TileST:
+      return tile_name(8);
     case Kernel::Skinny:
       return skinny_name(p);
     case Kernel::SplitK:
@@ -232,7 +234,7 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
   const int64_t tiles256 =
       ((M + TileInfo::BM - 1) / TileInfo::BM) * ((N + TileInfo::BN - 1) / TileInfo::BN) * batch;
   const bool tile_ok = K > 0 && (tiles256 >= 128 || (tiles256 >= 96 && K >= 4096));
-  if (tile_ok && tile_supports(p, false, false)) out->kernel = Kernel::TileW;
+  if (tile_ok && tile_supports(p, false, false)) out->kernel = Kernel::TileST;
   if (tile_ok && tile_supports(p, false, true)) out->kernel = Kernel::Tile16NN;
   if (tile_ok && tile_supports(p, true, true)) out->kernel = Kernel::Tile16TN;
   if (tile_ok && tile_supports(p, true, false)) out->kernel = Kernel::Tile16TT;
@@ -258,7 +260,7 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
   if (force && *force) {
     const Kernel all[] = {Kernel::Masked8,  Kernel::MaskedU,  Kernel::Small8,   Kernel::SmallU,  Kernel::Tile32,
                           Kernel::Tile16,   Kernel::Tile16NN, Kernel::TileW,    Kernel::TileWNN, Kernel::Tile16TN,
-                          Kernel::Tile16TT, Kernel::TileWTT,  Kernel::Skinny,   Kernel::SplitK};
+                          Kernel::Tile16TT, Kernel::TileWTT,  Kernel::Skinny,   Kernel::SplitK,  Kernel::TileST};
     Kernel want = Kernel::None;
     for (Kernel k : all)
       if (k != Kernel::Skinny && strcmp(force, kernel_name(k, p)) == 0) want = k;
@@ -274,7 +276,7 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
     if (want == Kernel::None) return fail(TSM_ERROR_INVALID_VALUE, "TSM_GEMM_KERNEL=%s names no kernel", force);
     const bool ok = want == Kernel::MaskedU || want == Kernel::SmallU ||
                     ((want == Kernel::Masked8 || want == Kernel::Small8) && a8 && b8) ||
-                    ((want == Kernel::Tile32 || want == Kernel::Tile16 || want == Kernel::TileW) && K > 0 &&
+                    ((want == Kernel::Tile32 || want == Kernel::Tile16 || want == Kernel::TileW || want == Kernel::TileST) && K > 0 &&
                      tile_supports(p, false, false)) ||
                     ((want == Kernel::Tile16NN || want == Kernel::TileWNN) && K > 0 && tile_supports(p, false, true)) ||
                     (want == Kernel::Tile16TN && K > 0 && tile_supports(p, true, true)) ||
@@ -336,6 +338,9 @@ int run(const Plan &pl, void *stream) {
       break;
     case Kernel::TileWTT:
       e = launch_tile(pl.p, 7, s);
+      break;
+    case Kernel::TileST:
+      e = launch_tile(pl.p, 8, s);
       break;
     case Kernel::Skinny:
       e = launch_skinny(pl.p, s);

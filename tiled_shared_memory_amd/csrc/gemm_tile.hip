@@ -98,6 +98,11 @@ template <> struct Ring<3> {
   __device__ static char *b() { return g_b3; }
 };
 
+// A third 64-deep A stage: with it the A slabs ride a 3-stage ring (160 KiB of
+// LDS with the two B stages), see substep_st.
+__shared__ __attribute__((aligned(1024))) char w_a2[WTILE_BYTES];
+__device__ __forceinline__ char *wa3(int s) { return s == 0 ? w_a0 : s == 1 ? w_a1 : w_a2; }
+
 template <int S> struct WRing;
 template <> struct WRing<0> {
   __device__ static char *a() { return w_a0; }
@@ -377,10 +382,55 @@ __device__ __forceinline__ void substep_w(CtxW &c, int j, Frags<16> (&fr)[2], Ac
   }
 }
 
+// Staggered refills (K-contiguous A and B, 64-deep slabs): A on a 3-stage
+// ring, B on a 2-stage one.  Sub-slice U of slab j (A in stage SA = j % 3, B
+// in stage SB = j % 2): U = 0 waits for slab j (only the A copies of slab j+1
+// may still be in flight), passes the barrier and refills the B stage freed by
+// slab j-1 with B's slab j+1; U = 1 refills the A stage freed by slab j-1 with
+// A's slab j+2.  Each half of a slab thus issues half of the copies (32
+// wave-loads per CU, where the two-stage ring issues all 64 in the first
+// half), and A's copies are requested two slabs ahead.
+template <bool BF16, int SA, int SB, int U>
+__device__ __forceinline__ void substep_st(CtxW &c, int j, Frags<16> (&fr)[2], Acc<16> &acc) {
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (U == 0) {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * LOADS) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+  read_frags<16, false, false, 2, U>(wa3(SA), WRing<SB>::b(), fr[U], c.wm, c.wn, c.lane);
+  if constexpr (U == 0) {
+    const int next = min(j + 1, c.nk - 1);  // the last slab again at the end keeps the copy count uniform
+    issue<2 * LOADS>(c.rb, c.offB, (uint32_t)next * c.kstepB, WRing<SB ^ 1>::b(), c.wave);
+  } else {
+    const int next = min(j + 2, c.nk - 1);
+    issue<2 * LOADS>(c.ra, c.offA, (uint32_t)next * c.kstepA, wa3((SA + 2) % 3), c.wave);
+  }
+  mma<BF16, 16>(fr[U ^ 1], acc);  // the previous sub-slice
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);
+  }
+}
+
+template <bool BF16, int J>
+__device__ __forceinline__ void slab_st(CtxW &c, int j, Frags<16> (&fr)[2], Acc<16> &acc) {
+  substep_st<BF16, J % 3, J % 2, 0>(c, j, fr, acc);
+  substep_st<BF16, J % 3, J % 2, 1>(c, j, fr, acc);
+}
+
 template <bool BF16, bool OUT16, int MI, bool ACOL, bool BROW, int KB>
 __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
   static_assert(KB == 1 || MI == 16, "64-deep slabs use 16x16x32 operands");
-  CtxT<LOADS * KB> c;
+  static_assert(KB != 3 || (!ACOL && !BROW), "staggered refills: K-contiguous operands");
+  constexpr int KD = KB == 3 ? 2 : KB;  // slab depth / 32 (KB == 3: 64-deep slabs, staggered refills)
+  CtxT<LOADS * KD> c;
   const int tid = threadIdx.x;
   c.lane = tid & 63;
   c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -453,23 +503,54 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
   c.ra = make_rsrc(A, (uint32_t)((ACOL ? (p.K - 1) * p.lda + vrows : (vrows - 1) * p.lda + p.K) * 2));
   c.rb = make_rsrc(B, (uint32_t)((BROW ? (p.K - 1) * p.ldb + vcols : (vcols - 1) * p.ldb + p.K) * 2));
   if constexpr (ACOL) {
-    slice_offsets_row<LOADS * KB>(c.offA, p.lda, c.wave, lane, (int)vrows);
-    c.kstepA = (uint32_t)(32 * KB * p.lda * 2);
+    slice_offsets_row<LOADS * KD>(c.offA, p.lda, c.wave, lane, (int)vrows);
+    c.kstepA = (uint32_t)(32 * KD * p.lda * 2);
   } else {
-    slice_offsets<LOADS * KB, KB>(c.offA, p.lda, c.wave, lane);
-    c.kstepA = 64 * KB;
+    slice_offsets<LOADS * KD, KD>(c.offA, p.lda, c.wave, lane);
+    c.kstepA = 64 * KD;
   }
   if constexpr (BROW) {
-    slice_offsets_row<LOADS * KB>(c.offB, p.ldb, c.wave, lane, vcols);
-    c.kstepB = (uint32_t)(32 * KB * p.ldb * 2);
+    slice_offsets_row<LOADS * KD>(c.offB, p.ldb, c.wave, lane, vcols);
+    c.kstepB = (uint32_t)(32 * KD * p.ldb * 2);
   } else {
-    slice_offsets<LOADS * KB, KB>(c.offB, p.ldb, c.wave, lane);
-    c.kstepB = 64 * KB;
+    slice_offsets<LOADS * KD, KD>(c.offB, p.ldb, c.wave, lane);
+    c.kstepB = 64 * KD;
   }
   // the host guarantees K is a positive multiple of 128
-  c.nk = (int)(p.K / (BK * KB));
+  c.nk = (int)(p.K / (BK * KD));
 
-  if constexpr (KB == 2) {
+  if constexpr (KB == 3) {
+    // prologue: A slabs 0 and 1, B slab 0 (the issue order the waits count on:
+    // A(0), B(0), A(1), then per slab j: B(j+1) in its first half, A(j+2) in its second)
+    issue<2 * LOADS>(c.ra, c.offA, 0, w_a0, c.wave);
+    issue<2 * LOADS>(c.rb, c.offB, 0, WRing<0>::b(), c.wave);
+    issue<2 * LOADS>(c.ra, c.offA, min(1, c.nk - 1) * c.kstepA, w_a1, c.wave);
+    Frags<16> fr[2];
+#pragma unroll
+    for (int i = 0; i < Frags<16>::NA; ++i) fr[1].a[0][i] = fr[1].b[0][i] = u32x4{0, 0, 0, 0};
+    // six slabs per trip: A's stage repeats every 3, B's every 2
+    int j = 0;
+    for (; j + 6 <= c.nk; j += 6) {
+      slab_st<BF16, 0>(c, j, fr, acc);
+      slab_st<BF16, 1>(c, j + 1, fr, acc);
+      slab_st<BF16, 2>(c, j + 2, fr, acc);
+      slab_st<BF16, 3>(c, j + 3, fr, acc);
+      slab_st<BF16, 4>(c, j + 4, fr, acc);
+      slab_st<BF16, 5>(c, j + 5, fr, acc);
+    }
+    // the remaining 2 or 4 slabs (nk is even)
+    if (j < c.nk) {
+      slab_st<BF16, 0>(c, j, fr, acc);
+      slab_st<BF16, 1>(c, j + 1, fr, acc);
+      if (j + 2 < c.nk) {
+        slab_st<BF16, 2>(c, j + 2, fr, acc);
+        slab_st<BF16, 3>(c, j + 3, fr, acc);
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    mma<BF16, 16>(fr[1], acc);  // the last sub-slice
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the duplicate tail copies
+  } else if constexpr (KB == 2) {
     issue<2 * LOADS>(c.ra, c.offA, 0, WRing<0>::a(), c.wave);
     issue<2 * LOADS>(c.rb, c.offB, 0, WRing<0>::b(), c.wave);
     Frags<16> fr[2];
@@ -643,8 +724,10 @@ hipError_t launch_tile(const Problem &p, int variant, hipStream_t stream) {
       return launch_mi<16, true, true, 1>(p, a, stream);
     case 6:
       return launch_mi<16, true, false, 1>(p, a, stream);
-    default:
+    case 7:
       return launch_mi<16, true, false, 2>(p, a, stream);
+    default:
+      return launch_mi<16, false, false, 3>(p, a, stream);
   }
 }
 
@@ -653,7 +736,8 @@ const char *tile_name(int variant) {
   // no suffix = A row-major, B column-major
   static const char *const names[] = {"tile_256x256x32_mi32",    "tile_256x256x32_mi16",   "tile_256x256x32_mi16_nn",
                                       "tile_256x256x64_mi16",    "tile_256x256x64_mi16_nn", "tile_256x256x32_mi16_tn",
-                                      "tile_256x256x32_mi16_tt", "tile_256x256x64_mi16_tt"};
+                                      "tile_256x256x32_mi16_tt", "tile_256x256x64_mi16_tt",
+                                      "tile_256x256x64_mi16_st"};
   return names[variant];
 }
 
