@@ -2,18 +2,23 @@
 
 A step is one C = A.B call through the C ABI on the headline workload (default:
 the square bf16 product 8192 x 8192 x 8192, A row-major, B column-major, f16
-output), inputs already resident in HBM.  Timing: W untimed warm-up steps, then
-K steps between two device synchronisations, measured with HIP events on the
-stream the kernels are launched on (torch's current stream).  As a second
-estimate, the median over 7 interleaved trials of (t(n2) - t(n1)) / (n2 - n1) is
-reported, which removes fixed launch overheads.
+output), inputs already resident in HBM.  Timing: the step runs untimed for at
+least --settle seconds (the GPU leaves its idle clock only after some tens of
+milliseconds of load: the first 10 steps after an idle gap average 0.87 ms,
+steps 40-50 0.74 ms, the settled rate 0.73 ms), then W untimed warm-up steps,
+then K steps between two device synchronisations, measured with HIP events on
+the stream the kernels are launched on (torch's current stream).  Before any
+timing, one step writes C over a NaN fill and every element is checked finite
+on the GPU.  As a second estimate, the median over 7 interleaved trials of
+(t(n2) - t(n1)) / (n2 - n1) is reported, which removes fixed launch overheads.
 
 Also reported:
   roofline      achieved algorithmic TFLOP/s (or GB/s) of the GEMM kernel against
                 the MI355X peak, plus HBM traffic from committed rocprofv3 counter
                 summaries when they belong to the current kernel source;
-  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
-                (whole output rows), on all host threads it uses;
+  cpu_baseline  the CPU oracle timed on the same workload (the whole product
+                when it takes under --cpu-max-seconds, else whole output rows),
+                on all host threads it uses;
   secondary     the skinny batched workload (16 x 16384 x 8192, batch 8) in
                 GB/s against HBM peak, unless --no-secondary.
 """
@@ -85,17 +90,32 @@ PROFILE_COMMANDS = {
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d RUN_DIR/trace -o bench -- "
              "python3 bench.py WORKLOAD_ARGS --no-cpu-baseline",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d RUN_DIR/fetch -o p -- "
-             "python3 bench.py WORKLOAD_ARGS --no-cpu-baseline --steps 5 --warmup 2",
+             "python3 bench.py WORKLOAD_ARGS --no-cpu-baseline --settle 0 --steps 5 --warmup 2",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d RUN_DIR/write -o p -- "
-             "python3 bench.py WORKLOAD_ARGS --no-cpu-baseline --steps 5 --warmup 2",
+             "python3 bench.py WORKLOAD_ARGS --no-cpu-baseline --settle 0 --steps 5 --warmup 2",
     "cal_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d RUN_DIR/cal_fetch -o c -- "
                  "python3 bench.py --calibrate-copy 1024",
     "cal_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d RUN_DIR/cal_write -o c -- "
                  "python3 bench.py --calibrate-copy 1024",
     "sq": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS "
           "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F16 GRBM_GUI_ACTIVE --output-format csv "
-          "-d RUN_DIR/sq -o p -- python3 bench.py WORKLOAD_ARGS --no-cpu-baseline --steps 5 --warmup 2",
+          "-d RUN_DIR/sq -o p -- python3 bench.py WORKLOAD_ARGS --no-cpu-baseline --settle 0 --steps 5 --warmup 2",
 }
+# Where the MFMA pipes lose cycles: the same passes on the headline kernel (KERNEL_ARGS: none) and on
+# torch.matmul (KERNEL_ARGS: --torch-reference), one pass per counter group.
+STALL_PASSES = {
+    "waits": "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_VALU_MFMA_BUSY_CYCLES "
+             "SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VMEM GRBM_GUI_ACTIVE",
+    "vmem_latency": "VmemLatency",
+    "lds_latency": "LdsLatency",
+    "fifo": "SQ_WAIT_INST_LDS SQ_LDS_DATA_FIFO_FULL SQ_LDS_CMD_FIFO_FULL SQ_VMEM_TA_ADDR_FIFO_FULL "
+            "SQ_VMEM_TA_CMD_FIFO_FULL SQ_ACTIVE_INST_SCA SQ_ACTIVE_INST_MISC SQ_INSTS_SALU GRBM_GUI_ACTIVE",
+    "l1": "TA_TA_BUSY TA_ADDR_STALLED_BY_TC_CYCLES TCP_TCC_READ_REQ_LATENCY TCP_TCC_READ_REQ "
+          "TCP_PENDING_STALL_CYCLES TCP_TCP_TA_DATA_STALL_CYCLES GRBM_GUI_ACTIVE",
+    "tlb": "TCP_UTCL1_SERIALIZATION_STALL TCP_TOTAL_CACHE_ACCESSES TCP_UTCL1_STALL_INFLIGHT_MAX GRBM_GUI_ACTIVE",
+}
+STALL_COMMAND = ("rocprofv3 --pmc COUNTERS --output-format csv -d RUN_DIR/stall_WHO_PASS -o p -- python3 bench.py "
+                 "KERNEL_ARGS --no-cpu-baseline --no-secondary --settle 0 --steps 5 --warmup 2")
 WORKLOAD_FLAGS = ("--workload", "--secondary", "--no-secondary")
 
 
@@ -168,6 +188,18 @@ def summarize(run_dir):
     for wl, kern, _ in jobs:
         lines.append(f"# {wl}: {kern} = {_pick(by_name, kern)}")
     lines.append("# __amd_rocclr_copyBuffer = input uploads")
+    # per-dispatch resources from the kernel trace: the run-time half of the zero-scratch check
+    trace = _csv(os.path.join(run_dir, "trace", "*kernel_trace.csv"))
+    res_cols = ("Scratch_Size", "VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "LDS_Block_Size")
+    resources = {}
+    for r in trace:
+        resources.setdefault(r["Kernel_Name"], set()).add(tuple(r.get(c, "?") for c in res_cols))
+    for wl, kern, _ in jobs:
+        sym = _pick(by_name, kern)
+        for vals in sorted(resources.get(sym, ())):
+            lines.append(f"# {kern} dispatch resources: " + ", ".join(f"{c} {v}" for c, v in zip(res_cols, vals)))
+            if vals[0] not in ("0", "0.0"):
+                raise SystemExit(f"--summarize: {kern} ran with Scratch_Size {vals[0]}")
     lines.append(",".join(f'"{c}"' for c in stats[0].keys()))
     for r in stats:
         lines.append(",".join(f'"{v}"' if k == "Name" else v for k, v in r.items()))
@@ -220,6 +252,56 @@ def summarize(run_dir):
                "commands": [cmd("fetch"), cmd("write"), cmd("cal_fetch"), cmd("cal_write")]}
         json.dump(rec, open(os.path.join(out, f"traffic_{wl}.json"), "w"), indent=1)
         print(f"{wl}: {kern}, HBM {hbm_r + hbm_w:.4g} B/launch ({(hbm_r + hbm_w) / w.bytes:.2f}x algorithmic)")
+    if os.path.isdir(os.path.join(run_dir, "stall_ours_waits")):
+        summarize_stalls(run_dir, jobs[0], src, per_kernel.get(jobs[0][1]))
+
+
+def summarize_stalls(run_dir, job, src, kern_hash):
+    """profiles/stall_counters__<kernel>__<workload>.txt: the STALL_PASSES counters of the headline kernel beside
+    torch.matmul's, averaged over the dispatches after the first, with the ratios that locate lost MFMA cycles."""
+    wl, kern, _ = job
+
+    def load(who):
+        vals = {}
+        for ps in STALL_PASSES:
+            rows = _csv(os.path.join(run_dir, f"stall_{who}_{ps}", "*counter_collection.csv"))
+            fam = "Cijk" if who == "ref" else KERNEL_SYMBOL[next(k for k in KERNEL_SYMBOL if kern.startswith(k))] + "<"
+            per = {}
+            for r in rows:
+                if fam in r["Kernel_Name"]:
+                    per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            for c, xs in per.items():
+                xs = xs[1:] if len(xs) > 1 else xs
+                vals[(c, ps)] = sum(xs) / len(xs)
+        return vals
+
+    ours, ref = load("ours"), load("ref")
+    cmd = lambda who, ps: " ".join(("cd /tmp && " + STALL_COMMAND.replace("COUNTERS", STALL_PASSES[ps])  # noqa: E731
+                                    .replace("WHO", who).replace("PASS", ps)
+                                    .replace("KERNEL_ARGS", "--torch-reference" if who == "ref" else "")).split())
+    txt = [f"# where the MFMA pipes lose cycles: {kern} beside torch.matmul (hipBLASLt) on {wl}, one MI355X",
+           f"# kernel source hash: {kern_hash} ({kern}'s sources); {src} (all of csrc/)",
+           "# averages per dispatch over the dispatches after the first; one pass per counter group:"]
+    txt += [f"#   {cmd('ours', ps)}" for ps in STALL_PASSES]
+    txt += ["#   the same with --torch-reference for the torch.matmul column",
+            f'"counter","pass","{kern}","torch.matmul"']
+    for (c, ps) in sorted(ours):
+        txt.append(f'"{c}","{ps}",{ours[(c, ps)]:.6g},{ref.get((c, ps), float("nan")):.6g}')
+
+    def derived(v):
+        g = v[("GRBM_GUI_ACTIVE", "waits")] / 8  # cycles per XCD
+        wc = v[("SQ_WAVE_CYCLES", "waits")]
+        return {"MFMA busy / (1024 SIMDs x cycles)": v[("SQ_VALU_MFMA_BUSY_CYCLES", "waits")] / (1024 * g),
+                "SQ_WAIT_ANY / SQ_WAVE_CYCLES": v[("SQ_WAIT_ANY", "waits")] / wc,
+                "L2 read latency (cycles)": v[("TCP_TCC_READ_REQ_LATENCY", "l1")] / v[("TCP_TCC_READ_REQ", "l1")],
+                "VMEM latency (cycles)": v[("VmemLatency", "vmem_latency")],
+                "LDS latency (cycles)": v[("LdsLatency", "lds_latency")]}
+    do, dr = derived(ours), derived(ref)
+    txt.append("# derived:")
+    txt += [f"#   {k}: {do[k]:.3f} ({kern}) vs {dr[k]:.3f} (torch.matmul)" for k in do]
+    name = f"stall_counters__{kern}__{wl}.txt"
+    open(os.path.join(ROOT, "profiles", name), "w").write("\n".join(txt) + "\n")
+    print(f"wrote profiles/{name}")
 
 
 class Setup:
@@ -275,6 +357,31 @@ class Setup:
     def step(self):
         self.call(*self.args, self.handle)
 
+    def settle(self, seconds):
+        """Run the step untimed for at least `seconds` of wall time (the GPU clock leaves its idle state)."""
+        torch = self.torch
+        t0, n = time.perf_counter(), 0
+        while True:
+            for _ in range(8):
+                self.step()
+            n += 8
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= seconds:
+                return {"seconds": round(time.perf_counter() - t0, 3), "steps": n}
+
+    def all_written(self):
+        """One step over a NaN-filled C: every output element must come back finite (checked on the GPU)."""
+        torch = self.torch
+        self.c.fill_(float("nan"))
+        self.step()
+        torch.cuda.synchronize()
+        if self.rows is not None:  # only the rows each group computes are written
+            c = self.c.view(self.w.batch, self.w.M, self.w.N)
+            ok = all(bool(torch.isfinite(c[g, :int(r)]).all()) for g, r in enumerate(self.rows))
+        else:
+            ok = bool(torch.isfinite(self.c).all())
+        return ok
+
     def time_steps(self, n):
         torch = self.torch
         e0 = torch.cuda.Event(enable_timing=True)
@@ -321,11 +428,11 @@ class Setup:
         return {"cells": ncells, "max_err_over_bound": ratio, "pass": bool(ratio <= 1.0 and np.all(np.isfinite(got)))}
 
 
-def cpu_baseline(orc, w, A, B, target_s):
-    """Oracle timed on whole output rows of problem 0; rows chosen for about target_s seconds.
+def cpu_baseline(orc, w, A, B, target_s, max_s):
+    """Oracle timed on problem 0 of the workload: the whole product when two short runs predict it takes at most
+    max_s seconds, else whole output rows chosen for about target_s seconds.
 
-    Two short runs fit t(rows) = fixed + per_row * rows (the fixed part decodes
-    B); the timed run then takes about target_s seconds.
+    The short runs fit t(rows) = fixed + per_row * rows (the fixed part decodes B).
     """
     def run(rows):
         t0 = time.perf_counter()
@@ -337,13 +444,14 @@ def cpu_baseline(orc, w, A, B, target_s):
     t1, t2 = run(r1), run(r2)
     per_row = max((t2 - t1) / max(r2 - r1, 1), 1e-6)
     fixed = max(t1 - per_row * r1, 0.0)
-    rows = max(1, min(w.M, int((target_s - fixed) / per_row)))
+    full = fixed + per_row * w.M <= max_s
+    rows = w.M if full else max(1, min(w.M, int((target_s - fixed) / per_row)))
     t = run(rows)
     flops = 2.0 * rows * w.N * w.K
+    what = (f"the whole product of problem 0 ({w.M} x {w.N} x {w.K} fp64 multiply-adds" if full else
+            f"rows 0..{rows - 1} of problem 0 ({rows} x {w.N} x {w.K} fp64 multiply-adds")
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": orc.threads(), "cpu": cpu_model(), "kind": "oracle",
-            "sample": f"rows 0..{rows - 1} of problem 0 ({rows} x {w.N} x {w.K} fp64 multiply-adds, "
-                      f"{t:.1f} s including the decode of B)",
-            "seconds": t}
+            "sample": f"{what}, {t:.1f} s including the decode of B)", "seconds": t, "full_product": full}
 
 
 def cpu_model() -> str:
@@ -433,6 +541,7 @@ def torch_reference(args, w, torch, tsm):
     else:  # batched products in 16-bit with a transposed right operand: made contiguous first
         a, b = a.contiguous(), b.contiguous()
     s.step = lambda: torch.matmul(a, b)
+    s.settle(args.settle)
     for _ in range(args.warmup):
         s.step()
     torch.cuda.synchronize()
@@ -451,7 +560,11 @@ def main():
     ap.add_argument("--workload", default="square_bf16_8192")
     ap.add_argument("--secondary", default="skinny_f16_16x16384x8192_b8")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the CPU-baseline sample")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of a sampled CPU baseline")
+    ap.add_argument("--cpu-max-seconds", type=float, default=90.0,
+                    help="time the oracle on the whole product when it is predicted to take at most this long")
+    ap.add_argument("--settle", type=float, default=0.3,
+                    help="seconds of untimed steps before the warm-up, so the GPU clock has left its idle state")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--torch-reference", action="store_true",
                     help="time torch.matmul on the workload's operands instead (a reference line, not the benchmark)")
@@ -504,7 +617,10 @@ def main():
         return
     act = {"none": 0, "relu": 1, "leaky_relu": 2}[args.activation]
     s = Setup(w, torch, tsm, act, args.slope if act == 2 else 0.0, workspace=not args.no_workspace)
-    log(f"kernel {s.kernel}; warm-up {args.warmup}")
+    written = s.all_written()
+    settle = s.settle(args.settle)
+    log(f"kernel {s.kernel}; every output written: {written}; settled {settle['steps']} steps in "
+        f"{settle['seconds']} s; warm-up {args.warmup}")
     for _ in range(args.warmup):
         s.step()
     torch.cuda.synchronize()
@@ -518,6 +634,8 @@ def main():
 
     orc = oracle.default()
     check = s.check_cells(orc)
+    check["every_output_written"] = written
+    check["pass"] = bool(check["pass"] and written)
     tflops = w.flops / (ms * 1e-3) / 1e12
     gbs = w.bytes / (ms * 1e-3) / 1e9
     compute_bound = w.flops / w.bytes > MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -551,6 +669,7 @@ def main():
         "pct_of_mfma_peak": 100.0 * tflops / MFMA_PEAK_TFLOPS,
         "hbm_gbs_algorithmic": gbs,
         "ms_per_step_interleaved_median": ms_interleaved,
+        "settle": settle,
         "check": check,
         "roofline": roof,
         "kernel_source_hash": kernel_source_hash(),
@@ -570,6 +689,8 @@ def main():
     if not args.no_secondary and args.secondary:
         w2 = lookup(args.secondary)
         s2 = Setup(w2, torch, tsm)
+        written2 = s2.all_written()
+        s2.settle(args.settle)
         for _ in range(max(3, args.warmup // 2)):
             s2.step()
         torch.cuda.synchronize()
@@ -577,6 +698,8 @@ def main():
         ms2 = s2.time_steps(n2) / n2
         ms2i = s2.interleaved_ms()
         check2 = s2.check_cells(orc)
+        check2["every_output_written"] = written2
+        check2["pass"] = bool(check2["pass"] and written2)
         gbs2 = w2.bytes / (ms2 * 1e-3) / 1e9
         result["secondary"] = {
             "workload": w2.name, "kernel": s2.kernel, "ms_per_step": ms2, "ms_per_step_interleaved_median": ms2i,
@@ -590,8 +713,8 @@ def main():
         del s2
 
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(orc, w, s_main.A, s_main.B, args.cpu_seconds)
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(orc, w, s_main.A, s_main.B, args.cpu_seconds, args.cpu_max_seconds)
     print(json.dumps(result), flush=True)
 
 
