@@ -231,6 +231,31 @@ int gemm_strided_batched_ws(int64_t M, int64_t N, int64_t K, const void *A, int6
                             int64_t ldc, int64_t strideC, int64_t batch, int dtype, int activation, float slope,
                             void *workspace, int64_t workspace_bytes, void *stream);
 
+/*
+ * gemm_strided_batched_noalloc -- gemm_strided_batched_ws for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the K split's partial sums go to a
+ * static scratch array of gemm_noalloc_scratch_bytes() (64 MiB) that the
+ * library holds on each GPU from its load until the process ends.  The call
+ * allocates nothing.  It splits K exactly when gemm_strided_batched_ws would
+ * with a workspace of gemm_workspace_bytes(M, N, K, batch) bytes; shapes that
+ * do not split run as gemm_strided_batched_act.
+ * Calls on one GPU share its scratch: calls that overlap on one GPU (other
+ * streams, other host threads) race and must not be issued.  The scratch
+ * needs no clearing (every partial read back was written by the same call).
+ * Arguments and errors as for gemm_strided_batched_act; additionally
+ * TSM_ERROR_NOT_SUPPORTED when the split would need more than the scratch
+ * holds (the detail names the size; use gemm_strided_batched_ws then), and
+ * TSM_ERROR_LAUNCH when the scratch's device address cannot be obtained.
+ */
+int gemm_strided_batched_noalloc(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a,
+                                 int64_t strideA, const void *B, int64_t ldb, int layout_b, int64_t strideB, void *C,
+                                 int64_t ldc, int64_t strideC, int64_t batch, int dtype, int activation, float slope,
+                                 void *stream);
+
+/* Bytes of the static scratch gemm_strided_batched_noalloc splits K through. */
+int64_t gemm_noalloc_scratch_bytes(void);
+
 /* Static text for a status code ("success", "invalid value", ...). */
 const char *tsm_status_string(int status);
 

@@ -426,3 +426,23 @@ def test_ragged_n_routes_to_the_tile_kernel():
                                     3) == "tile_256x256x32_mi16_nn"
     assert tsm.tsm_gemm_kernel_name(4096, 50257, 4096, A0, 4096, 0, 0, B0, 4096, 1, 0, C0, 50260, 0, 1,
                                     3).startswith("masked_")
+
+
+def test_noalloc_scratch_covers_every_split():
+    """The static scratch of the allocation-free entry point (64 MiB) holds every K split the planner makes:
+    about 256 workgroups with at most one 256 x 256 float32 partial tile each.  Swept over squares, decode-like
+    rows, deep K and batches; invalid arguments are rejected as by the other entry points (host logic only)."""
+    cap = tsm.gemm_noalloc_scratch_bytes()
+    assert cap == 64 << 20
+    most = 0
+    for M in list(range(16, 513, 48)) + list(range(512, 8193, 512)):
+        for N in (64, 256, 1024, 4096, 16384):
+            for K in (512, 2048, 8192, 65536):
+                for batch in (1, 2, 8):
+                    most = max(most, tsm.gemm_workspace_bytes(M, N, K, batch))
+    assert 0 < most <= cap
+    lib = tsm.load()
+    st = lib.gemm_strided_batched_noalloc(-1, 8, 8, A0, 8, 0, 0, B0, 8, 0, 0, C0, 8, 0, 1, 0, 0, 0.0, None)
+    assert st == tsm.TSM_ERROR_INVALID_VALUE
+    st = lib.gemm_strided_batched_noalloc(8, 8, 8, A0, 8, 0, 0, B0, 8, 0, 0, C0, 8, 0, 1, 9, 0, 0.0, None)
+    assert st == tsm.TSM_ERROR_INVALID_VALUE and "dtype" in tsm.tsm_last_error_detail()

@@ -13,7 +13,8 @@ from ._lib import (TSM_ACT_LEAKY_RELU, TSM_ACT_NONE, TSM_ACT_RELU, TSM_BF16_BF16
                    TSM_BF16_F32, TSM_COL, TSM_ERROR_INVALID_VALUE, TSM_ERROR_LAUNCH, TSM_ERROR_NOT_SUPPORTED,
                    TSM_F16_BF16, TSM_F16_F16, TSM_F16_F32, TSM_ROW, TSM_ROWSUM_BF16, TSM_ROWSUM_F16, TSM_ROWSUM_F32,
                    TSM_SUCCESS, TsmError, gemm, gemm_ex, gemm_grouped, gemm_strided_batched,
-                   gemm_strided_batched_act, gemm_strided_batched_ex, gemm_strided_batched_ws, gemm_workspace_bytes,
+                   gemm_noalloc_scratch_bytes, gemm_strided_batched_act, gemm_strided_batched_ex,
+                   gemm_strided_batched_noalloc, gemm_strided_batched_ws, gemm_workspace_bytes,
                    load, rowsum, tsm_gemm_grouped_kernel_name, tsm_gemm_kernel_name, tsm_gemm_ws_kernel_name,
                    tsm_last_error_detail, tsm_rowsum_kernel_name, tsm_status_string)
 

@@ -63,6 +63,9 @@ SIGNATURES = {
     "gemm_workspace_bytes": ([_I64, _I64, _I64, _I64], _I64),
     "gemm_strided_batched_ws": ([_I64, _I64, _I64, _PTR, _I64, _INT, _I64, _PTR, _I64, _INT, _I64, _PTR, _I64, _I64,
                                  _I64, _INT, _INT, ctypes.c_float, _PTR, _I64, _PTR], _INT),
+    "gemm_strided_batched_noalloc": ([_I64, _I64, _I64, _PTR, _I64, _INT, _I64, _PTR, _I64, _INT, _I64, _PTR, _I64,
+                                      _I64, _I64, _INT, _INT, ctypes.c_float, _PTR], _INT),
+    "gemm_noalloc_scratch_bytes": ([], _I64),
     "tsm_gemm_ws_kernel_name": ([_I64, _I64, _I64, _PTR, _I64, _INT, _I64, _PTR, _I64, _INT, _I64, _PTR, _I64, _I64,
                                  _I64, _INT, _PTR, _I64], ctypes.c_char_p),
 }
@@ -169,6 +172,18 @@ def gemm_strided_batched_ws(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b
     return _check(lib, lib.gemm_strided_batched_ws(M, N, K, _ptr(A), lda, layout_a, strideA, _ptr(B), ldb, layout_b,
                                                    strideB, _ptr(C), ldc, strideC, batch, dtype, activation, slope,
                                                    _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def gemm_strided_batched_noalloc(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, strideB, C, ldc, strideC,
+                                 batch, dtype, activation, slope, stream=None):
+    lib = load()
+    return _check(lib, lib.gemm_strided_batched_noalloc(M, N, K, _ptr(A), lda, layout_a, strideA, _ptr(B), ldb,
+                                                        layout_b, strideB, _ptr(C), ldc, strideC, batch, dtype,
+                                                        activation, slope, _stream(stream)))
+
+
+def gemm_noalloc_scratch_bytes():
+    return int(load().gemm_noalloc_scratch_bytes())
 
 
 def tsm_gemm_ws_kernel_name(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, strideB, C, ldc, strideC, batch,

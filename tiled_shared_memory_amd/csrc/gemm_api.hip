@@ -10,6 +10,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "gemm_internal.hpp"
 #include "tsm_gemm.h"
 
@@ -353,6 +355,55 @@ int run(const Plan &pl, void *stream) {
   return TSM_SUCCESS;
 }
 
+// The K split a planned problem takes given enough workspace (none: splits == 0).
+KSplit split_of(const Plan &pl) {
+  if (pl.kernel == Kernel::None || pl.forced) return KSplit{};
+  KSplit k = ksplit_plan(pl.p);
+  if (!k.splits) k = tsplit_plan(pl.p);
+  return k;
+}
+int64_t split_bytes(const Plan &pl, const KSplit &k) { return pl.p.batch * k.splits * pl.p.M * pl.p.N * 4; }
+
+// ---- static scratch (gemm_strided_batched_noalloc) -----------------------------
+// The partial sums of a K split, for callers that cannot allocate: one array
+// per GPU, held from the library's load until the process ends.  Calls on one
+// GPU share it, so calls that overlap on one GPU (two streams, or two host
+// threads) race on it.  The split needs no zeroed memory: pass 1 writes every
+// partial it reads back in pass 2.
+constexpr int64_t kScratchBytes = (int64_t)64 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+// Device address of `scratch` on device `dev`, looked up once per device with
+// that device current (the name `scratch` on the host is a stand-in, not a
+// device address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+int scratch_of(hipStream_t stream, void **out) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TSM_ERROR_LAUNCH, "cannot tell the stream's device: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(TSM_ERROR_NOT_SUPPORTED, "device %d beyond the scratch table", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    void *p = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess || !p)
+      return fail(TSM_ERROR_LAUNCH, "no address for the static scratch on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TSM_SUCCESS;
+}
+
 // Workspace of a K-split call: validated on the host; `ks` gets the split to
 // run (none when the problem does not split, the workspace is too small, or
 // a kernel is forced).
@@ -365,9 +416,8 @@ int ws_check(const Plan &pl, const void *ws, int64_t ws_bytes, KSplit *ks) {
   if (ranges_overlap(ws, ws_bytes, pl.p.C, pl.c_bytes)) return fail(TSM_ERROR_INVALID_VALUE, "workspace overlaps C");
   if (ranges_overlap(ws, ws_bytes, pl.p.A, pl.a_bytes)) return fail(TSM_ERROR_INVALID_VALUE, "workspace overlaps A");
   if (ranges_overlap(ws, ws_bytes, pl.p.B, pl.b_bytes)) return fail(TSM_ERROR_INVALID_VALUE, "workspace overlaps B");
-  KSplit k = ksplit_plan(pl.p);
-  if (!k.splits) k = tsplit_plan(pl.p);
-  if (!k.splits || pl.p.batch * k.splits * pl.p.M * pl.p.N * 4 > ws_bytes) return TSM_SUCCESS;
+  const KSplit k = split_of(pl);
+  if (!k.splits || split_bytes(pl, k) > ws_bytes) return TSM_SUCCESS;
   *ks = k;
   return TSM_SUCCESS;
 }
@@ -485,6 +535,30 @@ const char *tsm_gemm_ws_kernel_name(int64_t M, int64_t N, int64_t K, const void 
   if (tsm::ws_check(pl, workspace, workspace_bytes, &ks) != TSM_SUCCESS) return nullptr;
   return ks.splits ? tsm::ksplit_name(ks, pl.p.b_col) : tsm::kernel_name(pl.kernel, pl.p);
 }
+
+int gemm_strided_batched_noalloc(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a,
+                                 int64_t strideA, const void *B, int64_t ldb, int layout_b, int64_t strideB, void *C,
+                                 int64_t ldc, int64_t strideC, int64_t batch, int dtype, int activation, float slope,
+                                 void *stream) {
+  tsm::Plan pl;
+  int st = tsm::plan(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, strideB, C, ldc, strideC, batch, dtype,
+                     nullptr, false, activation, slope, &pl);
+  if (st != TSM_SUCCESS) return st;
+  const tsm::KSplit ks = tsm::split_of(pl);
+  if (!ks.splits) return tsm::run(pl, stream);
+  const int64_t need = tsm::split_bytes(pl, ks);
+  if (need > tsm::kScratchBytes)
+    return tsm::fail(TSM_ERROR_NOT_SUPPORTED,
+                     "the K split needs %lld bytes of scratch, the static scratch holds %lld (call "
+                     "gemm_strided_batched_ws with a workspace)",
+                     (long long)need, (long long)tsm::kScratchBytes);
+  void *ws = nullptr;
+  st = tsm::scratch_of((hipStream_t)stream, &ws);
+  if (st != TSM_SUCCESS) return st;
+  return tsm::run_ws(pl, ks, ws, stream);
+}
+
+int64_t gemm_noalloc_scratch_bytes(void) { return tsm::kScratchBytes; }
 
 int gemm_grouped(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a, int64_t strideA,
                  const void *B, int64_t ldb, int layout_b, int64_t strideB, void *C, int64_t ldc, int64_t strideC,
