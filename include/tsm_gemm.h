@@ -78,7 +78,10 @@ extern "C" {
 #define TSM_COL 1
 
 /*
- * gemm -- C := A.B for row-major A (M x K) and row-major B (K x N).
+ * gemm -- C := A.B for row-major A (M x K) and row-major B (K x N): the product
+ * of "The PTSS Cliff", section "The Arithmetic of 'Fully Unrolled K'" (each
+ * output cell the sum over k of A[i][k] * B[k][j]), with the K-tiled, LDS-staged
+ * blocking of its section "The Idea: Stage in SLM, Tile K".
  *   M, N, K   : sizes, >= 0.
  *   A, lda    : operand A and its leading dimension (>= max(1, K)).
  *   B, ldb    : operand B and its leading dimension (>= max(1, N)).
@@ -98,6 +101,10 @@ int gemm(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void
 /*
  * gemm_ex -- gemm with an explicit storage layout per operand
  * (layout_a, layout_b in {TSM_ROW, TSM_COL}); gemm is gemm_ex(TSM_ROW, TSM_ROW).
+ * The Intel XPU Triton README's matmul signature ("Use Proper Type
+ * Annotations") takes a row and a column stride per operand, so either storage
+ * order of A and B is the same product; here the two orders that keep one
+ * dimension contiguous are offered.
  * A column-major B (element (k, j) at B[j*ldb + k], ldb >= K) makes both operands
  * contiguous along K, the layout the square bf16 product uses.
  */
@@ -107,6 +114,12 @@ int gemm_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int lay
 /*
  * gemm_strided_batched -- batch independent products, problem z using
  *   A + z*strideA, B + z*strideB, C + z*strideC   (strides in elements, 64-bit).
+ * The per-problem slices follow the batched indexing of the Intel XPU Triton
+ * README (section "Use Tensor Descriptors to load tl.dot arguments and save
+ * results", one expert's slice of a 3-D operand per program); the offsets are
+ * formed in 64 bits, as its section "Avoid int32 Overflow" requires once a
+ * stride product passes 2^31 (the 8-problem skinny workload's B spans 2^31
+ * bytes).
  * strideA or strideB may be 0 (the operand is shared by every problem).
  * strideC must keep the outputs disjoint: strideC >= (M-1)*ldc + N when batch > 1.
  * batch = 0 succeeds without launching.  Other rules as for gemm.
@@ -115,7 +128,9 @@ int gemm_strided_batched(int64_t M, int64_t N, int64_t K, const void *A, int64_t
                          const void *B, int64_t ldb, int64_t strideB, void *C, int64_t ldc, int64_t strideC,
                          int64_t batch, int dtype, void *stream);
 
-/* gemm_strided_batched_ex -- gemm_strided_batched with per-operand layouts. */
+/* gemm_strided_batched_ex -- gemm_strided_batched with per-operand layouts
+ * (as gemm_ex: the README's per-operand strides, restricted to row- or
+ * column-major storage). */
 int gemm_strided_batched_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a,
                             int64_t strideA, const void *B, int64_t ldb, int layout_b, int64_t strideB, void *C,
                             int64_t ldc, int64_t strideC, int64_t batch, int dtype, void *stream);

@@ -446,3 +446,13 @@ def test_noalloc_scratch_covers_every_split():
     assert st == tsm.TSM_ERROR_INVALID_VALUE
     st = lib.gemm_strided_batched_noalloc(8, 8, 8, A0, 8, 0, 0, B0, 8, 0, 0, C0, 8, 0, 1, 9, 0, 0.0, None)
     assert st == tsm.TSM_ERROR_INVALID_VALUE and "dtype" in tsm.tsm_last_error_detail()
+
+
+@pytest.mark.parametrize("act,slope,status,needle", [(3, 0.0, 1, "activation"),
+                                                     (tsm.TSM_ACT_LEAKY_RELU, float("nan"), 1, "slope")])
+def test_bad_activation_rejected(act, slope, status, needle):
+    """Unknown activations and non-finite leaky slopes are rejected on the host before any GPU call."""
+    with pytest.raises(tsm.TsmError) as ei:
+        tsm.gemm_strided_batched_act(4, 4, 4, 0x7F0000000000, 4, 0, 0, 0x7F1000000000, 4, 0, 0, 0x7F2000000000, 4, 0,
+                                     1, 0, act, slope, 0)
+    assert ei.value.status == status and needle in ei.value.detail

@@ -8,7 +8,8 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import check, run, say
+from gpu_util import DTYPE, LAYOUT, alloc_c, check, run, say, to_device
+import tiled_shared_memory_amd as tsm
 from workloads import WORKLOADS
 from workloads.inputs import F16, BF16, integer_operands, make_operands
 
@@ -61,27 +62,36 @@ EXPECTED_KERNEL = {"square_bf16_8192": "tile_256x256x64_mi16_st", "skinny_f16_16
 
 
 @pytest.mark.parametrize("name", ["square_bf16_8192", "skinny_f16_16x16384x8192_b8"])
-def test_workload_sampled_parity(orc, big_inputs, name):
-    """Full-size workloads: sampled cells and whole rows from the oracle; every output finite."""
+def test_workload_full_size_parity(orc, big_inputs, name):
+    """Full-size workloads, every element against the oracle (computed in row chunks to bound host memory), on the
+    kernel the benchmark times; C is filled with NaN first, so an element the kernel never wrote fails."""
+    import torch
+
     w = WORKLOADS[name]
     A, B = big_inputs(name)
-    say(f"[gpu] {name} M={w.M} N={w.N} K={w.K} batch={w.batch}")
-    C = run(A, B, w.M, w.N, w.K, w.in_fmt, w.out_fmt, batch=w.batch, a_layout=w.a_layout, b_layout=w.b_layout,
-            kernel=EXPECTED_KERNEL.get(name))
-    assert np.all(np.isfinite(C))
-    rng = np.random.default_rng(77)
-    z, i, j = _sample_cells(rng, w.batch, w.M, w.N, 3000)
-    Cp, Sp = orc.gemm_points(A, B, w.M, w.N, w.K, w.in_fmt, z, i, j, strideA=A[0].size, strideB=B[0].size,
-                             a_layout=w.a_layout, b_layout=w.b_layout)
-    r1 = check(C[z, i, j], Cp, Sp, w.K, w.out_fmt, name + " cells")
-    # whole rows: the first, last and one in the middle of problem 0 and the last problem
-    rows = sorted({0, w.M // 2, w.M - 1})
-    for zz in sorted({0, w.batch - 1}):
-        for r in rows:
-            Cr, S = orc.gemm_rows(A[zz:zz + 1], B[zz:zz + 1], w.M, w.N, w.K, w.in_fmt, a_layout=w.a_layout,
-                                  b_layout=w.b_layout, row_begin=r, row_end=r + 1)
-            check(C[zz:zz + 1, r:r + 1], Cr, S, w.K, w.out_fmt, f"{name} row {r} of problem {zz}")
-    say(f"[gpu] {name}: max err/bound on sampled cells = {r1:.3e}")
+    say(f"[gpu] {name} M={w.M} N={w.N} K={w.K} batch={w.batch}, every element")
+    lda, ldb, ldc = w.lds()
+    sA, sB, sC = w.strides()
+    code = DTYPE[(w.in_fmt, w.out_fmt)]
+    a_buf, a_ptr = to_device(A)
+    b_buf, b_ptr = to_device(B)
+    c = alloc_c(w.batch, w.M, w.N, ldc, sC, w.out_fmt, fill=float("nan"))
+    args = (w.M, w.N, w.K, a_ptr, lda, LAYOUT[w.a_layout], sA, b_ptr, ldb, LAYOUT[w.b_layout], sB, c, ldc, sC,
+            w.batch, code)
+    assert tsm.tsm_gemm_kernel_name(*args).startswith(EXPECTED_KERNEL[name])
+    tsm.gemm_strided_batched_ex(*args, 0)
+    torch.cuda.synchronize()
+    host = c.float().cpu().numpy().astype(np.float64)[:w.batch * sC].reshape(w.batch, w.M, ldc)[:, :, :w.N]
+    del c, a_buf, b_buf
+    worst = 0.0
+    chunk = 1024
+    for z in range(w.batch):
+        for r0 in range(0, w.M, chunk):
+            r1 = min(w.M, r0 + chunk)
+            Cr, S = orc.gemm_rows(A[z:z + 1], B[z:z + 1], w.M, w.N, w.K, w.in_fmt, a_layout=w.a_layout,
+                                  b_layout=w.b_layout, row_begin=r0, row_end=r1)
+            worst = max(worst, check(host[z:z + 1, r0:r1], Cr, S, w.K, w.out_fmt, f"{name} problem {z} rows {r0}.."))
+    say(f"[gpu] {name}: every element within the bound, max err/bound = {worst:.3e}")
 
 
 EDGE_SHAPES = [(1, 1, 1), (1, 2, 3), (2, 3, 1), (3, 1, 2), (15, 17, 16), (16, 16, 16), (17, 15, 31),
@@ -516,3 +526,28 @@ def test_tile_ragged_n(orc, monkeypatch, shape, variant, b_layout):
         for i in range(M):
             o = z * M * ldc + i * ldc
             assert np.all(np.isnan(host[o + N:o + ldc])), f"C padding written at problem {z} row {i}"
+
+
+def test_batch_larger_than_one_flat_grid(orc):
+    """A batch whose tiles would need 2^32 or more work-items in one 1-D grid (2^24 + 3 problems of one 64 x 64
+    tile, 256 threads each) runs as 2-D grids of at most 65535 problems.  A and B are broadcast (stride 0), so
+    every problem's C equals the oracle's one product; C starts as NaN, so an unwritten problem fails."""
+    import torch
+
+    M = N = K = 16
+    batch = (1 << 24) + 3
+    A, B = make_operands(5, 1, M, N, K, F16, ("uniform", -1.0, 1.0), "row", "row")
+    a_buf, a_ptr = to_device(A)
+    b_buf, b_ptr = to_device(B)
+    c = torch.full((batch * M * N,), float("nan"), dtype=torch.float16, device="cuda")
+    args = (M, N, K, a_ptr, K, LAYOUT["row"], 0, b_ptr, N, LAYOUT["row"], 0, c, N, M * N, batch, DTYPE[(F16, "f16")])
+    assert tsm.tsm_gemm_kernel_name(*args).startswith("masked_")
+    say(f"[gpu] broadcast batch of {batch} problems {M}x{N}x{K}")
+    tsm.gemm_strided_batched_ex(*args, 0)
+    torch.cuda.synchronize()
+    cv = c.view(batch, M * N)
+    assert bool(torch.isfinite(cv).all())
+    assert bool((cv == cv[0]).all())
+    Cr, S = orc.gemm_rows(A, B, M, N, K, F16)
+    first = cv[0].float().cpu().numpy().astype(np.float64).reshape(1, M, N)
+    check(first, Cr, S, K, "f16", "broadcast batch")

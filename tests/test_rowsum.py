@@ -114,3 +114,19 @@ def test_rowsum_zero_columns_writes_zeros(orc):
     say("[gpu] rowsum C=0")
     got = run_rowsum(np.zeros(4, np.float32), 3, 0, 4, 1, "f32", fill=100.0)
     assert np.array_equal(got, [0.0, 0.0, 0.0])
+
+
+def test_rowsum_more_rows_than_one_launch_covers(orc):
+    """2^26 + 5 single-element rows: more work-items than one launch may have (64 per row), so the rows are
+    split over two launches.  A one-element row sums to that element exactly."""
+    import torch
+
+    R = (1 << 26) + 5
+    x = torch.arange(R, dtype=torch.float32, device="cuda")
+    x = (x % 1021) - 510.0  # exact small integers
+    out = torch.full((R,), float("nan"), dtype=torch.float32, device="cuda")
+    assert tsm.tsm_rowsum_kernel_name(R, 1, x.data_ptr(), 1, 1, tsm.TSM_ROWSUM_F32, out.data_ptr()).startswith("rowsum_wave")
+    say(f"[gpu] rowsum {R} rows of one element")
+    tsm.rowsum(R, 1, x.data_ptr(), 1, 1, tsm.TSM_ROWSUM_F32, out.data_ptr(), 0)
+    torch.cuda.synchronize()
+    assert bool(torch.equal(out, x))

@@ -437,7 +437,7 @@ int rowsum_check(int64_t R, int64_t C, const void *X, int64_t row_stride, int64_
     return fail(TSM_ERROR_INVALID_VALUE, "unknown xdtype %d", xdtype);
   if (R < 0 || C < 0) return fail(TSM_ERROR_INVALID_VALUE, "negative size R=%lld C=%lld", (long long)R, (long long)C);
   if (row_stride < 0 || col_stride < 0) return fail(TSM_ERROR_INVALID_VALUE, "negative stride");
-  *a = RowsumArgs{X, (float *)out, R, C, row_stride, col_stride,
+  *a = RowsumArgs{X, (float *)out, R, C, 0, row_stride, col_stride,
                   xdtype == TSM_ROWSUM_F32 ? (int)RowsumInfo::F32
                                            : xdtype == TSM_ROWSUM_F16 ? (int)RowsumInfo::F16 : (int)RowsumInfo::BF16};
   if (R == 0) return TSM_SUCCESS;

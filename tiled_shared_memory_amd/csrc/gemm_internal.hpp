@@ -172,6 +172,7 @@ struct RowsumArgs {
   const void *X;
   float *out;
   int64_t R, C;
+  int64_t r0;  // first row of this launch (launches cover at most kRowsPerLaunch rows)
   int64_t row_stride, col_stride;  // elements
   int fmt;
 };

@@ -368,7 +368,8 @@ __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
 template <int T, bool BF16, bool OUT16, bool A_KMAJ, bool B_KMAJ, int VEC>
 hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
   const int64_t tiles = (int64_t)base.tiles_m * base.tiles_n;
-  if (batch > 1 && tiles * batch <= 0x7fffffffLL) {
+  // one 1-D grid while its work-items stay below 2^32, else a 2-D grid
+  if (batch > 1 && tiles * batch * THREADS <= 0xffffffffLL) {
     KernelArgs a = base;
     a.z0 = 0;
     a.flat_batch = (int32_t)batch;

@@ -389,6 +389,7 @@ SkinnyPlan skinny_plan(const Problem &p) {
   if (pl.w != 64 && pl.w != 128 && pl.w != 256) return SkinnyPlan{};
   if (pl.w == 256 && pl.mb > 4) return SkinnyPlan{};
   if (p.N % pl.w) return SkinnyPlan{};
+  if ((p.N / pl.w) * 256 > 0xffffffffLL) return SkinnyPlan{};  // a launch's work-items stay below 2^32
   if (p.K % BK || p.K == 0) return SkinnyPlan{};
   if (((uintptr_t)p.A & 15) || ((uintptr_t)p.B & 15) || ((uintptr_t)p.C & 15)) return SkinnyPlan{};
   if (p.lda % 8 || p.ldb % 8 || p.ldc % 4) return SkinnyPlan{};

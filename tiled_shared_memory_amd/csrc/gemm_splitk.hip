@@ -192,7 +192,8 @@ bool splitk_supports(const Problem &p) {
   // a wave's B range (K / 16 rows, or 16 columns) and A rows must span less than 2 GiB
   if ((p.b_col ? 16 * p.ldb : (p.K / WAVES) * p.ldb) >= ((int64_t)1 << 30) || 16 * p.lda >= ((int64_t)1 << 30))
     return false;
-  if ((p.M / 16) * (p.N / 16) > 0x7fffffff / 2) return false;
+  // a launch's work-items (tiles x 1024 threads) stay below 2^32
+  if ((p.M / 16) * (p.N / 16) * (WAVES * 64) > 0xffffffffLL) return false;
   return true;
 }
 

@@ -1,8 +1,11 @@
-// Large-tile MFMA GEMM for gfx950: A row-major, full tiles.
+// Large-tile MFMA GEMM for gfx950.
 //
-// This is the fast path for M and N multiples of 256, K a multiple of 128 and
-// all rows 16-byte aligned, with B either K-contiguous (column-major) or
-// row-major.  The host routes every other problem to the masked kernel.
+// The fast path for K a multiple of 128, N a multiple of 8 and 16-byte
+// aligned rows, in every layout pair (A row- or column-major, B either way),
+// for problems whose 256 x 256 tiles fill most of the chip.  M and N need not
+// be multiples of 256: rows and columns past them load as zero and are not
+// stored (and a grouped call's rows past each problem's count likewise).  The
+// host sends everything else to the masked kernel.
 //
 // Blocking ("The PTSS Cliff", sections "The Idea: Stage in SLM, Tile K" and
 // "Choosing K_TILE"): a 256-thread workgroup owns a 256 x 256 tile of C and
@@ -16,8 +19,7 @@
 // straight into LDS (no VGPR round trip); one wave-wide load fills 1 KiB of
 // LDS, each lane fetching the global chunk that belongs at its LDS slot.  Rows
 // are XOR-swizzled in 16-byte chunks (see swz, swz_row) so that fragment reads
-// are free of bank conflicts.  Two ring shapes, both 128 KiB of the CU's
-// 160 KiB:
+// are free of bank conflicts.  Three ring shapes:
 //  * 32-deep slices, 4 stages: a slice is requested three slices before it is
 //    multiplied.  K-contiguous rows are 64 bytes.
 //  * 64-deep slabs, 2 stages: a slab is requested one slab (two 32-deep
@@ -25,6 +27,9 @@
 //    request carries a whole 128-byte line: half the requests of 64-byte rows
 //    for the same bytes, which is what limits the 32-deep ring on K-contiguous
 //    operands.
+//  * 64-deep slabs with staggered refills (the default for K-contiguous A and
+//    B): A on 3 stages, B on 2 (the whole 160 KiB); each half of a slab issues
+//    half of the copies (see substep_st).
 // Row-major B slices are 256 columns wide (512-byte rows); the B operand is
 // transposed on its way out of LDS by ds_read_b64_tr_b16.
 //
@@ -630,7 +635,8 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
 template <bool BF16, bool OUT16, int MI, bool ACOL, bool BROW, int KB>
 hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
   const int64_t tiles = (int64_t)base.tiles_m * base.tiles_n;
-  if (base.rows && batch <= kMaxCompactGroups && tiles * batch <= 0x7fffffffLL) {
+  // 1-D grids while their work-items stay below 2^32, else a 2-D grid
+  if (base.rows && batch <= kMaxCompactGroups && tiles * batch * 256 <= 0xffffffffLL) {
     // grouped call: one 1-D grid over every tile of every group; the kernel
     // maps the first (valid) ones to real tiles and the rest exit
     KernelArgs a = base;
@@ -640,7 +646,7 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
                        stream, a);
     return hipGetLastError();
   }
-  if (!base.rows && batch > 1 && tiles * batch <= 0x7fffffffLL) {
+  if (!base.rows && batch > 1 && tiles * batch * 256 <= 0xffffffffLL) {
     KernelArgs a = base;
     a.z0 = 0;
     a.flat_batch = (int32_t)batch;

@@ -114,7 +114,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 template <int FMT, bool VEC>
 __global__ __launch_bounds__(256) void rowsum_wave_kernel(RowsumArgs p) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t row = p.r0 + (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= p.R) return;  // uniform per wave; no barrier in this kernel
   const float s = wave_sum(partial<FMT, VEC>(p, row, lane, 64));
   if (lane == 0) p.out[row] = s;
@@ -125,20 +125,31 @@ template <int FMT, bool VEC>
 __global__ __launch_bounds__(256) void rowsum_block_kernel(RowsumArgs p) {
   __shared__ float wsum[4];
   const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
+  const int64_t row = p.r0 + blockIdx.x;
   const float s = wave_sum(partial<FMT, VEC>(p, row, tid, 256));
   if ((tid & 63) == 0) wsum[tid >> 6] = s;
   __syncthreads();
   if (tid == 0) p.out[row] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
 }
 
+// Rows per launch: a launch's work-items (blocks x 256) stay below 2^32.
+constexpr int64_t kBlocksPerLaunch = 0xffffffffLL / 256;
+
 template <int FMT, bool VEC>
-hipError_t launch_t(const RowsumArgs &a, bool block_per_row, hipStream_t stream) {
-  if (block_per_row)
-    hipLaunchKernelGGL((rowsum_block_kernel<FMT, VEC>), dim3((unsigned)a.R), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((rowsum_wave_kernel<FMT, VEC>), dim3((unsigned)((a.R + 3) / 4)), dim3(256), 0, stream, a);
-  return hipGetLastError();
+hipError_t launch_t(const RowsumArgs &args, bool block_per_row, hipStream_t stream) {
+  const int64_t per = block_per_row ? kBlocksPerLaunch : 4 * kBlocksPerLaunch;
+  for (int64_t r0 = 0; r0 < args.R; r0 += per) {
+    RowsumArgs a = args;
+    a.r0 = r0;
+    const int64_t rows = args.R - r0 < per ? args.R - r0 : per;
+    if (block_per_row)
+      hipLaunchKernelGGL((rowsum_block_kernel<FMT, VEC>), dim3((unsigned)rows), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((rowsum_wave_kernel<FMT, VEC>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <int FMT>
