@@ -294,8 +294,10 @@ __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
 
   // Software pipeline: registers hold the next D slices in flight while LDS
   // holds the current one (double-buffered), so a slice's loads have D slices
-  // of work to land behind instead of one.  The loop runs whole rounds of D
-  // slices; slices past K load as zeros (no memory access) and add nothing.
+  // of work to land behind instead of one.  Slices past K load as zeros (no
+  // memory access); the loop stops after the last slice that holds K, and in
+  // that slice after its last 16-deep step that does (the steps past K would
+  // add only zeros).
   constexpr int D = depth<T, VEC>();
   const int64_t nk = (p.K + BK - 1) / BK;
   Stage<T, VEC> ra[D], rb[D];
@@ -317,10 +319,13 @@ __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
   for (int64_t kt = 0; kt < nk; kt += D) {
 #pragma unroll
     for (int u = 0; u < D; ++u) {  // slice kt + u (D is even, so its buffer is u % 2)
+      if (kt + u >= nk) break;     // uniform
       const uint16_t *a_s = sA[u & 1];
       const uint16_t *b_s = sB[u & 1];
+      const int64_t krest = p.K - (kt + u) * BK;  // K left from this slice on
 #pragma unroll
       for (int ks = 0; ks < BK / 16; ++ks) {
+        if (ks > 0 && ks * 16 >= krest) break;  // uniform: the rest of the slice is padding
         const int kk = ks * 16 + (lane >> 5) * 8;
         u32x4 af[NB], bf[NB];
 #pragma unroll
