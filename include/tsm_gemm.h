@@ -209,8 +209,11 @@ int gemm_strided_batched_act(int64_t M, int64_t N, int64_t K, const void *A, int
  * splits K for a problem of this shape: batch * S * M * N * 4 for S chunks of
  * K (the largest S the operands' layouts may lead to), or 0 when the shape
  * does not split (its output tiles already occupy the chip, K is below 512 or
- * not a multiple of 64, or N is not a multiple of 64 or 8).  Depends on the
- * sizes only.  Negative sizes give 0.
+ * not a multiple of 64, or N is not a multiple of 64 or 8).  With stream-K
+ * requested (TSM_GEMM_SPLIT=streamk in the environment), also its need when
+ * larger: 2 * R * 256 * 256 * 4 bytes for R runs (R = the CU count of the
+ * current device, at most 256: 128 MiB).  Depends on the sizes (and then the
+ * CU count) only.  Negative sizes give 0.
  */
 int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t batch);
 
@@ -236,6 +239,17 @@ int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t batch);
  *                     kernel's split (up to 512 rows) needs row-major A, B
  *                     either way; the 256 x 256 tiles' split (above 128 rows,
  *                     one problem) takes any layout.
+ * With TSM_GEMM_SPLIT=streamk in the environment, stream-K (the work-centric
+ * decomposition of Osama et al., PPoPP 2023) replaces the tile split for 32
+ * to 224 tiles of 256 x 256 (one problem or a strided batch, more than 128
+ * rows, K a multiple of 128 from 2048 up): R workgroups, one per CU, take
+ * equal runs of 128-deep slices of the tiles in order; every run meets at
+ * most two tiles and stores a float32 partial tile for each into the
+ * workspace, and a second kernel adds each tile's partials in K order and
+ * stores C once.  The result is the same on every call on devices with the
+ * same CU count.  It is not the default: on MI355X it is slower than the
+ * plain kernel or the tile split for these shapes.  TSM_GEMM_SPLIT=none
+ * keeps the kernel that needs no workspace.
  * Two calls in flight at once must not share a workspace.  Other arguments,
  * rules and errors as for gemm_strided_batched_act; additionally
  * TSM_ERROR_INVALID_VALUE for negative workspace_bytes, a NULL workspace with

@@ -282,6 +282,33 @@ def test_workspace_bytes():
     assert tsm.gemm_workspace_bytes(-1, 256, 8192, 1) == 0
 
 
+def test_streamk_on_request_only(monkeypatch):
+    """Stream-K's workspace (two 256 x 256 float32 partial tiles for each of 256 runs) and route appear only with
+    TSM_GEMM_SPLIT=streamk; by default 144 tiles run unsplit and 128 take the two-chunk tile split."""
+    args = (3072, 3072, 8192, A0, 8192, 0, 0, B0, 8192, 1, 0, C0, 3072, 0, 1, 3)
+    monkeypatch.delenv("TSM_GEMM_SPLIT", raising=False)
+    assert tsm.gemm_workspace_bytes(3072, 3072, 8192, 1) == 0
+    assert tsm.tsm_gemm_ws_kernel_name(*args, W0, 1 << 30) == "tile_256x256x64_mi16_st"
+    assert tsm.gemm_workspace_bytes(4096, 2048, 8192, 1) == 2 * 4096 * 2048 * 4
+    monkeypatch.setenv("TSM_GEMM_SPLIT", "streamk")
+    need = tsm.gemm_workspace_bytes(3072, 3072, 8192, 1)
+    assert need == 2 * 256 * 256 * 256 * 4
+    assert tsm.tsm_gemm_ws_kernel_name(*args, W0, need) == "streamk_tile_256x256x32_mi16+reduce"
+    assert tsm.tsm_gemm_ws_kernel_name(*args, W0, need - 1) == "tile_256x256x64_mi16_st"
+    lay = {(0, 0): "_nn", (1, 0): "_tn", (1, 1): "_tt"}
+    for (la, lb), suffix in lay.items():
+        a2 = (3072, 3072, 8192, A0, 3072 if la else 8192, la, 0, B0, 8192 if lb else 3072, lb, 0, C0, 3072, 0, 1, 3)
+        assert tsm.tsm_gemm_ws_kernel_name(*a2, W0, need) == f"streamk_tile_256x256x32_mi16{suffix}+reduce"
+    # 225 tiles fill 7/8 of the CUs, and up to 128 rows belong to the streaming kernel: stream-K declines both
+    assert tsm.gemm_workspace_bytes(3840, 3840, 8192, 1) == 0
+    for M in (16, 128):
+        assert tsm.tsm_gemm_ws_kernel_name(M, 16384, 8192, A0, 8192, 0, 0, B0, 8192, 1, 0, C0, 16384, 0, 1, 3, W0,
+                                           1 << 30).startswith("skinny_")
+    monkeypatch.setenv("TSM_GEMM_SPLIT", "none")
+    assert tsm.tsm_gemm_ws_kernel_name(4096, 2048, 8192, A0, 8192, 0, 0, B0, 8192, 1, 0, C0, 2048, 0, 1, 3, W0,
+                                       1 << 30) == "tile_256x256x64_mi16_st"
+
+
 def _ws_args(M=256, N=256, K=8192, ws=W0, nbytes=None, lb=0):
     nbytes = tsm.gemm_workspace_bytes(M, N, K, 1) if nbytes is None else nbytes
     ldb = K if lb else N
@@ -429,9 +456,10 @@ def test_ragged_n_routes_to_the_tile_kernel():
 
 
 def test_noalloc_scratch_covers_every_split():
-    """The static scratch of the allocation-free entry point (64 MiB) holds every K split the planner makes:
-    about 256 workgroups with at most one 256 x 256 float32 partial tile each.  Swept over squares, decode-like
-    rows, deep K and batches; invalid arguments are rejected as by the other entry points (host logic only)."""
+    """The static scratch of the allocation-free entry point (64 MiB) holds every K split the planner makes by
+    default: about 256 workgroups with at most one 256 x 256 float32 partial tile each.  Swept over squares,
+    decode-like rows, deep K and batches; invalid arguments are rejected as by the other entry points (host logic
+    only)."""
     cap = tsm.gemm_noalloc_scratch_bytes()
     assert cap == 64 << 20
     most = 0

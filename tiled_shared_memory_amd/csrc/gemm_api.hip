@@ -10,6 +10,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "gemm_internal.hpp"
@@ -355,14 +356,43 @@ int run(const Plan &pl, void *stream) {
   return TSM_SUCCESS;
 }
 
+// CUs of the current device (looked up once per device).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Is stream-K requested (TSM_GEMM_SPLIT=streamk)?  Measured on MI355X it
+// loses to the plain kernel for 144-224 tiles of 256 x 256 and to the tile
+// split below (its runs meet the tiles at staggered K, which defeats the L2
+// sharing of operand panels, and its partial tiles cost a float32 round trip
+// through HBM), so it runs only on request.
+bool streamk_requested() {
+  const char *force = getenv("TSM_GEMM_SPLIT");
+  return force && strcmp(force, "streamk") == 0;
+}
+
 // The K split a planned problem takes given enough workspace (none: splits == 0).
+// TSM_GEMM_SPLIT=none keeps the kernel that needs no workspace, =streamk
+// takes stream-K wherever the problem allows it (tests and tuning).
 KSplit split_of(const Plan &pl) {
   if (pl.kernel == Kernel::None || pl.forced) return KSplit{};
   KSplit k = ksplit_plan(pl.p);
-  if (!k.splits) k = tsplit_plan(pl.p);
-  return k;
+  if (k.splits) return k;
+  const char *force = getenv("TSM_GEMM_SPLIT");
+  if (force && strcmp(force, "none") == 0) return KSplit{};
+  if (streamk_requested()) return sk_plan(pl.p, device_cus());
+  return tsplit_plan(pl.p);
 }
-int64_t split_bytes(const Plan &pl, const KSplit &k) { return pl.p.batch * k.splits * pl.p.M * pl.p.N * 4; }
+int64_t split_bytes(const Plan &pl, const KSplit &k) {
+  return k.sk_runs ? sk_workspace_bytes(k.sk_runs) : pl.p.batch * k.splits * pl.p.M * pl.p.N * 4;
+}
 
 // ---- static scratch (gemm_strided_batched_noalloc) -----------------------------
 // The partial sums of a K split, for callers that cannot allocate: one array
@@ -506,6 +536,10 @@ int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t batch) {
                                tsm::tsplit_shape(M, N, K, batch)};
   for (const tsm::KSplit &ks : cand)
     if (ks.splits && batch * ks.splits * M * N * 4 > most) most = batch * ks.splits * M * N * 4;
+  if (tsm::streamk_requested()) {
+    const tsm::KSplit sk = tsm::sk_shape(M, N, K, batch, tsm::device_cus());
+    if (sk.sk_runs && tsm::sk_workspace_bytes(sk.sk_runs) > most) most = tsm::sk_workspace_bytes(sk.sk_runs);
+  }
   return most;
 }
 

@@ -47,6 +47,8 @@ struct KernelArgs {
   // 0 splits means a plain launch
   int32_t splits, row_blocks;
   int64_t kchunk;  // K depth of every chunk but the last (a multiple of 64)
+  // large-tile kernel, stream-K: the partial slots (2 per workgroup, 256 x 256 float32 each)
+  float *sk_ws;
 };
 
 // Rows of problem z: M, or for a grouped product the caller's count for z
@@ -135,6 +137,7 @@ struct KSplit {
   int mb = 0, row_blocks = 0;
   int w = 64;  // columns per pass-1 workgroup (64 or 256)
   int tile_variant = -1;  // >= 0: pass 1 is that 256 x 256 kernel (a batch of the K chunks), not the skinny one
+  int sk_runs = 0;        // > 0: stream-K instead, tile_variant over this many runs (splits is then 2)
 };
 // Depends on the shape (and, through `wide`, on whether B is row-major);
 // workspace bytes = batch * splits * M * N * 4.
@@ -147,6 +150,11 @@ hipError_t launch_ksplit_pass1(const Problem &p, const KSplit &ks, float *ws, hi
 // pass 1 runs the K chunks as a strided batch of products into the workspace.
 KSplit tsplit_shape(int64_t M, int64_t N, int64_t K, int64_t batch);
 KSplit tsplit_plan(const Problem &p);
+// Stream-K over the 256 x 256 kernels, for single products and strided
+// batches of 256 x 256 tiles that leave part of the chip idle; `cus` is the
+// device's CU count.  Workspace bytes = sk_workspace_bytes(sk_runs).
+KSplit sk_shape(int64_t M, int64_t N, int64_t K, int64_t batch, int cus);
+KSplit sk_plan(const Problem &p, int cus);
 const char *ksplit_name(const KSplit &ks, bool b_col);
 
 // Split-K kernel for small M x N and deep K: 16 x 16 tiles, K split across the
@@ -161,6 +169,11 @@ const char *splitk_name(bool b_col);
 hipError_t launch_skinny(const Problem &p, hipStream_t stream);
 const char *skinny_name(const Problem &p);
 hipError_t launch_tile(const Problem &p, int variant, hipStream_t stream);
+// Stream-K over P workgroups (variants 2, 5, 6 and 8), then the fix-up of the
+// tiles that several workgroups share; ws holds 2 P partial tiles
+// (sk_workspace_bytes).
+hipError_t launch_tile_sk(const Problem &p, int variant, float *ws, int P, hipStream_t stream);
+inline int64_t sk_workspace_bytes(int P) { return (int64_t)P * 2 * TileInfo::BM * TileInfo::BN * 4; }
 const char *tile_name(int variant);
 
 // ---- row sums ----------------------------------------------------------------

@@ -63,14 +63,22 @@ __global__ __launch_bounds__(256) void ksplit_reduce_kernel(ReduceArgs r) {
 
 }  // namespace
 
+// Stream-K (on request only): runs at most 256 (the workspace holds 2
+// partial tiles per run), and tiles from 32 up.
+constexpr int64_t kSkMaxRuns = 256;
+constexpr int64_t kSkMinTiles = 32;
+
 KSplit tsplit_shape(int64_t M, int64_t N, int64_t K, int64_t batch) {
   KSplit ks;
   // up to 128 rows the skinny kernel's split fits better than 256-row tiles
   if (batch != 1 || M <= 128 || N < 8 || K % 128 || K < 1024) return ks;
   const int64_t tiles = ((M + TileInfo::BM - 1) / TileInfo::BM) * ((N + TileInfo::BN - 1) / TileInfo::BN);
-  if (tiles < 8 || tiles >= 128) return ks;
+  if (tiles < 8 || tiles > 128) return ks;
   // about one workgroup per CU, chunks of 512 or more that divide K into
-  // equal multiples of 128 (the chunks run as one strided batch)
+  // equal multiples of 128 (the chunks run as one strided batch).  At 128
+  // tiles two chunks fill the chip (4096 x 2048 x 8192: 111 us against 135 on
+  // the plain kernel); from 129 tiles two chunks need a second round and lose
+  // (3072 x 3072 x 8192: 182 against 133)
   int64_t splits = 256 / tiles;
   if (splits > K / 512) splits = K / 512;
   while (splits >= 2 && (K / 128) % splits) --splits;
@@ -114,7 +122,32 @@ KSplit tsplit_plan(const Problem &p) {
   return ks;
 }
 
+KSplit sk_shape(int64_t M, int64_t N, int64_t K, int64_t batch, int cus) {
+  KSplit ks;
+  // up to 128 rows the skinny kernel's split fits better than 256-row tiles
+  if (M <= 128 || K % 128 || K < 2048 || N < 8) return ks;
+  const int64_t T = ((M + TileInfo::BM - 1) / TileInfo::BM) * ((N + TileInfo::BN - 1) / TileInfo::BN) * batch;
+  const int64_t U = K / 128;
+  const int64_t P = cus < kSkMaxRuns ? cus : kSkMaxRuns;
+  // one run per tile at most (every run then meets at most two tiles), and
+  // worth it while the tiles leave an eighth of the CUs or more idle
+  if (T < kSkMinTiles || 8 * T > 7 * P || T * U > 0x7fffffffLL) return ks;
+  ks.splits = 2;
+  ks.sk_runs = (int)P;
+  return ks;
+}
+
+KSplit sk_plan(const Problem &p, int cus) {
+  KSplit ks = sk_shape(p.M, p.N, p.K, p.batch, cus);
+  if (!ks.splits || p.rows) return KSplit{};
+  if (!tile_supports(p, p.a_col, !p.b_col)) return KSplit{};
+  // the 32-deep kernels: two segments of the 64-deep ones in one workgroup spill
+  ks.tile_variant = p.a_col ? (p.b_col ? 6 : 5) : (p.b_col ? 1 : 2);
+  return ks;
+}
+
 hipError_t launch_ksplit(const Problem &p, const KSplit &ks, float *ws, hipStream_t stream) {
+  if (ks.sk_runs) return launch_tile_sk(p, ks.tile_variant, ws, ks.sk_runs, stream);
   hipError_t e = ks.tile_variant >= 0 ? launch_tile(tsplit_pass1_problem(p, ks, ws), ks.tile_variant, stream)
                                       : launch_ksplit_pass1(p, ks, ws, stream);
   if (e != hipSuccess) return e;

@@ -543,6 +543,18 @@ hipError_t launch_ksplit_pass1(const Problem &p, const KSplit &ks, float *ws, hi
 }
 
 const char *ksplit_name(const KSplit &ks, bool b_col) {
+  if (ks.sk_runs) {
+    switch (ks.tile_variant) {
+      case 1:
+        return "streamk_tile_256x256x32_mi16+reduce";
+      case 2:
+        return "streamk_tile_256x256x32_mi16_nn+reduce";
+      case 5:
+        return "streamk_tile_256x256x32_mi16_tn+reduce";
+      default:
+        return "streamk_tile_256x256x32_mi16_tt+reduce";
+    }
+  }
   if (ks.splits && ks.tile_variant == 3) return "ksplit_tile_256x256x64_mi16+reduce";
   if (ks.splits && ks.tile_variant == 2) return "ksplit_tile_256x256x32_mi16_nn+reduce";
   if (ks.splits && ks.tile_variant == 5) return "ksplit_tile_256x256x32_mi16_tn+reduce";

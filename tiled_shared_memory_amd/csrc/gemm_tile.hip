@@ -430,8 +430,13 @@ __device__ __forceinline__ void slab_st(CtxW &c, int j, Frags<16> (&fr)[2], Acc<
   substep_st<BF16, J % 3, J % 2, 1>(c, j, fr, acc);
 }
 
-template <bool BF16, bool OUT16, int MI, bool ACOL, bool BROW, int KB>
-__global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
+// One tile's product over k0 .. k0+kd (a multiple of 128): the whole K for
+// a data-parallel tile, one stream-K segment otherwise.  PART = false: the
+// sums go through the epilogue into C; PART = true: raw into the 256 x 256
+// float32 partial at `part`.
+template <bool BF16, bool OUT16, int MI, bool ACOL, bool BROW, int KB, bool PART>
+__device__ __forceinline__ void tile_run(const KernelArgs &p, int64_t z, int tm, int tn, int64_t k0, int64_t kd,
+                                         float *part) {
   static_assert(KB == 1 || MI == 16, "64-deep slabs use 16x16x32 operands");
   static_assert(KB != 3 || (!ACOL && !BROW), "staggered refills: K-contiguous operands");
   constexpr int KD = KB == 3 ? 2 : KB;  // slab depth / 32 (KB == 3: 64-deep slabs, staggered refills)
@@ -443,51 +448,15 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
   c.wn = c.wave & 1;
   const int lane = c.lane, wm = c.wm, wn = c.wn;
 
-  // ---- tile order: per-XCD regrouping, then groups of tile rows column by column
-  int tm, tn;
-  int64_t z;
-  if (p.compact_groups) {
-    // Grouped call: number only the tiles that hold rows, group after group,
-    // so the per-XCD regrouping spreads the real work evenly over the XCDs
-    // (the counts are in device memory; every workgroup reads them).
-    const int G = p.compact_groups;
-    int V = 0;
-    for (int g = 0; g < G; ++g) V += work_rows(p, g);
-    V *= p.tiles_n;
-    if ((int)blockIdx.x >= V) return;  // uniform
-    int pid = xcd_remap(blockIdx.x, V);
-    int g = 0;
-    for (; g < G - 1; ++g) {
-      const int t = work_rows(p, g) * p.tiles_n;
-      if (pid < t) break;
-      pid -= t;
-    }
-    tile_order(pid, work_rows(p, g), p.tiles_n, GROUP_M, tm, tn);
-    z = g;
-  } else if (p.flat_batch) {
-    // Strided batch: one 1-D grid over every tile of every problem, so the
-    // per-XCD regrouping gives each XCD a run of tiles of one problem (a
-    // 2-D grid would regroup within each problem only, and the 32 tiles
-    // resident on an XCD would come from several problems' panels:
-    // 8 x 2048 x 2048 x 4096 took 0.261 ms that way against 0.217 ms)
-    const int T = p.tiles_m * p.tiles_n;
-    const int pid = xcd_remap(blockIdx.x, T * p.flat_batch);
-    z = pid / T;
-    tile_order(pid - (int)z * T, p.tiles_m, p.tiles_n, group_rows(p.tiles_m), tm, tn);
-  } else {
-    tile_order(xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n), p.tiles_m, p.tiles_n, group_rows(p.tiles_m), tm, tn);
-    z = (int64_t)p.z0 + blockIdx.y;
-  }
-
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t M = rows_of(p, z);  // this problem's rows
   if (m0 >= M) return;              // the whole tile lies past them (uniform)
   const int64_t vrows = M - m0 < BM ? M - m0 : BM;
   const int vcols = (int)(p.N - n0 < BN ? p.N - n0 : BN);  // valid columns of this tile (N is a multiple of 8)
-  // row m0, k = 0: row-major A starts its panel at row m0, column-major A at column m0
-  const uint16_t *A = p.A + z * p.sA + (ACOL ? m0 : m0 * p.lda);
-  // column n0, k = 0: column-major B starts its panel at row n0, row-major B at column n0
-  const uint16_t *B = p.B + z * p.sB + (BROW ? n0 : n0 * p.ldb);
+  // row m0, k = k0: row-major A starts its panel at row m0, column-major A at column m0
+  const uint16_t *A = p.A + z * p.sA + (ACOL ? m0 + k0 * p.lda : m0 * p.lda + k0);
+  // column n0, k = k0: column-major B starts its panel at row n0, row-major B at column n0
+  const uint16_t *B = p.B + z * p.sB + (BROW ? n0 + k0 * p.ldb : n0 * p.ldb + k0);
 
   Acc<MI> acc;
   if constexpr (MI == 32) {
@@ -502,11 +471,12 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
       for (int j = 0; j < 8; ++j) acc.v[i][j] = f32x4{};
   }
 
-  // Buffer resources cover exactly the operand panels: the tile's valid rows
-  // of A (rows past M load as zero) and 256 rows, or K rows x 256 columns, of
-  // B.  The host keeps each extent below 1 GiB, so all offsets are 32-bit.
-  c.ra = make_rsrc(A, (uint32_t)((ACOL ? (p.K - 1) * p.lda + vrows : (vrows - 1) * p.lda + p.K) * 2));
-  c.rb = make_rsrc(B, (uint32_t)((BROW ? (p.K - 1) * p.ldb + vcols : (vcols - 1) * p.ldb + p.K) * 2));
+  // Buffer resources cover exactly the operand panels over k0 .. k0+kd: the
+  // tile's valid rows of A (rows past M load as zero) and 256 rows, or kd
+  // rows x 256 columns, of B.  The host keeps each extent below 1 GiB, so all
+  // offsets are 32-bit.
+  c.ra = make_rsrc(A, (uint32_t)((ACOL ? (kd - 1) * p.lda + vrows : (vrows - 1) * p.lda + kd) * 2));
+  c.rb = make_rsrc(B, (uint32_t)((BROW ? (kd - 1) * p.ldb + vcols : (vcols - 1) * p.ldb + kd) * 2));
   if constexpr (ACOL) {
     slice_offsets_row<LOADS * KD>(c.offA, p.lda, c.wave, lane, (int)vrows);
     c.kstepA = (uint32_t)(32 * KD * p.lda * 2);
@@ -521,8 +491,8 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
     slice_offsets<LOADS * KD, KD>(c.offB, p.ldb, c.wave, lane);
     c.kstepB = 64 * KD;
   }
-  // the host guarantees K is a positive multiple of 128
-  c.nk = (int)(p.K / (BK * KD));
+  // kd is a positive multiple of 128 (the host checks K, stream-K cuts it in 128s)
+  c.nk = (int)(kd / (BK * KD));
 
   if constexpr (KB == 3) {
     // prologue: A slabs 0 and 1, B slab 0 (the issue order the waits count on:
@@ -600,6 +570,29 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
   }
 
   // ---- epilogue: each register group holds C[m][n + 0..3]
+  if constexpr (PART) {
+    // a stream-K partial: the raw float32 sums of the whole 256 x 256 tile
+    // (rows and columns past M and N hold zeros), row-major, through a buffer
+    // resource: one lane offset, the block row in a scalar offset, the block
+    // column in the instruction's immediate
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(part, BM * BN * 4);
+    const uint32_t lo = (uint32_t)(((wm * 128 + (lane % MI)) * BN + wn * 128 + (MI == 32 ? 4 * (lane >> 5) : 4 * (lane >> 4))) * 4);
+#pragma unroll
+    for (int i = 0; i < 128 / MI; ++i)
+#pragma unroll
+      for (int j = 0; j < 128 / MI; ++j)
+#pragma unroll
+        for (int g = 0; g < (MI == 32 ? 4 : 1); ++g) {
+          f32x4 v;
+          if constexpr (MI == 32)
+            v = f32x4{acc.v[i][j][4 * g + 0], acc.v[i][j][4 * g + 1], acc.v[i][j][4 * g + 2], acc.v[i][j][4 * g + 3]};
+          else
+            v = acc.v[i][j];
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rp, lo + (j * MI + (MI == 32 ? 8 * g : 0)) * 4,
+                                                 i * MI * BN * 4, 0);
+        }
+    return;
+  }
   const int64_t ldc = p.ldc;
   const Epilogue ep = epilogue_of(p);
 #pragma unroll
@@ -632,9 +625,191 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
   }
 }
 
-template <bool BF16, bool OUT16, int MI, bool ACOL, bool BROW, int KB>
-hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
+
+// Tile (z, tm, tn) of linear index t over every tile of a launch: the tiles
+// of the groups' valid row blocks in a grouped call (group after group), else
+// problem after problem; within a problem, the grouped tile order.
+__device__ __forceinline__ void tile_of(const KernelArgs &p, int t, int64_t &z, int &tm, int &tn) {
+  if (p.compact_groups) {
+    int g = 0;
+    for (; g < p.compact_groups - 1; ++g) {
+      const int c = work_rows(p, g) * p.tiles_n;
+      if (t < c) break;
+      t -= c;
+    }
+    tile_order(t, work_rows(p, g), p.tiles_n, GROUP_M, tm, tn);
+    z = g;
+  } else {
+    const int T = p.tiles_m * p.tiles_n;
+    z = t / T;
+    tile_order(t - (int)z * T, p.tiles_m, p.tiles_n, group_rows(p.tiles_m), tm, tn);
+  }
+}
+
+// Tiles of a launch (grouped calls: the valid ones, from the counts in device memory).
+__device__ __forceinline__ int launch_tiles(const KernelArgs &p) {
+  if (!p.compact_groups) return p.tiles_m * p.tiles_n * p.flat_batch;
+  int V = 0;
+  for (int g = 0; g < p.compact_groups; ++g) V += work_rows(p, g);
+  return V * p.tiles_n;
+}
+
+// Stream-K: the 128-deep units of every tile (unit u is tile u / U, K from
+// 128 (u % U)), dealt to P workgroups as contiguous runs, the first r of
+// E + 1 units and the rest of E (the work-centric decomposition of Osama et
+// al., "Stream-K", PPoPP 2023).  Every segment (the part of a run inside one
+// tile) writes float32 partial sums; sk_reduce_kernel adds each tile's
+// partials in run order and stores the tile once: no atomics, no zeroed
+// memory, the same bits on every call ("A Dumb Triton Runtime Error", "The
+// Takeaway and the Final Fix": reduce, then store once).
+struct SkRuns {
+  int64_t U, E, r;
+  __device__ SkRuns(int64_t T, int64_t units, int P) : U(units) {
+    E = T * units / P;
+    r = T * units - E * P;
+  }
+  __device__ int64_t start(int64_t w) const { return w * E + (w < r ? w : r); }
+  __device__ int64_t owner(int64_t u) const {  // run holding unit u
+    const int64_t h = r * (E + 1);
+    return u < h ? u / (E + 1) : r + (u - h) / E;
+  }
+};
+
+template <bool BF16, bool OUT16, int MI, bool ACOL, bool BROW, int KB, bool SK>
+__global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
+  if constexpr (SK) {
+    // Run w (the per-XCD regrouping keeps consecutive runs, and so
+    // consecutive tiles, on one XCD).  The host launches at most one run per
+    // tile (T <= P), so a run has E + 1 <= U units and meets at most two
+    // tiles: its segment in the first goes to partial slot 2w, the one in the
+    // second to slot 2w + 1.  The two are written out (not a loop): a loop
+    // around the tile body holds its scalars across both and spills them.
+    const int P = gridDim.x;
+    const int w = xcd_remap(blockIdx.x, P);
+    const SkRuns runs(launch_tiles(p), p.K / 128, P);
+    const int U = (int)runs.U;  // the host keeps tiles x units below 2^31
+    const int b = (int)runs.start(w), e = (int)runs.start(w + 1);
+    // at most two segments (the host keeps a run within two tiles)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int u = s == 0 ? b : (b / U + 1) * U;  // the second segment starts at the next tile
+      if (u >= e) break;
+      const KernelArgs &q = p;
+      const int t = u / U;
+      const int k0 = u - t * U;
+      const int k1 = k0 + (e - u) < U ? k0 + (e - u) : U;
+      int64_t z;
+      int tm, tn;
+      tile_of(q, t, z, tm, tn);
+      float *part = q.sk_ws + (2 * (int64_t)w + s) * (BM * BN);
+      tile_run<BF16, OUT16, MI, ACOL, BROW, KB, true>(q, z, tm, tn, 128 * (int64_t)k0, 128 * (int64_t)(k1 - k0), part);
+      // the next segment's copies overwrite LDS stages whose last fragment
+      // reads other waves may not have made yet
+      __syncthreads();
+    }
+    return;
+  } else {
+    // ---- tile order: per-XCD regrouping, then groups of tile rows column by column
+    int tm, tn;
+    int64_t z;
+    if (p.compact_groups) {
+      // Grouped call: number only the tiles that hold rows, group after group,
+      // so the per-XCD regrouping spreads the real work evenly over the XCDs
+      // (the counts are in device memory; every workgroup reads them).
+      const int G = p.compact_groups;
+      int V = 0;
+      for (int g = 0; g < G; ++g) V += work_rows(p, g);
+      V *= p.tiles_n;
+      if ((int)blockIdx.x >= V) return;  // uniform
+      int pid = xcd_remap(blockIdx.x, V);
+      int g = 0;
+      for (; g < G - 1; ++g) {
+        const int t = work_rows(p, g) * p.tiles_n;
+        if (pid < t) break;
+        pid -= t;
+      }
+      tile_order(pid, work_rows(p, g), p.tiles_n, GROUP_M, tm, tn);
+      z = g;
+    } else if (p.flat_batch) {
+      // Strided batch: one 1-D grid over every tile of every problem, so the
+      // per-XCD regrouping gives each XCD a run of tiles of one problem (a
+      // 2-D grid would regroup within each problem only, and the 32 tiles
+      // resident on an XCD would come from several problems' panels:
+      // 8 x 2048 x 2048 x 4096 took 0.261 ms that way against 0.217 ms)
+      const int T = p.tiles_m * p.tiles_n;
+      const int pid = xcd_remap(blockIdx.x, T * p.flat_batch);
+      z = pid / T;
+      tile_order(pid - (int)z * T, p.tiles_m, p.tiles_n, group_rows(p.tiles_m), tm, tn);
+    } else {
+      tile_order(xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n), p.tiles_m, p.tiles_n, group_rows(p.tiles_m), tm, tn);
+      z = (int64_t)p.z0 + blockIdx.y;
+    }
+
+    tile_run<BF16, OUT16, MI, ACOL, BROW, KB, false>(p, z, tm, tn, 0, p.K, nullptr);
+  }
+}
+
+// Stream-K fix-up: each tile gets the sum of its segments' partials, added
+// in run order (which is K order), through the epilogue into C.  Block b
+// covers rows 16 (b % 16) .. +15 of tile b / 16, each thread 4 rows of 4
+// consecutive columns (a wave reads 1 KiB of one row at a time).
+template <bool OUT16>
+__global__ __launch_bounds__(256) void sk_reduce_kernel(KernelArgs p, int P) {
+  const int t = (int)(blockIdx.x >> 4);
+  const int T = launch_tiles(p);
+  if (t >= T) return;  // uniform (a grouped call's grid counts every tile)
+  const SkRuns runs(T, p.K / 128, P);
+  const int64_t u0 = (int64_t)t * runs.U;
+  const int64_t w0 = runs.owner(u0), w1 = runs.owner(u0 + runs.U - 1);
+  int64_t z;
+  int tm, tn;
+  tile_of(p, t, z, tm, tn);
+  const int tid = threadIdx.x;
+  const int col = 4 * (tid & 63);
+  const int row0 = 16 * (int)(blockIdx.x & 15) + 4 * (tid >> 6);
+  f32x4 acc[4] = {};
+  for (int64_t w = w0; w <= w1; ++w) {
+    // run w's segment in its first tile is in slot 2w, in its second in 2w + 1
+    const float *src = p.sk_ws + (2 * w + (runs.start(w) < u0 ? 1 : 0)) * (BM * BN) + row0 * BN + col;
+    f32x4 v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const f32x4 *>(src + q * BN);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] += v[q];
+  }
+  const int64_t n = (int64_t)tn * BN + col;
+  if (n >= p.N) return;  // N is a multiple of 8: groups of 4 lie wholly on one side
+  const int64_t M = rows_of(p, z);
+  const Epilogue ep = epilogue_of(p);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t m = (int64_t)tm * BM + row0 + q;
+    if (m >= M) break;
+    const int64_t at = z * p.sC + m * p.ldc + n;
+    store4<OUT16>(OUT16 ? (void *)((uint16_t *)p.C + at) : (void *)((float *)p.C + at), ep, acc[q][0], acc[q][1],
+                  acc[q][2], acc[q][3]);
+  }
+}
+
+template <bool BF16, bool OUT16, int MI, bool ACOL, bool BROW, int KB, bool SK>
+hipError_t launch_t(const KernelArgs &base, int64_t batch, int P, hipStream_t stream) {
   const int64_t tiles = (int64_t)base.tiles_m * base.tiles_n;
+  if constexpr (SK) {
+    // P runs over every tile of every problem (valid tiles of a grouped
+    // call), then the fix-up over the same tiles
+    KernelArgs a = base;
+    a.z0 = 0;
+    if (base.rows)
+      a.compact_groups = (int32_t)batch;
+    else
+      a.flat_batch = (int32_t)batch;
+    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT16, MI, ACOL, BROW, KB, true>), dim3((unsigned)P), dim3(256), 0,
+                       stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((sk_reduce_kernel<OUT16>), dim3((unsigned)(tiles * batch * 16)), dim3(256), 0, stream, a, P);
+    return hipGetLastError();
+  }
   // 1-D grids while their work-items stay below 2^32, else a 2-D grid
   if (base.rows && batch <= kMaxCompactGroups && tiles * batch * 256 <= 0xffffffffLL) {
     // grouped call: one 1-D grid over every tile of every group; the kernel
@@ -642,7 +817,7 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
     KernelArgs a = base;
     a.z0 = 0;
     a.compact_groups = (int32_t)batch;
-    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT16, MI, ACOL, BROW, KB>), dim3((unsigned)(tiles * batch)), dim3(256), 0,
+    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT16, MI, ACOL, BROW, KB, false>), dim3((unsigned)(tiles * batch)), dim3(256), 0,
                        stream, a);
     return hipGetLastError();
   }
@@ -650,7 +825,7 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
     KernelArgs a = base;
     a.z0 = 0;
     a.flat_batch = (int32_t)batch;
-    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT16, MI, ACOL, BROW, KB>), dim3((unsigned)(tiles * batch)), dim3(256), 0,
+    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT16, MI, ACOL, BROW, KB, false>), dim3((unsigned)(tiles * batch)), dim3(256), 0,
                        stream, a);
     return hipGetLastError();
   }
@@ -658,7 +833,7 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
     KernelArgs a = base;
     a.z0 = (int32_t)z0;
     const int64_t nz = batch - z0 < kMaxGridY ? batch - z0 : kMaxGridY;
-    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT16, MI, ACOL, BROW, KB>), dim3((unsigned)tiles, (unsigned)nz), dim3(256), 0,
+    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT16, MI, ACOL, BROW, KB, false>), dim3((unsigned)tiles, (unsigned)nz), dim3(256), 0,
                        stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -666,13 +841,36 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, hipStream_t stream) {
   return hipSuccess;
 }
 
-template <int MI, bool ACOL, bool BROW, int KB>
-hipError_t launch_mi(const Problem &p, const KernelArgs &a, hipStream_t stream) {
+template <int MI, bool ACOL, bool BROW, int KB, bool SK = false>
+hipError_t launch_mi(const Problem &p, const KernelArgs &a, hipStream_t stream, int P = 0) {
   if (p.in_bf16)
-    return p.out16 ? launch_t<true, true, MI, ACOL, BROW, KB>(a, p.batch, stream)
-                     : launch_t<true, false, MI, ACOL, BROW, KB>(a, p.batch, stream);
-  return p.out16 ? launch_t<false, true, MI, ACOL, BROW, KB>(a, p.batch, stream)
-                   : launch_t<false, false, MI, ACOL, BROW, KB>(a, p.batch, stream);
+    return p.out16 ? launch_t<true, true, MI, ACOL, BROW, KB, SK>(a, p.batch, P, stream)
+                     : launch_t<true, false, MI, ACOL, BROW, KB, SK>(a, p.batch, P, stream);
+  return p.out16 ? launch_t<false, true, MI, ACOL, BROW, KB, SK>(a, p.batch, P, stream)
+                   : launch_t<false, false, MI, ACOL, BROW, KB, SK>(a, p.batch, P, stream);
+}
+
+KernelArgs tile_args(const Problem &p) {
+  KernelArgs a{};
+  a.A = p.A;
+  a.B = p.B;
+  a.C = p.C;
+  a.M = p.M;
+  a.N = p.N;
+  a.K = p.K;
+  a.lda = p.lda;
+  a.ldb = p.ldb;
+  a.ldc = p.ldc;
+  a.sA = p.sA;
+  a.sB = p.sB;
+  a.sC = p.sC;
+  a.rows = p.rows;
+  a.act = p.act;
+  a.slope = p.slope;
+  a.out_bf16 = p.out_bf16;
+  a.tiles_m = (int32_t)((p.M + BM - 1) / BM);
+  a.tiles_n = (int32_t)((p.N + BN - 1) / BN);
+  return a;
 }
 
 }  // namespace
@@ -696,25 +894,7 @@ bool tile_supports(const Problem &p, bool a_col, bool b_row) {
 }
 
 hipError_t launch_tile(const Problem &p, int variant, hipStream_t stream) {
-  KernelArgs a{};
-  a.A = p.A;
-  a.B = p.B;
-  a.C = p.C;
-  a.M = p.M;
-  a.N = p.N;
-  a.K = p.K;
-  a.lda = p.lda;
-  a.ldb = p.ldb;
-  a.ldc = p.ldc;
-  a.sA = p.sA;
-  a.sB = p.sB;
-  a.sC = p.sC;
-  a.rows = p.rows;
-  a.act = p.act;
-  a.slope = p.slope;
-  a.out_bf16 = p.out_bf16;
-  a.tiles_m = (int32_t)((p.M + BM - 1) / BM);
-  a.tiles_n = (int32_t)((p.N + BN - 1) / BN);
+  const KernelArgs a = tile_args(p);
   switch (variant) {
     case 0:
       return launch_mi<32, false, false, 1>(p, a, stream);
@@ -734,6 +914,23 @@ hipError_t launch_tile(const Problem &p, int variant, hipStream_t stream) {
       return launch_mi<16, true, false, 2>(p, a, stream);
     default:
       return launch_mi<16, false, false, 3>(p, a, stream);
+  }
+}
+
+hipError_t launch_tile_sk(const Problem &p, int variant, float *ws, int P, hipStream_t stream) {
+  KernelArgs a = tile_args(p);
+  a.sk_ws = ws;
+  switch (variant) {
+    case 2:
+      return launch_mi<16, false, true, 1, true>(p, a, stream, P);
+    case 5:
+      return launch_mi<16, true, true, 1, true>(p, a, stream, P);
+    case 6:
+      return launch_mi<16, true, false, 1, true>(p, a, stream, P);
+    case 1:
+      return launch_mi<16, false, false, 1, true>(p, a, stream, P);
+    default:
+      return hipErrorInvalidValue;
   }
 }
 
