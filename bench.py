@@ -242,6 +242,20 @@ def summarize(run_dir):
                 f"algorithmic {w.bytes:.6g} ({(hbm_r + hbm_w) / w.bytes:.2f}x)",
                 f"# kernel-trace average {float(trace_row['AverageNs']) / 1e6:.4f} ms over {trace_row['Calls']} "
                 f"calls; bench.py ms_per_step in the same run {ms:.4f} ms"]
+        red = None
+        if kern.endswith("+reduce"):
+            # the split's second kernel: the workspace round trip (pass 1 writes the partials, pass 2 reads them)
+            rname = lambda t: next((n for n in t if "tsm::" in n and "reduce_kernel<" in n), None)  # noqa: E731
+            rf, rw, rt = rname(fetch), rname(write), rname(by_name)
+            if rf and rw and rt:
+                red = {"read": fetch[rf]["FETCH_SIZE"] * 1024 * fscale, "write": write[rw]["WRITE_SIZE"] * 1024 * wscale,
+                       "avg_duration_ns": float(by_name[rt][0]["AverageNs"])}
+                txt += [f"[{rf}]",
+                        f"FETCH_SIZE = {fetch[rf]['FETCH_SIZE']:.6g} KiB, WRITE_SIZE = {write[rw]['WRITE_SIZE']:.6g} KiB",
+                        f"# pass 2 HBM bytes = {red['read'] + red['write']:.6g} (read {red['read']:.6g}, write "
+                        f"{red['write']:.6g}); kernel-trace average {red['avg_duration_ns'] / 1e6:.4f} ms",
+                        f"# both passes: {hbm_r + hbm_w + red['read'] + red['write']:.6g} B per call "
+                        f"({(hbm_r + hbm_w + red['read'] + red['write']) / w.bytes:.2f}x algorithmic)"]
         open(os.path.join(out, f"counters__{kern}__{wl}.txt"), "w").write("\n".join(txt) + "\n")
         rec = {"kernel": kern, "workload": wl, "source_hash": per_kernel.get(kern), "hbm_bytes_per_launch": hbm_r + hbm_w,
                "hbm_read_bytes_per_launch": hbm_r, "hbm_write_bytes_per_launch": hbm_w,
@@ -250,6 +264,9 @@ def summarize(run_dir):
                "calibration": f"FETCH_SIZE/WRITE_SIZE of a 1 GiB device-to-device copy (bench.py --calibrate-copy "
                               f"1024): {copy_f:.0f} KiB fetched, {copy_w:.0f} KiB written",
                "commands": [cmd("fetch"), cmd("write"), cmd("cal_fetch"), cmd("cal_write")]}
+        if red:
+            rec["pass2_hbm_bytes_per_call"] = red["read"] + red["write"]
+            rec["pass2_avg_duration_ns"] = red["avg_duration_ns"]
         json.dump(rec, open(os.path.join(out, f"traffic_{wl}.json"), "w"), indent=1)
         print(f"{wl}: {kern}, HBM {hbm_r + hbm_w:.4g} B/launch ({(hbm_r + hbm_w) / w.bytes:.2f}x algorithmic)")
     if os.path.isdir(os.path.join(run_dir, "stall_ours_waits")):
