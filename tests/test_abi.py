@@ -282,6 +282,17 @@ def test_workspace_bytes():
     assert tsm.gemm_workspace_bytes(-1, 256, 8192, 1) == 0
 
 
+def test_launch_limits_planned_on_the_host():
+    """Calls whose one-launch grid would reach 2^32 work-items still plan (the kernels then launch as 2-D grids
+    of at most 65535 problems, or row sums in chunks of rows); the GPU tests run the first and the last."""
+    big = (1 << 24) + 3  # 64 x 64 masked tiles of 256 threads: 2^32 + 768 work-items in one 1-D grid
+    assert tsm.tsm_gemm_kernel_name(16, 16, 16, A0, 16, 0, 0, B0, 16, 0, 0, C0, 16, 256, big, 0).startswith("masked_")
+    # 256 x 256 tiles: a 1-D grid over 2^24 + 3 of them would need 2^32 + 768 work-items too
+    assert tsm.tsm_gemm_kernel_name(256, 256, 128, A0, 128, 0, 0, B0, 128, 1, 0, C0, 256, 65536, big,
+                                    3) == "tile_256x256x64_mi16_st"
+    assert tsm.tsm_rowsum_kernel_name((1 << 26) + 5, 16, A0, 16, 1, tsm.TSM_ROWSUM_F32, C0).startswith("rowsum_wave")
+
+
 def test_streamk_on_request_only(monkeypatch):
     """Stream-K's workspace (two 256 x 256 float32 partial tiles for each of 256 runs) and route appear only with
     TSM_GEMM_SPLIT=streamk; by default 144 tiles run unsplit and 128 take the two-chunk tile split."""
