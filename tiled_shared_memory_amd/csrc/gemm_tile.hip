@@ -46,7 +46,9 @@
 //
 // Epilogue: the operands are fed to the MFMA as (B, A), which makes the
 // accumulator layout hold 4 consecutive columns of one row per register
-// group, so each lane stores 8 bytes (f16) or 16 bytes (float32) at a time.
+// group, so each lane stores 8 bytes (f16) or 16 bytes (float32) at a time,
+// through a buffer resource over the tile's valid part of C (no per-row
+// branches, one 32-bit lane offset per column block).
 #include "gemm_internal.hpp"
 #include "mfma.hpp"
 
@@ -593,19 +595,37 @@ __device__ __forceinline__ void tile_run(const KernelArgs &p, int64_t z, int tm,
         }
     return;
   }
-  const int64_t ldc = p.ldc;
+  // C through a buffer resource that ends at the tile's last valid element:
+  // rows past M (ragged or grouped problems) lie beyond it, and column groups
+  // past N (N is a multiple of 8: groups of 4 lie wholly on one side) get an
+  // offset beyond it, so every store is unconditional.  The host keeps
+  // 256 rows of C below 2^31 bytes.  One lane offset per column block, the
+  // row block added as a constant.
   const Epilogue ep = epilogue_of(p);
+  constexpr int ES = OUT16 ? 2 : 4;
+  const int64_t ldc = p.ldc;
+  const int64_t vr = M - m0 < BM ? M - m0 : BM;
+  const int vc = (int)(p.N - n0 < BN ? p.N - n0 : BN);
+  const __amdgpu_buffer_rsrc_t rc =
+      make_rsrc((char *)p.C + (z * p.sC + m0 * ldc + n0) * ES, (uint32_t)(((vr - 1) * ldc + vc) * ES));
+  const int lr = wm * 128 + (lane % MI);
+  const int lcol = wn * 128 + (MI == 32 ? 4 * (lane >> 5) : 4 * (lane >> 4));
+  uint32_t coff[128 / MI][MI == 32 ? 4 : 1];
+#pragma unroll
+  for (int j = 0; j < 128 / MI; ++j)
+#pragma unroll
+    for (int g = 0; g < (MI == 32 ? 4 : 1); ++g) {
+      // 32x32: group g covers columns 8g + 4*(lane/32) .. +3; 16x16: 4*(lane/16) .. +3
+      const int col = lcol + j * MI + (MI == 32 ? 8 * g : 0);
+      coff[j][g] = col < vc ? (uint32_t)((lr * ldc + col) * ES) : kOutside;
+    }
 #pragma unroll
   for (int i = 0; i < 128 / MI; ++i) {
-    const int64_t m = m0 + wm * 128 + i * MI + (lane % MI);
-    if (m >= M) continue;  // rows past M (ragged or grouped problems)
+    const uint32_t roff = (uint32_t)(i * MI * ldc * ES);
 #pragma unroll
     for (int j = 0; j < 128 / MI; ++j) {
 #pragma unroll
       for (int g = 0; g < (MI == 32 ? 4 : 1); ++g) {
-        // 32x32: group g covers columns 8g + 4*(lane/32) .. +3; 16x16: 4*(lane/16) .. +3
-        const int64_t n = n0 + wn * 128 + j * MI + (MI == 32 ? 8 * g + 4 * (lane >> 5) : 4 * (lane >> 4));
-        if (n >= p.N) continue;  // columns past N (N is a multiple of 8: groups of 4 lie wholly on one side)
         float v0, v1, v2, v3;
         if constexpr (MI == 32) {
           v0 = acc.v[i][j][4 * g + 0];
@@ -618,8 +638,19 @@ __device__ __forceinline__ void tile_run(const KernelArgs &p, int64_t z, int tm,
           v2 = acc.v[i][j][2];
           v3 = acc.v[i][j][3];
         }
-        const int64_t at = z * p.sC + m * ldc + n;
-        store4<OUT16>(OUT16 ? (void *)((uint16_t *)p.C + at) : (void *)((float *)p.C + at), ep, v0, v1, v2, v3);
+        v0 = ep.apply(v0);
+        v1 = ep.apply(v1);
+        v2 = ep.apply(v2);
+        v3 = ep.apply(v3);
+        if constexpr (OUT16) {
+          u32x2 v;
+          v[0] = (uint32_t)ep.to16(v0) | ((uint32_t)ep.to16(v1) << 16);
+          v[1] = (uint32_t)ep.to16(v2) | ((uint32_t)ep.to16(v3) << 16);
+          __builtin_amdgcn_raw_buffer_store_b64(v, rc, coff[j][g] + roff, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{v0, v1, v2, v3}), rc,
+                                                 coff[j][g] + roff, 0, 0);
+        }
       }
     }
   }
@@ -889,6 +920,8 @@ bool tile_supports(const Problem &p, bool a_col, bool b_row) {
   if (((uintptr_t)p.A & 15) || ((uintptr_t)p.B & 15) || ((uintptr_t)p.C & 15)) return false;
   if (p.lda % 8 || p.ldb % 8) return false;
   if (p.ldc % 4) return false;  // 8-byte (f16) / 16-byte (float32) row stores
+  // 32-bit store offsets: 256 rows of C below 2^31 bytes
+  if (256 * p.ldc * (p.out16 ? 2 : 4) >= (int64_t)1 << 31) return false;
   if (p.batch > 1 && (p.sA % 8 || p.sB % 8 || p.sC % 4)) return false;
   return true;
 }
