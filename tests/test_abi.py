@@ -270,7 +270,8 @@ def test_general_kernel_leading_dimension_limit():
 
 def test_workspace_bytes():
     """The K split's workspace depends on the shape only: batch * chunks * M * N * 4 bytes, or 0."""
-    assert tsm.gemm_workspace_bytes(256, 256, 8192, 1) == 16 * 256 * 256 * 4  # sixteen 512-deep chunks
+    # 32-row blocks in eight 1024-deep chunks (64-row blocks would need sixteen chunks of 512, one ring round)
+    assert tsm.gemm_workspace_bytes(256, 256, 8192, 1) == 8 * 256 * 256 * 4
     assert tsm.gemm_workspace_bytes(16, 4096, 4096, 1) == 4 * 16 * 4096 * 4
     assert tsm.gemm_workspace_bytes(100, 192, 1344, 1) == 5 * 100 * 192 * 4  # chunks of 320, the last 64 deep
     assert tsm.gemm_workspace_bytes(8192, 8192, 8192, 1) == 0  # enough output tiles
@@ -327,7 +328,9 @@ def _ws_args(M=256, N=256, K=8192, ws=W0, nbytes=None, lb=0):
 
 
 def test_workspace_routing(monkeypatch):
-    assert tsm.tsm_gemm_ws_kernel_name(*_ws_args()) == "ksplit_skinny_m64_n64_k64+reduce"
+    assert tsm.tsm_gemm_ws_kernel_name(*_ws_args()) == "ksplit_skinny_m32_n64_k64+reduce"
+    # chunks deep enough with 64-row blocks keep them (256 x 512 x 8192: eight 1024-deep chunks)
+    assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(N=512)) == "ksplit_skinny_m64_n64_k64+reduce"
     assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(M=16, N=4096, K=4096)) == "ksplit_skinny_m16_n64_k64+reduce"
     assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(M=24, N=4096, K=4096)) == "ksplit_skinny_m32_n64_k64+reduce"
     # 32 to 127 panels of 256 columns: split those (512-byte row segments of B)
@@ -339,9 +342,9 @@ def test_workspace_routing(monkeypatch):
     args[12] = 1026  # ldc
     assert not tsm.tsm_gemm_ws_kernel_name(*args).startswith("ksplit_")
     # a K-contiguous B splits the same way
-    assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(lb=1, nbytes=1 << 30)) == "ksplit_skinny_m64_n64_k64_t+reduce"
+    assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(lb=1, nbytes=1 << 30)) == "ksplit_skinny_m32_n64_k64_t+reduce"
     # too little workspace, none or a forced kernel: the kernel that needs none
-    assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(nbytes=16 * 256 * 256 * 4 - 4)).startswith("splitk_")
+    assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(nbytes=8 * 256 * 256 * 4 - 4)).startswith("splitk_")
     assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(ws=0, nbytes=0)).startswith("splitk_")
     monkeypatch.setenv("TSM_GEMM_KERNEL", "masked_64x64x64_vec8")
     assert tsm.tsm_gemm_ws_kernel_name(*_ws_args()) == "masked_64x64x64_vec8"

@@ -450,10 +450,10 @@ hipError_t launch_skinny(const Problem &p, hipStream_t stream) {
   return launch_shape<8, 64>(p, a, stream);
 }
 
-KSplit ksplit_shape(int64_t M, int64_t N, int64_t K, int64_t batch, bool wide) {
+namespace {
+// The split with row blocks of 16 * mb rows (splits 0: none).
+KSplit ksplit_for(int64_t M, int64_t N, int64_t K, int64_t batch, bool wide, int mb) {
   KSplit ks;
-  if (M < 1 || N < 64 || N % 64 || K % BK || K < 512 || batch < 1) return ks;
-  const int mb = M <= 16 ? 1 : M <= 32 ? 2 : 4;
   const int64_t row_blocks = (M + 16 * mb - 1) / (16 * mb);
   // every row block reads all of B again: beyond 512 rows the 256 x 256
   // kernels' split (tsplit_shape) reads less
@@ -486,6 +486,25 @@ KSplit ksplit_shape(int64_t M, int64_t N, int64_t K, int64_t batch, bool wide) {
   ks.mb = mb;
   ks.row_blocks = (int)row_blocks;
   ks.w = w;
+  return ks;
+}
+}  // namespace
+
+KSplit ksplit_shape(int64_t M, int64_t N, int64_t K, int64_t batch, bool wide) {
+  if (M < 1 || N < 64 || N % 64 || K % BK || K < 512 || batch < 1) return KSplit{};
+  const int mb = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+  KSplit ks = ksplit_for(M, N, K, batch, wide, mb);
+  // 64-row blocks whose chunks would not fill two rounds of the 64-column
+  // kernel's ring: 32-row blocks reach about as many workgroups with deeper
+  // chunks (and fewer partial slabs), which the ring then pipelines
+  // (256 x 256 x 8192: 32-row blocks in 8 chunks 8.5 us, 64-row blocks in 16
+  // chunks 10.2; 256 x 256 x 4096 7.8 against 9.7; 128 x 256 x 8192 8.3
+  // against 10.4).  Where 64-row chunks are deep enough the extra re-reads of
+  // B lose (256 x 512 x 8192: 11.6 against 10.7).
+  if (mb == 4 && ks.splits && ks.w == 64 && ks.kchunk < 2 * Shape<4, 64>::NS * BK) {
+    const KSplit k2 = ksplit_for(M, N, K, batch, wide, 2);
+    if (k2.splits && k2.w == 64 && k2.kchunk > ks.kchunk) ks = k2;
+  }
   return ks;
 }
 
