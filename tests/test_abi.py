@@ -294,6 +294,34 @@ def test_launch_limits_planned_on_the_host():
     assert tsm.tsm_rowsum_kernel_name((1 << 26) + 5, 16, A0, 16, 1, tsm.TSM_ROWSUM_F32, C0).startswith("rowsum_wave")
 
 
+def test_hybrid_routing(monkeypatch):
+    """A little over whole rounds of 256 x 256 tiles: whole rounds data-parallel, the last round's tiles cut into
+    s equal chunks of K (s * leftover <= 256 runs, s dividing K / 128), one float32 partial tile per run."""
+    monkeypatch.delenv("TSM_GEMM_SPLIT", raising=False)
+
+    def route(M, N, K, la=0, lb=1, nbytes=None):
+        need = tsm.gemm_workspace_bytes(M, N, K, 1) if nbytes is None else nbytes
+        return tsm.tsm_gemm_ws_kernel_name(M, N, K, A0, M if la else K, la, 0, B0, K if lb else N, lb, 0, C0, N, 0, 1,
+                                           3, W0, need)
+
+    tile = 256 * 256 * 4
+    for M, leftover, chunks in ((4352, 16, 16), (4608, 32, 8), (5120, 64, 4), (6144, 128, 2)):
+        assert tsm.gemm_workspace_bytes(M, 4096, 8192, 1) == leftover * chunks * tile
+        assert route(M, 4096, 8192) == "hybrid_tile_256x256x64_mi16_st+reduce"
+    # 289 tiles: 33 left over; 7 chunks do not divide K / 128 = 16, so 4
+    assert tsm.gemm_workspace_bytes(4352, 4104, 2048, 1) == 33 * 4 * tile
+    assert route(4352, 4096, 8192, la=0, lb=0) == "hybrid_tile_256x256x32_mi16_nn+reduce"
+    assert route(4352, 4096, 8192, la=1, lb=0) == "hybrid_tile_256x256x32_mi16_tn+reduce"
+    assert route(4352, 4096, 8192, la=1, lb=1) == "hybrid_tile_256x256x32_mi16_tt+reduce"
+    # whole rounds, or more than half a round left over: no split; one byte short: no split
+    for M, N in ((4096, 4096), (7168, 4096), (5120, 5120)):
+        assert tsm.gemm_workspace_bytes(M, N, 8192, 1) == 0
+        assert route(M, N, 8192, nbytes=1 << 30) == "tile_256x256x64_mi16_st"
+    assert route(4352, 4096, 8192, nbytes=16 * 16 * tile - 1) == "tile_256x256x64_mi16_st"
+    # its workspace fits the allocation-free entry point's scratch
+    assert 16 * 16 * tile <= tsm.gemm_noalloc_scratch_bytes()
+
+
 def test_streamk_on_request_only(monkeypatch):
     """Stream-K's workspace (two 256 x 256 float32 partial tiles for each of 256 runs) and route appear only with
     TSM_GEMM_SPLIT=streamk; by default 144 tiles run unsplit and 128 take the two-chunk tile split."""

@@ -388,9 +388,19 @@ KSplit split_of(const Plan &pl) {
   const char *force = getenv("TSM_GEMM_SPLIT");
   if (force && strcmp(force, "none") == 0) return KSplit{};
   if (streamk_requested()) return sk_plan(pl.p, device_cus());
-  return tsplit_plan(pl.p);
+  k = tsplit_plan(pl.p);
+  if (k.splits) return k;
+  // a little over whole rounds of 256 x 256 tiles: the hybrid, on the large-tile
+  // kernel the plan chose for the whole rounds
+  const int dp_variant = pl.kernel == Kernel::TileST     ? 8
+                         : pl.kernel == Kernel::Tile16NN ? 2
+                         : pl.kernel == Kernel::Tile16TN ? 5
+                         : pl.kernel == Kernel::Tile16TT ? 6
+                                                         : -1;
+  return dp_variant >= 0 ? hybrid_plan(pl.p, device_cus(), dp_variant) : KSplit{};
 }
 int64_t split_bytes(const Plan &pl, const KSplit &k) {
+  if (k.dp_tiles) return hybrid_workspace_bytes(k);
   return k.sk_runs ? sk_workspace_bytes(k.sk_runs) : pl.p.batch * k.splits * pl.p.M * pl.p.N * 4;
 }
 
@@ -536,6 +546,8 @@ int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t batch) {
                                tsm::tsplit_shape(M, N, K, batch)};
   for (const tsm::KSplit &ks : cand)
     if (ks.splits && batch * ks.splits * M * N * 4 > most) most = batch * ks.splits * M * N * 4;
+  const tsm::KSplit hy = tsm::hybrid_shape(M, N, K, batch, tsm::device_cus());
+  if (hy.splits && tsm::hybrid_workspace_bytes(hy) > most) most = tsm::hybrid_workspace_bytes(hy);
   if (tsm::streamk_requested()) {
     const tsm::KSplit sk = tsm::sk_shape(M, N, K, batch, tsm::device_cus());
     if (sk.sk_runs && tsm::sk_workspace_bytes(sk.sk_runs) > most) most = tsm::sk_workspace_bytes(sk.sk_runs);

@@ -49,6 +49,12 @@ struct KernelArgs {
   int64_t kchunk;  // K depth of every chunk but the last (a multiple of 64)
   // large-tile kernel, stream-K: the partial slots (2 per workgroup, 256 x 256 float32 each)
   float *sk_ws;
+  // large-tile kernel, one problem, a range of its tiles in the grouped tile order: tiles
+  // tile0 .. tile0 + tile_count - 1 (tile_count 0: all of them)
+  int32_t tile0, tile_count;
+  // stream-K with runs aligned to whole chunks of one tile (the hybrid's remainder): one
+  // partial slot per run instead of two
+  int32_t sk_aligned;
 };
 
 // Rows of problem z: M, or for a grouped product the caller's count for z
@@ -138,6 +144,9 @@ struct KSplit {
   int w = 64;  // columns per pass-1 workgroup (64 or 256)
   int tile_variant = -1;  // >= 0: pass 1 is that 256 x 256 kernel (a batch of the K chunks), not the skinny one
   int sk_runs = 0;        // > 0: stream-K instead, tile_variant over this many runs (splits is then 2)
+  // > 0: the hybrid instead: this many whole rounds of tiles data-parallel on dp_variant, the
+  // remaining tiles in `splits` chunks of K on tile_variant (stream-K runs of one chunk each)
+  int dp_tiles = 0, dp_variant = -1;
 };
 // Depends on the shape (and, through `wide`, on whether B is row-major);
 // workspace bytes = batch * splits * M * N * 4.
@@ -155,6 +164,11 @@ KSplit tsplit_plan(const Problem &p);
 // device's CU count.  Workspace bytes = sk_workspace_bytes(sk_runs).
 KSplit sk_shape(int64_t M, int64_t N, int64_t K, int64_t batch, int cus);
 KSplit sk_plan(const Problem &p, int cus);
+// The hybrid for one problem a little over whole rounds of 256 x 256 tiles.
+// Workspace bytes = hybrid_workspace_bytes(ks).
+KSplit hybrid_shape(int64_t M, int64_t N, int64_t K, int64_t batch, int cus);
+KSplit hybrid_plan(const Problem &p, int cus, int dp_variant);
+inline int64_t hybrid_workspace_bytes(const KSplit &ks) { return (int64_t)ks.sk_runs * TileInfo::BM * TileInfo::BN * 4; }
 const char *ksplit_name(const KSplit &ks, bool b_col);
 
 // Split-K kernel for small M x N and deep K: 16 x 16 tiles, K split across the
@@ -169,10 +183,17 @@ const char *splitk_name(bool b_col);
 hipError_t launch_skinny(const Problem &p, hipStream_t stream);
 const char *skinny_name(const Problem &p);
 hipError_t launch_tile(const Problem &p, int variant, hipStream_t stream);
-// Stream-K over P workgroups (variants 2, 5, 6 and 8), then the fix-up of the
+// Stream-K over P workgroups (variants 1, 2, 5 and 6), then the fix-up of the
 // tiles that several workgroups share; ws holds 2 P partial tiles
 // (sk_workspace_bytes).
 hipError_t launch_tile_sk(const Problem &p, int variant, float *ws, int P, hipStream_t stream);
+// One problem of more than one round of tiles: the first `dp_tiles` tiles (whole
+// rounds) on the data-parallel kernel `variant`, and the remaining ones split
+// `splits` ways in K as aligned stream-K runs on `sk_variant` (one run per chunk,
+// one 256 x 256 float32 partial slot per run: (tiles - dp_tiles) * splits * 256 KiB
+// of workspace), then their fix-up.
+hipError_t launch_tile_hybrid(const Problem &p, int variant, int sk_variant, int dp_tiles, int splits, float *ws,
+                              hipStream_t stream);
 inline int64_t sk_workspace_bytes(int P) { return (int64_t)P * 2 * TileInfo::BM * TileInfo::BN * 4; }
 const char *tile_name(int variant);
 

@@ -146,7 +146,39 @@ KSplit sk_plan(const Problem &p, int cus) {
   return ks;
 }
 
+KSplit hybrid_shape(int64_t M, int64_t N, int64_t K, int64_t batch, int cus) {
+  KSplit ks;
+  // one problem of more than 128 rows (fewer belong to the streaming kernel's split)
+  if (batch != 1 || M <= 128 || N < 8 || K % 128 || K < 2048) return ks;
+  const int64_t T = ((M + TileInfo::BM - 1) / TileInfo::BM) * ((N + TileInfo::BN - 1) / TileInfo::BN);
+  const int64_t P = cus < kSkMaxRuns ? cus : kSkMaxRuns;
+  if (T <= P || T > 0x7fffffffLL / 2) return ks;
+  const int64_t rem = T % P;
+  if (rem == 0) return ks;
+  // the last round's rem tiles in s equal chunks of K, one run each: s rem <= P runs,
+  // chunks a whole number of 128-deep units
+  const int64_t U = K / 128;
+  int64_t s = P / rem;
+  while (s >= 2 && U % s) --s;
+  if (s < 2) return ks;
+  ks.splits = (int)s;
+  ks.dp_tiles = (int)(T - rem);
+  ks.sk_runs = (int)(rem * s);
+  return ks;
+}
+
+KSplit hybrid_plan(const Problem &p, int cus, int dp_variant) {
+  KSplit ks = hybrid_shape(p.M, p.N, p.K, p.batch, cus);
+  if (!ks.splits || p.rows) return KSplit{};
+  if (!tile_supports(p, p.a_col, !p.b_col)) return KSplit{};
+  ks.dp_variant = dp_variant;
+  ks.tile_variant = p.a_col ? (p.b_col ? 6 : 5) : (p.b_col ? 1 : 2);  // the remainder on the 32-deep kernels
+  return ks;
+}
+
 hipError_t launch_ksplit(const Problem &p, const KSplit &ks, float *ws, hipStream_t stream) {
+  if (ks.dp_tiles)
+    return launch_tile_hybrid(p, ks.dp_variant, ks.tile_variant, ks.dp_tiles, ks.splits, ws, stream);
   if (ks.sk_runs) return launch_tile_sk(p, ks.tile_variant, ws, ks.sk_runs, stream);
   hipError_t e = ks.tile_variant >= 0 ? launch_tile(tsplit_pass1_problem(p, ks, ws), ks.tile_variant, stream)
                                       : launch_ksplit_pass1(p, ks, ws, stream);

@@ -566,6 +566,18 @@ hipError_t launch_ksplit_pass1(const Problem &p, const KSplit &ks, float *ws, hi
 }
 
 const char *ksplit_name(const KSplit &ks, bool b_col) {
+  if (ks.dp_tiles) {
+    switch (ks.dp_variant) {
+      case 8:
+        return "hybrid_tile_256x256x64_mi16_st+reduce";
+      case 2:
+        return "hybrid_tile_256x256x32_mi16_nn+reduce";
+      case 5:
+        return "hybrid_tile_256x256x32_mi16_tn+reduce";
+      default:
+        return "hybrid_tile_256x256x32_mi16_tt+reduce";
+    }
+  }
   if (ks.sk_runs) {
     switch (ks.tile_variant) {
       case 1:

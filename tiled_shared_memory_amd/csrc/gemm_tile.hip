@@ -661,6 +661,7 @@ __device__ __forceinline__ void tile_run(const KernelArgs &p, int64_t z, int tm,
 // of the groups' valid row blocks in a grouped call (group after group), else
 // problem after problem; within a problem, the grouped tile order.
 __device__ __forceinline__ void tile_of(const KernelArgs &p, int t, int64_t &z, int &tm, int &tn) {
+  t += p.tile0;
   if (p.compact_groups) {
     int g = 0;
     for (; g < p.compact_groups - 1; ++g) {
@@ -679,6 +680,7 @@ __device__ __forceinline__ void tile_of(const KernelArgs &p, int t, int64_t &z, 
 
 // Tiles of a launch (grouped calls: the valid ones, from the counts in device memory).
 __device__ __forceinline__ int launch_tiles(const KernelArgs &p) {
+  if (p.tile_count) return p.tile_count;
   if (!p.compact_groups) return p.tiles_m * p.tiles_n * p.flat_batch;
   int V = 0;
   for (int g = 0; g < p.compact_groups; ++g) V += work_rows(p, g);
@@ -732,7 +734,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
       int64_t z;
       int tm, tn;
       tile_of(q, t, z, tm, tn);
-      float *part = q.sk_ws + (2 * (int64_t)w + s) * (BM * BN);
+      float *part = q.sk_ws + (q.sk_aligned ? (int64_t)w : 2 * (int64_t)w + s) * (BM * BN);
       tile_run<BF16, OUT16, MI, ACOL, BROW, KB, true>(q, z, tm, tn, 128 * (int64_t)k0, 128 * (int64_t)(k1 - k0), part);
       // the next segment's copies overwrite LDS stages whose last fragment
       // reads other waves may not have made yet
@@ -772,7 +774,9 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
       z = pid / T;
       tile_order(pid - (int)z * T, p.tiles_m, p.tiles_n, group_rows(p.tiles_m), tm, tn);
     } else {
-      tile_order(xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n), p.tiles_m, p.tiles_n, group_rows(p.tiles_m), tm, tn);
+      // (a hybrid launch covers the first tile_count tiles of the order)
+      tile_order(xcd_remap(blockIdx.x, p.tile_count ? p.tile_count : p.tiles_m * p.tiles_n), p.tiles_m, p.tiles_n,
+                 group_rows(p.tiles_m), tm, tn);
       z = (int64_t)p.z0 + blockIdx.y;
     }
 
@@ -801,7 +805,9 @@ __global__ __launch_bounds__(256) void sk_reduce_kernel(KernelArgs p, int P) {
   f32x4 acc[4] = {};
   for (int64_t w = w0; w <= w1; ++w) {
     // run w's segment in its first tile is in slot 2w, in its second in 2w + 1
-    const float *src = p.sk_ws + (2 * w + (runs.start(w) < u0 ? 1 : 0)) * (BM * BN) + row0 * BN + col;
+    // (aligned runs, one segment each: slot w)
+    const int64_t slot = p.sk_aligned ? w : 2 * w + (runs.start(w) < u0 ? 1 : 0);
+    const float *src = p.sk_ws + slot * (BM * BN) + row0 * BN + col;
     f32x4 v[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const f32x4 *>(src + q * BN);
@@ -824,7 +830,8 @@ __global__ __launch_bounds__(256) void sk_reduce_kernel(KernelArgs p, int P) {
 
 template <bool BF16, bool OUT16, int MI, bool ACOL, bool BROW, int KB, bool SK>
 hipError_t launch_t(const KernelArgs &base, int64_t batch, int P, hipStream_t stream) {
-  const int64_t tiles = (int64_t)base.tiles_m * base.tiles_n;
+  // (a data-parallel launch over the first tile_count tiles of one problem covers just those)
+  const int64_t tiles = !SK && base.tile_count ? base.tile_count : (int64_t)base.tiles_m * base.tiles_n;
   if constexpr (SK) {
     // P runs over every tile of every problem (valid tiles of a grouped
     // call), then the fix-up over the same tiles
@@ -926,8 +933,7 @@ bool tile_supports(const Problem &p, bool a_col, bool b_row) {
   return true;
 }
 
-hipError_t launch_tile(const Problem &p, int variant, hipStream_t stream) {
-  const KernelArgs a = tile_args(p);
+hipError_t launch_tile_args(const Problem &p, const KernelArgs &a, int variant, hipStream_t stream) {
   switch (variant) {
     case 0:
       return launch_mi<32, false, false, 1>(p, a, stream);
@@ -950,6 +956,10 @@ hipError_t launch_tile(const Problem &p, int variant, hipStream_t stream) {
   }
 }
 
+hipError_t launch_tile(const Problem &p, int variant, hipStream_t stream) {
+  return launch_tile_args(p, tile_args(p), variant, stream);
+}
+
 hipError_t launch_tile_sk(const Problem &p, int variant, float *ws, int P, hipStream_t stream) {
   KernelArgs a = tile_args(p);
   a.sk_ws = ws;
@@ -962,6 +972,40 @@ hipError_t launch_tile_sk(const Problem &p, int variant, float *ws, int P, hipSt
       return launch_mi<16, true, false, 1, true>(p, a, stream, P);
     case 1:
       return launch_mi<16, false, false, 1, true>(p, a, stream, P);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_tile_hybrid(const Problem &p, int variant, int sk_variant, int dp_tiles, int splits, float *ws,
+                              hipStream_t stream) {
+  const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  if (p.batch != 1 || p.rows || dp_tiles <= 0 || dp_tiles >= tiles || splits < 1) return hipErrorInvalidValue;
+  // whole rounds: the first dp_tiles tiles of the order, one workgroup each
+  {
+    KernelArgs a = tile_args(p);
+    a.tile_count = dp_tiles;
+    const hipError_t e = launch_tile_args(p, a, variant, stream);
+    if (e != hipSuccess) return e;
+  }
+  // the rest: splits aligned runs per tile (stream-K runs of exactly one chunk)
+  Problem q = p;
+  KernelArgs a = tile_args(q);
+  a.sk_ws = ws;
+  a.tile0 = dp_tiles;
+  a.tile_count = (int32_t)(tiles - dp_tiles);
+  a.sk_aligned = 1;
+  if ((p.K / 128) % splits) return hipErrorInvalidValue;  // every run one whole chunk of one tile
+  const int P = (int)(tiles - dp_tiles) * splits;
+  switch (sk_variant) {
+    case 1:
+      return launch_mi<16, false, false, 1, true>(q, a, stream, P);
+    case 2:
+      return launch_mi<16, false, true, 1, true>(q, a, stream, P);
+    case 5:
+      return launch_mi<16, true, true, 1, true>(q, a, stream, P);
+    case 6:
+      return launch_mi<16, true, false, 1, true>(q, a, stream, P);
     default:
       return hipErrorInvalidValue;
   }
