@@ -189,7 +189,7 @@ hipError_t launch_tile(const Problem &p, int variant, hipStream_t stream);
 hipError_t launch_tile_sk(const Problem &p, int variant, float *ws, int P, hipStream_t stream);
 // One problem of more than one round of tiles: the first `dp_tiles` tiles (whole
 // rounds) on the data-parallel kernel `variant`, and the remaining ones split
-// `splits` ways in K as aligned stream-K runs on `sk_variant` (one run per chunk,
+// `splits` ways in K as aligned stream-K runs on `sk_variant` (2, 5, 6 or 8; one run per chunk,
 // one 256 x 256 float32 partial slot per run: (tiles - dp_tiles) * splits * 256 KiB
 // of workspace), then their fix-up.
 hipError_t launch_tile_hybrid(const Problem &p, int variant, int sk_variant, int dp_tiles, int splits, float *ws,

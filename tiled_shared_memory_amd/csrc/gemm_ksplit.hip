@@ -172,7 +172,7 @@ KSplit hybrid_plan(const Problem &p, int cus, int dp_variant) {
   if (!ks.splits || p.rows) return KSplit{};
   if (!tile_supports(p, p.a_col, !p.b_col)) return KSplit{};
   ks.dp_variant = dp_variant;
-  ks.tile_variant = p.a_col ? (p.b_col ? 6 : 5) : (p.b_col ? 1 : 2);  // the remainder on the 32-deep kernels
+  ks.tile_variant = dp_variant;  // the leftover tiles' runs on the same kernel (one segment each)
   return ks;
 }
 

@@ -708,9 +708,27 @@ struct SkRuns {
   }
 };
 
-template <bool BF16, bool OUT16, int MI, bool ACOL, bool BROW, int KB, bool SK>
+// SK: 0 data-parallel; 1 stream-K, runs of up to two segments; 2 stream-K runs
+// that are one whole chunk of one tile (the hybrid's leftover tiles).
+template <bool BF16, bool OUT16, int MI, bool ACOL, bool BROW, int KB, int SK>
 __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
-  if constexpr (SK) {
+  if constexpr (SK == 2) {
+    // Aligned run w: exactly one chunk of one tile (the host makes the chunk
+    // count divide the tile's units), its partial in slot w.
+    const int P = gridDim.x;
+    const int w = xcd_remap(blockIdx.x, P);
+    const SkRuns runs(launch_tiles(p), p.K / 128, P);
+    const int U = (int)runs.U;
+    const int b = (int)runs.start(w), e = (int)runs.start(w + 1);
+    const int t = b / U;
+    const int k0 = b - t * U;
+    int64_t z;
+    int tm, tn;
+    tile_of(p, t, z, tm, tn);
+    tile_run<BF16, OUT16, MI, ACOL, BROW, KB, true>(p, z, tm, tn, 128 * (int64_t)k0, 128 * (int64_t)(e - b),
+                                                    p.sk_ws + (int64_t)w * (BM * BN));
+    return;
+  } else if constexpr (SK == 1) {
     // Run w (the per-XCD regrouping keeps consecutive runs, and so
     // consecutive tiles, on one XCD).  The host launches at most one run per
     // tile (T <= P), so a run has E + 1 <= U units and meets at most two
@@ -734,7 +752,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
       int64_t z;
       int tm, tn;
       tile_of(q, t, z, tm, tn);
-      float *part = q.sk_ws + (q.sk_aligned ? (int64_t)w : 2 * (int64_t)w + s) * (BM * BN);
+      float *part = q.sk_ws + (2 * (int64_t)w + s) * (BM * BN);
       tile_run<BF16, OUT16, MI, ACOL, BROW, KB, true>(q, z, tm, tn, 128 * (int64_t)k0, 128 * (int64_t)(k1 - k0), part);
       // the next segment's copies overwrite LDS stages whose last fragment
       // reads other waves may not have made yet
@@ -828,11 +846,11 @@ __global__ __launch_bounds__(256) void sk_reduce_kernel(KernelArgs p, int P) {
   }
 }
 
-template <bool BF16, bool OUT16, int MI, bool ACOL, bool BROW, int KB, bool SK>
+template <bool BF16, bool OUT16, int MI, bool ACOL, bool BROW, int KB, int SK>
 hipError_t launch_t(const KernelArgs &base, int64_t batch, int P, hipStream_t stream) {
   // (a data-parallel launch over the first tile_count tiles of one problem covers just those)
   const int64_t tiles = !SK && base.tile_count ? base.tile_count : (int64_t)base.tiles_m * base.tiles_n;
-  if constexpr (SK) {
+  if constexpr (SK != 0) {
     // P runs over every tile of every problem (valid tiles of a grouped
     // call), then the fix-up over the same tiles
     KernelArgs a = base;
@@ -841,7 +859,7 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, int P, hipStream_t st
       a.compact_groups = (int32_t)batch;
     else
       a.flat_batch = (int32_t)batch;
-    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT16, MI, ACOL, BROW, KB, true>), dim3((unsigned)P), dim3(256), 0,
+    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT16, MI, ACOL, BROW, KB, SK>), dim3((unsigned)P), dim3(256), 0,
                        stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -855,7 +873,7 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, int P, hipStream_t st
     KernelArgs a = base;
     a.z0 = 0;
     a.compact_groups = (int32_t)batch;
-    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT16, MI, ACOL, BROW, KB, false>), dim3((unsigned)(tiles * batch)), dim3(256), 0,
+    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT16, MI, ACOL, BROW, KB, 0>), dim3((unsigned)(tiles * batch)), dim3(256), 0,
                        stream, a);
     return hipGetLastError();
   }
@@ -863,7 +881,7 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, int P, hipStream_t st
     KernelArgs a = base;
     a.z0 = 0;
     a.flat_batch = (int32_t)batch;
-    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT16, MI, ACOL, BROW, KB, false>), dim3((unsigned)(tiles * batch)), dim3(256), 0,
+    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT16, MI, ACOL, BROW, KB, 0>), dim3((unsigned)(tiles * batch)), dim3(256), 0,
                        stream, a);
     return hipGetLastError();
   }
@@ -871,7 +889,7 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, int P, hipStream_t st
     KernelArgs a = base;
     a.z0 = (int32_t)z0;
     const int64_t nz = batch - z0 < kMaxGridY ? batch - z0 : kMaxGridY;
-    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT16, MI, ACOL, BROW, KB, false>), dim3((unsigned)tiles, (unsigned)nz), dim3(256), 0,
+    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT16, MI, ACOL, BROW, KB, 0>), dim3((unsigned)tiles, (unsigned)nz), dim3(256), 0,
                        stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -879,7 +897,7 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, int P, hipStream_t st
   return hipSuccess;
 }
 
-template <int MI, bool ACOL, bool BROW, int KB, bool SK = false>
+template <int MI, bool ACOL, bool BROW, int KB, int SK = 0>
 hipError_t launch_mi(const Problem &p, const KernelArgs &a, hipStream_t stream, int P = 0) {
   if (p.in_bf16)
     return p.out16 ? launch_t<true, true, MI, ACOL, BROW, KB, SK>(a, p.batch, P, stream)
@@ -965,13 +983,13 @@ hipError_t launch_tile_sk(const Problem &p, int variant, float *ws, int P, hipSt
   a.sk_ws = ws;
   switch (variant) {
     case 2:
-      return launch_mi<16, false, true, 1, true>(p, a, stream, P);
+      return launch_mi<16, false, true, 1, 1>(p, a, stream, P);
     case 5:
-      return launch_mi<16, true, true, 1, true>(p, a, stream, P);
+      return launch_mi<16, true, true, 1, 1>(p, a, stream, P);
     case 6:
-      return launch_mi<16, true, false, 1, true>(p, a, stream, P);
+      return launch_mi<16, true, false, 1, 1>(p, a, stream, P);
     case 1:
-      return launch_mi<16, false, false, 1, true>(p, a, stream, P);
+      return launch_mi<16, false, false, 1, 1>(p, a, stream, P);
     default:
       return hipErrorInvalidValue;
   }
@@ -997,15 +1015,17 @@ hipError_t launch_tile_hybrid(const Problem &p, int variant, int sk_variant, int
   a.sk_aligned = 1;
   if ((p.K / 128) % splits) return hipErrorInvalidValue;  // every run one whole chunk of one tile
   const int P = (int)(tiles - dp_tiles) * splits;
+  // one segment per run: the data-parallel kernel of the layout fits (the
+  // staggered-refill one included)
   switch (sk_variant) {
-    case 1:
-      return launch_mi<16, false, false, 1, true>(q, a, stream, P);
     case 2:
-      return launch_mi<16, false, true, 1, true>(q, a, stream, P);
+      return launch_mi<16, false, true, 1, 2>(q, a, stream, P);
     case 5:
-      return launch_mi<16, true, true, 1, true>(q, a, stream, P);
+      return launch_mi<16, true, true, 1, 2>(q, a, stream, P);
     case 6:
-      return launch_mi<16, true, false, 1, true>(q, a, stream, P);
+      return launch_mi<16, true, false, 1, 2>(q, a, stream, P);
+    case 8:
+      return launch_mi<16, false, false, 3, 2>(q, a, stream, P);
     default:
       return hipErrorInvalidValue;
   }
