@@ -207,7 +207,8 @@ int gemm_strided_batched_act(int64_t M, int64_t N, int64_t K, const void *A, int
 /*
  * gemm_workspace_bytes -- bytes of workspace with which gemm_strided_batched_ws
  * splits K for a problem of this shape: batch * S * M * N * 4 for S chunks of
- * K (the largest S the operands' layouts may lead to), or 0 when the shape
+ * K (the largest S the operands' layouts may lead to), or for the hybrid
+ * r * s * 256 * 256 * 4 (see gemm_strided_batched_ws), or 0 when the shape
  * does not split (its output tiles already occupy the chip, K is below 512 or
  * not a multiple of 64, or N is not a multiple of 64 or 8).  With stream-K
  * requested (TSM_GEMM_SPLIT=streamk in the environment), also its need when
@@ -239,6 +240,12 @@ int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t batch);
  *                     kernel's split (up to 512 rows) needs row-major A, B
  *                     either way; the 256 x 256 tiles' split (above 128 rows,
  *                     one problem) takes any layout.
+ * One problem of more than 256 tiles of 256 x 256 whose last round of 256 tiles
+ * is at most half full (more than 128 rows, K a multiple of 128 from 2048 up)
+ * takes the hybrid: the whole rounds run unsplit, and each of the r leftover
+ * tiles is cut into s equal chunks of K (s r <= 256), whose float32 partial
+ * tiles go to the workspace (r s * 256 * 256 * 4 bytes, at most 64 MiB) and
+ * are added in K order before C is stored once.
  * With TSM_GEMM_SPLIT=streamk in the environment, stream-K (the work-centric
  * decomposition of Osama et al., PPoPP 2023) replaces the tile split for 32
  * to 224 tiles of 256 x 256 (one problem or a strided batch, more than 128
