@@ -1,7 +1,7 @@
 """The allocation-free entry point (static scratch) against the workspace entry point, through the C ABI.
 
-Both run the same K split with the same kernels, so the outputs must agree bit for bit; the second call of the
-pair is a smaller problem, so it reuses the scratch the first one left behind.  Each result is also checked
+Both run the same K split with the same kernels, so the outputs must agree bit for bit; every call after the first
+is a smaller problem, so it reuses the scratch the one before left behind.  Each result is also checked
 against the oracle within the stated bound.
 """
 
@@ -15,8 +15,11 @@ from workloads.inputs import BF16, F16, make_operands
 
 pytestmark = pytest.mark.gpu
 
-# (M, N, K, batch), operand format, output format, A layout, B layout; the second is smaller than the first
-CASES = [((256, 256, 8192, 1), F16, "f32", "row", "row"), ((64, 512, 2048, 2), BF16, "f16", "row", "col")]
+# (M, N, K, batch), operand format, output format, A layout, B layout; each smaller than the one before: the
+# hybrid (272 tiles, its 16 leftover tiles in 16 chunks: all 64 MiB of the scratch), the streaming kernel's split,
+# the same split on a batch
+CASES = [((4352, 4096, 2048, 1), BF16, "f16", "row", "col"), ((256, 256, 8192, 1), F16, "f32", "row", "row"),
+         ((64, 512, 2048, 2), BF16, "f16", "row", "col")]
 
 
 def test_noalloc_matches_workspace_entry_twice(orc):
