@@ -48,6 +48,7 @@ def log(msg):
 # Sources that define each kernel family's device code (with the shared headers
 # below): a counter record stays valid while these are unchanged.
 KERNEL_FILES = {"tile_": ("gemm_tile.hip",), "skinny_": ("gemm_skinny.hip",),
+                "hybrid_": ("gemm_tile.hip", "gemm_ksplit.hip"), "streamk_": ("gemm_tile.hip", "gemm_ksplit.hip"),
                 "ksplit_": ("gemm_skinny.hip", "gemm_ksplit.hip", "gemm_tile.hip"),
                 "splitk_": ("gemm_splitk.hip",), "masked_": ("gemm_masked.hip",), "rowsum_": ("rowsum.hip",)}
 SHARED_FILES = ("gemm_internal.hpp", "mfma.hpp")
@@ -129,7 +130,10 @@ def workload_args(argv):
                 out.append(next(it, ""))
     return " ".join(out)
 KERNEL_SYMBOL = {"tile_": "gemm_tile_kernel", "skinny_": "gemm_skinny_kernel", "splitk_": "gemm_splitk_kernel",
-                 "ksplit_": "gemm_skinny_kernel",  # the K-split pass; its reduction is the short second kernel
+                 # the split's first pass; its reduction is the short last kernel (for the hybrid: the
+                 # data-parallel launch over the whole rounds)
+                 "ksplit_tile_": "gemm_tile_kernel", "hybrid_": "gemm_tile_kernel", "streamk_": "gemm_tile_kernel",
+                 "ksplit_": "gemm_skinny_kernel",
                  "masked_": "gemm_masked_kernel", "rowsum_wave": "rowsum_wave_kernel",
                  "rowsum_block": "rowsum_block_kernel"}
 
@@ -159,7 +163,8 @@ def _pick(table, kernel):
     names = [n for n in table if fam + "<" in n]
     if not names:
         raise SystemExit(f"--summarize: no {fam} entry")
-    return max(names, key=lambda n: table[n][1] if isinstance(table[n], tuple) else 0)
+    # equal counts (the hybrid's two launches): the data-parallel instance (last template argument 0)
+    return max(names, key=lambda n: (table[n][1] if isinstance(table[n], tuple) else 0, ", 0>(" in n))
 
 
 def summarize(run_dir):

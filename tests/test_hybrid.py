@@ -70,3 +70,17 @@ def test_hybrid_activation_padded_and_sentinel(orc, act, slope):
     host = raw.float().cpu().numpy().reshape(-1)
     for i in range(0, M, 97):
         assert np.all(host[i * ldc + N:(i + 1) * ldc] == 100.0)
+
+
+def test_partial_round_workload_full_size(orc):
+    """The 4352 x 4096 x 8192 workload (272 tiles) the benchmark times through the workspace, every element."""
+    from workloads import PARTIAL
+
+    w = PARTIAL["partial_bf16_4352x4096x8192"]
+    A, B = w.operands()
+    say(f"[gpu] {w.name} through the workspace")
+    C = run_ws(A, B, w.M, w.N, w.K, w.in_fmt, w.out_fmt, fill=float("nan"),
+               expect="hybrid_tile_256x256x64_mi16_st+reduce", a_layout=w.a_layout, b_layout=w.b_layout)
+    Cr, S = orc.gemm_rows(A, B, w.M, w.N, w.K, w.in_fmt, a_layout=w.a_layout, b_layout=w.b_layout)
+    ratio = check(C, Cr, S, w.K, w.out_fmt, w.name)
+    say(f"[gpu] {w.name}: max err/bound = {ratio:.3e}")
