@@ -296,7 +296,7 @@ def test_launch_limits_planned_on_the_host():
 
 def test_hybrid_routing(monkeypatch):
     """A little over whole rounds of 256 x 256 tiles: whole rounds data-parallel, the last round's tiles cut into
-    s equal chunks of K (s * leftover <= 256 runs, s dividing K / 128), one float32 partial tile per run."""
+    s equal chunks of K (s * leftover <= 256 runs, s <= 8, s dividing K / 128), one float32 partial tile per run."""
     monkeypatch.delenv("TSM_GEMM_SPLIT", raising=False)
 
     def route(M, N, K, la=0, lb=1, nbytes=None):
@@ -305,7 +305,7 @@ def test_hybrid_routing(monkeypatch):
                                            3, W0, need)
 
     tile = 256 * 256 * 4
-    for M, leftover, chunks in ((4352, 16, 16), (4608, 32, 8), (5120, 64, 4), (6144, 128, 2)):
+    for M, leftover, chunks in ((4352, 16, 8), (4608, 32, 8), (5120, 64, 4), (6144, 128, 2)):
         assert tsm.gemm_workspace_bytes(M, 4096, 8192, 1) == leftover * chunks * tile
         assert route(M, 4096, 8192) == "hybrid_tile_256x256x64_mi16_st+reduce"
     # 289 tiles: 33 left over; 7 chunks do not divide K / 128 = 16, so 4
@@ -317,9 +317,9 @@ def test_hybrid_routing(monkeypatch):
     for M, N in ((4096, 4096), (7168, 4096), (5120, 5120)):
         assert tsm.gemm_workspace_bytes(M, N, 8192, 1) == 0
         assert route(M, N, 8192, nbytes=1 << 30) == "tile_256x256x64_mi16_st"
-    assert route(4352, 4096, 8192, nbytes=16 * 16 * tile - 1) == "tile_256x256x64_mi16_st"
+    assert route(4352, 4096, 8192, nbytes=16 * 8 * tile - 1) == "tile_256x256x64_mi16_st"
     # its workspace fits the allocation-free entry point's scratch
-    assert 16 * 16 * tile <= tsm.gemm_noalloc_scratch_bytes()
+    assert 256 * tile <= tsm.gemm_noalloc_scratch_bytes()
 
 
 def test_streamk_on_request_only(monkeypatch):

@@ -20,7 +20,7 @@ DP = {("row", "col"): "tile_256x256x64_mi16_st", ("row", "row"): "tile_256x256x3
       ("col", "row"): "tile_256x256x32_mi16_tn", ("col", "col"): "tile_256x256x32_mi16_tt"}
 
 # (M, N, K, A layout, B layout): 272, 288, 320 and 384 tiles (a last round of 16, 32, 64 and 128 tiles, cut into
-# 16, 8, 4 and 2 chunks), ragged M and N (289 tiles: 33 left over, 4 chunks since K / 128 = 16 is not a multiple
+# 8, 8, 4 and 2 chunks), ragged M and N (289 tiles: 33 left over, 4 chunks since K / 128 = 16 is not a multiple
 # of 7), every layout pair
 SHAPES = [(4352, 4096, 2048, "row", "col"), (4600, 4104, 2048, "row", "col"), (4608, 4096, 2048, "row", "row"),
           (5120, 4096, 2048, "col", "row"), (6144, 4096, 2048, "col", "col"), (4352, 4104, 2048, "row", "col")]
