@@ -154,3 +154,19 @@ def test_plain_ragged_m_on_tile_kernel(orc, monkeypatch, variant, b_layout):
     C = run(A, B, M, N, K, BF16, "f32", b_layout=b_layout, ldc=N + 4, fill=float("nan"), kernel=variant)
     Cr, S = orc.gemm_rows(A, B, M, N, K, BF16, b_layout=b_layout)
     check(C, Cr, S, K, "f32", f"ragged M {variant}")
+
+
+def test_moe_workload_full_size(orc):
+    """The grouped workload the benchmark times (8 groups of up to 4096 rows, 2048 x 4096 weights stored
+    K-contiguous, bf16 -> f16, the seeded routing counts), every valid element against the oracle, every row past
+    the counts untouched."""
+    from workloads import GROUPED
+
+    w = GROUPED["moe_bf16_e8_t16384_n2048_k4096"]
+    rows = [int(x) for x in w.rows()]
+    A, B = w.operands()
+    say(f"[gpu] {w.name} rows={rows}")
+    C = run_grouped(A, B, w.M, w.N, w.K, w.in_fmt, w.out_fmt, rows, a_layout=w.a_layout, b_layout=w.b_layout,
+                    kernel="tile_256x256x64_mi16_st")
+    check_grouped(orc, C, A, B, w.M, w.N, w.K, w.in_fmt, w.out_fmt, rows, a_layout=w.a_layout, b_layout=w.b_layout,
+                  what=w.name)
