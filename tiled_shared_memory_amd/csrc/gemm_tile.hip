@@ -44,6 +44,12 @@
 // Intel XPU Triton README's matmul signature, GROUP_SIZE_M), so the workgroups
 // resident on one XCD share A and B panels in that XCD's L2.
 //
+// K ranges: the tile body (tile_run) takes any K range that is a multiple of
+// 128, so the same kernels also run stream-K (equal runs of 128-deep units
+// over the tiles, float32 partial tiles, then sk_reduce_kernel's fixed-order
+// fix-up) and the hybrid (whole rounds of tiles data-parallel, the last
+// round's tiles in equal chunks of K).
+//
 // Epilogue: the operands are fed to the MFMA as (B, A), which makes the
 // accumulator layout hold 4 consecutive columns of one row per register
 // group, so each lane stores 8 bytes (f16) or 16 bytes (float32) at a time,
@@ -714,7 +720,9 @@ template <bool BF16, bool OUT16, int MI, bool ACOL, bool BROW, int KB, int SK>
 __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
   if constexpr (SK == 2) {
     // Aligned run w: exactly one chunk of one tile (the host makes the chunk
-    // count divide the tile's units), its partial in slot w.
+    // count divide the tile's units, so e - b = U / chunks and the run starts
+    // on a chunk boundary), its partial in slot w (sk_aligned tells the
+    // fix-up).
     const int P = gridDim.x;
     const int w = xcd_remap(blockIdx.x, P);
     const SkRuns runs(launch_tiles(p), p.K / 128, P);
@@ -745,15 +753,14 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
     for (int s = 0; s < 2; ++s) {
       const int u = s == 0 ? b : (b / U + 1) * U;  // the second segment starts at the next tile
       if (u >= e) break;
-      const KernelArgs &q = p;
       const int t = u / U;
       const int k0 = u - t * U;
       const int k1 = k0 + (e - u) < U ? k0 + (e - u) : U;
       int64_t z;
       int tm, tn;
-      tile_of(q, t, z, tm, tn);
-      float *part = q.sk_ws + (2 * (int64_t)w + s) * (BM * BN);
-      tile_run<BF16, OUT16, MI, ACOL, BROW, KB, true>(q, z, tm, tn, 128 * (int64_t)k0, 128 * (int64_t)(k1 - k0), part);
+      tile_of(p, t, z, tm, tn);
+      float *part = p.sk_ws + (2 * (int64_t)w + s) * (BM * BN);
+      tile_run<BF16, OUT16, MI, ACOL, BROW, KB, true>(p, z, tm, tn, 128 * (int64_t)k0, 128 * (int64_t)(k1 - k0), part);
       // the next segment's copies overwrite LDS stages whose last fragment
       // reads other waves may not have made yet
       __syncthreads();
