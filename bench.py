@@ -49,6 +49,7 @@ def log(msg):
 # below): a counter record stays valid while these are unchanged.
 KERNEL_FILES = {"tile_": ("gemm_tile.hip",), "skinny_": ("gemm_skinny.hip",),
                 "hybrid_": ("gemm_tile.hip", "gemm_ksplit.hip"), "streamk_": ("gemm_tile.hip", "gemm_ksplit.hip"),
+                "band_": ("gemm_tile.hip", "gemm_masked.hip", "gemm_skinny.hip", "gemm_splitk.hip"),
                 "ksplit_": ("gemm_skinny.hip", "gemm_ksplit.hip", "gemm_tile.hip"),
                 "splitk_": ("gemm_splitk.hip",), "masked_": ("gemm_masked.hip",), "rowsum_": ("rowsum.hip",)}
 SHARED_FILES = ("gemm_internal.hpp", "mfma.hpp")
@@ -133,6 +134,8 @@ KERNEL_SYMBOL = {"tile_": "gemm_tile_kernel", "skinny_": "gemm_skinny_kernel", "
                  # the split's first pass; its reduction is the short last kernel (for the hybrid: the
                  # data-parallel launch over the whole rounds)
                  "ksplit_tile_": "gemm_tile_kernel", "hybrid_": "gemm_tile_kernel", "streamk_": "gemm_tile_kernel",
+                 # row bands: the large-tile launch over the whole rounds, then the rest on its own kernel
+                 "band_": "gemm_tile_kernel",
                  "ksplit_": "gemm_skinny_kernel",
                  "masked_": "gemm_masked_kernel", "rowsum_wave": "rowsum_wave_kernel",
                  "rowsum_block": "rowsum_block_kernel"}

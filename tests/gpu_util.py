@@ -92,6 +92,19 @@ def run(A, B, M, N, K, in_fmt, out_fmt, *, batch=1, a_layout="row", b_layout="ro
     return (res, c) if keep else res
 
 
+_WORKLOAD_REF = {}
+
+
+def workload_reference(orc, w):
+    """(A, B, C_ref, S) of a named workload, the oracle's result computed once per test session."""
+    if w.name not in _WORKLOAD_REF:
+        A, B = w.operands()
+        Cr, S = orc.gemm_rows(A, B, w.M, w.N, w.K, w.in_fmt, batch=w.batch, a_layout=w.a_layout,
+                              b_layout=w.b_layout)
+        _WORKLOAD_REF[w.name] = (A, B, Cr, S)
+    return _WORKLOAD_REF[w.name]
+
+
 def check(C_gpu, C_ref, S, K, out_fmt, what="", act=0, slope=0.0):
     """Element-wise acceptance: |C_gpu - act(C_ref)| <= oracle.bound(...) (K*2^-24*S scaled for the
     activation, plus half an ulp of a 16-bit output); returns max err/bound."""

@@ -317,9 +317,43 @@ def test_hybrid_routing(monkeypatch):
     for M, N in ((4096, 4096), (7168, 4096), (5120, 5120)):
         assert tsm.gemm_workspace_bytes(M, N, 8192, 1) == 0
         assert route(M, N, 8192, nbytes=1 << 30) == "tile_256x256x64_mi16_st"
-    assert route(4352, 4096, 8192, nbytes=16 * 8 * tile - 1) == "tile_256x256x64_mi16_st"
+    # one byte short: the row bands, which need no workspace
+    assert route(4352, 4096, 8192, nbytes=16 * 8 * tile - 1) == "band_tile_256x256x64_mi16_st+masked_64x64x64_vec8"
     # its workspace fits the allocation-free entry point's scratch
     assert 256 * tile <= tsm.gemm_noalloc_scratch_bytes()
+
+
+def test_band_routing(monkeypatch):
+    """Plain calls a little over whole rounds of 256 x 256 tiles: the rows of the whole rounds on the large-tile
+    kernel, the rest as a problem of their own, when that problem goes to the streaming kernel, to 64 x 64 tiles or
+    to one round of 128 x 128 tiles; otherwise one kernel."""
+    monkeypatch.delenv("TSM_GEMM_KERNEL", raising=False)
+
+    def route(M, N, K, la=0, lb=1, batch=1):
+        return tsm.tsm_gemm_kernel_name(M, N, K, A0, M if la else K, la, M * K, B0, K if lb else N, lb, N * K, C0, N,
+                                        M * N, batch, 3)
+
+    st = "band_tile_256x256x64_mi16_st+"
+    assert route(4160, 4096, 8192) == st + "skinny_m64_n64_k64_t"
+    assert route(4224, 4096, 8192) == st + "skinny_m128_n64_k64_t"
+    assert route(4352, 4096, 8192) == st + "masked_64x64x64_vec8"
+    assert route(4864, 4096, 8192) == st + "masked_64x64x64_vec8"
+    assert route(5120, 4096, 8192) == st + "masked_128x128x32_vec8"  # 256 tiles of 128 x 128: one round
+    assert route(8448, 4096, 8192) == st + "masked_64x64x64_vec8"  # two whole rounds, then 256 rows
+    # 12 tiles a row: 21 rows (252 tiles) fill the round, 256 rows are left
+    assert route(5632, 3072, 8192) == st + "masked_64x64x64_vec8"
+    assert route(4352, 4096, 8192, la=0, lb=0) == "band_tile_256x256x32_mi16_nn+masked_64x64x64_vec8"
+    assert route(4352, 4096, 8192, la=1, lb=0) == "band_tile_256x256x32_mi16_tn+masked_64x64x64_vec8"
+    assert route(4352, 4096, 8192, la=1, lb=1) == "band_tile_256x256x32_mi16_tt+masked_64x64x64_vec8"
+    assert route(4224, 4096, 8192, la=0, lb=0) == "band_tile_256x256x32_mi16_nn+skinny_m128_n64_k64"
+    # more than one round of 128 x 128 tiles left, or enough for the large-tile kernel: one kernel
+    for M in (5376, 5632, 5888):
+        assert route(M, 4096, 8192) == "tile_256x256x64_mi16_st"
+    # whole rounds; a batch; a forced kernel: one kernel
+    assert route(8192, 8192, 8192) == "tile_256x256x64_mi16_st"
+    assert route(4352, 4096, 8192, batch=2) == "tile_256x256x64_mi16_st"
+    monkeypatch.setenv("TSM_GEMM_KERNEL", "tile_256x256x64_mi16_st")
+    assert route(4352, 4096, 8192) == "tile_256x256x64_mi16_st"
 
 
 def test_streamk_on_request_only(monkeypatch):

@@ -12,6 +12,8 @@
 
 #include <atomic>
 #include <mutex>
+#include <set>
+#include <string>
 
 #include "gemm_internal.hpp"
 #include "tsm_gemm.h"
@@ -93,6 +95,11 @@ struct Plan {
   Kernel kernel = Kernel::None;
   bool forced = false;                      // TSM_GEMM_KERNEL named the kernel
   int64_t a_bytes = 0, b_bytes = 0, c_bytes = 0;  // operand extents (A and B only when K > 0)
+  // Row bands (band_rows > 0): rows [0, band_rows) run on `kernel`, rows
+  // [band_rows, M) as a problem of their own, `low` on `low_kernel`.
+  int64_t band_rows = 0;
+  Problem low;
+  Kernel low_kernel = Kernel::None;
 };
 
 // Can an operand be read with 16-byte vectors along its contiguous dimension?
@@ -108,7 +115,8 @@ bool vec8_ok(const void *X, int64_t contiguous_extent, int64_t ld, int64_t strid
 // rows: null for plain (batched) products; for grouped products the device
 // array of per-problem row counts (each clamped to [0, M] by the kernels).
 // act, slope: the epilogue activation (TSM_ACT_*) and the leaky-ReLU slope.
-int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a, int64_t strideA, const void *B,
+// One kernel for the whole problem; plan() below may then cut it in row bands.
+int plan_one(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a, int64_t strideA, const void *B,
          int64_t ldb, int layout_b, int64_t strideB, void *C, int64_t ldc, int64_t strideC, int64_t batch, int dtype,
          const int32_t *rows, bool grouped, int act, float slope, Plan *out) {
   g_detail[0] = '\0';
@@ -300,62 +308,6 @@ int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout
   return TSM_SUCCESS;
 }
 
-int run(const Plan &pl, void *stream) {
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e = hipSuccess;
-  switch (pl.kernel) {
-    case Kernel::None:
-      return TSM_SUCCESS;
-    case Kernel::Masked8:
-      e = launch_masked(pl.p, 8, 128, s);
-      break;
-    case Kernel::MaskedU:
-      e = launch_masked(pl.p, 0, 128, s);
-      break;
-    case Kernel::Small8:
-      e = launch_masked(pl.p, 8, 64, s);
-      break;
-    case Kernel::SmallU:
-      e = launch_masked(pl.p, 0, 64, s);
-      break;
-    case Kernel::Tile32:
-      e = launch_tile(pl.p, 0, s);
-      break;
-    case Kernel::Tile16:
-      e = launch_tile(pl.p, 1, s);
-      break;
-    case Kernel::Tile16NN:
-      e = launch_tile(pl.p, 2, s);
-      break;
-    case Kernel::TileW:
-      e = launch_tile(pl.p, 3, s);
-      break;
-    case Kernel::TileWNN:
-      e = launch_tile(pl.p, 4, s);
-      break;
-    case Kernel::Tile16TN:
-      e = launch_tile(pl.p, 5, s);
-      break;
-    case Kernel::Tile16TT:
-      e = launch_tile(pl.p, 6, s);
-      break;
-    case Kernel::TileWTT:
-      e = launch_tile(pl.p, 7, s);
-      break;
-    case Kernel::TileST:
-      e = launch_tile(pl.p, 8, s);
-      break;
-    case Kernel::Skinny:
-      e = launch_skinny(pl.p, s);
-      break;
-    case Kernel::SplitK:
-      e = launch_splitk(pl.p, s);
-      break;
-  }
-  if (e != hipSuccess) return fail(TSM_ERROR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
-  return TSM_SUCCESS;
-}
-
 // CUs of the current device (looked up once per device).
 int device_cus() {
   static std::atomic<int> cache[64];
@@ -366,6 +318,121 @@ int device_cus() {
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
   cache[dev].store(n, std::memory_order_relaxed);
   return n;
+}
+
+bool is_tile256(Kernel k) {
+  return k == Kernel::TileST || k == Kernel::Tile16NN || k == Kernel::Tile16TN || k == Kernel::Tile16TT;
+}
+
+// Row bands for one plain product a little over whole rounds of 256 x 256
+// tiles (a round: one tile per CU).  The large-tile kernel takes about as long
+// over a last round of 16 tiles as over a full one, each workgroup's time being
+// one tile's K loop.  The rows past the whole rounds run better as a problem
+// of their own, after the whole rounds, when its kernel spreads them over every
+// CU in smaller tiles.  Measured with bf16 operands (K = 2048-8192; N = 4096
+// with 4096 rows plus 64-1792, N = 3072, 8192 and 16384): bottom rows that go
+// to the streaming kernel, to 64 x 64 tiles or to one round of 128 x 128 tiles
+// gain 4-32% (4352 x 4096 x 8192: 235 us against 308; 5120 x 4096 x 8192: 295
+// against 311); a bottom that needs a second round of 128 x 128 tiles or the
+// large-tile kernel loses 1-9%, so those keep one kernel.  The bands are
+// disjoint rows of C, each computed by its kernel alone.
+int plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a, int64_t strideA, const void *B,
+         int64_t ldb, int layout_b, int64_t strideB, void *C, int64_t ldc, int64_t strideC, int64_t batch, int dtype,
+         const int32_t *rows, bool grouped, int act, float slope, Plan *out) {
+  const int st = plan_one(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, strideB, C, ldc, strideC, batch,
+                          dtype, rows, grouped, act, slope, out);
+  if (st != TSM_SUCCESS || out->forced || !is_tile256(out->kernel) || batch != 1 || grouped) return st;
+  const Problem &p = out->p;
+  const int64_t tn = (N + TileInfo::BN - 1) / TileInfo::BN;
+  const int64_t T = ((M + TileInfo::BM - 1) / TileInfo::BM) * tn;
+  const int64_t P = device_cus();
+  if (T <= P || T % P == 0) return st;
+  // the tile rows that fill the whole rounds (up to a row's tiles short of
+  // them when N's tile count does not divide the CU count)
+  const int64_t top = T / P * P / tn * TileInfo::BM;
+  if (top <= 0 || top >= M) return st;
+  Plan low;
+  const int64_t es = p.out16 ? 2 : 4;
+  const int ls = plan_one(M - top, N, K, p.A + top * (p.a_col ? 1 : lda), lda, layout_a, 0, B, ldb, layout_b, 0,
+                          (char *)C + top * ldc * es, ldc, 0, 1, dtype, nullptr, false, act, slope, &low);
+  g_detail[0] = '\0';
+  if (ls != TSM_SUCCESS) return st;
+  const Kernel k = low.kernel;
+  bool ok = k == Kernel::Skinny || k == Kernel::SplitK || k == Kernel::Small8 || k == Kernel::SmallU;
+  if (k == Kernel::Masked8 || k == Kernel::MaskedU)
+    ok = ((M - top + MaskedInfo::BM - 1) / MaskedInfo::BM) * ((N + MaskedInfo::BN - 1) / MaskedInfo::BN) <= P;
+  if (!ok) return st;
+  out->band_rows = top;
+  out->low = low.p;
+  out->low_kernel = k;
+  return st;
+}
+
+hipError_t launch(Kernel k, const Problem &p, hipStream_t s) {
+  switch (k) {
+    case Kernel::None:
+      return hipSuccess;
+    case Kernel::Masked8:
+      return launch_masked(p, 8, 128, s);
+    case Kernel::MaskedU:
+      return launch_masked(p, 0, 128, s);
+    case Kernel::Small8:
+      return launch_masked(p, 8, 64, s);
+    case Kernel::SmallU:
+      return launch_masked(p, 0, 64, s);
+    case Kernel::Tile32:
+      return launch_tile(p, 0, s);
+    case Kernel::Tile16:
+      return launch_tile(p, 1, s);
+    case Kernel::Tile16NN:
+      return launch_tile(p, 2, s);
+    case Kernel::TileW:
+      return launch_tile(p, 3, s);
+    case Kernel::TileWNN:
+      return launch_tile(p, 4, s);
+    case Kernel::Tile16TN:
+      return launch_tile(p, 5, s);
+    case Kernel::Tile16TT:
+      return launch_tile(p, 6, s);
+    case Kernel::TileWTT:
+      return launch_tile(p, 7, s);
+    case Kernel::TileST:
+      return launch_tile(p, 8, s);
+    case Kernel::Skinny:
+      return launch_skinny(p, s);
+    case Kernel::SplitK:
+      return launch_splitk(p, s);
+  }
+  return hipSuccess;
+}
+
+int run(const Plan &pl, void *stream) {
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (pl.band_rows) {
+    Problem top = pl.p;
+    top.M = pl.band_rows;
+    e = launch(pl.kernel, top, s);
+    if (e == hipSuccess) e = launch(pl.low_kernel, pl.low, s);
+  } else {
+    e = launch(pl.kernel, pl.p, s);
+  }
+  if (e != hipSuccess) return fail(TSM_ERROR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return TSM_SUCCESS;
+}
+
+// What a plan launches: one kernel's name, or "band_<top>+<bottom>" for row
+// bands (composed names are kept until the process ends, so every returned
+// string stays valid).
+const char *plan_name(const Plan &pl) {
+  const char *top = kernel_name(pl.kernel, pl.p);
+  if (!pl.band_rows || !top) return top;
+  const char *low = kernel_name(pl.low_kernel, pl.low);
+  if (!low) return nullptr;
+  static std::mutex mu;
+  static std::set<std::string> names;
+  std::lock_guard<std::mutex> lock(mu);
+  return names.insert(std::string("band_") + top + "+" + low).first->c_str();
 }
 
 // Is stream-K requested (TSM_GEMM_SPLIT=streamk)?  Measured on MI355X it
@@ -579,7 +646,7 @@ const char *tsm_gemm_ws_kernel_name(int64_t M, int64_t N, int64_t K, const void 
     return nullptr;
   tsm::KSplit ks;
   if (tsm::ws_check(pl, workspace, workspace_bytes, &ks) != TSM_SUCCESS) return nullptr;
-  return ks.splits ? tsm::ksplit_name(ks, pl.p.b_col) : tsm::kernel_name(pl.kernel, pl.p);
+  return ks.splits ? tsm::ksplit_name(ks, pl.p.b_col) : tsm::plan_name(pl);
 }
 
 int gemm_strided_batched_noalloc(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a,
@@ -657,7 +724,7 @@ const char *tsm_gemm_kernel_name(int64_t M, int64_t N, int64_t K, const void *A,
   if (tsm::plan(M, N, K, A, lda, layout_a, strideA, B, ldb, layout_b, strideB, C, ldc, strideC, batch, dtype, nullptr,
                 false, TSM_ACT_NONE, 0.f, &pl) != TSM_SUCCESS)
     return nullptr;
-  return tsm::kernel_name(pl.kernel, pl.p);
+  return tsm::plan_name(pl);
 }
 
 const char *tsm_gemm_grouped_kernel_name(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a,
