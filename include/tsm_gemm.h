@@ -130,7 +130,15 @@ int gemm_strided_batched(int64_t M, int64_t N, int64_t K, const void *A, int64_t
 
 /* gemm_strided_batched_ex -- gemm_strided_batched with per-operand layouts
  * (as gemm_ex: the README's per-operand strides, restricted to row- or
- * column-major storage). */
+ * column-major storage).
+ * Row bands: one problem (batch 1) of more than one round of 256 x 256 tiles
+ * (a round: one tile per CU) whose last round is partly empty may run as two
+ * launches on the stream, one after the other: the rows that fill whole rounds
+ * on the 256 x 256 kernel, the remaining rows as a problem of their own on the
+ * kernel chosen for that problem.  Each element of C is computed by one of the
+ * two.  This applies to every plain entry point (gemm to
+ * gemm_strided_batched_act, and gemm_strided_batched_ws and _noalloc when they
+ * do not split). */
 int gemm_strided_batched_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layout_a,
                             int64_t strideA, const void *B, int64_t ldb, int layout_b, int64_t strideB, void *C,
                             int64_t ldc, int64_t strideC, int64_t batch, int dtype, void *stream);
@@ -245,7 +253,10 @@ int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t batch);
  * takes the hybrid: the whole rounds run unsplit, and each of the r leftover
  * tiles is cut into s equal chunks of K (s r <= 256), whose float32 partial
  * tiles go to the workspace (r s * 256 * 256 * 4 bytes, at most 64 MiB) and
- * are added in K order before C is stored once.
+ * are added in K order before C is stored once.  Where row bands (see
+ * gemm_strided_batched_ex) also apply, the hybrid is taken only for K above
+ * 4096 with more than 64 rows past the whole rounds; TSM_GEMM_SPLIT=hybrid in
+ * the environment takes it wherever it applies.
  * With TSM_GEMM_SPLIT=streamk in the environment, stream-K (the work-centric
  * decomposition of Osama et al., PPoPP 2023) replaces the tile split for 32
  * to 224 tiles of 256 x 256 (one problem or a strided batch, more than 128

@@ -319,6 +319,16 @@ def test_hybrid_routing(monkeypatch):
         assert route(M, N, 8192, nbytes=1 << 30) == "tile_256x256x64_mi16_st"
     # one byte short: the row bands, which need no workspace
     assert route(4352, 4096, 8192, nbytes=16 * 8 * tile - 1) == "band_tile_256x256x64_mi16_st+masked_64x64x64_vec8"
+    # the row bands, not the hybrid, up to K = 4096 or with at most 64 rows past the whole rounds ...
+    assert route(4352, 4096, 4096) == "band_tile_256x256x64_mi16_st+masked_64x64x64_vec8"
+    assert route(4160, 4096, 8192) == "band_tile_256x256x64_mi16_st+skinny_m64_n64_k64_t"
+    assert route(4352, 4104, 2048) == "band_tile_256x256x64_mi16_st+masked_64x64x64_vec8"
+    # ... where the bands would lose, the hybrid at any depth (80 tiles left: 2 chunks)
+    assert route(5376, 4096, 2048) == "hybrid_tile_256x256x64_mi16_st+reduce"
+    # ... and wherever it applies when asked for
+    monkeypatch.setenv("TSM_GEMM_SPLIT", "hybrid")
+    for M, N, K in ((4352, 4096, 4096), (4160, 4096, 8192), (4352, 4104, 2048)):
+        assert route(M, N, K) == "hybrid_tile_256x256x64_mi16_st+reduce"
     # its workspace fits the allocation-free entry point's scratch
     assert 256 * tile <= tsm.gemm_noalloc_scratch_bytes()
 

@@ -16,14 +16,16 @@ from workloads.inputs import BF16, F16, make_operands
 pytestmark = pytest.mark.gpu
 
 # (M, N, K, batch), operand format, output format, A layout, B layout; each smaller than the one before: the
-# hybrid (272 tiles, its 16 leftover tiles in 16 chunks: all 64 MiB of the scratch), the streaming kernel's split,
-# the same split on a batch
+# hybrid (272 tiles, its 16 leftover tiles in 8 chunks: 32 MiB of the scratch; asked for, since at this depth the
+# plain call's row bands are the default), the streaming kernel's split, the same split on a batch
 CASES = [((4352, 4096, 2048, 1), BF16, "f16", "row", "col"), ((256, 256, 8192, 1), F16, "f32", "row", "row"),
          ((64, 512, 2048, 2), BF16, "f16", "row", "col")]
 
 
-def test_noalloc_matches_workspace_entry_twice(orc):
+def test_noalloc_matches_workspace_entry_twice(orc, monkeypatch):
     import torch
+
+    monkeypatch.setenv("TSM_GEMM_SPLIT", "hybrid")
 
     for (M, N, K, batch), fin, fout, la, lb in CASES:
         A, B = make_operands(M + N + K + batch, batch, M, N, K, fin, ("uniform", -1.0, 1.0), la, lb)

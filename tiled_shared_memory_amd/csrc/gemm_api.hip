@@ -447,7 +447,8 @@ bool streamk_requested() {
 
 // The K split a planned problem takes given enough workspace (none: splits == 0).
 // TSM_GEMM_SPLIT=none keeps the kernel that needs no workspace, =streamk
-// takes stream-K wherever the problem allows it (tests and tuning).
+// takes stream-K wherever the problem allows it, =hybrid the hybrid over row
+// bands (tests and tuning).
 KSplit split_of(const Plan &pl) {
   if (pl.kernel == Kernel::None || pl.forced) return KSplit{};
   KSplit k = ksplit_plan(pl.p);
@@ -457,6 +458,14 @@ KSplit split_of(const Plan &pl) {
   if (streamk_requested()) return sk_plan(pl.p, device_cus());
   k = tsplit_plan(pl.p);
   if (k.splits) return k;
+  // Row bands (no workspace) beat the hybrid up to K = 4096, and while at most
+  // 64 rows lie past the whole rounds (4096 columns, bf16: 4352 x 4096 x 2048
+  // 69 us against 78; x 4096: 121 against 124; 4160 x 4096 x 8192: 208 against
+  // 218).  From K = 6144 the hybrid wins for more rows (4352 x 4096 x 8192: 219
+  // against 230; 5120 x 4096 x 6144: 192 against 217).  TSM_GEMM_SPLIT=hybrid
+  // takes the hybrid wherever it applies (tests and tuning).
+  const bool want_hybrid = force && strcmp(force, "hybrid") == 0;
+  if (pl.band_rows && !want_hybrid && (pl.p.K <= 4096 || pl.p.M - pl.band_rows <= 64)) return KSplit{};
   // a little over whole rounds of 256 x 256 tiles: the hybrid, on the large-tile
   // kernel the plan chose for the whole rounds
   const int dp_variant = pl.kernel == Kernel::TileST     ? 8
