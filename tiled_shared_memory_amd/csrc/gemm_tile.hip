@@ -438,15 +438,56 @@ __device__ __forceinline__ void slab_st(CtxW &c, int j, Frags<16> (&fr)[2], Acc<
   substep_st<BF16, J % 3, J % 2, 1>(c, j, fr, acc);
 }
 
+// ---- Staged 16-bit epilogue.  Each wave converts its 128 x 128 quadrant into
+// LDS (128 rows of 256 bytes, free once every wave is past its last fragment
+// read), then stores it back 4 rows x 256 bytes per instruction: 16 B per lane,
+// whole 128-byte lines.  Stores straight from the 16 x 16 accumulator layout
+// touch 16 rows of C per instruction, 32 bytes each; on this chip such stores
+// drain at about 15 GB/s per CU whatever the load on the memory system, while
+// 4-row stores drain at the chip's write bandwidth.
+//
+// The 16-byte chunk c of quadrant row r sits at chunk c ^ (r % 16): the 8-byte
+// writes of lanes 0..31 (16 rows, 2 column groups) then fall in 64 distinct
+// 8-byte bank slots, and each 256-byte row is read back whole by 16 lanes.
+
+// Wave w's staging area: a 64-deep ring's 32 KiB stage (w_a0, w_a1, w_b0 and
+// w_b1 exist in both such rings), or for the 32-deep ring two 16 KiB stages,
+// A stage w for quadrant rows 0..63 and B stage w for rows 64..127.
+template <int KB>
+__device__ __forceinline__ char *stage_lo(int wave) {
+  if constexpr (KB == 1) return wave == 0 ? g_a0 : wave == 1 ? g_a1 : wave == 2 ? g_a2 : g_a3;
+  return wave == 0 ? w_a0 : wave == 1 ? w_a1 : wave == 2 ? w_b0 : w_b1;
+}
+template <int KB>
+__device__ __forceinline__ char *stage_hi(int wave) {
+  if constexpr (KB == 1) return (wave == 0 ? g_b0 : wave == 1 ? g_b1 : wave == 2 ? g_b2 : g_b3) - 64 * 256;
+  return stage_lo<KB>(wave);
+}
+
+// Two values of C as a 32-bit pair of f16 (FMT = 0) or bf16 (FMT = 1), each
+// rounded to nearest even by the hardware's packed conversion.
+template <int FMT>
+__device__ __forceinline__ uint32_t pack16(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  if constexpr (FMT == 0) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, h2));
+  } else {
+    typedef __bf16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, h2));
+  }
+}
+
 // One tile's product over k0 .. k0+kd (a multiple of 128): the whole K for
 // a data-parallel tile, one stream-K segment otherwise.  PART = false: the
 // sums go through the epilogue into C; PART = true: raw into the 256 x 256
 // float32 partial at `part`.
-template <bool BF16, bool OUT16, int MI, bool ACOL, bool BROW, int KB, bool PART>
+template <bool BF16, int OUT, int MI, bool ACOL, bool BROW, int KB, bool PART>
 __device__ __forceinline__ void tile_run(const KernelArgs &p, int64_t z, int tm, int tn, int64_t k0, int64_t kd,
                                          float *part) {
   static_assert(KB == 1 || MI == 16, "64-deep slabs use 16x16x32 operands");
   static_assert(KB != 3 || (!ACOL && !BROW), "staggered refills: K-contiguous operands");
+  constexpr bool OUT16 = OUT != 0;
   constexpr int KD = KB == 3 ? 2 : KB;  // slab depth / 32 (KB == 3: 64-deep slabs, staggered refills)
   CtxT<LOADS * KD> c;
   const int tid = threadIdx.x;
@@ -603,10 +644,40 @@ __device__ __forceinline__ void tile_run(const KernelArgs &p, int64_t z, int tm,
   }
   // C through a buffer resource that ends at the tile's last valid element:
   // rows past M (ragged or grouped problems) lie beyond it, and column groups
-  // past N (N is a multiple of 8: groups of 4 lie wholly on one side) get an
-  // offset beyond it, so every store is unconditional.  The host keeps
-  // 256 rows of C below 2^31 bytes.  One lane offset per column block, the
-  // row block added as a constant.
+  // past N (N is a multiple of 8: groups of 4 or 8 lie wholly on one side) get
+  // an offset beyond it, so every store is unconditional.  The host keeps
+  // 256 rows of C below 2^31 bytes.
+  if constexpr ((OUT == 1 || OUT == 2) && MI == 16) {
+    __syncthreads();  // every wave is past its last fragment read and copy
+    char *const lo = stage_lo<KB == 1 ? 1 : 2>(c.wave), *const hi = stage_hi<KB == 1 ? 1 : 2>(c.wave);
+    const int t = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        u32x2 v;
+        v[0] = pack16<OUT - 1>(acc.v[i][j][0], acc.v[i][j][1]);
+        v[1] = pack16<OUT - 1>(acc.v[i][j][2], acc.v[i][j][3]);
+        *reinterpret_cast<u32x2 *>((i < 4 ? lo : hi) + (16 * i + t) * 256 + ((32 * j + 8 * g) ^ (16 * t))) = v;
+      }
+    // a wave reads back only what it wrote, and its LDS operations complete in order
+    const int64_t ldc = p.ldc;
+    const int64_t vr = M - m0 < BM ? M - m0 : BM;
+    const int vc = (int)(p.N - n0 < BN ? p.N - n0 : BN);
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc((char *)p.C + (z * p.sC + m0 * ldc + n0) * 2, (uint32_t)(((vr - 1) * ldc + vc) * 2));
+    const int col = wn * 128 + 8 * t;  // this lane's 8 columns in every row it stores
+    const uint32_t coff = col < vc ? (uint32_t)(col * 2) : kOutside;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const int row = 4 * k + g;  // quadrant row
+      const u32x4 d = *reinterpret_cast<const u32x4 *>((k < 16 ? lo : hi) + row * 256 + (t ^ (row & 15)) * 16);
+      __builtin_amdgcn_raw_buffer_store_b128(d, rc, coff + (uint32_t)((wm * 128 + row) * ldc * 2), 0, 0);
+    }
+    return;
+  }
+  // float32 output (and the 32x32 variant): straight from the accumulators,
+  // one lane offset per column block, the row block added as a constant.
   const Epilogue ep = epilogue_of(p);
   constexpr int ES = OUT16 ? 2 : 4;
   const int64_t ldc = p.ldc;
@@ -716,7 +787,7 @@ struct SkRuns {
 
 // SK: 0 data-parallel; 1 stream-K, runs of up to two segments; 2 stream-K runs
 // that are one whole chunk of one tile (the hybrid's leftover tiles).
-template <bool BF16, bool OUT16, int MI, bool ACOL, bool BROW, int KB, int SK>
+template <bool BF16, int OUT, int MI, bool ACOL, bool BROW, int KB, int SK>
 __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
   if constexpr (SK == 2) {
     // Aligned run w: exactly one chunk of one tile (the host makes the chunk
@@ -733,7 +804,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
     int64_t z;
     int tm, tn;
     tile_of(p, t, z, tm, tn);
-    tile_run<BF16, OUT16, MI, ACOL, BROW, KB, true>(p, z, tm, tn, 128 * (int64_t)k0, 128 * (int64_t)(e - b),
+    tile_run<BF16, OUT, MI, ACOL, BROW, KB, true>(p, z, tm, tn, 128 * (int64_t)k0, 128 * (int64_t)(e - b),
                                                     p.sk_ws + (int64_t)w * (BM * BN));
     return;
   } else if constexpr (SK == 1) {
@@ -760,7 +831,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
       int tm, tn;
       tile_of(p, t, z, tm, tn);
       float *part = p.sk_ws + (2 * (int64_t)w + s) * (BM * BN);
-      tile_run<BF16, OUT16, MI, ACOL, BROW, KB, true>(p, z, tm, tn, 128 * (int64_t)k0, 128 * (int64_t)(k1 - k0), part);
+      tile_run<BF16, OUT, MI, ACOL, BROW, KB, true>(p, z, tm, tn, 128 * (int64_t)k0, 128 * (int64_t)(k1 - k0), part);
       // the next segment's copies overwrite LDS stages whose last fragment
       // reads other waves may not have made yet
       __syncthreads();
@@ -805,7 +876,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(KernelArgs p) {
       z = (int64_t)p.z0 + blockIdx.y;
     }
 
-    tile_run<BF16, OUT16, MI, ACOL, BROW, KB, false>(p, z, tm, tn, 0, p.K, nullptr);
+    tile_run<BF16, OUT, MI, ACOL, BROW, KB, false>(p, z, tm, tn, 0, p.K, nullptr);
   }
 }
 
@@ -853,7 +924,7 @@ __global__ __launch_bounds__(256) void sk_reduce_kernel(KernelArgs p, int P) {
   }
 }
 
-template <bool BF16, bool OUT16, int MI, bool ACOL, bool BROW, int KB, int SK>
+template <bool BF16, int OUT, int MI, bool ACOL, bool BROW, int KB, int SK>
 hipError_t launch_t(const KernelArgs &base, int64_t batch, int P, hipStream_t stream) {
   // (a data-parallel launch over the first tile_count tiles of one problem covers just those)
   const int64_t tiles = !SK && base.tile_count ? base.tile_count : (int64_t)base.tiles_m * base.tiles_n;
@@ -866,11 +937,11 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, int P, hipStream_t st
       a.compact_groups = (int32_t)batch;
     else
       a.flat_batch = (int32_t)batch;
-    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT16, MI, ACOL, BROW, KB, SK>), dim3((unsigned)P), dim3(256), 0,
+    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT, MI, ACOL, BROW, KB, SK>), dim3((unsigned)P), dim3(256), 0,
                        stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((sk_reduce_kernel<OUT16>), dim3((unsigned)(tiles * batch * 16)), dim3(256), 0, stream, a, P);
+    hipLaunchKernelGGL((sk_reduce_kernel<OUT != 0>), dim3((unsigned)(tiles * batch * 16)), dim3(256), 0, stream, a, P);
     return hipGetLastError();
   }
   // 1-D grids while their work-items stay below 2^32, else a 2-D grid
@@ -880,7 +951,7 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, int P, hipStream_t st
     KernelArgs a = base;
     a.z0 = 0;
     a.compact_groups = (int32_t)batch;
-    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT16, MI, ACOL, BROW, KB, 0>), dim3((unsigned)(tiles * batch)), dim3(256), 0,
+    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT, MI, ACOL, BROW, KB, 0>), dim3((unsigned)(tiles * batch)), dim3(256), 0,
                        stream, a);
     return hipGetLastError();
   }
@@ -888,7 +959,7 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, int P, hipStream_t st
     KernelArgs a = base;
     a.z0 = 0;
     a.flat_batch = (int32_t)batch;
-    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT16, MI, ACOL, BROW, KB, 0>), dim3((unsigned)(tiles * batch)), dim3(256), 0,
+    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT, MI, ACOL, BROW, KB, 0>), dim3((unsigned)(tiles * batch)), dim3(256), 0,
                        stream, a);
     return hipGetLastError();
   }
@@ -896,7 +967,7 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, int P, hipStream_t st
     KernelArgs a = base;
     a.z0 = (int32_t)z0;
     const int64_t nz = batch - z0 < kMaxGridY ? batch - z0 : kMaxGridY;
-    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT16, MI, ACOL, BROW, KB, 0>), dim3((unsigned)tiles, (unsigned)nz), dim3(256), 0,
+    hipLaunchKernelGGL((gemm_tile_kernel<BF16, OUT, MI, ACOL, BROW, KB, 0>), dim3((unsigned)tiles, (unsigned)nz), dim3(256), 0,
                        stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -904,13 +975,25 @@ hipError_t launch_t(const KernelArgs &base, int64_t batch, int P, hipStream_t st
   return hipSuccess;
 }
 
+// Output mode of a launch (a template parameter, so that each kernel carries
+// one epilogue): 0 float32; 1 f16 and 2 bf16, no activation (the staged
+// epilogue); 3 16-bit with an activation, the format read at run time.
+// Stream-K launches write float32 partials: 0 or 3 (their fix-up stores).
+template <bool BF16, int MI, bool ACOL, bool BROW, int KB, int SK>
+hipError_t launch_out(const Problem &p, const KernelArgs &a, hipStream_t stream, int P) {
+  if (!p.out16) return launch_t<BF16, 0, MI, ACOL, BROW, KB, SK>(a, p.batch, P, stream);
+  if constexpr (SK == 0) {
+    if (p.act == 0)
+      return p.out_bf16 ? launch_t<BF16, 2, MI, ACOL, BROW, KB, SK>(a, p.batch, P, stream)
+                        : launch_t<BF16, 1, MI, ACOL, BROW, KB, SK>(a, p.batch, P, stream);
+  }
+  return launch_t<BF16, 3, MI, ACOL, BROW, KB, SK>(a, p.batch, P, stream);
+}
+
 template <int MI, bool ACOL, bool BROW, int KB, int SK = 0>
 hipError_t launch_mi(const Problem &p, const KernelArgs &a, hipStream_t stream, int P = 0) {
-  if (p.in_bf16)
-    return p.out16 ? launch_t<true, true, MI, ACOL, BROW, KB, SK>(a, p.batch, P, stream)
-                     : launch_t<true, false, MI, ACOL, BROW, KB, SK>(a, p.batch, P, stream);
-  return p.out16 ? launch_t<false, true, MI, ACOL, BROW, KB, SK>(a, p.batch, P, stream)
-                   : launch_t<false, false, MI, ACOL, BROW, KB, SK>(a, p.batch, P, stream);
+  return p.in_bf16 ? launch_out<true, MI, ACOL, BROW, KB, SK>(p, a, stream, P)
+                   : launch_out<false, MI, ACOL, BROW, KB, SK>(p, a, stream, P);
 }
 
 KernelArgs tile_args(const Problem &p) {
