@@ -441,14 +441,17 @@ __device__ __forceinline__ void slab_st(CtxW &c, int j, Frags<16> (&fr)[2], Acc<
 // ---- Staged 16-bit epilogue.  Each wave converts its 128 x 128 quadrant into
 // LDS (128 rows of 256 bytes, free once every wave is past its last fragment
 // read), then stores it back 4 rows x 256 bytes per instruction: 16 B per lane,
-// whole 128-byte lines.  Stores straight from the 16 x 16 accumulator layout
-// touch 16 rows of C per instruction, 32 bytes each; on this chip such stores
-// drain at about 15 GB/s per CU whatever the load on the memory system, while
-// 4-row stores drain at the chip's write bandwidth.
+// whole 128-byte lines, non-temporal.  A store straight from the 16 x 16
+// accumulator layout touches 16 rows of C, 32 bytes each: on the 8192^3
+// product that cost 64 L1 accesses per store instruction (TCP accesses
+// 1.53e8 per call against 1.38e8 now) and serialized address translations
+// (TCP_UTCL1_SERIALIZATION_STALL 1.0e7 cycles, now 0), and the call took 2.4%
+// longer.
 //
-// The 16-byte chunk c of quadrant row r sits at chunk c ^ (r % 16): the 8-byte
-// writes of lanes 0..31 (16 rows, 2 column groups) then fall in 64 distinct
-// 8-byte bank slots, and each 256-byte row is read back whole by 16 lanes.
+// The 16-byte chunk c of quadrant row r sits at chunk c ^ (r % 16), so that
+// the 8-byte writes of 16 rows at one column group spread over the banks and
+// each 256-byte row is read back whole by 16 lanes (the epilogue's LDS bank
+// conflicts come to 1.5% of the kernel's LDS cycles).
 
 // Wave w's staging area: a 64-deep ring's 32 KiB stage (w_a0, w_a1, w_b0 and
 // w_b1 exist in both such rings), or for the 32-deep ring two 16 KiB stages,
@@ -477,6 +480,12 @@ __device__ __forceinline__ uint32_t pack16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, h2));
   }
 }
+
+// Cache-policy bit "nt" of a buffer store (non-temporal: C is written once
+// and not read again by the kernel).  With whole-line stores it shortened the
+// 8192^3 product by 1.8% (0.724 against 0.738 ms, one box, interleaved); the
+// write-back policies sc0 / sc1 changed nothing.
+constexpr int kNonTemporal = 2;
 
 // One tile's product over k0 .. k0+kd (a multiple of 128): the whole K for
 // a data-parallel tile, one stream-K segment otherwise.  PART = false: the
@@ -672,7 +681,7 @@ __device__ __forceinline__ void tile_run(const KernelArgs &p, int64_t z, int tm,
     for (int k = 0; k < 32; ++k) {
       const int row = 4 * k + g;  // quadrant row
       const u32x4 d = *reinterpret_cast<const u32x4 *>((k < 16 ? lo : hi) + row * 256 + (t ^ (row & 15)) * 16);
-      __builtin_amdgcn_raw_buffer_store_b128(d, rc, coff + (uint32_t)((wm * 128 + row) * ldc * 2), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(d, rc, coff + (uint32_t)((wm * 128 + row) * ldc * 2), 0, kNonTemporal);
     }
     return;
   }
