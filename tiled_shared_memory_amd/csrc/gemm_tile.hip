@@ -403,7 +403,18 @@ __device__ __forceinline__ void substep_w(CtxW &c, int j, Frags<16> (&fr)[2], Ac
 // A's slab j+2.  Each half of a slab thus issues half of the copies (32
 // wave-loads per CU, where the two-stage ring issues all 64 in the first
 // half), and A's copies are requested two slabs ahead.
-template <bool BF16, int SA, int SB, int U>
+// The first MFMAs of a tile: from a zero accumulator operand (an inline
+// constant), so the accumulators need no zeroing.
+template <bool BF16>
+__device__ __forceinline__ void mma_init(const Frags<16> &f, Acc<16> &acc) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc.v[i][j] = mfma_16x16x32<BF16>(f.b[0][j], f.a[0][i], f32x4{});
+}
+// MODE 1: the tile's first sub-slice, which has no previous one to multiply;
+// MODE 2: the second, whose multiply starts the accumulators.
+template <bool BF16, int SA, int SB, int U, int MODE = 0>
 __device__ __forceinline__ void substep_st(CtxW &c, int j, Frags<16> (&fr)[2], Acc<16> &acc) {
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (U == 0) {
@@ -419,7 +430,8 @@ __device__ __forceinline__ void substep_st(CtxW &c, int j, Frags<16> (&fr)[2], A
     const int next = min(j + 2, c.nk - 1);
     issue<2 * LOADS>(c.ra, c.offA, (uint32_t)next * c.kstepA, wa3((SA + 2) % 3), c.wave);
   }
-  mma<BF16, 16>(fr[U ^ 1], acc);  // the previous sub-slice
+  if constexpr (MODE == 0) mma<BF16, 16>(fr[U ^ 1], acc);  // the previous sub-slice
+  else if constexpr (MODE == 2) mma_init<BF16>(fr[U ^ 1], acc);
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);
@@ -432,6 +444,12 @@ __device__ __forceinline__ void substep_st(CtxW &c, int j, Frags<16> (&fr)[2], A
   }
 }
 
+// Slab 0 (A and B in stage 0): the peeled first trip of the ring.
+template <bool BF16>
+__device__ __forceinline__ void slab_first(CtxW &c, Frags<16> (&fr)[2], Acc<16> &acc) {
+  substep_st<BF16, 0, 0, 0, 1>(c, 0, fr, acc);
+  substep_st<BF16, 0, 0, 1, 2>(c, 0, fr, acc);
+}
 template <bool BF16, int J>
 __device__ __forceinline__ void slab_st(CtxW &c, int j, Frags<16> (&fr)[2], Acc<16> &acc) {
   substep_st<BF16, J % 3, J % 2, 0>(c, j, fr, acc);
@@ -516,8 +534,9 @@ __device__ __forceinline__ void tile_run(const KernelArgs &p, int64_t z, int tm,
   // column n0, k = k0: column-major B starts its panel at row n0, row-major B at column n0
   const uint16_t *B = p.B + z * p.sB + (BROW ? n0 + k0 * p.ldb : n0 * p.ldb + k0);
 
-  Acc<MI> acc;
-  if constexpr (MI == 32) {
+  Acc<MI> acc;  // the staggered ring's first multiply defines it (mma_init); the others start from zeros
+  if constexpr (KB == 3) {
+  } else if constexpr (MI == 32) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -559,25 +578,25 @@ __device__ __forceinline__ void tile_run(const KernelArgs &p, int64_t z, int tm,
     issue<2 * LOADS>(c.rb, c.offB, 0, WRing<0>::b(), c.wave);
     issue<2 * LOADS>(c.ra, c.offA, min(1, c.nk - 1) * c.kstepA, w_a1, c.wave);
     Frags<16> fr[2];
-#pragma unroll
-    for (int i = 0; i < Frags<16>::NA; ++i) fr[1].a[0][i] = fr[1].b[0][i] = u32x4{0, 0, 0, 0};
+    slab_first<BF16>(c, fr, acc);
     // six slabs per trip: A's stage repeats every 3, B's every 2
-    int j = 0;
+    int j = 1;
     for (; j + 6 <= c.nk; j += 6) {
-      slab_st<BF16, 0>(c, j, fr, acc);
-      slab_st<BF16, 1>(c, j + 1, fr, acc);
-      slab_st<BF16, 2>(c, j + 2, fr, acc);
-      slab_st<BF16, 3>(c, j + 3, fr, acc);
-      slab_st<BF16, 4>(c, j + 4, fr, acc);
-      slab_st<BF16, 5>(c, j + 5, fr, acc);
+      slab_st<BF16, 1>(c, j, fr, acc);
+      slab_st<BF16, 2>(c, j + 1, fr, acc);
+      slab_st<BF16, 3>(c, j + 2, fr, acc);
+      slab_st<BF16, 4>(c, j + 3, fr, acc);
+      slab_st<BF16, 5>(c, j + 4, fr, acc);
+      slab_st<BF16, 6>(c, j + 5, fr, acc);
     }
-    // the remaining 2 or 4 slabs (nk is even)
-    if (j < c.nk) {
-      slab_st<BF16, 0>(c, j, fr, acc);
-      slab_st<BF16, 1>(c, j + 1, fr, acc);
-      if (j + 2 < c.nk) {
-        slab_st<BF16, 2>(c, j + 2, fr, acc);
-        slab_st<BF16, 3>(c, j + 3, fr, acc);
+    // the remaining 1, 3 or 5 slabs (nk is even)
+    slab_st<BF16, 1>(c, j, fr, acc);
+    if (j + 1 < c.nk) {
+      slab_st<BF16, 2>(c, j + 1, fr, acc);
+      slab_st<BF16, 3>(c, j + 2, fr, acc);
+      if (j + 3 < c.nk) {
+        slab_st<BF16, 4>(c, j + 3, fr, acc);
+        slab_st<BF16, 5>(c, j + 4, fr, acc);
       }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
