@@ -275,6 +275,31 @@ def test_tile_kernel_padded_ld_and_strides(orc, monkeypatch, variant):
     check(C, Cr, S, K, "f32", f"{variant} padded")
 
 
+@pytest.mark.parametrize("variant", ["tile_256x256x32_mi16", "tile_256x256x64_mi16", "tile_256x256x64_mi16_st"])
+@pytest.mark.parametrize("out_fmt", ["f16", "bf16"])
+def test_staged_epilogue_ragged_and_misaligned_rows(orc, monkeypatch, variant, out_fmt):
+    """16-bit output through the LDS-staged epilogue: ragged M and N (rows and 8-column groups past them are not
+    stored), ldc = N + 4, so every other row of C starts 8 bytes off a 16-byte boundary, and a batch stride that
+    shifts the second problem by 8 bytes; C prefilled with NaN, its padding and the rows past M must stay NaN."""
+    monkeypatch.setenv("TSM_GEMM_KERNEL", variant)
+    M, N, K, batch = 300, 264, 256, 2
+    ldc = N + 4
+    sC = (M + 3) * ldc  # 81204 elements: 4 mod 8
+    A, B = make_operands(103, batch, M, N, K, BF16, ("uniform", -1.0, 1.0), "row", "col")
+    say(f"[gpu] staged epilogue {variant} {out_fmt} ldc={ldc} sC={sC}")
+    C, raw = run(A, B, M, N, K, BF16, out_fmt, batch=batch, a_layout="row", b_layout="col", ldc=ldc, sC=sC,
+                 kernel=variant, fill=float("nan"), keep=True)
+    Cr, S = orc.gemm_rows(A, B, M, N, K, BF16, batch=batch, a_layout="row", b_layout="col")
+    check(C, Cr, S, K, out_fmt, f"{variant} staged epilogue")
+    host = raw.float().cpu().numpy()
+    for z in range(batch):
+        for i in range(M - 1):
+            assert np.all(np.isnan(host[z * sC + i * ldc + N:z * sC + (i + 1) * ldc])), f"padding of row {i} written"
+    # the first problem's last row padding and its three spare rows, up to the second problem
+    assert np.all(np.isnan(host[(M - 1) * ldc + N:sC])), "C past the first problem's rows was written"
+    assert np.all(np.isnan(host[sC + (M - 1) * ldc + N:])), "C past the last row was written"
+
+
 SKINNY = "skinny_"
 SKINNY_SHAPES = [(16, 256, 256, 1), (1, 512, 256, 1), (5, 256, 512, 3), (16, 768, 1024, 2), (12, 256, 256, 2)]
 
