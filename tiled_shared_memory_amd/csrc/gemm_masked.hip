@@ -16,9 +16,9 @@
 // operand along its contiguous dimension.  VEC = 8: one 16-byte load, when the
 // base, the leading dimension, the batch stride and the contiguous extent
 // allow it.  VEC = 0 (any 2-byte alignment, e.g. rows of 777 elements): one
-// dword-aligned 16-byte load and one 4-byte load cover the vector; a 16-bit
-// funnel shift (v_alignbit_b32) realigns it and a mask clears the elements
-// past the contiguous extent.  Elements outside M, N or K read as zero in both
+// dword-aligned 16-byte load and one 4-byte load cover the vector; one byte
+// permute per dword realigns it and, in K's last slice, clears the elements
+// past K.  Elements outside M, N or K read as zero in both
 // operands: "A Dumb Triton Runtime Error", Step 2 on masked loads, where the
 // padding must be the additive identity (a -inf or garbage pad would poison the
 // sum); the masked K loop of the Intel XPU Triton README ("Use Tensor
@@ -102,17 +102,12 @@ constexpr int depth() {
 }
 
 // Staging registers for one operand tile (T x BK elements): 8-element vectors,
-// and with VEC = 0 the dword after each 16-byte load, the thread's funnel
-// shift (0 or 16 bits: the stride between a thread's vectors is even, so it is
-// one for all of them) and its count of elements inside the contiguous extent
-// (the same for all of a thread's vectors too).
+// and with VEC = 0 the dword after each 16-byte load.
 template <int T, int VEC>
 struct Stage {
   static constexpr int kLoads = (T * bk<T>()) / (THREADS * 8);  // vectors per thread
   u32x4 v[kLoads];
   uint32_t tail[VEC == 0 ? kLoads : 1];
-  uint32_t shift;
-  int valid;
 };
 
 // One operand of one tile, fixed for the whole K loop.
@@ -137,8 +132,53 @@ __device__ __forceinline__ Src make_src(const uint16_t *X, int64_t ld, int64_t o
   return Src{p - delta, ld, end - at + delta, (int)(outer_total - o0 < T ? outer_total - o0 : T), delta};
 }
 
-__device__ __forceinline__ uint32_t funnel(uint32_t hi, uint32_t lo, uint32_t shift) {
-  return __builtin_amdgcn_alignbit(hi, lo, shift);
+// Thread tid's first vector of a slice: (o_t, k_t .. +7) when K is the
+// contiguous dimension, (o_t .. +7, k_t) otherwise.  Its offset from the
+// slice's corner advances by an even number of elements per vector.
+template <int T, bool KMAJ>
+__device__ __forceinline__ void first_vector(int tid, int &o_t, int &k_t) {
+  constexpr int PER_ROW = KMAJ ? bk<T>() / 8 : T / 8;  // vectors per row of the contiguous dimension
+  const int row_t = tid / PER_ROW, col_t = (tid % PER_ROW) * 8;
+  o_t = KMAJ ? row_t : col_t;
+  k_t = KMAJ ? col_t : row_t;
+}
+
+// VEC = 0: byte selectors of v_perm_b32 that turn a thread's five loaded
+// dwords into its 8 elements.  The realignment (by 0 or 2 bytes) is the
+// element offset's parity, the same for all of the thread's vectors and
+// slices.  Elements past K would multiply real sums (they are the next row's
+// first elements), so in K's last slice a K-contiguous operand's selectors
+// also zero them (selector byte 0x0c reads as zero).  Elements past M or N need
+// no clearing: they only reach rows or columns of the tile that are never
+// stored.  One v_perm_b32 per dword replaces the funnel shift, the mask and
+// the mask's selects.
+struct Realign {
+  uint32_t sel;      // every slice but K's last
+  uint32_t last[4];  // K's last slice, per dword of the vector
+};
+
+template <int T, bool KMAJ>
+__device__ __forceinline__ Realign make_realign(const Src &src, int64_t K, int tid) {
+  int o_t, k_t;
+  first_vector<T, KMAJ>(tid, o_t, k_t);
+  const uint32_t ld = (uint32_t)src.ld;
+  const uint32_t off = (KMAJ ? (uint32_t)o_t * ld + (uint32_t)k_t : (uint32_t)k_t * ld + (uint32_t)o_t) + src.delta;
+  Realign r;
+  // bytes 2..5 of {hi, lo} when the vector starts 2 bytes into its first dword
+  r.sel = (off & 1u) ? 0x05040302u : 0x03020100u;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r.last[j] = r.sel;
+  if constexpr (KMAJ) {
+    constexpr int BK = bk<T>();
+    const int64_t nk = (K + BK - 1) / BK;
+    const int valid = (int)(K - (nk - 1) * BK) - k_t;  // the vector's elements below K in the last slice
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t keep = valid >= 2 * j + 2 ? 0xffffffffu : (valid == 2 * j + 1 ? 0x0000ffffu : 0u);
+      r.last[j] = (r.sel & keep) | (0x0c0c0c0cu & ~keep);
+    }
+  }
+  return r;
 }
 
 // Fetch the OUTER x BK slice starting at (o0, k0) of an operand.
@@ -172,20 +212,19 @@ __device__ __forceinline__ void fetch(Stage<T, VEC> &st, const Src &src, int64_t
   // the 128-tile kernels out of scalar registers)
   constexpr int PER_ROW = KMAJ ? BK / 8 : T / 8;  // vectors per row of the contiguous dimension
   constexpr int STEP = THREADS / PER_ROW;         // rows advanced per vector (even)
-  const int row_t = tid / PER_ROW, col_t = (tid % PER_ROW) * 8;
-  const int o_t = KMAJ ? row_t : col_t, k_t = KMAJ ? col_t : row_t;
+  int o_t, k_t;
+  first_vector<T, KMAJ>(tid, o_t, k_t);
   const uint32_t ld = (uint32_t)src.ld;
   uint32_t stride;
   asm("v_mov_b32 %0, %1" : "=v"(stride) : "s"(STEP * ld * 2u));
   uint32_t off = (KMAJ ? (uint32_t)o_t * ld + (uint32_t)k_t : (uint32_t)k_t * ld + (uint32_t)o_t);
   off = (off + src.delta) * 2u;
+  // VEC = 0: the loads start at the dword holding the vector's first element;
+  // the fifth dword only matters when that element is its upper half
+  uint32_t unshifted = 0;
   if constexpr (VEC == 0) {
-    // the element offset's parity picks the funnel shift; the loads start at
-    // the dword below
-    st.shift = (off & 2u) * 8u;
+    unshifted = (off & 2u) ? 0u : kOutside;
     off &= ~3u;
-    // elements of the vector inside the contiguous extent (K, or M / N)
-    st.valid = KMAJ ? k_left - k_t : o_left - o_t;
   }
 #pragma unroll
   for (int r = 0; r < Stage<T, VEC>::kLoads; ++r, off += stride) {
@@ -198,42 +237,37 @@ __device__ __forceinline__ void fetch(Stage<T, VEC> &st, const Src &src, int64_t
     const uint32_t outside = ((uint32_t)(o_left - 1 - o) | (uint32_t)(k_left - 1 - k)) & kOutside;
     const uint32_t voff = off | outside;
     st.v[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, 0, 0));
-    if constexpr (VEC == 0) {
-      // the fifth dword only matters when the vector is shifted
-      const uint32_t unshifted = st.shift ? 0u : kOutside;
-      st.tail[r] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (voff + 16u) | unshifted, 0, 0);
-    }
+    if constexpr (VEC == 0)
+      st.tail[r] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (voff | unshifted) + 16u, 0, 0);
   }
 }
 
-// Vector r of a stage as 8 elements: realigned and masked for VEC = 0.
+// Vector r of a stage as 8 elements: as loaded (VEC = 8), or dword j taken
+// from dwords j and j + 1 by selector sel[j] (VEC = 0).
 template <int T, int VEC>
-__device__ __forceinline__ u32x4 vector_of(const Stage<T, VEC> &st, int r) {
+__device__ __forceinline__ u32x4 vector_of(const Stage<T, VEC> &st, int r, const uint32_t (&sel)[4]) {
   if constexpr (VEC == 8) {
     return st.v[r];
   } else {
     const u32x4 w = st.v[r];
-    const uint32_t s = st.shift;
-    u32x4 e{funnel(w[1], w[0], s), funnel(w[2], w[1], s), funnel(w[3], w[2], s), funnel(st.tail[r], w[3], s)};
-    // keep elements 0 .. valid-1
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t m = st.valid >= 2 * j + 2 ? 0xffffffffu : (st.valid == 2 * j + 1 ? 0x0000ffffu : 0u);
-      e[j] &= m;
-    }
-    return e;
+    return u32x4{__builtin_amdgcn_perm(w[1], w[0], sel[0]), __builtin_amdgcn_perm(w[2], w[1], sel[1]),
+                 __builtin_amdgcn_perm(w[3], w[2], sel[2]), __builtin_amdgcn_perm(st.tail[r], w[3], sel[3])};
   }
 }
 
 // Write the staged slice into its LDS tile: [outer][PITCH] when K is the
 // contiguous dimension, [BK][T] (swizzled) otherwise.
+// last: the slice is K's last (uniform; selects the K-clearing selectors).
 template <int T, bool KMAJ, int VEC>
-__device__ __forceinline__ void commit(const Stage<T, VEC> &st, uint16_t *s, int tid) {
+__device__ __forceinline__ void commit(const Stage<T, VEC> &st, uint16_t *s, int tid, const Realign &rl, bool last) {
   constexpr int BK = bk<T>(), PITCH = pitch<T>();
+  uint32_t sel[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sel[j] = KMAJ && last ? rl.last[j] : rl.sel;
 #pragma unroll
   for (int r = 0; r < Stage<T, VEC>::kLoads; ++r) {
     const int v = tid + r * THREADS;
-    const u32x4 e = vector_of<T, VEC>(st, r);
+    const u32x4 e = vector_of<T, VEC>(st, r, sel);
     if constexpr (KMAJ) {
       constexpr int PER_ROW = BK / 8;
       const int o = v / PER_ROW, k = (v % PER_ROW) * 8;
@@ -285,6 +319,11 @@ __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
   const uint16_t *B = p.B + z * p.sB;
   const Src src_a = make_src<T, A_KMAJ, VEC>(A, p.lda, M, p.K, m0);
   const Src src_b = make_src<T, B_KMAJ, VEC>(B, p.ldb, p.N, p.K, n0);
+  Realign rl_a{}, rl_b{};
+  if constexpr (VEC == 0) {
+    rl_a = make_realign<T, A_KMAJ>(src_a, p.K, tid);
+    rl_b = make_realign<T, B_KMAJ>(src_b, p.K, tid);
+  }
 
   f32x16 acc[NB][NB];
 #pragma unroll
@@ -295,11 +334,10 @@ __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
   // Software pipeline: registers hold the next D slices in flight while LDS
   // holds the current one (double-buffered), so a slice's loads have D slices
   // of work to land behind instead of one.  Slices past K load as zeros (no
-  // memory access); the loop stops after the last slice that holds K, and in
-  // that slice after its last 16-deep step that does (the steps past K would
-  // add only zeros).
+  // memory access).
   constexpr int D = depth<T, VEC>();
-  const int64_t nk = (p.K + BK - 1) / BK;
+  constexpr int STEPS = BK / 16;  // 16-deep MFMA steps per slice
+  const int nk = (int)((p.K + BK - 1) / BK);  // K <= 2^31 - 1 (host check)
   Stage<T, VEC> ra[D], rb[D];
   if (nk > 0) {
 #pragma unroll
@@ -307,53 +345,74 @@ __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
       fetch<T, A_KMAJ, VEC>(ra[u], src_a, p.K, u * BK, tid);
       fetch<T, B_KMAJ, VEC>(rb[u], src_b, p.K, u * BK, tid);
     }
-    commit<T, A_KMAJ, VEC>(ra[0], sA[0], tid);
-    commit<T, B_KMAJ, VEC>(rb[0], sB[0], tid);
+    commit<T, A_KMAJ, VEC>(ra[0], sA[0], tid, rl_a, nk == 1);
+    commit<T, B_KMAJ, VEC>(rb[0], sB[0], tid, rl_b, nk == 1);
     // registers then hold slices 1 .. D: slice D goes where slice 0 was
     fetch<T, A_KMAJ, VEC>(ra[0], src_a, p.K, D * BK, tid);
     fetch<T, B_KMAJ, VEC>(rb[0], src_b, p.K, D * BK, tid);
   }
   __syncthreads();
 
-  // at slice t: LDS buffer t % 2 holds slice t, registers slices t+1 .. t+D
-  for (int64_t kt = 0; kt < nk; kt += D) {
+  // The fragments of step ks of the slice in LDS buffers a_s, b_s.
+  auto step_fragments = [&](const uint16_t *a_s, const uint16_t *b_s, int ks, u32x4(&af)[NB], u32x4(&bf)[NB]) {
+    const int kk = ks * 16 + (lane >> 5) * 8;
 #pragma unroll
-    for (int u = 0; u < D; ++u) {  // slice kt + u (D is even, so its buffer is u % 2)
-      if (kt + u >= nk) break;     // uniform
-      const uint16_t *a_s = sA[u & 1];
-      const uint16_t *b_s = sB[u & 1];
-      const int64_t krest = p.K - (kt + u) * BK;  // K left from this slice on
+    for (int i = 0; i < NB; ++i) {
+      if constexpr (A_KMAJ)
+        af[i] = *reinterpret_cast<const u32x4 *>(a_s + (wm * W + i * 32 + (lane & 31)) * PITCH + kk);
+      else
+        af[i] = read_omaj<T>(a_s, wm * W + i * 32, ks, lane);
+      if constexpr (B_KMAJ)
+        bf[i] = *reinterpret_cast<const u32x4 *>(b_s + (wn * W + i * 32 + (lane & 31)) * PITCH + kk);
+      else
+        bf[i] = read_omaj<T>(b_s, wn * W + i * 32, ks, lane);
+    }
+  };
+  auto step_mma = [&](const u32x4(&af)[NB], const u32x4(&bf)[NB]) {
 #pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        if (ks > 0 && ks * 16 >= krest) break;  // uniform: the rest of the slice is padding
-        const int kk = ks * 16 + (lane >> 5) * 8;
-        u32x4 af[NB], bf[NB];
+    for (int i = 0; i < NB; ++i)
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
-          if constexpr (A_KMAJ)
-            af[i] = *reinterpret_cast<const u32x4 *>(a_s + (wm * W + i * 32 + (lane & 31)) * PITCH + kk);
-          else
-            af[i] = read_omaj<T>(a_s, wm * W + i * 32, ks, lane);
-          if constexpr (B_KMAJ)
-            bf[i] = *reinterpret_cast<const u32x4 *>(b_s + (wn * W + i * 32 + (lane & 31)) * PITCH + kk);
-          else
-            bf[i] = read_omaj<T>(b_s, wn * W + i * 32, ks, lane);
-        }
+      for (int j = 0; j < NB; ++j) acc[i][j] = mfma_32x32x16<BF16>(af[i], bf[j], acc[i][j]);
+  };
+
+  // At slice t: LDS buffer t % 2 holds slice t, registers slices t+1 .. t+D.
+  // Every slice before K's last is whole, and runs without a branch: its
+  // fragment reads, its MFMAs, the next slice's commit and the refill form one
+  // block, so the reads' latencies overlap and the commit's VALU work and
+  // loads interleave with the MFMAs.
+  for (int kt = 0; kt < nk - 1; kt += D) {
 #pragma unroll
-        for (int i = 0; i < NB; ++i)
+    for (int u = 0; u < D; ++u) {        // slice kt + u (D is even, so its buffer is u % 2)
+      if (kt + u >= nk - 1) break;       // uniform: K's last slice runs after the loop
+      u32x4 af[STEPS][NB], bf[STEPS][NB];
 #pragma unroll
-          for (int j = 0; j < NB; ++j) acc[i][j] = mfma_32x32x16<BF16>(af[i], bf[j], acc[i][j]);
-      }
+      for (int ks = 0; ks < STEPS; ++ks) step_fragments(sA[u & 1], sB[u & 1], ks, af[ks], bf[ks]);
+#pragma unroll
+      for (int ks = 0; ks < STEPS; ++ks) step_mma(af[ks], bf[ks]);
       // slice kt+u+1 (fetched D slices ago) into the other LDS buffer, whose
       // last readers passed the previous barrier; then refill its registers
       // with slice kt+u+1+D
-      const int nx = (u + 1) % D;  // a constant once the loop is unrolled
-      commit<T, A_KMAJ, VEC>(ra[nx], sA[(u + 1) & 1], tid);
-      commit<T, B_KMAJ, VEC>(rb[nx], sB[(u + 1) & 1], tid);
-      const int64_t kf = (kt + u + 1 + D) * BK;
+      const int nx = (u + 1) % D;          // a constant once the loop is unrolled
+      const bool last = kt + u + 2 == nk;  // the slice committed is K's last
+      commit<T, A_KMAJ, VEC>(ra[nx], sA[(u + 1) & 1], tid, rl_a, last);
+      commit<T, B_KMAJ, VEC>(rb[nx], sB[(u + 1) & 1], tid, rl_b, last);
+      const int64_t kf = (int64_t)(kt + u + 1 + D) * BK;
       fetch<T, A_KMAJ, VEC>(ra[nx], src_a, p.K, kf, tid);
       fetch<T, B_KMAJ, VEC>(rb[nx], src_b, p.K, kf, tid);
       __syncthreads();
+    }
+  }
+  // K's last slice, in buffer (nk - 1) % 2: it stops after its last 16-deep
+  // step that holds K (the steps past K would add only zeros).
+  if (nk > 0) {
+    const int lb = (nk - 1) & 1;
+    const int krest = (int)(p.K - (int64_t)(nk - 1) * BK);  // K in this slice
+#pragma unroll
+    for (int ks = 0; ks < STEPS; ++ks) {
+      if (ks > 0 && ks * 16 >= krest) break;  // uniform
+      u32x4 af[NB], bf[NB];
+      step_fragments(sA[lb], sB[lb], ks, af, bf);
+      step_mma(af, bf);
     }
   }
 
