@@ -165,8 +165,8 @@ def test_kernel_selection_by_layout_and_shape():
 
 
 def test_mid_size_selection():
-    """The 256 x 256 kernels from 128 tiles (96 once K >= 4096), whatever the layouts; below that the masked
-    kernels (64 x 64 tiles under 256 tiles of 128 x 128), and split-K up to 9 such tiles with K-contiguous B, 4
+    """The 256 x 256 kernels from 72 tiles, whatever the layouts; below that the masked
+    kernels (64 x 64 tiles under 180 tiles of 128 x 128), and split-K up to 9 such tiles with K-contiguous B, 4
     with row-major B."""
     B0 = 0x7E0000000000
 
@@ -177,9 +177,16 @@ def test_mid_size_selection():
     assert pick(3072, 1024, 1) == "tile_256x256x64_mi16_st"  # 144 tiles
     assert pick(3072, 1024, 0) == "tile_256x256x32_mi16_nn"
     assert pick(2560, 8192, 0) == "tile_256x256x32_mi16_nn"  # 100 tiles, deep K
-    assert pick(2560, 2048, 0) == "masked_128x128x32_vec8"  # 100 tiles, 400 of 128 x 128
+    assert pick(2560, 2048, 0) == "tile_256x256x32_mi16_nn"  # 100 tiles
+    assert pick(2304, 1024, 1) == "tile_256x256x64_mi16_st"  # 81 tiles
+    assert pick(2304, 1024, 1, m=2048) == "tile_256x256x64_mi16_st"  # 72 tiles
+    assert pick(2560, 512, 0) == "tile_256x256x32_mi16_nn"  # 100 tiles, short K
+    assert pick(2304, 512, 1, m=2048) == "tile_256x256x64_mi16_st"  # 72 tiles, short K
+    assert pick(2048, 2048, 1) == "masked_128x128x32_vec8"  # 64 tiles
     assert pick(2048, 8192, 1) == "masked_128x128x32_vec8"  # 64 tiles, 256 of 128 x 128
     assert pick(2048, 8192, 0) == "masked_128x128x32_vec8"
+    assert pick(1792, 8192, 1) == "masked_128x128x32_vec8"  # 196 of 128 x 128
+    assert pick(1664, 8192, 1) == "masked_64x64x64_vec8"  # 169 of 128 x 128
     assert pick(1536, 8192, 1) == "masked_64x64x64_vec8"  # 144 of 128 x 128
     assert pick(1024, 8192, 0) == "masked_64x64x64_vec8"
     assert pick(384, 8192, 1) == "splitk_16x16_w16_t"  # 9 of 128 x 128
@@ -347,7 +354,7 @@ def test_band_routing(monkeypatch):
     assert route(4160, 4096, 8192) == st + "skinny_m64_n64_k64_t"
     assert route(4224, 4096, 8192) == st + "skinny_m128_n64_k64_t"
     assert route(4352, 4096, 8192) == st + "masked_64x64x64_vec8"
-    assert route(4864, 4096, 8192) == st + "masked_64x64x64_vec8"
+    assert route(4864, 4096, 8192) == st + "masked_128x128x32_vec8"  # 768 rows left: 192 tiles of 128 x 128
     assert route(5120, 4096, 8192) == st + "masked_128x128x32_vec8"  # 256 tiles of 128 x 128: one round
     assert route(8448, 4096, 8192) == st + "masked_64x64x64_vec8"  # two whole rounds, then 256 rows
     # 12 tiles a row: 21 rows (252 tiles) fill the round, 256 rows are left

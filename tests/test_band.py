@@ -23,7 +23,7 @@ SHAPES = [
     (4160, 4096, 1024, "row", "col", (F16, "f32"), "skinny_m64"),           # 64 rows left
     (4224, 4096, 1024, "row", "row", (BF16, "bf16"), "skinny_m128"),        # 128 rows, row-major B
     (5120, 4096, 1024, "col", "row", (F16, "f16"), "masked_128x128x32"),    # one round of 128 x 128 tiles
-    (4600, 4104, 1024, "row", "col", (BF16, "f32"), "masked_64x64x64"),     # ragged; 15 rows of 17 tiles fill the round
+    (4600, 4104, 1024, "row", "col", (BF16, "f32"), "masked_128x128x32"),   # ragged; 15 rows of 17 tiles fill the round, 198 tiles of 128 x 128 left
     (4608, 4096, 1024, "col", "col", (BF16, "f16"), "masked_64x64x64"),
     (8448, 4096, 1024, "row", "col", (F16, "bf16"), "masked_64x64x64"),     # two whole rounds
 ]

@@ -222,10 +222,11 @@ int plan_one(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int la
   const bool b8 = K == 0 || vec8_ok(B, p.b_col ? K : N, ldb, p.sB, batch);
   out->kernel = (a8 && b8) ? Kernel::Masked8 : Kernel::MaskedU;
   const int64_t masked_tiles = tiles * batch;
-  // fewer than 256 tiles of 128 x 128 (one round of workgroups): 64 x 64
-  // tiles, four times the workgroups (1536 x 1536 x 2048: 25 us against 28;
-  // 2048 x 2048 x 2048: 35 against 31)
-  if (masked_tiles < 256) out->kernel = (a8 && b8) ? Kernel::Small8 : Kernel::SmallU;
+  // fewer than 180 tiles of 128 x 128: 64 x 64 tiles, four times the
+  // workgroups (1664 x 1664 x 2048, 169 tiles: 24.4 us against 28.3; 1792 x
+  // 1792, 196 tiles: 29.2 against 28.4 at K = 2048, 100.9 against 92.8 at
+  // K = 8192)
+  if (masked_tiles < 180) out->kernel = (a8 && b8) ? Kernel::Small8 : Kernel::SmallU;
   // few output tiles and deep K: take the parallelism from K.  The 64 x 64
   // masked tiles walk K at a fixed pace per workgroup for any grid below the
   // CU count (about 36 us for K = 8192 with K-contiguous B, 40 us with
@@ -236,15 +237,16 @@ int plan_one(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int la
   const bool splitk_ok = K > 0 && splitk_supports(p);
   if (splitk_ok && masked_tiles <= (p.b_col ? 9 : 4)) out->kernel = Kernel::SplitK;
   // The 256 x 256 kernels take about the same time per round of up to 256
-  // tiles (one workgroup per CU) whatever the tile count, about 8 TFLOP/s
-  // per tile.  Measured on squares from 256 to 4096 with K from 512 to 8192
-  // and every layout, they overtake the masked kernels from 128 tiles, or
-  // from 96 once K >= 4096 (2560 x 2560 x 8192: 146 us against 167; at
-  // 2048 x 2048 x 8192, 64 tiles, the masked kernels take 93-110 us against
-  // 138-148).
+  // tiles (one workgroup per CU) whatever the tile count.  They overtake the
+  // masked kernels from 72 tiles (2560 x 2560, 100 tiles: 13.7 us against
+  // 16.1 at K = 512; 2304 x 2304, 81 tiles: 22.1 against 24.4 at K = 1024,
+  // 124.6 against 140.4 at K = 8192; 2048 x 2304, 72 tiles: 13.5 against
+  // 15.4 for 128 x 128 tiles at K = 512, 124.9 against 132.1 at K = 8192); at
+  // 64 tiles the masked kernels stay ahead (2048 x 2048 x 8192: 92.9 against
+  // 124.7).
   const int64_t tiles256 =
       ((M + TileInfo::BM - 1) / TileInfo::BM) * ((N + TileInfo::BN - 1) / TileInfo::BN) * batch;
-  const bool tile_ok = K > 0 && (tiles256 >= 128 || (tiles256 >= 96 && K >= 4096));
+  const bool tile_ok = K > 0 && tiles256 >= 72;
   if (tile_ok && tile_supports(p, false, false)) out->kernel = Kernel::TileST;
   if (tile_ok && tile_supports(p, false, true)) out->kernel = Kernel::Tile16NN;
   if (tile_ok && tile_supports(p, true, true)) out->kernel = Kernel::Tile16TN;
