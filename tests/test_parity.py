@@ -206,6 +206,32 @@ def test_ldc_padding_untouched_and_inside_overwritten():
         torch.cuda.synchronize()
 
 
+
+@pytest.mark.parametrize("out_fmt", ["f32", "f16"])
+def test_masked_wide_ldc(out_fmt):
+    """C rows 2^23 + 8 elements apart: with float32 output, 64 rows of C span more than 2^31 bytes and the general
+    kernel's stores take 64-bit addresses; with f16 output they stay relative to the tile's corner, at offsets up
+    to 2^30.  Exact integer products; the padding between rows keeps its NaN fill."""
+    import torch
+
+    M, N, K, ldc = 5, 72, 96, (1 << 23) + 8
+    A, B = integer_operands(21, 1, M, N, K, F16)
+    say(f"[gpu] wide ldc {ldc} {out_fmt}")
+    C, raw = run(A, B, M, N, K, F16, out_fmt, ldc=ldc, fill=float("nan"), keep=True, kernel="masked_64x64x64")
+    ai = np.asarray(A[0].view(np.float16), np.float64)
+    bi = np.asarray(B[0].view(np.float16), np.float64)
+    want = ai @ bi
+    if out_fmt == "f16":
+        want = want.astype(np.float16).astype(np.float64)
+    assert np.array_equal(C[0], want)
+    host = raw.cpu().numpy()
+    for i in range(M - 1):
+        gap = host[i * ldc + N:i * ldc + N + 4096]
+        assert np.all(np.isnan(gap.astype(np.float32))), i
+        assert np.all(np.isnan(host[(i + 1) * ldc - 4096:(i + 1) * ldc].astype(np.float32))), i
+    torch.cuda.synchronize()
+
+
 TILE = "tile_256x256x"
 TILE_SHAPES = [(256, 256, 128, 1), (512, 768, 384, 1), (256, 512, 1024, 3), (768, 256, 256, 2)]
 # every large-tile variant with the B layout it reads

@@ -417,6 +417,49 @@ __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
   }
 
   void *C = OUT16 ? (void *)((uint16_t *)p.C + z * p.sC) : (void *)((float *)p.C + z * p.sC);
+  // Epilogue: buffer stores relative to the tile's corner, through a resource
+  // that ends after the tile's last element inside M x N.  A lane whose column
+  // lies past N gets an offset past the resource; rows past M lie past its end
+  // (ldc >= N), so no store needs a branch, and the offsets are one scalar
+  // multiple of ldc apart.  The activation is a uniform branch around the
+  // stores.  When T rows of C span 2^31 bytes or more (an offset could then
+  // wrap), the stores take 64-bit addresses instead, and so do the 128-tile
+  // realigning kernels with both operands contiguous along M or N, where the
+  // buffer form spilled two scalar registers.
+  constexpr int ES = OUT16 ? 2 : 4;
+  constexpr bool kBufferStores = !(T == 128 && VEC == 0 && !A_KMAJ && !B_KMAJ);
+  const int mvalid = (int)(M - m0 < T ? M - m0 : T), nvalid = (int)(p.N - n0 < T ? p.N - n0 : T);
+  const int64_t span = ((int64_t)(mvalid - 1) * p.ldc + nvalid) * ES;
+  if (kBufferStores && (int64_t)T * p.ldc * ES < 0x7fffffff) {
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<char *>(C) + (m0 * p.ldc + n0) * ES, (short)0, (int)span, 0x00020000);
+    const uint32_t row_bytes = (uint32_t)p.ldc * ES;
+    const int act = __builtin_amdgcn_readfirstlane(ep.act);
+    auto stores = [&](auto with_act) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int lcol = wn * W + j * 32 + (lane & 31);
+          const uint32_t coff = lcol < nvalid ? (uint32_t)lcol * ES : kOutside;
+          const uint32_t lane_off = (uint32_t)(wm * W + i * 32 + 4 * (lane >> 5)) * row_bytes + coff;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const uint32_t off = lane_off + (uint32_t)(8 * (r >> 2) + (r & 3)) * row_bytes;
+            const float v = decltype(with_act)::value ? ep.apply(acc[i][j][r]) : acc[i][j][r];
+            if constexpr (OUT16)
+              __builtin_amdgcn_raw_buffer_store_b16(ep.to16(v), rc, off, 0, 0);
+            else
+              __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rc, off, 0, 0);
+          }
+        }
+    };
+    if (act == 0)
+      stores(std::false_type{});
+    else
+      stores(std::true_type{});
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < NB; ++i)
 #pragma unroll
