@@ -127,29 +127,33 @@ def test_masked_variants(orc, monkeypatch, variant, shape):
 
 @pytest.mark.parametrize("variant", ["masked_128x128x32_vecu", "masked_64x64x64_vecu"])
 @pytest.mark.parametrize("offsets", [(0, 0), (1, 0), (0, 1), (1, 3)], ids=lambda o: f"off{o[0]}{o[1]}")
-def test_masked_realigned_loads(orc, monkeypatch, variant, offsets):
+@pytest.mark.parametrize("pad", [2, 1], ids=["oddld", "evenld"])
+def test_masked_realigned_loads(orc, monkeypatch, variant, offsets, pad):
     """The realigned 16-byte loads: operands whose rows start at every 2-byte alignment (odd leading dimensions,
     odd base offsets, odd batch strides), in all four layout pairs, with vectors cut by the contiguous extent
-    (K = 203, M = 137, N = 75: odd, so every row and problem is ragged against the 8-element vectors)."""
+    (K = 203, M = 137, N = 75: odd, so every row and problem is ragged against the 8-element vectors).  With even
+    leading dimensions, an operand whose base offset is even too starts every vector on a dword and loads no fifth
+    dword: offsets (0, 0), (1, 0), (0, 1) and (1, 3) give both, B, A and neither operand that form."""
     M, N, K, batch = 137, 75, 203, 2
     monkeypatch.setenv("TSM_GEMM_KERNEL", variant)
     for a_layout in ("row", "col"):
         for b_layout in ("row", "col"):
             A, B = make_operands(M + N + K + offsets[0], batch, M, N, K, BF16, ("uniform", -1.0, 1.0), a_layout,
                                  b_layout)
-            # two elements of padding on odd extents: odd leading dimensions (consecutive rows alternate between 0
-            # and 2 mod 4 bytes) and odd batch strides (odd rows times odd ld)
-            Ap = np.zeros(A.shape[:2] + (A.shape[2] + 2,), np.uint16)
+            # padding on odd extents: pad 2 gives odd leading dimensions (consecutive rows alternate between 0 and
+            # 2 mod 4 bytes) and odd batch strides (odd rows times odd ld); pad 1 gives even ones
+            Ap = np.zeros(A.shape[:2] + (A.shape[2] + pad,), np.uint16)
             Ap[:, :, :A.shape[2]] = A
-            Bp = np.zeros(B.shape[:2] + (B.shape[2] + 2,), np.uint16)
+            Bp = np.zeros(B.shape[:2] + (B.shape[2] + pad,), np.uint16)
             Bp[:, :, :B.shape[2]] = B
-            assert Ap.shape[2] % 2 and Bp.shape[2] % 2 and Ap[0].size % 2 and Bp[0].size % 2
-            say(f"[gpu] {variant} realigned offsets={offsets} A:{a_layout} B:{b_layout}")
+            odd = pad % 2 == 0
+            assert all(bool(x % 2) == odd for x in (Ap.shape[2], Bp.shape[2], Ap[0].size, Bp[0].size))
+            say(f"[gpu] {variant} realigned offsets={offsets} pad={pad} A:{a_layout} B:{b_layout}")
             C = run(Ap, Bp, M, N, K, BF16, "f32", batch=batch, a_layout=a_layout, b_layout=b_layout,
                     lda=Ap.shape[2], ldb=Bp.shape[2], a_off=offsets[0], b_off=offsets[1], fill=float("nan"),
                     kernel=variant)
             Cr, S = orc.gemm_rows(A, B, M, N, K, BF16, batch=batch, a_layout=a_layout, b_layout=b_layout)
-            check(C, Cr, S, K, "f32", f"{variant} offsets={offsets} {a_layout}/{b_layout}")
+            check(C, Cr, S, K, "f32", f"{variant} offsets={offsets} pad={pad} {a_layout}/{b_layout}")
 
 
 @pytest.mark.parametrize("shape", EDGE_SHAPES, ids=lambda s: "x".join(map(str, s)))

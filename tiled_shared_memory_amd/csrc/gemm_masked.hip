@@ -94,6 +94,16 @@ __device__ __forceinline__ u32x4 read_omaj(const uint16_t *s, int cb, int ks, in
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
+// Load modes (VEC): 8 = 16-byte loads of both operands; 0-3 = realigning
+// loads, where bit 0 (A) and bit 1 (B) mark an even operand: its leading
+// dimension and batch stride are even and its base lies on a dword, so every
+// vector starts on a dword and needs no fifth dword; one contiguous along M or
+// N then needs no byte permute either.
+template <int VEC>
+constexpr bool realigning() {
+  return VEC != 8;
+}
+
 // Slices in flight in registers (even: the LDS buffers alternate): 4 x 32 k
 // on 128-tiles, 2 x 64 k on 64-tiles (the same k distance ahead).
 template <int T, int VEC>
@@ -107,7 +117,7 @@ template <int T, int VEC>
 struct Stage {
   static constexpr int kLoads = (T * bk<T>()) / (THREADS * 8);  // vectors per thread
   u32x4 v[kLoads];
-  uint32_t tail[VEC == 0 ? kLoads : 1];
+  uint32_t tail[realigning<VEC>() ? kLoads : 1];
 };
 
 // One operand of one tile, fixed for the whole K loop.
@@ -126,7 +136,7 @@ template <int T, bool KMAJ, int VEC>
 __device__ __forceinline__ Src make_src(const uint16_t *X, int64_t ld, int64_t outer_total, int64_t K, int64_t o0) {
   const int64_t at = KMAJ ? o0 * ld : o0;
   const uint16_t *p = X + at;
-  const uint32_t delta = VEC == 0 ? (uint32_t)(((uintptr_t)p >> 1) & 1) : 0u;
+  const uint32_t delta = realigning<VEC>() ? (uint32_t)(((uintptr_t)p >> 1) & 1) : 0u;
   // the operand's storage ends after row outer_total - 1 (K contiguous) or k row K - 1
   const int64_t end = KMAJ ? (outer_total - 1) * ld + K : (K - 1) * ld + outer_total;
   return Src{p - delta, ld, end - at + delta, (int)(outer_total - o0 < T ? outer_total - o0 : T), delta};
@@ -188,7 +198,7 @@ __device__ __forceinline__ Realign make_realign(const Src &src, int64_t K, int t
 // keeps a slice's span below 2^31 bytes): elements outside the matrix get an
 // offset with bit 31 set, past the buffer resource, and load as zero without a
 // branch.
-template <int T, bool KMAJ, int VEC>
+template <int T, bool KMAJ, int VEC, bool EVEN>
 __device__ __forceinline__ void fetch(Stage<T, VEC> &st, const Src &src, int64_t K, int64_t k0, int tid) {
   constexpr int BK = bk<T>();
   const int64_t koff = KMAJ ? k0 : k0 * src.ld;
@@ -198,7 +208,7 @@ __device__ __forceinline__ void fetch(Stage<T, VEC> &st, const Src &src, int64_t
   // memory (the range check is per dword).  Every dword inside lies in a page
   // the operand uses.
   int64_t records = 0x7fffffff;
-  if constexpr (VEC == 0) {
+  if constexpr (realigning<VEC>()) {
     const int64_t bytes = ((src.rest - koff) * 2 + 3) & ~(int64_t)3;
     records = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
   }
@@ -222,7 +232,7 @@ __device__ __forceinline__ void fetch(Stage<T, VEC> &st, const Src &src, int64_t
   // VEC = 0: the loads start at the dword holding the vector's first element;
   // the fifth dword only matters when that element is its upper half
   uint32_t unshifted = 0;
-  if constexpr (VEC == 0) {
+  if constexpr (realigning<VEC>()) {
     unshifted = (off & 2u) ? 0u : kOutside;
     off &= ~3u;
   }
@@ -237,28 +247,30 @@ __device__ __forceinline__ void fetch(Stage<T, VEC> &st, const Src &src, int64_t
     const uint32_t outside = ((uint32_t)(o_left - 1 - o) | (uint32_t)(k_left - 1 - k)) & kOutside;
     const uint32_t voff = off | outside;
     st.v[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, 0, 0));
-    if constexpr (VEC == 0)
+    if constexpr (realigning<VEC>() && !EVEN)
       st.tail[r] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (voff | unshifted) + 16u, 0, 0);
   }
 }
 
-// Vector r of a stage as 8 elements: as loaded (VEC = 8), or dword j taken
-// from dwords j and j + 1 by selector sel[j] (VEC = 0).
-template <int T, int VEC>
+// Vector r of a stage as 8 elements: as loaded (16-byte loads, or an even
+// operand contiguous along M or N), or dword j taken from dwords j and j + 1 by
+// selector sel[j] (an even operand's selectors never take the fifth dword).
+template <int T, int VEC, bool KMAJ, bool EVEN>
 __device__ __forceinline__ u32x4 vector_of(const Stage<T, VEC> &st, int r, const uint32_t (&sel)[4]) {
-  if constexpr (VEC == 8) {
+  if constexpr (!realigning<VEC>() || (EVEN && !KMAJ)) {
     return st.v[r];
   } else {
     const u32x4 w = st.v[r];
+    const uint32_t fifth = EVEN ? 0u : st.tail[r];
     return u32x4{__builtin_amdgcn_perm(w[1], w[0], sel[0]), __builtin_amdgcn_perm(w[2], w[1], sel[1]),
-                 __builtin_amdgcn_perm(w[3], w[2], sel[2]), __builtin_amdgcn_perm(st.tail[r], w[3], sel[3])};
+                 __builtin_amdgcn_perm(w[3], w[2], sel[2]), __builtin_amdgcn_perm(fifth, w[3], sel[3])};
   }
 }
 
 // Write the staged slice into its LDS tile: [outer][PITCH] when K is the
 // contiguous dimension, [BK][T] (swizzled) otherwise.
 // last: the slice is K's last (uniform; selects the K-clearing selectors).
-template <int T, bool KMAJ, int VEC>
+template <int T, bool KMAJ, int VEC, bool EVEN>
 __device__ __forceinline__ void commit(const Stage<T, VEC> &st, uint16_t *s, int tid, const Realign &rl, bool last) {
   constexpr int BK = bk<T>(), PITCH = pitch<T>();
   uint32_t sel[4];
@@ -267,7 +279,7 @@ __device__ __forceinline__ void commit(const Stage<T, VEC> &st, uint16_t *s, int
 #pragma unroll
   for (int r = 0; r < Stage<T, VEC>::kLoads; ++r) {
     const int v = tid + r * THREADS;
-    const u32x4 e = vector_of<T, VEC>(st, r, sel);
+    const u32x4 e = vector_of<T, VEC, KMAJ, EVEN>(st, r, sel);
     if constexpr (KMAJ) {
       constexpr int PER_ROW = BK / 8;
       const int o = v / PER_ROW, k = (v % PER_ROW) * 8;
@@ -319,8 +331,9 @@ __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
   const uint16_t *B = p.B + z * p.sB;
   const Src src_a = make_src<T, A_KMAJ, VEC>(A, p.lda, M, p.K, m0);
   const Src src_b = make_src<T, B_KMAJ, VEC>(B, p.ldb, p.N, p.K, n0);
+  constexpr bool EA = realigning<VEC>() && (VEC & 1), EB = realigning<VEC>() && (VEC & 2);
   Realign rl_a{}, rl_b{};
-  if constexpr (VEC == 0) {
+  if constexpr (realigning<VEC>()) {
     rl_a = make_realign<T, A_KMAJ>(src_a, p.K, tid);
     rl_b = make_realign<T, B_KMAJ>(src_b, p.K, tid);
   }
@@ -342,14 +355,14 @@ __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
   if (nk > 0) {
 #pragma unroll
     for (int u = 0; u < D; ++u) {
-      fetch<T, A_KMAJ, VEC>(ra[u], src_a, p.K, u * BK, tid);
-      fetch<T, B_KMAJ, VEC>(rb[u], src_b, p.K, u * BK, tid);
+      fetch<T, A_KMAJ, VEC, EA>(ra[u], src_a, p.K, u * BK, tid);
+      fetch<T, B_KMAJ, VEC, EB>(rb[u], src_b, p.K, u * BK, tid);
     }
-    commit<T, A_KMAJ, VEC>(ra[0], sA[0], tid, rl_a, nk == 1);
-    commit<T, B_KMAJ, VEC>(rb[0], sB[0], tid, rl_b, nk == 1);
+    commit<T, A_KMAJ, VEC, EA>(ra[0], sA[0], tid, rl_a, nk == 1);
+    commit<T, B_KMAJ, VEC, EB>(rb[0], sB[0], tid, rl_b, nk == 1);
     // registers then hold slices 1 .. D: slice D goes where slice 0 was
-    fetch<T, A_KMAJ, VEC>(ra[0], src_a, p.K, D * BK, tid);
-    fetch<T, B_KMAJ, VEC>(rb[0], src_b, p.K, D * BK, tid);
+    fetch<T, A_KMAJ, VEC, EA>(ra[0], src_a, p.K, D * BK, tid);
+    fetch<T, B_KMAJ, VEC, EB>(rb[0], src_b, p.K, D * BK, tid);
   }
   __syncthreads();
 
@@ -394,11 +407,11 @@ __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
       // with slice kt+u+1+D
       const int nx = (u + 1) % D;          // a constant once the loop is unrolled
       const bool last = kt + u + 2 == nk;  // the slice committed is K's last
-      commit<T, A_KMAJ, VEC>(ra[nx], sA[(u + 1) & 1], tid, rl_a, last);
-      commit<T, B_KMAJ, VEC>(rb[nx], sB[(u + 1) & 1], tid, rl_b, last);
+      commit<T, A_KMAJ, VEC, EA>(ra[nx], sA[(u + 1) & 1], tid, rl_a, last);
+      commit<T, B_KMAJ, VEC, EB>(rb[nx], sB[(u + 1) & 1], tid, rl_b, last);
       const int64_t kf = (int64_t)(kt + u + 1 + D) * BK;
-      fetch<T, A_KMAJ, VEC>(ra[nx], src_a, p.K, kf, tid);
-      fetch<T, B_KMAJ, VEC>(rb[nx], src_b, p.K, kf, tid);
+      fetch<T, A_KMAJ, VEC, EA>(ra[nx], src_a, p.K, kf, tid);
+      fetch<T, B_KMAJ, VEC, EB>(rb[nx], src_b, p.K, kf, tid);
       __syncthreads();
     }
   }
@@ -427,7 +440,7 @@ __global__ __launch_bounds__(THREADS) void gemm_masked_kernel(KernelArgs p) {
   // realigning kernels with both operands contiguous along M or N, where the
   // buffer form spilled two scalar registers.
   constexpr int ES = OUT16 ? 2 : 4;
-  constexpr bool kBufferStores = !(T == 128 && VEC == 0 && !A_KMAJ && !B_KMAJ);
+  constexpr bool kBufferStores = !(T == 128 && realigning<VEC>() && !A_KMAJ && !B_KMAJ);
   const int mvalid = (int)(M - m0 < T ? M - m0 : T), nvalid = (int)(p.N - n0 < T ? p.N - n0 : T);
   const int64_t span = ((int64_t)(mvalid - 1) * p.ldc + nvalid) * ES;
   if (kBufferStores && (int64_t)T * p.ldc * ES < 0x7fffffff) {
@@ -534,8 +547,23 @@ hipError_t launch_masked(const Problem &p, int vec, int tile, hipStream_t stream
   a.out_bf16 = p.out_bf16;
   a.tiles_m = (int32_t)((p.M + tile - 1) / tile);
   a.tiles_n = (int32_t)((p.N + tile - 1) / tile);
-  if (tile == 64) return vec == 8 ? dispatch_types<64, 8>(p, a, stream) : dispatch_types<64, 0>(p, a, stream);
-  return vec == 8 ? dispatch_types<128, 8>(p, a, stream) : dispatch_types<128, 0>(p, a, stream);
+  // realigning loads: the even operands (see the load modes above)
+  auto even = [&](const void *X, int64_t ld, int64_t stride) {
+    return ((uintptr_t)X & 3) == 0 && ld % 2 == 0 && (p.batch == 1 || stride % 2 == 0);
+  };
+  const int mode = vec == 8 ? 8 : (even(p.A, p.lda, p.sA) ? 1 : 0) | (even(p.B, p.ldb, p.sB) ? 2 : 0);
+  switch (tile * 16 + mode) {
+    case 64 * 16 + 8: return dispatch_types<64, 8>(p, a, stream);
+    case 64 * 16 + 0: return dispatch_types<64, 0>(p, a, stream);
+    case 64 * 16 + 1: return dispatch_types<64, 1>(p, a, stream);
+    case 64 * 16 + 2: return dispatch_types<64, 2>(p, a, stream);
+    case 64 * 16 + 3: return dispatch_types<64, 3>(p, a, stream);
+    case 128 * 16 + 8: return dispatch_types<128, 8>(p, a, stream);
+    case 128 * 16 + 0: return dispatch_types<128, 0>(p, a, stream);
+    case 128 * 16 + 1: return dispatch_types<128, 1>(p, a, stream);
+    case 128 * 16 + 2: return dispatch_types<128, 2>(p, a, stream);
+    default: return dispatch_types<128, 3>(p, a, stream);
+  }
 }
 
 const char *masked_name(int vec, int tile) {
