@@ -15,10 +15,12 @@
 // Loads: each thread fetches vectors of 8 contiguous 16-bit elements of an
 // operand along its contiguous dimension.  VEC = 8: one 16-byte load, when the
 // base, the leading dimension, the batch stride and the contiguous extent
-// allow it.  VEC = 0 (any 2-byte alignment, e.g. rows of 777 elements): one
+// allow it.  Otherwise (any 2-byte alignment, e.g. rows of 777 elements) one
 // dword-aligned 16-byte load and one 4-byte load cover the vector; one byte
 // permute per dword realigns it and, in K's last slice, clears the elements
-// past K.  Elements outside M, N or K read as zero in both
+// past K; an operand whose vectors all start on a dword skips the 4-byte load
+// (and, contiguous along M or N, the permute).  Elements outside M, N or K read
+// as zero in both
 // operands: "A Dumb Triton Runtime Error", Step 2 on masked loads, where the
 // padding must be the additive identity (a -inf or garbage pad would poison the
 // sum); the masked K loop of the Intel XPU Triton README ("Use Tensor
@@ -112,7 +114,7 @@ constexpr int depth() {
 }
 
 // Staging registers for one operand tile (T x BK elements): 8-element vectors,
-// and with VEC = 0 the dword after each 16-byte load.
+// and with realigning loads the dword after each 16-byte load.
 template <int T, int VEC>
 struct Stage {
   static constexpr int kLoads = (T * bk<T>()) / (THREADS * 8);  // vectors per thread
@@ -124,7 +126,7 @@ struct Stage {
 struct Src {
   const uint16_t *base;  // element (o0, k = 0) of the tile, one element lower when that sits at 2 mod 4 bytes
   int64_t ld;
-  int64_t rest;          // elements from base to the operand's last element + 1 (VEC = 0)
+  int64_t rest;          // elements from base to the operand's last element + 1 (realigning loads)
   int o_left;            // rows (outer) of the tile inside the matrix, at most T
   uint32_t delta;        // 1 when base was moved down one element
 };
@@ -153,7 +155,7 @@ __device__ __forceinline__ void first_vector(int tid, int &o_t, int &k_t) {
   k_t = KMAJ ? col_t : row_t;
 }
 
-// VEC = 0: byte selectors of v_perm_b32 that turn a thread's five loaded
+// Realigning loads: byte selectors of v_perm_b32 that turn a thread's five loaded
 // dwords into its 8 elements.  The realignment (by 0 or 2 bytes) is the
 // element offset's parity, the same for all of the thread's vectors and
 // slices.  Elements past K would multiply real sums (they are the next row's
@@ -202,7 +204,7 @@ template <int T, bool KMAJ, int VEC, bool EVEN>
 __device__ __forceinline__ void fetch(Stage<T, VEC> &st, const Src &src, int64_t K, int64_t k0, int tid) {
   constexpr int BK = bk<T>();
   const int64_t koff = KMAJ ? k0 : k0 * src.ld;
-  // VEC = 0: the resource starts at the dword holding the slice's corner and
+  // Realigning loads: the resource starts at the dword holding the slice's corner and
   // ends at the dword holding the operand's last element, so the dwords a
   // vector's cover reads past that end load as zero instead of touching
   // memory (the range check is per dword).  Every dword inside lies in a page
@@ -229,7 +231,7 @@ __device__ __forceinline__ void fetch(Stage<T, VEC> &st, const Src &src, int64_t
   asm("v_mov_b32 %0, %1" : "=v"(stride) : "s"(STEP * ld * 2u));
   uint32_t off = (KMAJ ? (uint32_t)o_t * ld + (uint32_t)k_t : (uint32_t)k_t * ld + (uint32_t)o_t);
   off = (off + src.delta) * 2u;
-  // VEC = 0: the loads start at the dword holding the vector's first element;
+  // realigning loads start at the dword holding the vector's first element;
   // the fifth dword only matters when that element is its upper half
   uint32_t unshifted = 0;
   if constexpr (realigning<VEC>()) {
