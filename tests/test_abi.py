@@ -420,8 +420,11 @@ def test_workspace_routing(monkeypatch):
     assert tsm.tsm_gemm_ws_kernel_name(*args).startswith("ksplit_tile_")
     args[12] = 1026  # ldc
     assert not tsm.tsm_gemm_ws_kernel_name(*args).startswith("ksplit_")
-    # a K-contiguous B splits the same way
-    assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(lb=1, nbytes=1 << 30)) == "ksplit_skinny_m32_n64_k64_t+reduce"
+    # a K-contiguous B splits the same way from 9 tiles of 128 x 128; up to 4 the split inside the workgroup stays
+    assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(M=384, N=384, lb=1, nbytes=1 << 30)).startswith("ksplit_skinny_")
+    assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(lb=1, nbytes=1 << 30)) == "splitk_16x16_w16_t"
+    # over 128 rows and K below 2048: no split
+    assert not tsm.tsm_gemm_ws_kernel_name(*_ws_args(M=512, N=512, K=1024, nbytes=1 << 30)).startswith("ksplit_")
     # too little workspace, none or a forced kernel: the kernel that needs none
     assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(nbytes=8 * 256 * 256 * 4 - 4)).startswith("splitk_")
     assert tsm.tsm_gemm_ws_kernel_name(*_ws_args(ws=0, nbytes=0)).startswith("splitk_")

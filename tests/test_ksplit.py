@@ -49,12 +49,12 @@ def run_ws(A, B, M, N, K, in_fmt, out_fmt, *, batch=1, lda=None, ldb=None, ldc=N
 
 SPLIT = "ksplit_"
 SHAPES = [(256, 256, 8192, 1), (16, 4096, 4096, 1), (100, 192, 1344, 1), (48, 128, 2048, 3), (1, 64, 512, 2),
-          (200, 320, 960, 1),
+          (200, 320, 2112, 1),
           # 256-column panels
           (16, 8192, 1024, 1), (40, 8192, 2048, 1), (8, 4096, 1088, 2)]
 
 
-@pytest.mark.parametrize("shape", [(256, 256, 2048, 1), (16, 4096, 1024, 1), (100, 192, 1344, 2)],
+@pytest.mark.parametrize("shape", [(384, 384, 2048, 1), (16, 4096, 1024, 1), (100, 192, 1344, 2)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_ksplit_col_b(orc, shape):
     """The skinny kernel's split with a K-contiguous B."""
@@ -96,15 +96,15 @@ def test_largek_workload_through_the_workspace(orc):
     say(f"[gpu] {w.name} workspace: max err/bound = {ratio:.3e}")
 
 
-TILE_SPLIT = [(640, 768, 1536, "row", "col"), (600, 520, 1024, "row", "row"), (1000, 512, 2048, "row", "row"),
-              (600, 2304, 1024, "row", "col"), (520, 1024, 2048, "col", "row"), (768, 1024, 1024, "col", "col")]
+TILE_SPLIT = [(640, 768, 8192, "row", "col"), (600, 520, 8192, "row", "row"), (1000, 512, 8192, "row", "row"),
+              (600, 2304, 8192, "row", "col"), (520, 1024, 8192, "col", "row"), (1792, 1280, 8192, "col", "col")]
 
 
 @pytest.mark.parametrize("shape", TILE_SPLIT, ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("in_fmt,out_fmt", [(BF16, "f16"), (F16, "f32")])
 def test_tile_split_parity(orc, shape, in_fmt, out_fmt):
-    """The 256 x 256 kernels' split (products of 8-127 such tiles, more than 128 rows): the K chunks run as a
-    strided batch into the workspace, ragged M and N, both B layouts."""
+    """The 256 x 256 kernels' split (products of 8-128 such tiles, more than 128 rows, K >= 8192, or K >= 4096
+    from 64 tiles): the K chunks run as a strided batch into the workspace, ragged M and N, both B layouts."""
     M, N, K, a_layout, b_layout = shape
     A, B = make_operands(M + N + K, 1, M, N, K, in_fmt, ("uniform", -1.0, 1.0), a_layout, b_layout)
     say(f"[gpu] tile split {shape} {in_fmt}->{out_fmt}")

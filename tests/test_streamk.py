@@ -107,7 +107,7 @@ def test_streamk_activation_padded_and_sentinel(orc, act, slope):
 def test_streamk_off_gives_the_tile_split_or_no_split(orc, monkeypatch):
     """Without the request the same shape takes the tile split, and with TSM_GEMM_SPLIT=none the kernel that
     needs no workspace; all three pass."""
-    M, N, K = 2048, 1024, 2048
+    M, N, K = 2048, 1024, 8192
     A, B = make_operands(505, 1, M, N, K, BF16, ("uniform", -1.0, 1.0), "row", "col")
     Cr, S = orc.gemm_rows(A, B, M, N, K, BF16, b_layout="col")
     for mode, expect in ((None, "ksplit_tile_"), ("none", "masked_")):

@@ -453,6 +453,12 @@ bool streamk_requested() {
 // bands (tests and tuning).
 KSplit split_of(const Plan &pl) {
   if (pl.kernel == Kernel::None || pl.forced) return KSplit{};
+  // The in-workgroup split with a K-contiguous B over at most 4 tiles of
+  // 128 x 128 beats the workspace split at every K measured (256 x 256 x 2048:
+  // 5.4 us against 8.8; x 8192: 8.4 against 9.2); from 9 tiles the workspace
+  // split wins (384 x 384 x 4096: 12.1 against 13.8).
+  const int64_t tiles128 = ((pl.p.M + 127) / 128) * ((pl.p.N + 127) / 128) * pl.p.batch;
+  if (pl.kernel == Kernel::SplitK && pl.p.b_col && tiles128 <= 4) return KSplit{};
   KSplit k = ksplit_plan(pl.p);
   if (k.splits) return k;
   const char *force = getenv("TSM_GEMM_SPLIT");

@@ -74,6 +74,15 @@ KSplit tsplit_shape(int64_t M, int64_t N, int64_t K, int64_t batch) {
   if (batch != 1 || M <= 128 || N < 8 || K % 128 || K < 1024) return ks;
   const int64_t tiles = ((M + TileInfo::BM - 1) / TileInfo::BM) * ((N + TileInfo::BN - 1) / TileInfo::BN);
   if (tiles < 8 || tiles > 128) return ks;
+  // The plain route wins below K = 4096, and below K = 8192 under 64 tiles:
+  // pass 1's tile kernel carries a fixed cost of several microseconds per
+  // tile (its first slabs and its epilogue) that a short chunk does not
+  // amortize, and the general kernel's 64 x 64 tiles run such shapes fast
+  // (bf16, plain against split, us: 1024^2 x 4096 23.5 against 29.1, x 8192
+  // 41.6 against 37.3; 2048 x 1024 x 4096 30.8 against 37.8; 1536^2 x 4096
+  // 40.1 against 37.2; 2048^2 x 2048 27.3 against 37.1, x 4096 49.9 against
+  // 46.4)
+  if (K < 4096 || (tiles < 64 && K < 8192)) return ks;
   // about one workgroup per CU, chunks of 512 or more that divide K into
   // equal multiples of 128 (the chunks run as one strided batch).  At 128
   // tiles two chunks fill the chip (4096 x 2048 x 8192: 111 us against 135 on

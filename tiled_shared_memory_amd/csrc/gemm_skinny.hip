@@ -492,6 +492,10 @@ KSplit ksplit_for(int64_t M, int64_t N, int64_t K, int64_t batch, bool wide, int
 
 KSplit ksplit_shape(int64_t M, int64_t N, int64_t K, int64_t batch, bool wide) {
   if (M < 1 || N < 64 || N % 64 || K % BK || K < 512 || batch < 1) return KSplit{};
+  // over 128 rows the general kernel's 64 x 64 tiles run short K faster than
+  // the split's two launches (512 x 512 x 1024: 7.3 us against 9.7; 256 x 256
+  // x 1024: 7.2 against 8.8; at K = 2048 the split wins, 10.0 against 11.5)
+  if (M > 128 && K < 2048) return KSplit{};
   const int mb = M <= 16 ? 1 : M <= 32 ? 2 : 4;
   KSplit ks = ksplit_for(M, N, K, batch, wide, mb);
   // 64-row blocks whose chunks would not fill two rounds of the 64-column
