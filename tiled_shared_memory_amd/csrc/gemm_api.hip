@@ -457,7 +457,8 @@ KSplit split_of(const Plan &pl) {
   // 128 x 128 beats the workspace split at every K measured (256 x 256 x 2048:
   // 5.4 us against 8.8; x 8192: 8.4 against 9.2); from 9 tiles the workspace
   // split wins (384 x 384 x 4096: 12.1 against 13.8).
-  const int64_t tiles128 = ((pl.p.M + 127) / 128) * ((pl.p.N + 127) / 128) * pl.p.batch;
+  const int64_t tiles128 =
+      ((pl.p.M + MaskedInfo::BM - 1) / MaskedInfo::BM) * ((pl.p.N + MaskedInfo::BN - 1) / MaskedInfo::BN) * pl.p.batch;
   if (pl.kernel == Kernel::SplitK && pl.p.b_col && tiles128 <= 4) return KSplit{};
   KSplit k = ksplit_plan(pl.p);
   if (k.splits) return k;
